@@ -1,0 +1,339 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something outside its own code: hand-worked
+values, a textbook special case computed with a library matmul, brute force
+over subsets, or an exact invariant of the method. A plausible mistake in the
+oracle (a dropped term, a flipped sign or compare, a transposed operand, a
+reversed tie-break) fails at least one of these; test_oracle_mutations.py
+plants such mistakes and checks that it does.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from activation_sparse_gated_gate_amd import inputs
+from conftest import GOLDEN
+
+# ---------------------------------------------------------------------------
+# Hand-worked golden cases (tests/golden/hand_worked.txt)
+# ---------------------------------------------------------------------------
+X = np.array([[1.0, 2.0]])
+WG = np.array([[1.0, 0.0], [0.5, -1.0], [1.0, 1.0]])
+WU = np.array([[2.0, 1.0], [1.0, 1.0], [-1.0, 1.0]])
+WD = np.array([[1.0, -1.0], [100.0, 100.0], [2.0, 0.5]])
+A_T = np.array([[1.0, 1.0]])
+B_T = np.array([[2.0], [-1.0], [0.5]])
+
+
+def _golden():
+    cases = {}
+    with open(os.path.join(GOLDEN, "hand_worked.txt")) as fh:
+        for line in fh:
+            if not line.startswith("case "):
+                continue
+            _, name, field, *vals = line.split()
+            cases.setdefault(name, {})[field] = vals
+    return cases
+
+
+def _eval(expr):
+    s = {"s0": 1.0 / (1.0 + math.exp(-1.0)), "s2": 3.0 / (1.0 + math.exp(-3.0))}
+    return float(eval(expr, {"__builtins__": {}}, s))
+
+
+GOLD = _golden()
+
+
+@pytest.mark.parametrize("case", sorted(GOLD))
+def test_golden_hand_worked(case):
+    c = GOLD[case]
+    if case == "lopa":
+        r = oracle.forward("lopa", X, WU, WD, lopa_a=A_T, lopa_b=B_T, tau=float(c["tau"][0]), tau_f32=False)
+        np.testing.assert_array_equal(r.z[0], [float(v) for v in c["z"]])
+    elif case.startswith("topk"):
+        r = oracle.forward("topk", X, WU, WD, w_gate=WG, k=int(c["k"][0]))
+    elif case == "dense_shift":
+        r = oracle.forward("dense_relu", X, WU, WD, w_gate=WG, tau=float(c["tau"][0]), tau_f32=False)
+    else:
+        r = oracle.forward("threshold", X, WU, WD, w_gate=WG, tau=float(c["tau"][0]), tau_f32=False)
+    assert list(np.nonzero(r.mask[0])[0]) == [int(v) for v in c["active"]]
+    want = np.array([_eval(v) for v in c["y"]])
+    np.testing.assert_allclose(r.y[0], want, rtol=1e-15, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Masked dense == sparse skip, bit for bit (skipping only drops zero terms)
+# ---------------------------------------------------------------------------
+def _rand_layer(seed, d, f, dtype, rank=0):
+    return inputs.make_layer(seed, d, f, dtype, rank=rank, with_gate=True)
+
+
+@pytest.mark.parametrize("mode", ["threshold", "topk", "lopa", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+def test_masked_dense_equals_sparse_skip(mode, dtype):
+    d, f, n = 64, 200, 3
+    lay = _rand_layer(1, d, f, dtype, rank=16)
+    x = inputs.make_x(1, n, d, dtype)
+    kw = dict(w_gate=lay.w_gate, lopa_a=lay.lopa_a, lopa_b=lay.lopa_b, tau=0.8, k=37)
+    dense = oracle.forward(mode, x, lay.w_up, lay.w_down, skip=False, **kw)
+    sparse = oracle.forward(mode, x, lay.w_up, lay.w_down, skip=True, **kw)
+    assert np.array_equal(dense.mask, sparse.mask)
+    assert np.array_equal(dense.h, sparse.h)
+    assert np.array_equal(dense.y.view(np.uint64), sparse.y.view(np.uint64))
+    if mode in ("threshold", "lopa"):
+        assert 0 < dense.mask.sum() < n * f  # the case really is sparse
+
+
+# ---------------------------------------------------------------------------
+# Gate: textbook GEMV special cases
+# ---------------------------------------------------------------------------
+def test_gate_one_hot_picks_a_column():
+    d, f = 16, 33
+    wg = inputs.make_layer(2, d, f, inputs.F32).w_gate
+    for j in (0, 5, d - 1):
+        x = np.zeros((1, d), dtype=np.float32)
+        x[0, j] = 1.0
+        z = oracle.gate_full(x, wg)
+        np.testing.assert_array_equal(z[0], wg[:, j].astype(np.float64))
+
+
+def test_gate_identity_returns_x():
+    d = 32
+    x = inputs.make_x(3, 4, d, inputs.F32)
+    z = oracle.gate_full(x, np.eye(d, dtype=np.float32))
+    np.testing.assert_array_equal(z, x.astype(np.float64))
+
+
+def test_bf16_widening_is_exact():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F7F, 0x8000], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0078125, 2.0 ** -133, 3.3895313892515355e38, -0.0]
+    got = oracle.widen(bits)
+    np.testing.assert_array_equal(got, want)
+    assert math.copysign(1.0, got[-1]) == -1.0
+
+
+# ---------------------------------------------------------------------------
+# Whole forward: textbook FFNs (library matmuls on fp64 copies)
+# ---------------------------------------------------------------------------
+def _f64(a):
+    a = np.asarray(a)
+    return inputs.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+def test_tau_zero_is_textbook_reglu(dtype):
+    """With tau = 0 the shifted-ReLU gate is ReGLU: (max(xWg^T,0) * xWu^T) Wd."""
+    d, f, n = 48, 130, 5
+    lay = _rand_layer(4, d, f, dtype)
+    x = inputs.make_x(4, n, d, dtype)
+    r = oracle.forward("threshold", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=0.0)
+    xv, g, u, dn = _f64(x), _f64(lay.w_gate), _f64(lay.w_up), _f64(lay.w_down)
+    ref = (np.maximum(xv @ g.T, 0.0) * (xv @ u.T)) @ dn
+    np.testing.assert_allclose(r.y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+def test_topk_all_channels_is_textbook_swiglu(dtype):
+    """Top-K with K = d_ff keeps every channel: SwiGLU (SiLU(xWg^T) * xWu^T) Wd."""
+    d, f, n = 40, 96, 3
+    lay = _rand_layer(5, d, f, dtype)
+    x = inputs.make_x(5, n, d, dtype)
+    r = oracle.forward("topk", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, k=f)
+    assert r.mask.all()
+    xv, g, u, dn = _f64(x), _f64(lay.w_gate), _f64(lay.w_up), _f64(lay.w_down)
+    zz = xv @ g.T
+    ref = (zz / (1.0 + np.exp(-zz)) * (xv @ u.T)) @ dn
+    np.testing.assert_allclose(r.y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_threshold_below_min_is_dense():
+    """A threshold below every pre-activation keeps every channel: the sparse
+    forward equals the dense evaluation of the same shifted gate."""
+    d, f, n = 32, 77, 2
+    lay = _rand_layer(6, d, f, inputs.F32)
+    x = inputs.make_x(6, n, d, inputs.F32)
+    z = oracle.gate_full(x, lay.w_gate)
+    tau = float(np.float32(z.min() - 1.0))
+    sp = oracle.forward("threshold", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=tau)
+    de = oracle.forward("dense_relu", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=tau)
+    assert sp.mask.all()
+    assert np.array_equal(sp.y, de.y)
+    xv, g, u, dn = _f64(x), _f64(lay.w_gate), _f64(lay.w_up), _f64(lay.w_down)
+    ref = ((xv @ g.T - tau) * (xv @ u.T)) @ dn  # linear-gated GLU
+    np.testing.assert_allclose(sp.y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_threshold_above_max_gives_zero():
+    d, f = 32, 50
+    lay = _rand_layer(7, d, f, inputs.F32)
+    x = inputs.make_x(7, 2, d, inputs.F32)
+    z = oracle.gate_full(x, lay.w_gate)
+    r = oracle.forward("threshold", x, lay.w_up, lay.w_down, w_gate=lay.w_gate,
+                       tau=float(z.max()) + 1.0)
+    assert r.mask.sum() == 0
+    assert np.all(r.y == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Selection: brute force over subsets
+# ---------------------------------------------------------------------------
+def test_threshold_set_brute_force():
+    """{i : z_i > tau} is the unique subset maximising sum(z_i - tau) once no
+    z_i equals tau; check it against all 2^F subsets."""
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        f = 9
+        z = rng.standard_normal((1, f))
+        tau = float(rng.standard_normal() * 0.5)
+        mask, _ = oracle.select_threshold(z, tau)
+        best, best_set = -np.inf, None
+        for m in range(1 << f):
+            s = [i for i in range(f) if m >> i & 1]
+            v = float(np.sum(z[0, s] - tau)) if s else 0.0
+            if v > best:
+                best, best_set = v, s
+        assert list(np.nonzero(mask[0])[0]) == best_set
+
+
+def test_topk_set_brute_force():
+    """The Top-K set is the K-subset with the largest sum of SiLU keys (keys
+    distinct); check against every K-subset."""
+    rng = np.random.default_rng(12)
+    for trial in range(20):
+        f = 10
+        k = int(rng.integers(1, f + 1))
+        z = rng.standard_normal((1, f)) * 2.0
+        mask, g, kth = oracle.select_topk(z, k)
+        keys = z[0] / (1.0 + np.exp(-z[0]))
+        best = max(itertools.combinations(range(f), k), key=lambda c: sum(keys[list(c)]))
+        assert list(np.nonzero(mask[0])[0]) == sorted(best)
+        assert kth[0] == sorted(keys)[::-1][k - 1]
+
+
+def test_topk_ties_go_to_lower_index():
+    z = np.array([[0.5, 2.0, 1.0, 2.0, 1.0, 2.0]])
+    mask, _, _ = oracle.select_topk(z, 2)
+    assert list(np.nonzero(mask[0])[0]) == [1, 3]
+    mask, _, _ = oracle.select_topk(z, 4)
+    assert list(np.nonzero(mask[0])[0]) == [1, 2, 3, 5]
+
+
+def test_topk_negative_keys_rank_by_signed_silu():
+    """SiLU has its minimum near z = -1.28: a large negative z has a key closer
+    to 0 than z = -1.28, so it ranks above it."""
+    z = np.array([[-1.28, -6.0, -0.1]])
+    mask, g, _ = oracle.select_topk(z, 2)
+    assert list(np.nonzero(mask[0])[0]) == [1, 2]
+
+
+def test_topk_rejects_bad_k():
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros((1, 4)), 0)
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros((1, 4)), 5)
+
+
+# ---------------------------------------------------------------------------
+# LoPA
+# ---------------------------------------------------------------------------
+def test_lopa_full_rank_identity_is_standard_gate():
+    """A = I (rank = d_model) and B = W_gate^T reproduce the full gate exactly."""
+    d, f, n = 32, 70, 3
+    lay = _rand_layer(8, d, f, inputs.F32)
+    x = inputs.make_x(8, n, d, inputs.F32)
+    a_t = np.eye(d, dtype=np.float32)
+    b_t = lay.w_gate  # B^T stored [F][r] with r = d is W_gate itself
+    lo = oracle.forward("lopa", x, lay.w_up, lay.w_down, lopa_a=a_t, lopa_b=b_t, tau=0.3)
+    st = oracle.forward("threshold", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=0.3)
+    assert np.array_equal(lo.z, st.z)
+    assert np.array_equal(lo.mask, st.mask)
+    assert np.array_equal(lo.y, st.y)
+
+
+def test_lopa_equals_product_gate():
+    """(xA)B = x(AB): the low-rank gate is a gate with W_gate = A.B."""
+    d, f, n, r = 48, 90, 4, 8
+    lay = _rand_layer(9, d, f, inputs.BF16, rank=r)
+    x = inputs.make_x(9, n, d, inputs.BF16)
+    t, z = oracle.gate_lopa(x, lay.lopa_a, lay.lopa_b)
+    a = _f64(lay.lopa_a).T          # [d][r]
+    b = _f64(lay.lopa_b).T          # [r][F]
+    np.testing.assert_allclose(t, _f64(x) @ a, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z, _f64(x) @ (a @ b), rtol=1e-11, atol=1e-12)
+
+
+def test_lopa_variance_recipe_gives_unit_std():
+    """A, B with variance 1/sqrt(d r) give the gate pre-activation std ~ 1."""
+    w = inputs.WORKLOADS["lopa_gate_bf16_d4096_f11008"]
+    lay = inputs.make_layer(0, w.d_model, w.d_ff, w.dtype, rank=256, with_gate=False)
+    x = inputs.make_x(0, 1, w.d_model, w.dtype)
+    _, z = oracle.gate_lopa(x, lay.lopa_a, lay.lopa_b)
+    assert 0.8 < z.std() < 1.25
+
+
+# ---------------------------------------------------------------------------
+# Exact invariants of the whole forward
+# ---------------------------------------------------------------------------
+def test_homogeneity_threshold_exact():
+    """z(2x) = 2z, so with tau -> 2 tau the set is unchanged, g doubles and u
+    doubles: y(2x, 2tau) = 4 y(x, tau), exactly in binary floating point."""
+    d, f, n = 64, 150, 3
+    lay = _rand_layer(10, d, f, inputs.F32)
+    x = inputs.make_x(10, n, d, inputs.F32)
+    a = oracle.forward("threshold", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=0.75)
+    b = oracle.forward("threshold", 2.0 * x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=1.5)
+    assert np.array_equal(a.mask, b.mask)
+    assert np.array_equal(4.0 * a.y, b.y)
+
+
+@pytest.mark.parametrize("mode", ["threshold", "topk"])
+def test_channel_permutation_equivariance(mode):
+    d, f, n = 32, 64, 3
+    lay = _rand_layer(13, d, f, inputs.F32)
+    x = inputs.make_x(13, n, d, inputs.F32)
+    perm = np.random.default_rng(13).permutation(f)
+    a = oracle.forward(mode, x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=0.5, k=11)
+    b = oracle.forward(mode, x, lay.w_up[perm], lay.w_down[perm], w_gate=lay.w_gate[perm], tau=0.5, k=11)
+    assert np.array_equal(a.mask[:, perm], b.mask)
+    np.testing.assert_allclose(a.y, b.y, rtol=1e-13, atol=1e-14)
+
+
+def test_union_is_or_of_token_sets():
+    mask = np.array([[1, 0, 0, 1], [0, 0, 1, 1], [0, 0, 0, 0]], dtype=np.uint8)
+    un, cnt = oracle.union(mask)
+    assert list(un) == [1, 0, 1, 1] and cnt == 3
+
+
+def test_tau_rounded_to_f32():
+    """The oracle compares against the same fp32 tau the GPU receives: a
+    pre-activation equal to fp32(tau) is not active."""
+    zf = float(np.float32(1.2816))
+    r = oracle.forward("threshold", np.array([[1.0]]), np.ones((1, 1)), np.ones((1, 1)),
+                       w_gate=np.array([[zf]]), tau=1.2816)
+    assert r.z[0, 0] == zf and r.mask[0, 0] == 0
+
+
+# ---------------------------------------------------------------------------
+# Statistical pin: sparsity follows the normal quantile of the threshold
+# ---------------------------------------------------------------------------
+def _phi(v):
+    return 0.5 * (1.0 + math.erf(v / math.sqrt(2.0)))
+
+
+def test_sparsity_matches_normal_quantile():
+    """With W_gate ~ N(0, 1/d), z_i | x ~ N(0, |x|^2/d) iid, so the active
+    fraction is 1 - Phi(tau sqrt(d)/|x|) up to binomial noise (4 sigma)."""
+    w = inputs.WORKLOADS["llama7b_ffn_bf16_d4096_f11008"]
+    lay = inputs.make_layer(0, w.d_model, w.d_ff, w.dtype)
+    x = inputs.make_x(0, 1, w.d_model, w.dtype)
+    z = oracle.gate_full(x, lay.w_gate)
+    xn = float(np.linalg.norm(_f64(x)))
+    for tau in w.taus:
+        mask, _ = oracle.select_threshold(z, float(np.float32(tau)))
+        p = 1.0 - _phi(tau * math.sqrt(w.d_model) / xn)
+        sigma = math.sqrt(p * (1 - p) / w.d_ff)
+        assert abs(mask.mean() - p) < 4 * sigma + 1e-3, (tau, mask.mean(), p)

@@ -1,0 +1,75 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins in
+test_oracle.py catch every one (all on the CPU).
+
+Each mutation edits one spot of sffn_oracle.c (a dropped term, a flipped sign
+or compare, a transposed operand, a wrong token index, a reversed order),
+builds it to a temporary shared object, and runs the pin suite against it in a
+child process through SFFN_ORACLE_SO. The suite must fail for each one. All
+mutated index expressions stay inside their arrays.
+"""
+import concurrent.futures
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "sffn_oracle.c")
+
+MUTATIONS = {
+    "non_strict_threshold": ("mask[e] = z[e] > tau;", "mask[e] = z[e] >= tau;"),
+    "threshold_gate_sign": ("double v = z[e] - tau;\n        mask[e] = z[e] > tau;",
+                            "double v = tau - z[e];\n        mask[e] = z[e] > tau;"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "gate_drops_last_term": (
+        "for (int j = 0; j < d; ++j)\n                acc += elem(x, x_dt, (long)t * d + j) * elem(wg,",
+        "for (int j = 0; j < d - 1; ++j)\n                acc += elem(x, x_dt, (long)t * d + j) * elem(wg,"),
+    "gate_transposed": ("elem(wg, w_dt, (long)i * d + j)", "elem(wg, w_dt, (long)j * F + i)"),
+    "up_transposed": ("elem(wu, w_dt, (long)i * d + j)", "elem(wu, w_dt, (long)j * F + i)"),
+    "down_transposed": ("elem(wd, w_dt, (long)i * d + c)", "elem(wd, w_dt, (long)c * F + i)"),
+    "up_wrong_token": ("u += elem(x, x_dt, (long)t * d + j)", "u += elem(x, x_dt, (long)0 * d + j)"),
+    "up_drops_gate": ("h[e] = (mask[e] ? 1.0 : 0.0) * g[e] * u;", "h[e] = (mask[e] ? 1.0 : 0.0) * u;"),
+    "down_drops_last_channel": ("for (int i = 0; i < F; ++i) {\n            long e = (long)t * F + i;\n            if (skip && !mask[e])\n                continue;\n            double hv",
+                                "for (int i = 0; i < F - 1; ++i) {\n            long e = (long)t * F + i;\n            if (skip && !mask[e])\n                continue;\n            double hv"),
+    "topk_ascending": ("if (a->s > b->s) return -1;\n    if (a->s < b->s) return 1;",
+                       "if (a->s > b->s) return 1;\n    if (a->s < b->s) return -1;"),
+    "topk_ties_to_higher_index": ("return (a->i > b->i) - (a->i < b->i);",
+                                  "return (a->i < b->i) - (a->i > b->i);"),
+    "topk_off_by_one": ("for (int q = 0; q < K; ++q)", "for (int q = 1; q < K; ++q)"),
+    "lopa_a_transposed": ("elem(at, w_dt, (long)k * d + j)", "elem(at, w_dt, (long)j * r + k)"),
+    "lopa_b_transposed": ("elem(bt, w_dt, (long)i * r + k)", "elem(bt, w_dt, (long)k * F + i)"),
+    "union_and": ("any |= mask[(long)t * F + i];", "any &= mask[(long)t * F + i];"),
+    "bf16_widen_shift": ("<< 16;", "<< 15;"),
+}
+
+
+def _run(name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: anchor found {src.count(old)} times"
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "m.c")
+        so = os.path.join(td, "m.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", c, "-o", so, "-lm"])
+        env = dict(os.environ, SFFN_ORACLE_SO=so, PYTHONDONTWRITEBYTECODE="1")
+        p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            os.path.join(ROOT, "tests", "test_oracle.py")],
+                           cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=300)
+        return name, p.returncode
+
+
+def test_every_planted_mistake_is_caught():
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        results = dict(ex.map(_run, sorted(MUTATIONS)))
+    survived = [k for k, rc in results.items() if rc == 0]
+    assert not survived, f"pins did not catch: {survived}"
+
+
+def test_unmutated_oracle_passes_the_pins():
+    p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=300)
+    assert p.returncode == 0, p.stdout.decode()[-2000:]

@@ -1,0 +1,738 @@
+// Decode-regime kernels (1..8 tokens): every weight row is streamed from HBM
+// once and dotted with all tokens, whose chunks sit in registers.
+//
+// Pipeline per forward (modes as in include/sffn.h):
+//   threshold  k_gate<SELECT_UP>: gate GEMV, shifted-ReLU select, and the W_up
+//              rows of the channels just found active -> k_down -> k_reduce
+//   LoPA       k_lopa_xa (x.A partials) -> k_gate<SELECT_UP> on B with t = x.A
+//              -> k_down -> k_reduce
+//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk (radix select) -> k_up
+//              -> k_down -> k_reduce
+//   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
+//              -> k_reduce
+//
+// The gate is computed first and in full; only the channels it leaves active
+// read their W_up and W_down rows ("Model Casting and Low-Parameter Gating",
+// Abstract). Those rows are contiguous in the channel-major weights, so an
+// active channel costs two contiguous row reads ("Mixture-of-Channels" blog
+// summary, "Dentro il 'mixture'": load only the active channels' weights).
+//
+// Work is split evenly per compute unit: under full load a CU draws about
+// 1/256 of the HBM bandwidth, so a kernel lasts as long as its most loaded CU.
+// Active channels are byte flags act[t][i] with one writer each, so any row
+// partition works without atomics. No kernel waits on another workgroup:
+// cross-workgroup results go through global memory and the next kernel.
+#include "device_common.h"
+#include "sffn_internal.h"
+
+namespace sffn {
+
+enum GateKind { KEYS = 0, SELECT_UP = 1, DENSE = 2 };
+
+// ---------------------------------------------------------------------------
+// Row-dot engine. A lane group of LPR lanes owns R rows; lane li covers the
+// 8-element chunks j = 8*li + s*8*LPR of every row. Each batch issues all its
+// weight loads (128-bit, non-temporal: weights are read once per forward) and
+// the matching x chunks of the NT tokens (small and cache-resident) before any
+// arithmetic; rows whose bit is clear in `valid` are not read. Products
+// accumulate in fp32 per lane (packed bf16 dot2 when both sides are bf16) and
+// are summed over the lane group, so every lane of a group ends with all
+// R x NT results.
+// ---------------------------------------------------------------------------
+template <typename TW, typename TX, int NT, int R, int LPR, int MAXS>
+struct RowDot {
+    static constexpr int STEP = LPR * 8;
+    float acc[R][NT];
+
+    // x: token t starts at x + t*ldx; tokens >= n read as zero. With tpart
+    // (LoPA, TX = float) the chunk is the in-order sum of ks partial slices
+    // tpart[s][t][.] of stride ps floats.
+    __device__ __forceinline__ void run(const TW *const rows[R], uint32_t valid, int len, int li, const TX *x,
+                                        int ldx, int n, const float *tpart = nullptr, int ks = 0, size_t ps = 0)
+    {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
+        for (int jb = li * 8; jb < len; jb += MAXS * STEP) {
+            typename Ld8<TW>::raw w[MAXS][R];
+            typename Ld8<TX>::raw xv[MAXS][NT];
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int j = jb + s * STEP;
+                    w[s][r] = (((valid >> r) & 1u) && j < len) ? Ld8<TW>::load_nt(rows[r] + j) : Ld8<TW>::zero();
+                }
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int j = jb + s * STEP;
+                    xv[s][t] = Ld8<TX>::zero();
+                    if (t < n && j < len) {
+                        if constexpr (sizeof(TX) == 4) {
+                            if (tpart) {
+                                for (int p = 0; p < ks; ++p)
+                                    Ld8<TX>::add(xv[s][t], Ld8<TX>::load(reinterpret_cast<const TX *>(
+                                                               tpart + (size_t)p * ps + (size_t)t * ldx + j)));
+                                continue;
+                            }
+                        }
+                        xv[s][t] = Ld8<TX>::load(x + (size_t)t * ldx + j);
+                    }
+                }
+#pragma unroll
+            for (int s = 0; s < MAXS; ++s)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[r][t] = dot8<TW, TX>(w[s][r], xv[s][t], acc[r][t]);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[r][t] = group_sum<LPR>(acc[r][t]);
+    }
+};
+
+// Rows per lane group by token count: x chunks are reused over the rows.
+template <int NT>
+struct RowsPer {
+    static constexpr int v = NT <= 2 ? 1 : NT / 2;
+};
+
+// Chunks per batch, keeping the weight and x registers of a batch near 96.
+template <typename TW, typename TX, int NT, int R>
+struct Batch {
+    static constexpr int per = R * (sizeof(TW) == 2 ? 4 : 8) + NT * (sizeof(TX) == 2 ? 4 : 8);
+    static constexpr int raw = 96 / per;
+    static constexpr int v = raw >= 8 ? 8 : raw >= 4 ? 4 : raw >= 2 ? 2 : 1;
+};
+
+// ---------------------------------------------------------------------------
+// Gate kernel. Lane group q of wavefront gw (4 wavefronts per workgroup, LPR
+// lanes per group) owns rows (gw * 64/LPR + q) * R .. + R-1: every wavefront
+// gets the same small share, and there are many wavefronts per CU.
+//   z = x . W_gate[i]   (or t . B[i] for LoPA, t = x.A in fp32)
+//   KEYS:      g = SiLU(z) for the Top-K select that follows
+//   SELECT_UP: active = z > tau, g = z - tau; then the group reads the W_up
+//              rows of its channels that some token selected and writes
+//              h[i][t] = g * (x_t . W_up[i]) for the selecting tokens, else 0
+//   DENSE:     every channel; gate and up rows are read together,
+//              g = max(z - tau, 0) or SiLU(z), h = g * u
+// h is stored channel-major, hbuf[i][t] (8 token slots per channel).
+// ---------------------------------------------------------------------------
+template <typename TW, typename TX, int NT, int LPR, int KIND>
+__global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
+                                              const TW *__restrict__ xu, int d,
+                                              const float *__restrict__ tpart, int ks,
+                                              const TW *__restrict__ wg, const TW *__restrict__ wu,
+                                              int F, int mode, float tau,
+                                              float *__restrict__ gsel, uint8_t *__restrict__ act,
+                                              float *__restrict__ hbuf, float *__restrict__ debug_z)
+{
+    constexpr int SUB = 64 / LPR;
+    constexpr int R = RowsPer<NT>::v;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = lane / LPR, li = lane % LPR;
+    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
+    const int nv = max(0, min(R, F - row0));
+    const uint32_t vmask = (1u << nv) - 1u;
+
+    float zz[R][NT], uu[R][NT];
+    if constexpr (KIND == DENSE) {
+        const TW *rows[2 * R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rows[r] = wg + (size_t)(row0 + r) * L;
+            rows[R + r] = wu + (size_t)(row0 + r) * L;
+        }
+        RowDot<TW, TX, NT, 2 * R, LPR, Batch<TW, TX, NT, 2 * R>::v> dot;
+        dot.run(rows, vmask | (vmask << R), L, li, xg, L, n);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                zz[r][t] = dot.acc[r][t];
+                uu[r][t] = dot.acc[R + r][t];
+            }
+    } else {
+        const TW *rows[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) rows[r] = wg + (size_t)(row0 + r) * L;
+        RowDot<TW, TX, NT, R, LPR, Batch<TW, TX, NT, R>::v> dot;
+        dot.run(rows, vmask, L, li, xg, L, n, tpart, ks, (size_t)kDecodeMaxTokens * L);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) zz[r][t] = dot.acc[r][t];
+    }
+
+    // ---- activation and selection (every lane of the group has every z) ----
+    float gv[R][NT];      // gate value of a selected (row, token), else 0
+    uint32_t amask = 0;   // rows some token selected
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int i = row0 + r;
+            const float z = zz[r][t];
+            float g;
+            bool a;
+            if constexpr (KIND == SELECT_UP) {
+                a = z > tau;
+                g = z - tau;
+            } else if constexpr (KIND == KEYS) {
+                a = false;
+                g = silu(z);
+            } else {
+                a = true;
+                g = mode == SFFN_DENSE ? fmaxf(z - tau, 0.f) : silu(z);
+            }
+            const bool live = r < nv && t < n;
+            a = a && live;
+            gv[r][t] = a ? g : 0.f;
+            if (a) amask |= 1u << r;
+            if (live && li == ((r * NT + t) & (LPR - 1))) {
+                gsel[(size_t)t * F + i] = g;
+                if (debug_z) debug_z[(size_t)t * F + i] = z;
+                if constexpr (KIND == SELECT_UP) act[(size_t)t * F + i] = a ? 1 : 0;
+                if constexpr (KIND == DENSE) hbuf[(size_t)i * kDecodeMaxTokens + t] = g * uu[r][t];
+            }
+        }
+    if constexpr (KIND == SELECT_UP) {
+        if (__ballot(amask != 0) == 0) return;  // nothing selected in this wavefront
+        const TW *urows[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) urows[r] = wu + (size_t)(row0 + r) * d;
+        RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+        up.run(urows, amask, d, li, xu, d, n);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
+                    hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token Top-K of the SiLU keys (one workgroup per token). MSD radix select
+// over order-preserving 32-bit keys, 8 bits per pass with a 256-bin LDS
+// histogram (radix k-selection as in Alabi, Blanchard, Gordon & Steinbach,
+// "Fast k-Selection Algorithms for Graphics Processing Units", 2012). After
+// four passes the K-th largest key is known exactly, together with how many
+// keys equal to it still belong to the set; those are taken in ascending
+// channel order, so ties go to the lower index. Output: act[t][i].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ gsel, int F, int K,
+                                               uint8_t *__restrict__ act)
+{
+    __shared__ int hist[256];
+    __shared__ int sh_digit, sh_need;
+    __shared__ int scan_scratch[16];
+    const int t = blockIdx.x;
+    const float *s = gsel + (size_t)t * F;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    uint32_t prefix = 0, pmask = 0;
+    int need = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int i = tid; i < F; i += blockDim.x) {
+            const uint32_t key = f2key(s[i]);
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane l owns bins 255-4l .. 252-4l (descending)
+            int c[4], tot = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[e] = hist[255 - (lane * 4 + e)];
+                tot += c[e];
+            }
+            int run = wave_incl_scan(tot) - tot;  // keys in higher bins
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (run < need && need <= run + c[e]) {
+                    sh_digit = 255 - (lane * 4 + e);
+                    sh_need = need - run;
+                }
+                run += c[e];
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh_digit << shift;
+        pmask |= 0xffu << shift;
+        need = sh_need;
+        __syncthreads();
+    }
+    const uint32_t kth = prefix;
+
+    // Contiguous channel segments per thread: the count of keys equal to the
+    // K-th before a channel is an exclusive block scan.
+    const int seg = (F + blockDim.x - 1) / blockDim.x;
+    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+    int eq_local = 0;
+    for (int i = i0; i < i1; ++i) eq_local += f2key(s[i]) == kth;
+    int eq_before = block_incl_scan(eq_local, scan_scratch) - eq_local;
+    uint8_t *a = act + (size_t)t * F;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t key = f2key(s[i]);
+        uint8_t on = key > kth;
+        if (key == kth) {
+            on = eq_before < need;
+            ++eq_before;
+        }
+        a[i] = on;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Up kernel (Top-K): the gate kernel's row partition; each lane group reads
+// the W_up rows of its channels that some token selected.
+// h[i][t] = g[t][i] * (x_t . W_up[i]) if token t selected i, else 0.
+// ---------------------------------------------------------------------------
+template <typename TW, int NT, int LPR>
+__global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int d,
+                                            const TW *__restrict__ wu, int F,
+                                            const uint8_t *__restrict__ act,
+                                            const float *__restrict__ gsel, float *__restrict__ hbuf)
+{
+    constexpr int SUB = 64 / LPR;
+    constexpr int R = RowsPer<NT>::v;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = lane / LPR, li = lane % LPR;
+    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
+    const int nv = max(0, min(R, F - row0));
+    float gv[R][NT];
+    uint32_t amask = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            gv[r][t] = 0.f;
+            if (r < nv && t < n && act[(size_t)t * F + row0 + r]) {
+                gv[r][t] = gsel[(size_t)t * F + row0 + r];
+                amask |= 1u << r;
+            }
+        }
+    if (__ballot(amask != 0) == 0) return;
+    const TW *rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
+    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+    up.run(rows, amask, d, li, x, d, n);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
+                hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
+}
+
+// ---------------------------------------------------------------------------
+// Down kernel: partial y over one channel group.
+// Workgroup (s, g) takes output columns [128 s, 128 s + 128) and channels
+// [F g / G, F (g+1) / G). It lists that range's channels selected by any token
+// (every channel in the dense modes) in LDS in ascending order, then its 16
+// row streams (4 per wavefront, 16 lanes x 8 columns each) read the 256-byte
+// segments of those W_down rows, UNR rows per stream in flight:
+//   part[g][t][c] = sum_i h[i][t] * W_down[i][c]   (fixed order).
+// ---------------------------------------------------------------------------
+template <typename TW, int NT, int UNR>
+__global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, int d, int n,
+                                              const uint8_t *__restrict__ act, int dense,
+                                              const float *__restrict__ hbuf, float *__restrict__ part)
+{
+    extern __shared__ __align__(16) char smem[];
+    int *list = reinterpret_cast<int *>(smem);
+    __shared__ float red[4][NT][kDownSliceCols];
+    __shared__ int scan_scratch[4];
+    __shared__ int total;
+    const int s = blockIdx.x, g = blockIdx.y, G = gridDim.y;
+    const int cb = (int)(((long long)F * g) / G), ce = (int)(((long long)F * (g + 1)) / G);
+    const int tid = threadIdx.x;
+
+    // ---- channels of this group selected by some token, ascending ----
+    const int len = ce - cb;
+    const int seg = (len + blockDim.x - 1) / blockDim.x;  // <= 32, fixed on the host
+    const int i0 = cb + min(len, tid * seg), i1 = cb + min(len, tid * seg + seg);
+    uint32_t sel = 0;  // bit k: channel i0 + k
+    for (int i = i0; i < i1; ++i) {
+        bool any = dense != 0;
+        for (int t = 0; t < n && !any; ++t) any = act[(size_t)t * F + i] != 0;
+        sel |= (uint32_t)any << (i - i0);
+    }
+    const int local = __popc(sel);
+    const int incl = block_incl_scan(local, scan_scratch);
+    int pos = incl - local;
+    while (sel) {
+        const int b = __ffs(sel) - 1;
+        sel &= sel - 1;
+        list[pos++] = i0 + b;
+    }
+    if (tid == blockDim.x - 1) total = incl;
+    __syncthreads();
+    const int cnt = total;
+
+    const int wave = tid >> 6, lane = tid & 63;
+    const int rs = wave * 4 + (lane >> 4), c8 = lane & 15;
+    const int col = s * kDownSliceCols + c8 * 8;
+    const bool colok = col < d;
+
+    float acc[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
+
+    if (colok) {
+        for (int k0 = rs; k0 < cnt; k0 += 16 * UNR) {
+            typename Ld8<TW>::raw qv[UNR];
+            float hv[UNR][NT];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int k = k0 + 16 * u;
+                if (k < cnt) {
+                    const int i = list[k];
+                    qv[u] = Ld8<TW>::load(wd + (size_t)i * d + col);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) hv[u][t] = hbuf[(size_t)i * kDecodeMaxTokens + t];
+                } else {
+                    qv[u] = Ld8<TW>::zero();
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) hv[u][t] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                float wv[8];
+                Ld8<TW>::cvt(qv[u], wv);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(hv[u][t], wv[e], acc[t][e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = acc[t][e];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            acc[t][e] = v;
+        }
+    if (lane < 16) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][t][c8 * 8 + e] = acc[t][e];
+    }
+    __syncthreads();
+    const int c0 = s * kDownSliceCols;
+    for (int e = tid; e < NT * kDownSliceCols; e += blockDim.x) {
+        const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
+        if (t < n && c0 + c < d)
+            part[((size_t)g * kDecodeMaxTokens + t) * d + c0 + c] =
+                ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
+    }
+}
+
+// y[t][c] = sum over groups g (ascending) of part[g][t][c]. Loads are issued
+// in batches of 16 so the group loop is not one round trip per group.
+__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ part, int G, int n, int d,
+                                                float *__restrict__ y)
+{
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n * d) return;
+    const int t = e / d, c = e - t * d;
+    const float *p = part + (size_t)t * d + c;
+    const size_t gs = (size_t)kDecodeMaxTokens * d;
+    float v = 0.f;
+    for (int g0 = 0; g0 < G; g0 += 16) {
+        float b[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) b[u] = g0 + u < G ? p[(size_t)(g0 + u) * gs] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v += b[u];
+    }
+    y[e] = v;
+}
+
+// ---------------------------------------------------------------------------
+// LoPA first product, partials: workgroup (b, s) takes 16 rows of A^T (4 per
+// wavefront) and the d-slice s; tpart[s][t][k] = x_t[slice] . A^T[k][slice].
+// The gate kernel sums the slices in order.
+// ---------------------------------------------------------------------------
+template <typename TW, int NT>
+__global__ __launch_bounds__(256) void k_lopa_xa(const TW *__restrict__ x, int n, int d,
+                                                 const TW *__restrict__ at, int r, int chunk,
+                                                 float *__restrict__ tpart)
+{
+    const int b = blockIdx.x, s = blockIdx.y;
+    const int j0 = s * chunk, len = max(0, min(d - j0, chunk));
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row0 = b * kLopaRowsPerWG + wave * 4;
+    const int nv = max(0, min(4, r - row0));
+    const TW *rows[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rows[q] = at + (size_t)(row0 + q) * d + j0;
+    RowDot<TW, TW, NT, 4, 64, Batch<TW, TW, NT, 4>::v> dot;
+    dot.run(rows, (1u << nv) - 1u, len, lane, x + j0, d, n);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (q < nv && t < n && lane == ((q * NT + t) & 63))
+                tpart[((size_t)s * kDecodeMaxTokens + t) * r + row0 + q] = dot.acc[q][t];
+}
+
+// ---------------------------------------------------------------------------
+// Optional outputs: each token's ascending active list and count (every
+// channel in the dense modes), and the union size. Workgroup b < n handles
+// token b; workgroup n counts the union.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_emit_lists(const uint8_t *__restrict__ act, int F, int n, int dense,
+                                                    int32_t *__restrict__ active_idx,
+                                                    int32_t *__restrict__ active_cnt,
+                                                    int32_t *__restrict__ union_cnt)
+{
+    __shared__ int scan_scratch[4];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (dense) {
+        if (b < n) {
+            if (active_idx)
+                for (int i = tid; i < F; i += blockDim.x) active_idx[(size_t)b * F + i] = i;
+            if (tid == 0 && active_cnt) active_cnt[b] = F;
+        } else if (tid == 0 && union_cnt) {
+            *union_cnt = F;
+        }
+        return;
+    }
+    const int seg = (F + blockDim.x - 1) / blockDim.x;
+    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+    if (b == n) {
+        int local = 0;
+        for (int i = i0; i < i1; ++i) {
+            bool any = false;
+            for (int t = 0; t < n && !any; ++t) any = act[(size_t)t * F + i] != 0;
+            local += any;
+        }
+        const int incl = block_incl_scan(local, scan_scratch);
+        if (tid == blockDim.x - 1 && union_cnt) *union_cnt = incl;
+        return;
+    }
+    const uint8_t *a = act + (size_t)b * F;
+    int local = 0;
+    for (int i = i0; i < i1; ++i) local += a[i] != 0;
+    const int incl = block_incl_scan(local, scan_scratch);
+    int pos = incl - local;
+    if (active_idx)
+        for (int i = i0; i < i1; ++i)
+            if (a[i]) active_idx[(size_t)b * F + pos++] = i;
+    if (tid == blockDim.x - 1 && active_cnt) active_cnt[b] = incl;
+}
+
+__global__ void k_zero_ints(int *__restrict__ p, int count)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+static int lpr_for(int len)
+{
+    if (len >= 512) return 64;
+    if (len >= 256) return 32;
+    return 16;
+}
+
+static int nt_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+// Workgroups (4 wavefronts) for a row partition of `rows` rows in groups of
+// R rows per LPR lanes.
+static int row_blocks(int rows, int lpr, int R)
+{
+    const int per_wave = (64 / lpr) * R;
+    const int waves = (rows + per_wave - 1) / per_wave;
+    return max(1, (waves + 3) / 4);
+}
+
+// 16 channel groups, more for very wide layers so that a thread of the list
+// prologue scans at most 32 channels of its group.
+static int down_groups(const sffn_ctx &c)
+{
+    const int F = c.shape.d_ff;
+    const int G = max(16, (F + 256 * 32 - 1) / (256 * 32));
+    return max(1, min(min(G, kDownGroupsMax), F));
+}
+
+static size_t down_lds(const sffn_ctx &c)
+{
+    const int F = c.shape.d_ff, G = down_groups(c);
+    return (size_t)4 * ((F + G - 1) / G + 1);
+}
+
+static int lopa_split(const sffn_ctx &c)
+{
+    const int d = c.shape.d_model, r = c.shape.rank;
+    const int blocks = (r + kLopaRowsPerWG - 1) / kLopaRowsPerWG;
+    int ks = (2 * c.n_cu + blocks - 1) / blocks;
+    ks = min(ks, kLopaSplitMax);
+    ks = min(ks, max(1, d / 512));
+    return max(ks, 1);
+}
+
+static int lopa_chunk(const sffn_ctx &c, int ks)
+{
+    const int d = c.shape.d_model;
+    int chunk = (d + ks - 1) / ks;
+    return (chunk + 7) / 8 * 8;
+}
+
+hipError_t device_setup(sffn_ctx &c)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int cu = 0, lds = 0;
+    e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    c.n_cu = cu > 0 ? cu : 1;
+    // Dynamic LDS stays within 64 KB per workgroup (static LDS comes on top).
+    c.lds_max = (size_t)min(lds, 65536) - 4096;
+    return hipSuccess;
+}
+
+bool decode_fits(const sffn_ctx &c, int, int) { return down_lds(c) <= c.lds_max; }
+
+hipError_t launch_init(sffn_ctx &c, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
+    return hipGetLastError();
+}
+
+template <typename TW, typename TX, int NT, int KIND>
+static void launch_gate(hipStream_t st, int lpr, const TX *xg, int n, int L, const TW *xu, int d, const float *tpart,
+                        int ks, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel, uint8_t *act,
+                        float *hbuf, float *dz)
+{
+    const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
+#define SFFN_G(LP)                                                                                          \
+    hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart, ks, wg, wu, \
+                       F, mode, tau, gsel, act, hbuf, dz)
+    if (lpr == 64) SFFN_G(64);
+    else if (lpr == 32) SFFN_G(32);
+    else SFFN_G(16);
+#undef SFFN_G
+}
+
+template <typename TW, int NT>
+static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
+{
+    const sffn_shape &S = c.shape;
+    const int d = S.d_model, F = S.d_ff, n = a.n;
+    char *ws = c.ws;
+    uint8_t *act = reinterpret_cast<uint8_t *>(ws + c.L.act);
+    float *gsel = reinterpret_cast<float *>(ws + c.L.gsel);
+    float *hbuf = reinterpret_cast<float *>(ws + c.L.hbuf);
+    float *part = reinterpret_cast<float *>(ws + c.L.part);
+    const TW *x = static_cast<const TW *>(a.x);
+    const TW *wg = static_cast<const TW *>(a.w.w_gate);
+    const TW *wu = static_cast<const TW *>(a.w.w_up);
+    const TW *wdn = static_cast<const TW *>(a.w.w_down);
+    hipStream_t st = a.stream;
+    const bool dense = a.mode == SFFN_DENSE || a.mode == SFFN_DENSE_SILU;
+    hipEvent_t ev0 = static_cast<hipEvent_t>(c.ev_start), ev1 = static_cast<hipEvent_t>(c.ev_stop);
+    hipError_t e;
+
+    // ---- gate (+ select, + up for threshold / LoPA / dense) ----
+    if (a.mode == SFFN_LOPA) {
+        const int r = S.rank;
+        float *tpart = reinterpret_cast<float *>(ws + c.L.tpart);
+        const int ks = lopa_split(c), chunk = lopa_chunk(c, ks);
+        const int blocks = (r + kLopaRowsPerWG - 1) / kLopaRowsPerWG;
+        hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(blocks, ks), dim3(256), 0, st, x, n, d,
+                           static_cast<const TW *>(a.w.lopa_a), r, chunk, tpart);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (ev0) hipEventRecord(ev0, st);
+        const TW *bt = static_cast<const TW *>(a.w.lopa_b);
+        // the gate rows (length r) and the up rows (length d) share the lane
+        // groups, sized for the shorter of the two
+        launch_gate<TW, float, NT, SELECT_UP>(st, lpr_for(min(r, d)), nullptr, n, r, x, d, tpart, ks, bt, wu, F,
+                                              a.mode, a.tau, gsel, act, hbuf, a.debug_z);
+    } else {
+        if (ev0) hipEventRecord(ev0, st);
+        if (dense)
+            launch_gate<TW, TW, NT, DENSE>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
+                                           act, hbuf, a.debug_z);
+        else if (a.mode == SFFN_TOPK)
+            launch_gate<TW, TW, NT, KEYS>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
+                                          act, hbuf, a.debug_z);
+        else
+            launch_gate<TW, TW, NT, SELECT_UP>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau,
+                                               gsel, act, hbuf, a.debug_z);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1) hipEventRecord(ev1, st);
+
+    // ---- Top-K: select, then the up rows ----
+    if (a.mode == SFFN_TOPK) {
+        hipLaunchKernelGGL(k_topk, dim3(n), dim3(1024), 0, st, gsel, F, a.k, act);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int lpr = lpr_for(d);
+        const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
+        if (lpr == 64)
+            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+        else if (lpr == 32)
+            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+        else
+            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+
+    // ---- down partials, then the ordered reduction ----
+    const int slices = (d + kDownSliceCols - 1) / kDownSliceCols;
+    const int G = down_groups(c);
+    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, G), dim3(256), down_lds(c), st, wdn, F, d, n, act,
+                       dense ? 1 : 0, hbuf, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_reduce, dim3((n * d + 255) / 256), dim3(256), 0, st, part, G, n, d, a.y);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    // ---- optional outputs ----
+    if (a.active_idx || a.active_cnt || a.union_cnt) {
+        hipLaunchKernelGGL(k_emit_lists, dim3(n + 1), dim3(256), 0, st, act, F, n, dense ? 1 : 0, a.active_idx,
+                           a.active_cnt, a.union_cnt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <typename TW>
+static hipError_t run_decode_nt(sffn_ctx &c, const FwdArgs &a)
+{
+    switch (nt_for(a.n)) {
+    case 1: return run_decode<TW, 1>(c, a);
+    case 2: return run_decode<TW, 2>(c, a);
+    case 4: return run_decode<TW, 4>(c, a);
+    default: return run_decode<TW, 8>(c, a);
+    }
+}
+
+hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a)
+{
+    if (c.shape.dtype == SFFN_BF16) return run_decode_nt<bf16_t>(c, a);
+    return run_decode_nt<float>(c, a);
+}
+
+}  // namespace sffn

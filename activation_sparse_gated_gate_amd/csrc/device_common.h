@@ -1,0 +1,179 @@
+// Device helpers shared by the HIP kernels: 128-bit loads of 8 elements,
+// bf16 widening, wavefront reductions and scans, Top-K key encoding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sffn {
+
+typedef uint16_t bf16_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// bf16 is the upper half of an IEEE binary32: widening is a shift.
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Eight consecutive elements: one 128-bit load for bf16, two for fp32.
+template <typename T>
+struct Ld8;
+
+template <>
+struct Ld8<bf16_t> {
+    struct raw {
+        uint4 q;
+    };
+    static __device__ __forceinline__ raw load(const bf16_t *p)
+    {
+        raw r;
+        r.q = *reinterpret_cast<const uint4 *>(p);
+        return r;
+    }
+    // Streaming load for weights read once per forward (non-temporal hint).
+    static __device__ __forceinline__ raw load_nt(const bf16_t *p)
+    {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        raw r;
+        r.q = make_uint4(v.x, v.y, v.z, v.w);
+        return r;
+    }
+    static __device__ __forceinline__ raw zero()
+    {
+        raw r;
+        r.q = make_uint4(0, 0, 0, 0);
+        return r;
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const raw &r)
+    {
+        *reinterpret_cast<uint4 *>(p) = r.q;
+    }
+    static __device__ __forceinline__ void cvt(const raw &r, float v[8])
+    {
+        v[0] = bf_lo(r.q.x); v[1] = bf_hi(r.q.x);
+        v[2] = bf_lo(r.q.y); v[3] = bf_hi(r.q.y);
+        v[4] = bf_lo(r.q.z); v[5] = bf_hi(r.q.z);
+        v[6] = bf_lo(r.q.w); v[7] = bf_hi(r.q.w);
+    }
+};
+
+template <>
+struct Ld8<float> {
+    struct raw {
+        float4 a, b;
+    };
+    static __device__ __forceinline__ raw load(const float *p)
+    {
+        raw r;
+        r.a = reinterpret_cast<const float4 *>(p)[0];
+        r.b = reinterpret_cast<const float4 *>(p)[1];
+        return r;
+    }
+    static __device__ __forceinline__ raw load_nt(const float *p)
+    {
+        const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+        const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p) + 1);
+        raw r;
+        r.a = make_float4(a.x, a.y, a.z, a.w);
+        r.b = make_float4(b.x, b.y, b.z, b.w);
+        return r;
+    }
+    static __device__ __forceinline__ void add(raw &r, const raw &o)
+    {
+        r.a.x += o.a.x; r.a.y += o.a.y; r.a.z += o.a.z; r.a.w += o.a.w;
+        r.b.x += o.b.x; r.b.y += o.b.y; r.b.z += o.b.z; r.b.w += o.b.w;
+    }
+    static __device__ __forceinline__ raw zero()
+    {
+        raw r;
+        r.a = make_float4(0.f, 0.f, 0.f, 0.f);
+        r.b = r.a;
+        return r;
+    }
+    static __device__ __forceinline__ void store(float *p, const raw &r)
+    {
+        reinterpret_cast<float4 *>(p)[0] = r.a;
+        reinterpret_cast<float4 *>(p)[1] = r.b;
+    }
+    static __device__ __forceinline__ void cvt(const raw &r, float v[8])
+    {
+        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+    }
+};
+
+// c + sum of the 8 products w[e] * x[e], accumulated in fp32. For bf16 x bf16
+// this is four packed v_dot2_f32_bf16 (bf16 products are exact in fp32).
+template <typename TW, typename TX>
+__device__ __forceinline__ float dot8(const typename Ld8<TW>::raw &w, const typename Ld8<TX>::raw &x, float c)
+{
+    if constexpr (sizeof(TW) == 2 && sizeof(TX) == 2) {
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.q.x), __builtin_bit_cast(bf16x2_t, x.q.x), c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.q.y), __builtin_bit_cast(bf16x2_t, x.q.y), c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.q.z), __builtin_bit_cast(bf16x2_t, x.q.z), c, false);
+        c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.q.w), __builtin_bit_cast(bf16x2_t, x.q.w), c, false);
+        return c;
+    } else {
+        float wv[8], xv[8];
+        Ld8<TW>::cvt(w, wv);
+        Ld8<TX>::cvt(x, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c = fmaf(wv[e], xv[e], c);
+        return c;
+    }
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64). Every lane of a
+// group ends with the same bits: each butterfly step adds the same two
+// operands on both partner lanes, and fp32 addition commutes exactly.
+template <int G>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Inclusive prefix sum across one 64-lane wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// Inclusive prefix sum across the whole workgroup (blockDim.x a multiple of
+// 64, at most 1024). `scratch` holds one int per wavefront. Contains
+// barriers: every thread of the block must call it.
+__device__ __forceinline__ int block_incl_scan(int v, int *scratch)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    v = wave_incl_scan(v);
+    if (lane == 63) scratch[wave] = v;
+    __syncthreads();
+    int add = 0;
+    for (int w = 0; w < wave; ++w) add += scratch[w];
+    (void)nw;
+    __syncthreads();
+    return v + add;
+}
+
+// Order-preserving map from fp32 to uint32 (larger float -> larger key).
+// -0 is folded onto +0 so that equal values get equal keys.
+__device__ __forceinline__ uint32_t f2key(float f)
+{
+    uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
+
+}  // namespace sffn

@@ -1,0 +1,83 @@
+// Internal declarations shared by the C ABI (abi.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sffn.h"
+
+namespace sffn {
+
+// Token counts up to this use the GEMV kernels (each weight row read once for
+// all tokens); larger batches use the MFMA union path.
+constexpr int kDecodeMaxTokens = 8;
+
+// Control block (int32 slots) at the start of the workspace, zeroed by the
+// first forward on a handle; reserved for counters of the batched path.
+constexpr int kCtrlInts = 1024;
+
+constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
+constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
+constexpr int kLopaSplitMax = 16;    // split of d_model in the LoPA x.A kernel
+constexpr int kLopaRowsPerWG = 16;
+
+constexpr int kMaxDff = 262144;
+
+struct Layout {
+    int words;        // ceil(d_ff / 32)
+    int ntp;          // padded decode token count (8)
+    size_t ctrl;      // int32 [kCtrlInts]
+    size_t act;       // uint8 [max(ntp, max_tokens)][d_ff]  per-token active flags (0/1)
+    size_t gsel;      // decode: fp32 [ntp][d_ff] gate values; batched: bf16 [T][d_ff]
+    size_t uidx;      // int32 [d_ff] ascending union list
+    size_t hbuf;      // decode: fp32 [d_ff][ntp] gated up values; batched: bf16 [T][d_ff]
+    size_t part;      // fp32 [kDownGroupsMax][ntp][d_model] down-projection partials
+    size_t tpart;     // fp32 [kLopaSplitMax][ntp][rank] LoPA partial x.A
+    size_t tvec;      // fp32 [ntp][rank] LoPA x.A
+    size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
+    size_t ubits;     // batched: uint32 [words] union bitmap
+    size_t total;
+};
+
+bool shape_ok(const sffn_shape &s);
+Layout make_layout(const sffn_shape &s);
+
+struct FwdArgs {
+    const void *x;
+    int n;
+    sffn_weights w;
+    int mode;
+    float tau;
+    int k;
+    float *y;
+    int32_t *active_idx;
+    int32_t *active_cnt;
+    int32_t *union_cnt;
+    float *debug_z;
+    hipStream_t stream;
+};
+
+}  // namespace sffn
+
+struct sffn_ctx {
+    sffn_shape shape;
+    char *ws;
+    size_t ws_bytes;
+    sffn::Layout L;
+    bool inited;        // control block zeroed on the device
+    int n_cu;           // compute units, read on the first forward
+    size_t lds_max;     // bytes of LDS one workgroup may allocate
+    void *ev_start;     // optional hipEvent_t pair around the dominant kernel
+    void *ev_stop;
+};
+
+namespace sffn {
+hipError_t device_setup(sffn_ctx &c);
+hipError_t launch_init(sffn_ctx &c, hipStream_t s);
+hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a);
+hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
+// Host-side check that the decode kernels' LDS needs fit; false -> unsupported.
+bool decode_fits(const sffn_ctx &c, int n, int mode);
+}  // namespace sffn

@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse gated-FFN forward on one MI355X.
+
+A step is one forward of a Llama-7B-shaped FFN layer (d_model 4096, d_ff
+11008, bf16 weights, fp32 accumulate) for one decode token: gate GEMV +
+shifted-ReLU select, sparse up projection, split down projection. The headline
+point is tau = 1.2816 (about 90% of channels inactive). Weights come from the
+seeded synthetic recipe (random init, no trained checkpoint).
+
+To measure HBM rather than the 256 MB Infinity Cache, steps rotate over
+several device copies of the layer, so more than 512 MB of other weights are
+read between two uses of a copy.
+
+Prints one JSON line. Besides the contract fields it carries:
+  roofline      the gate kernel (the dominant one): algorithmic bytes per launch
+                over its mean duration from HIP events recorded around it on the
+                forward's stream during the timed region, against 8 TB/s;
+  step_roofline the whole step: touched bytes (x, gate weights, active W_up and
+                W_down rows, y) over the step time, against 8 TB/s;
+  sweep         every tau of the workload: sparsity, step time, tokens/s, HBM
+                fraction, and the speedup over this library's dense forward;
+  cpu_baseline  the CPU oracle (plain C, fp64, one thread) on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+WORKLOAD = "llama7b_ffn_bf16_d4096_f11008"
+HEADLINE_TAU = 1.2816
+METRIC = "sparse FFN layer tokens/s + % HBM roofline at batch 1, 50–99% sparsity"
+GATE_SRC = os.path.join(ROOT, "activation_sparse_gated_gate_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_llama7b_bf16_pmc.md")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--copies", type=int, default=8, help="layer copies rotated to defeat the Infinity Cache")
+    p.add_argument("--no-sweep", action="store_true", help="headline point only")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0 = skip)")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="after timing, run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def sha256(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per gate launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith(("traffic_bytes_per_launch", "source_sha256")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != sha256(GATE_SRC):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library's forward is a single-GPU kernel path and "
+              "no multi-GPU path is built. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from activation_sparse_gated_gate_amd import inputs
+    from activation_sparse_gated_gate_amd import sffn as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = inputs.WORKLOADS[WORKLOAD]
+    d, f, n = wl.d_model, wl.d_ff, 1
+    es = 2
+
+    # ---- inputs resident in HBM before timing ----
+    lay = inputs.make_layer(0, d, f, wl.dtype)
+    x_h = inputs.make_x(0, n, d, wl.dtype)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+    base = [dev(lay.w_gate), dev(lay.w_up), dev(lay.w_down)]
+    copies = [base] + [[t.clone() for t in base] for _ in range(max(1, args.copies) - 1)]
+    weights = [S.SparseFFN.weights(w_gate=g, w_up=u, w_down=dn) for g, u, dn in copies]
+    x = dev(x_h)
+    y = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    ucnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ffn = S.SparseFFN(d, f, n, wl.dtype)
+    stream = torch.cuda.current_stream()
+
+    def run(mode, tau, steps, warmup, rotate=True, events=None):
+        L = len(weights) if rotate else 1
+        for s in range(warmup):
+            ffn.forward(x, weights[s % L], mode, y, tau=tau)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            if events is not None:
+                ffn.set_profile_events(*events[s])
+            ffn.forward(x, weights[s % L], mode, y, tau=tau)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if events is not None:
+            ffn.set_profile_events(None, None)
+        return (t1 - t0) / steps
+
+    def active_count(mode, tau):
+        ffn.forward(x, weights[0], mode, y, tau=tau, union_cnt=ucnt)
+        torch.cuda.synchronize()
+        return int(ucnt.item())
+
+    # ---- headline: timed region with events around the gate kernel ----
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:  # torch creates the underlying hipEvent_t on first record
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    sec = run("threshold", HEADLINE_TAU, args.steps, args.warmup, events=ev)
+    gate_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    n_act = active_count("threshold", HEADLINE_TAU)
+    gate_bytes = f * d * es + n * d * es
+    touched = lambda na: n * d * es + f * d * es + 2 * na * d * es + n * d * 4  # noqa: E731
+    roofline = {
+        "bound": "hbm",
+        "kernel": "k_gate (gate GEMV + threshold select)",
+        "achieved": round(gate_bytes / (gate_ms * 1e-3) / 1e9, 1),
+        "peak": PEAK_HBM / 1e9,
+        "unit": "GB/s",
+        "frac": round(gate_bytes / (gate_ms * 1e-3) / PEAK_HBM, 4),
+        "traffic": read_traffic(),
+        "algorithmic_bytes_per_launch": gate_bytes,
+        "mean_launch_us": round(gate_ms * 1e3, 2),
+    }
+    step_roofline = {
+        "touched_bytes": touched(n_act),
+        "achieved_GBps": round(touched(n_act) / sec / 1e9, 1),
+        "frac": round(touched(n_act) / sec / PEAK_HBM, 4),
+    }
+    plain_sec = run("threshold", HEADLINE_TAU, args.steps, 5)
+    hot_sec = run("threshold", HEADLINE_TAU, args.steps, 5, rotate=False)
+
+    # ---- sweep over tau, with the dense forward as denominator ----
+    sweep = []
+    dense_sec = run("dense_relu", 0.0, max(50, args.steps // 4), 10)
+    if not args.no_sweep:
+        for tau in wl.taus:
+            na = active_count("threshold", tau)
+            s = run("threshold", tau, max(50, args.steps // 2), 10)
+            sweep.append({
+                "tau": tau, "sparsity": round(1 - na / f, 4), "active": na,
+                "us_per_step": round(s * 1e6, 2), "tokens_per_s": round(n / s, 1),
+                "hbm_frac": round(touched(na) / s / PEAK_HBM, 4),
+                "speedup_vs_dense": round(dense_sec / s, 3),
+                "byte_bound_speedup": round(3 * f * d * es / touched(na), 3),
+            })
+
+    # ---- optional plain copy for counter calibration ----
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb * (1 << 20), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # ---- CPU oracle baseline (bounded sample) ----
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+
+        oracle.lib()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.forward("threshold", x_h, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=HEADLINE_TAU)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        cpu = {"value": round(reps * n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} single-token forwards (tau={HEADLINE_TAU}, sparse skip, fp64) of the "
+                         f"same layer, {el:.1f} s, one thread"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(n / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) token, N(0,1/d_in) weights, random init)",
+        "config": {"workload": WORKLOAD, "d_model": d, "d_ff": f, "tokens": n, "mode": "threshold",
+                   "tau": HEADLINE_TAU, "sparsity": round(1 - n_act / f, 4), "layer_copies": len(weights)},
+        "roofline": roofline,
+        "step_roofline": step_roofline,
+        "ms_per_step_without_events": round(plain_sec * 1e3, 5),
+        "hot_cache_ms_per_step": round(hot_sec * 1e3, 5),
+        "dense_ms_per_step": round(dense_sec * 1e3, 5),
+        "speedup_vs_dense": round(dense_sec / sec, 3),
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * sffn.h -- C ABI of the activation-sparse gated-FFN forward for MI355X (gfx950).
+ *
+ * The operation (one FFN layer, per token x of width d_model, d_ff channels):
+ *
+ *   z_i   = x . W_gate[i]                      gate pre-activation
+ *           or (x . A) . B[:, i]               LoPA low-rank gate, rank r
+ *   active = { i : z_i > tau }                 shifted-ReLU threshold, or
+ *            the K channels of largest SiLU(z) per-token Top-K
+ *   g_i   = z_i - tau   (threshold, LoPA)      gate value of an active channel
+ *           SiLU(z_i)   (Top-K)
+ *   y     = sum over active i of  g_i * (x . W_up[i]) * W_down[i]
+ *
+ * Sources: "Model Casting and Low-Parameter Gating: Towards More Sparsely
+ * Activated FFNs" (paper detail page), Abstract -- compute the gating matrix's
+ * output first and, because it is highly sparse, skip the two other matrices
+ * for the zeroed channels; LoPA gating gives the gating matrix a low-FLOP,
+ * low-parameter form. "Mixture-of-Channels: Exploiting Sparse FFNs for
+ * Efficient LLMs Pre-Training and Inference" (blog summary), sections "Dentro il
+ * 'mixture'" and "'Dentro MoC'" -- per token keep the Top-K channels of the
+ * SwiGLU gate as a binary mask and, at inference, load only the weight rows and
+ * columns of the active channels.
+ *
+ * Layout (all row-major, element type = the shape's dtype unless stated):
+ *   x        [n_tokens][d_model]
+ *   W_gate   [d_ff][d_model]   row i = channel i (this is nn.Linear(d, F).weight)
+ *   W_up     [d_ff][d_model]   row i = channel i (nn.Linear(d, F).weight)
+ *   W_down   [d_ff][d_model]   row i = channel i; the TRANSPOSE of
+ *                              nn.Linear(F, d).weight, made contiguous once
+ *   lopa_a   [rank][d_model]   A stored transposed (row k = column k of A)
+ *   lopa_b   [d_ff][rank]      B stored transposed (row i = column i of B)
+ *   y        [n_tokens][d_model] fp32, always
+ *
+ * Ownership: every pointer passed to sffn_forward is caller-owned device
+ * memory that the library borrows for the duration of the work it enqueues on
+ * `stream`; the library never allocates, copies or repacks. The workspace is
+ * caller-allocated device memory of at least sffn_workspace_bytes(shape)
+ * bytes, owned by the caller and used exclusively by one handle; a handle
+ * must not run forwards on two streams at once. A handle holds only host-side
+ * metadata. Nothing here is thread-safe per handle.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * enqueued; a failed check returns a negative status and enqueues nothing. A
+ * failed kernel launch returns SFFN_ERR_HIP. Device faults surface at the
+ * caller's next synchronisation. No C++ exception crosses this boundary.
+ * sffn_forward never synchronises and never reads device memory on the host.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SFFN_OK = 0,
+    SFFN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad mode/k/n */
+    SFFN_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+    SFFN_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    SFFN_ERR_WORKSPACE = -4    /* workspace null, misaligned or too small */
+} sffn_status;
+
+typedef enum { SFFN_F32 = 0, SFFN_BF16 = 1 } sffn_dtype;
+
+typedef enum {
+    SFFN_THRESHOLD = 0,  /* full gate; active = z > tau; g = z - tau            */
+    SFFN_TOPK = 1,       /* full gate; active = per-token Top-K of SiLU(z); g = SiLU(z);
+                            ties go to the lower channel index                   */
+    SFFN_LOPA = 2,       /* low-rank gate (x.A).B; active = z > tau; g = z - tau  */
+    SFFN_DENSE = 3,      /* full gate; every channel computed, g = max(z - tau, 0) */
+    SFFN_DENSE_SILU = 4  /* full gate; every channel computed, g = SiLU(z) (SwiGLU) */
+} sffn_mode;
+
+/* Shape of a layer and the largest batch a handle serves.
+ *   d_model    > 0, multiple of 8
+ *   d_ff       >= 1 (need not be a multiple of anything), at most 262144
+ *   rank       0 for a full gate; otherwise the LoPA rank, a multiple of 8
+ *   max_tokens >= 1; forwards take 0 <= n_tokens <= max_tokens
+ *   dtype      SFFN_F32 or SFFN_BF16 (weights and x; y is fp32) */
+typedef struct {
+    int d_model;
+    int d_ff;
+    int rank;
+    int max_tokens;
+    int dtype;
+} sffn_shape;
+
+/* Device pointers to one layer's weights (layouts above). Each must be 16-byte
+ * aligned. w_gate is required for THRESHOLD/TOPK/DENSE/DENSE_SILU, lopa_a and
+ * lopa_b for LOPA; unused ones may be NULL. */
+typedef struct {
+    const void *w_gate;
+    const void *lopa_a;
+    const void *lopa_b;
+    const void *w_up;
+    const void *w_down;
+} sffn_weights;
+
+typedef struct sffn_ctx *sffn_handle;
+
+/* Bytes of device workspace a handle with this shape needs; 0 if the shape is
+ * invalid. Pure host arithmetic. */
+size_t sffn_workspace_bytes(const sffn_shape *shape);
+
+/* Create a handle. `workspace` is caller-owned device memory (256-byte
+ * aligned, >= sffn_workspace_bytes(shape)); the library initialises it on the
+ * first forward. Makes no HIP call. Returns SFFN_ERR_INVALID_ARG for a bad
+ * shape or null `out`, SFFN_ERR_WORKSPACE for a bad workspace. */
+sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspace_bytes,
+                        sffn_handle *out);
+
+/* One forward pass over n_tokens tokens, enqueued on `stream` (a hipStream_t;
+ * NULL = the null stream).
+ *   x           device, [n_tokens][d_model], shape dtype
+ *   w           host struct of device weight pointers
+ *   mode        an sffn_mode
+ *   tau         threshold for THRESHOLD, LOPA and DENSE (compared in fp32)
+ *   k           Top-K size for TOPK, 1 <= k <= d_ff (ignored otherwise)
+ *   y           device, [n_tokens][d_model] fp32, written
+ * Optional outputs (NULL to skip):
+ *   active_idx  device int32 [n_tokens][d_ff]: row t holds token t's active
+ *               channels in ascending order in its first active_cnt[t] slots
+ *   active_cnt  device int32 [n_tokens]: active channels per token
+ *   union_cnt   device int32 [1]: channels active for at least one token
+ *   debug_z     device fp32 [n_tokens][d_ff]: the gate pre-activation z
+ * A token with no active channel gets y = 0. n_tokens = 0 returns SFFN_OK and
+ * enqueues nothing. LOPA needs a handle created with rank > 0; TOPK, THRESHOLD
+ * and the dense modes need w_gate. */
+sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const sffn_weights *w,
+                         int mode, float tau, int k, float *y, int32_t *active_idx,
+                         int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream);
+
+/* Record two caller-created hipEvent_t (passed as void*) around the dominant
+ * kernel of every later forward on this handle (the gate kernel, or the gate
+ * GEMM on the batched path): ev_start before it, ev_stop after it, on the
+ * forward's stream. Pass NULLs to stop. Host-side only; no HIP call here. */
+sffn_status sffn_set_profile_events(sffn_handle handle, void *ev_start, void *ev_stop);
+
+/* Release a handle (host metadata only; the workspace stays the caller's). */
+sffn_status sffn_destroy(sffn_handle handle);
+
+/* Static string naming a status code (never NULL). */
+const char *sffn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

@@ -1,0 +1,125 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the HIP
+path through the C ABI, and compare with the oracle under the parity rule.
+
+Parity rule (one per point):
+  * active sets: identical, except channels whose oracle pre-activation
+    (threshold, LoPA) or SiLU key (Top-K) lies within 1e-5 of the decision
+    boundary; those are counted and reported;
+  * y: max-abs error over max-abs value, against the oracle evaluated on the
+    GPU's own active set (so a band decision does not count as an arithmetic
+    error), at most 1e-5 for fp32 layers and 2e-2 for bf16 layers.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+from activation_sparse_gated_gate_amd import inputs
+from activation_sparse_gated_gate_amd import sffn as S
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+@dataclasses.dataclass
+class GpuOut:
+    y: np.ndarray
+    idx: np.ndarray
+    cnt: np.ndarray
+    union: int
+    z: np.ndarray
+    sets: np.ndarray  # [n][F] bool
+
+
+def run_gpu(lay: inputs.Layer, x: np.ndarray, mode: str, tau: float = 0.0, k: int = 0,
+            max_tokens: Optional[int] = None, ffn: Optional[S.SparseFFN] = None, repeat: int = 1) -> GpuOut:
+    n, d = x.shape
+    f = lay.d_ff
+    if ffn is None:
+        ffn = S.SparseFFN(d, f, max_tokens or max(1, n), lay.dtype, lay.rank)
+    tens = dict(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down),
+                lopa_a=dev(lay.lopa_a), lopa_b=dev(lay.lopa_b))
+    w = S.SparseFFN.weights(**tens)
+    xt = dev(x)
+    y = torch.full((max(n, 1), d), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((max(n, 1), f), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+    ucnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    z = torch.full((max(n, 1), f), float("nan"), dtype=torch.float32, device="cuda")
+    for _ in range(repeat):
+        ffn.forward(xt, w, mode, y, tau=tau, k=k, active_idx=idx, active_cnt=cnt, union_cnt=ucnt, debug_z=z)
+    torch.cuda.synchronize()
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    sets = np.zeros((n, f), dtype=bool)
+    for t in range(n):
+        c = int(cnt_h[t])
+        assert 0 <= c <= f, f"token {t}: count {c}"
+        row = idx_h[t, :c]
+        assert np.all((row >= 0) & (row < f)), f"token {t}: index out of range"
+        assert np.all(np.diff(row) > 0), f"token {t}: active list not strictly ascending"
+        sets[t, row] = True
+    return GpuOut(y=y.cpu().numpy()[:n], idx=idx_h, cnt=cnt_h, union=int(ucnt.item()),
+                  z=z.cpu().numpy()[:n], sets=sets)
+
+
+def oracle_forward(lay: inputs.Layer, x: np.ndarray, mode: str, tau: float = 0.0, k: int = 0):
+    return oracle.forward(mode, x, lay.w_up, lay.w_down, w_gate=lay.w_gate, lopa_a=lay.lopa_a,
+                          lopa_b=lay.lopa_b, tau=tau, k=k)
+
+
+@dataclasses.dataclass
+class Report:
+    band: int
+    band_flips: int
+    active_mean: float
+    union: int
+    rel_err: float
+    z_err: float
+
+
+def compare(lay: inputs.Layer, x: np.ndarray, mode: str, ref: oracle.Result, got: GpuOut,
+            tol: Optional[float] = None) -> Report:
+    n, f = ref.mask.shape
+    oset = ref.mask.astype(bool)
+    diff = oset ^ got.sets
+    outside = diff & ~ref.band
+    assert not outside.any(), (f"{int(outside.sum())} active-set mismatches outside the band, first at "
+                               f"{np.argwhere(outside)[:5].tolist()}")
+    assert np.array_equal(got.cnt[:n], got.sets.sum(axis=1))
+    un_gpu = int(got.sets.any(axis=0).sum())
+    assert got.union == un_gpu, (got.union, un_gpu)
+    # y against the oracle on the GPU's own set (identical to ref.y when no band flips)
+    if diff.any():
+        y_ref = oracle.forward_with_mask(x, lay.w_up, lay.w_down, ref.g, got.sets.astype(np.uint8))
+    else:
+        y_ref = ref.y
+    scale = float(np.max(np.abs(y_ref))) if y_ref.size else 0.0
+    err = float(np.max(np.abs(got.y - y_ref))) if y_ref.size else 0.0
+    rel = err / scale if scale > 0 else err
+    tol = TOL[lay.dtype] if tol is None else tol
+    assert np.all(np.isfinite(got.y))
+    assert rel <= tol, f"y rel err {rel:.3e} > {tol:.1e}"
+    z_err = float(np.max(np.abs(got.z - ref.z))) if ref.z.size else 0.0
+    rep = Report(band=int(ref.band.sum()), band_flips=int(diff.sum()),
+                 active_mean=float(got.sets.sum(axis=1).mean()), union=got.union, rel_err=rel, z_err=z_err)
+    say(f"    parity: band={rep.band} flips={rep.band_flips} active/token={rep.active_mean:.1f} "
+        f"union={rep.union} y_rel_err={rep.rel_err:.2e} z_max_abs_err={rep.z_err:.2e}")
+    return rep

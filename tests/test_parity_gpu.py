@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every case names itself before it touches the GPU. Workloads follow the
+seeded recipe in activation_sparse_gated_gate_amd/inputs.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_gated_gate_amd import inputs
+from activation_sparse_gated_gate_amd import sffn as S
+from gpu_harness import compare, oracle_forward, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+W = inputs.WORKLOADS
+# The decode kernels accumulate exact bf16 products in fp32, so their error is
+# ~1e-6 of |y|; this guard sits far inside the 2e-2 contract to catch a dropped
+# or doubled channel (each contributes ~1/sqrt(active) of |y|).
+DECODE_GUARD = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    S.lib()
+
+
+def _layer(wl, seed=0, rank=0):
+    return inputs.make_layer(seed, wl.d_model, wl.d_ff, wl.dtype, rank=rank, with_gate=(rank == 0))
+
+
+# ---------------------------------------------------------------------------
+# Workload points
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 8])
+def test_tiny_fp32_threshold(n):
+    wl = W["tiny_swiglu_fp32_d256_f1024"]
+    say(f"case tiny fp32 d=256 F=1024 n={n} tau=1.2816 threshold")
+    lay = _layer(wl)
+    x = inputs.make_x(0, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, "threshold", tau=1.2816)
+    got = run_gpu(lay, x, "threshold", tau=1.2816)
+    compare(lay, x, "threshold", ref, got)
+
+
+@pytest.fixture(scope="module")
+def llama_layer():
+    wl = W["llama7b_ffn_bf16_d4096_f11008"]
+    return _layer(wl), inputs.make_x(0, 1, wl.d_model, wl.dtype)
+
+
+@pytest.mark.parametrize("tau", W["llama7b_ffn_bf16_d4096_f11008"].taus)
+def test_llama7b_threshold_sweep(llama_layer, tau):
+    lay, x = llama_layer
+    say(f"case llama7b bf16 d=4096 F=11008 n=1 tau={tau} threshold")
+    ref = oracle_forward(lay, x, "threshold", tau=tau)
+    got = run_gpu(lay, x, "threshold", tau=tau)
+    rep = compare(lay, x, "threshold", ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
+@pytest.mark.parametrize("rank", W["lopa_gate_bf16_d4096_f11008"].ranks)
+@pytest.mark.parametrize("n", W["lopa_gate_bf16_d4096_f11008"].tokens)
+def test_lopa(rank, n):
+    wl = W["lopa_gate_bf16_d4096_f11008"]
+    say(f"case lopa bf16 d=4096 F=11008 r={rank} n={n} tau=1.2816")
+    lay = _layer(wl, rank=rank)
+    x = inputs.make_x(0, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, "lopa", tau=1.2816)
+    got = run_gpu(lay, x, "lopa", tau=1.2816)
+    rep = compare(lay, x, "lopa", ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
+@pytest.mark.parametrize("k", W["moc_topk_bf16_d2048_f5632"].ks)
+def test_moc_topk_decode(k):
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    say(f"case moc topk bf16 d=2048 F=5632 n=1 K={k}")
+    lay = _layer(wl)
+    x = inputs.make_x(0, 1, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, "topk", k=k)
+    got = run_gpu(lay, x, "topk", k=k)
+    rep = compare(lay, x, "topk", ref, got)
+    assert (got.cnt[:1] == k).all()
+    assert rep.rel_err <= DECODE_GUARD
+
+
+# ---------------------------------------------------------------------------
+# Shapes that span several tiles and ragged tails, every mode and dtype
+# ---------------------------------------------------------------------------
+RAGGED = [(264, 1000), (64, 37), (136, 333), (1024, 2049)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,f", RAGGED)
+@pytest.mark.parametrize("n", [1, 3, 8])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "dense_relu", "dense_silu"])
+def test_ragged_shapes(dtype, d, f, n, mode):
+    say(f"case ragged {dtype} d={d} F={f} n={n} {mode}")
+    lay = inputs.make_layer(3, d, f, dtype)
+    x = inputs.make_x(3, n, d, dtype)
+    k = max(1, f // 5)
+    ref = oracle_forward(lay, x, mode, tau=0.9, k=k)
+    got = run_gpu(lay, x, mode, tau=0.9, k=k, max_tokens=8)
+    rep = compare(lay, x, mode, ref, got)
+    assert rep.rel_err <= (1e-5 if dtype == "f32" else DECODE_GUARD)
+
+
+@pytest.mark.parametrize("rank", [8, 64, 264])
+@pytest.mark.parametrize("n", [1, 5])
+def test_lopa_ragged(rank, n):
+    d, f = 520, 1001
+    say(f"case lopa ragged bf16 d={d} F={f} r={rank} n={n}")
+    lay = inputs.make_layer(4, d, f, "bf16", rank=rank, with_gate=False)
+    x = inputs.make_x(4, n, d, "bf16")
+    ref = oracle_forward(lay, x, "lopa", tau=0.5)
+    got = run_gpu(lay, x, "lopa", tau=0.5, max_tokens=8)
+    compare(lay, x, "lopa", ref, got)
+
+
+# ---------------------------------------------------------------------------
+# Degenerate cases of the method
+# ---------------------------------------------------------------------------
+def test_tau_above_every_preactivation_gives_zero():
+    say("case tau above max z -> y = 0")
+    lay = inputs.make_layer(5, 256, 700, "bf16")
+    x = inputs.make_x(5, 2, 256, "bf16")
+    got = run_gpu(lay, x, "threshold", tau=1e6)
+    assert (got.cnt[:2] == 0).all() and got.union == 0
+    assert np.all(got.y == 0.0)
+
+
+def test_tau_below_every_preactivation_equals_dense():
+    say("case tau below min z == dense")
+    lay = inputs.make_layer(6, 256, 700, "bf16")
+    x = inputs.make_x(6, 2, 256, "bf16")
+    sp = run_gpu(lay, x, "threshold", tau=-1e6)
+    de = run_gpu(lay, x, "dense_relu", tau=-1e6)
+    assert sp.sets.all() and sp.union == 700
+    ref = oracle_forward(lay, x, "dense_relu", tau=-1e6)
+    compare(lay, x, "threshold", ref, sp)
+    np.testing.assert_allclose(sp.y, de.y, rtol=1e-5, atol=1e-5 * np.abs(de.y).max())
+
+
+def test_topk_all_channels_equals_swiglu():
+    say("case topk K=F == dense SiLU")
+    lay = inputs.make_layer(7, 512, 640, "bf16")
+    x = inputs.make_x(7, 3, 512, "bf16")
+    tk = run_gpu(lay, x, "topk", k=640)
+    assert tk.sets.all()
+    ref = oracle_forward(lay, x, "dense_silu")
+    compare(lay, x, "topk", ref, tk)
+
+
+def test_topk_k1_and_ties():
+    say("case topk K=1 and exact ties")
+    d, f = 64, 96
+    lay = inputs.make_layer(8, d, f, "f32")
+    # duplicate gate rows make exact ties between channels 5, 40 and 77
+    lay.w_gate[40] = lay.w_gate[5]
+    lay.w_gate[77] = lay.w_gate[5]
+    x = inputs.make_x(8, 2, d, "f32")
+    for k in (1, 2, 3):
+        ref = oracle_forward(lay, x, "topk", k=k)
+        got = run_gpu(lay, x, "topk", k=k)
+        compare(lay, x, "topk", ref, got, tol=1e-5)
+
+
+def test_exact_dyadic_case_is_bit_exact():
+    """Inputs on a coarse dyadic grid make every fp32 partial sum exact, so the
+    GPU must equal the oracle bit for bit in any summation order."""
+    say("case dyadic exact")
+    rng = np.random.default_rng(9)
+    d, f, n = 32, 80, 3
+    grid = lambda shape: (rng.integers(-2, 3, size=shape) / 4.0).astype(np.float32)  # noqa: E731
+    lay = inputs.Layer(d, f, "f32", 0, grid((f, d)), grid((f, d)), grid((f, d)))
+    x = grid((n, d))
+    for mode, tau in (("threshold", 0.25), ("threshold", 0.0), ("dense_relu", -1.0)):
+        ref = oracle_forward(lay, x, mode, tau=tau)
+        got = run_gpu(lay, x, mode, tau=tau)
+        assert np.array_equal(got.sets, ref.mask.astype(bool))
+        assert np.array_equal(got.y.astype(np.float64), ref.y)
+
+
+def test_zero_tokens_writes_nothing():
+    say("case n=0")
+    ffn = S.SparseFFN(64, 100, 4, "bf16")
+    wt = torch.zeros(100, 64, dtype=torch.int16, device="cuda")
+    w = S.SparseFFN.weights(w_gate=wt, w_up=wt, w_down=wt)
+    xy = torch.full((1, 64), 3.0, device="cuda")
+    S.sffn_forward(ffn.handle, xy.data_ptr(), 0, w, S.SFFN_THRESHOLD, 0.0, 0, xy.data_ptr())
+    torch.cuda.synchronize()
+    assert torch.all(xy == 3.0)
+
+
+def test_repeated_forwards_are_bitwise_deterministic():
+    say("case determinism x20 on llama7b 90%")
+    wl = W["llama7b_ffn_bf16_d4096_f11008"]
+    lay = _layer(wl)
+    x = inputs.make_x(0, 1, wl.d_model, wl.dtype)
+    ffn = S.SparseFFN(wl.d_model, wl.d_ff, 1, "bf16")
+    first = run_gpu(lay, x, "threshold", tau=1.2816, ffn=ffn)
+    for _ in range(3):
+        again = run_gpu(lay, x, "threshold", tau=1.2816, ffn=ffn, repeat=5)
+        assert np.array_equal(first.y.view(np.uint32), again.y.view(np.uint32))
+        assert np.array_equal(first.sets, again.sets)
+
+
+def test_channel_permutation_permutes_the_set():
+    say("case channel permutation")
+    d, f = 256, 512
+    lay = inputs.make_layer(10, d, f, "bf16")
+    x = inputs.make_x(10, 2, d, "bf16")
+    perm = np.random.default_rng(10).permutation(f)
+    plain = run_gpu(lay, x, "threshold", tau=0.8)
+    lay_p = inputs.Layer(d, f, "bf16", 0, lay.w_gate[perm], lay.w_up[perm], lay.w_down[perm])
+    permd = run_gpu(lay_p, x, "threshold", tau=0.8)
+    assert np.array_equal(plain.sets[:, perm], permd.sets)
+    np.testing.assert_allclose(plain.y, permd.y, rtol=0, atol=1e-5 * np.abs(plain.y).max())
+
+
+def test_handle_reuse_across_modes_and_batch_sizes():
+    """One handle and workspace serve forwards of different modes and token
+    counts back to back (the counters in the workspace reset themselves)."""
+    say("case handle reuse")
+    d, f = 512, 1500
+    lay = inputs.make_layer(11, d, f, "bf16")
+    ffn = S.SparseFFN(d, f, 8, "bf16")
+    for n, mode in ((1, "threshold"), (8, "topk"), (3, "dense_relu"), (5, "threshold"), (2, "topk")):
+        x = inputs.make_x(11 + n, n, d, "bf16")
+        ref = oracle_forward(lay, x, mode, tau=1.0, k=100)
+        got = run_gpu(lay, x, mode, tau=1.0, k=100, ffn=ffn)
+        compare(lay, x, mode, ref, got)

@@ -22,6 +22,8 @@
 // Active channels are byte flags act[t][i] with one writer each, so any row
 // partition works without atomics. No kernel waits on another workgroup:
 // cross-workgroup results go through global memory and the next kernel.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "sffn_internal.h"
 
@@ -621,15 +623,23 @@ hipError_t launch_init(sffn_ctx &c, hipStream_t s)
     return hipGetLastError();
 }
 
+// The gate kernel; with profiling events set, they take the kernel's own
+// begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
 template <typename TW, typename TX, int NT, int KIND>
-static void launch_gate(hipStream_t st, int lpr, const TX *xg, int n, int L, const TW *xu, int d, const float *tpart,
-                        int ks, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel, uint8_t *act,
-                        float *hbuf, float *dz)
+static void launch_gate(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
+                        const TW *xu, int d, const float *tpart, int ks, const TW *wg, const TW *wu, int F, int mode,
+                        float tau, float *gsel, uint8_t *act, float *hbuf, float *dz)
 {
     const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
-#define SFFN_G(LP)                                                                                          \
-    hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart, ks, wg, wu, \
-                       F, mode, tau, gsel, act, hbuf, dz)
+#define SFFN_G(LP)                                                                                               \
+    do {                                                                                                         \
+        if (ev0)                                                                                                 \
+            hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
+                                  xu, d, tpart, ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                 \
+        else                                                                                                     \
+            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart,   \
+                               ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                                   \
+    } while (0)
     if (lpr == 64) SFFN_G(64);
     else if (lpr == 32) SFFN_G(32);
     else SFFN_G(16);
@@ -664,26 +674,23 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
         hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(blocks, ks), dim3(256), 0, st, x, n, d,
                            static_cast<const TW *>(a.w.lopa_a), r, chunk, tpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (ev0) hipEventRecord(ev0, st);
         const TW *bt = static_cast<const TW *>(a.w.lopa_b);
         // the gate rows (length r) and the up rows (length d) share the lane
         // groups, sized for the shorter of the two
-        launch_gate<TW, float, NT, SELECT_UP>(st, lpr_for(min(r, d)), nullptr, n, r, x, d, tpart, ks, bt, wu, F,
+        launch_gate<TW, float, NT, SELECT_UP>(st, ev0, ev1, lpr_for(min(r, d)), nullptr, n, r, x, d, tpart, ks, bt, wu, F,
                                               a.mode, a.tau, gsel, act, hbuf, a.debug_z);
     } else {
-        if (ev0) hipEventRecord(ev0, st);
         if (dense)
-            launch_gate<TW, TW, NT, DENSE>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
+            launch_gate<TW, TW, NT, DENSE>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
                                            act, hbuf, a.debug_z);
         else if (a.mode == SFFN_TOPK)
-            launch_gate<TW, TW, NT, KEYS>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
+            launch_gate<TW, TW, NT, KEYS>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
                                           act, hbuf, a.debug_z);
         else
-            launch_gate<TW, TW, NT, SELECT_UP>(st, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau,
+            launch_gate<TW, TW, NT, SELECT_UP>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau,
                                                gsel, act, hbuf, a.debug_z);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev1) hipEventRecord(ev1, st);
 
     // ---- Top-K: select, then the up rows ----
     if (a.mode == SFFN_TOPK) {

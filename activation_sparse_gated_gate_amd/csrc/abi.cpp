@@ -40,14 +40,16 @@ Layout make_layout(const sffn_shape &s)
     };
     L.ctrl = take((size_t)kCtrlInts * 4);
     L.act = take(rows * F);
+    const size_t FP = (F + 7) / 8 * 8;  // bf16 rows padded to 16 bytes
     L.gsel = take(batched ? (ntp * F * 4 > T * F * 2 ? ntp * F * 4 : T * F * 2) : ntp * F * 4);
     L.uidx = take(F * 4);
-    L.hbuf = take(batched ? (F * ntp * 4 > T * F * 2 ? F * ntp * 4 : T * F * 2) : F * ntp * 4);
+    L.hbuf = take(batched ? (F * ntp * 4 > T * FP * 2 ? F * ntp * 4 : T * FP * 2) : F * ntp * 4);
     L.part = take((size_t)kDownGroupsMax * ntp * d * 4);
     L.tpart = take(r ? (size_t)kLopaSplitMax * ntp * r * 4 : 0);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(batched ? T * F * 4 : 0);
     L.ubits = take((size_t)L.words * 4);
+    L.bpart = take(batched && T < 512 ? 8 * T * (F > d ? F : d) * 4 : 0);
     L.total = off;
     return L;
 }

@@ -1,9 +1,546 @@
-// Batched / prefill regime (more than 8 tokens): the union-of-active-channels
-// path on bf16 MFMA. Not built yet: the dispatcher reports it as unsupported.
+// Batched / prefill regime (more than 8 tokens): the union of the tokens'
+// active channels, computed on bf16 MFMA.
+//
+//   1. gate GEMM   Z = X . W_gate^T (fp32 accumulate); epilogue: select from
+//                  the fp32 value, store the gate value G (bf16, 0 when the
+//                  channel is off for that token) and OR the union bitmap
+//                  (Top-K: store the SiLU keys; k_topk selects per token)
+//   2. compaction  union bitmap -> ascending union list U, its size N
+//   3. up GEMM     Uu = X . W_up[U]^T over the gathered rows; epilogue
+//                  H[t][j] = bf16(g[t][U[j]] * Uu[t][j])
+//   4. down GEMM   Y = H . W_down[U, :] (rows gathered by U, fp32 output)
+//
+// A channel that no token selected reads neither W_up nor W_down: the gate is
+// computed first and the other two matrices only for what it kept ("Model
+// Casting and Low-Parameter Gating", Abstract; "Mixture-of-Channels" blog
+// summary, "Dentro il 'mixture'"). Over a batch the kept set is the union of
+// the tokens' sets; the selection itself is per token and taken from the fp32
+// accumulator, never from a rounded value.
+//
+// GEMM tiles use v_mfma_f32_32x32x16_bf16 (operand lane l: row l%32, k
+// 8*(l/32)..+7; accumulator register i: row 8*(i/4) + 4*(l/32) + i%4, column
+// l%32) or v_mfma_f32_16x16x32_bf16 (row l%16, k 8*(l/16)..+7; register i:
+// row 4*(l/16) + i, column l%16). Tiles of A and B are staged in LDS (double
+// buffered, K step 32); B is stored [n][k] in LDS, so the down projection's
+// row-major W_down rows are transposed on their way in. When the grid would be
+// too small, K is split and the fp32 partials are summed in order by a second
+// kernel that applies the same epilogue.
+#include "device_common.h"
 #include "sffn_internal.h"
 
 namespace sffn {
 
-hipError_t launch_batched(sffn_ctx &, const FwdArgs &) { return hipErrorNotSupported; }
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t_;
+
+constexpr int kBK = 32;           // K step of a tile
+constexpr int kPitch = kBK + 8;   // LDS row pitch in bf16 (80 bytes, 16-byte aligned rows)
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+enum EpiKind { EPI_GATE = 0, EPI_UP = 1, EPI_DOWN = 2 };
+
+struct EpiArgs {
+    int kind;
+    int mode;           // sffn_mode (gate)
+    float tau;
+    int T, F, d;
+    uint16_t *G;        // [T][F] bf16 gate values (gate writes, up reads)
+    float *keys;        // [T][F] fp32 SiLU keys (Top-K)
+    const uint8_t *act; // [T][F] Top-K flags (up reads)
+    float *debug_z;     // [T][F] optional
+    uint32_t *ubits;    // union bitmap (gate)
+    const int32_t *uidx;  // union list (up)
+    uint16_t *H;        // [T][hld] bf16 (up writes)
+    int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
+    float *Y;           // [T][d] fp32 (down writes)
+};
+
+// One output element. Returns the union bit for the gate (1 if the channel is
+// kept for this token).
+__device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v)
+{
+    if (e.kind == EPI_GATE) {
+        const size_t o = (size_t)m * e.F + n;
+        if (e.debug_z) e.debug_z[o] = v;
+        if (e.mode == SFFN_TOPK) {
+            e.keys[o] = silu(v);
+            return false;
+        }
+        if (e.mode == SFFN_THRESHOLD) {
+            const bool a = v > e.tau;
+            e.G[o] = a ? f2bf(v - e.tau) : (uint16_t)0;
+            return a;
+        }
+        e.G[o] = f2bf(e.mode == SFFN_DENSE ? fmaxf(v - e.tau, 0.f) : silu(v));
+        return true;
+    }
+    if (e.kind == EPI_UP) {
+        const int i = e.uidx[n];
+        const size_t o = (size_t)m * e.F + i;
+        float g;
+        if (e.mode == SFFN_TOPK) g = e.act[o] ? e.keys[o] : 0.f;
+        else g = bf2f(e.G[o]);
+        e.H[(size_t)m * e.hld + n] = f2bf(g * v);
+        return false;
+    }
+    e.Y[(size_t)m * e.d + n] = v;
+    return false;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM  C[M x N] = A[M x K] . B, A row-major (K contiguous, leading dim lda).
+//   BNN = false: B rows are the N outputs, K contiguous: row n at
+//                B + rowmap(n) * ldb (rowmap = bidx or identity)
+//   BNN = true:  B rows are the K inputs, N contiguous: row k at
+//                B + rowmap(k) * ldb
+// Limits: rows m < M; columns n < nlim; k < klim. nlim / klim come from
+// *ncount when it is set (device-side union size), else from N / K.
+// Split-K: blockIdx.z takes K range [klim z / S, klim (z+1) / S) rounded to
+// the K step; with S > 1 the fp32 tile goes to part[z][m][n].
+// ---------------------------------------------------------------------------
+template <int MF, int TM, int TN, int WM, int WN, bool BNN>
+__global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
+                                                     const bf16_t *__restrict__ B, int ldb,
+                                                     const int32_t *__restrict__ bidx, const int *__restrict__ ncount,
+                                                     int ncount_is_k, float *__restrict__ part, int part_ld,
+                                                     EpiArgs epi)
+{
+    constexpr int NTHR = 64 * WM * WN;
+    constexpr int BM = MF * TM * WM, BN = MF * TN * WN;
+    constexpr int ACC = MF == 32 ? 16 : 4;
+    typedef __attribute__((ext_vector_type(ACC))) float accv;
+    __shared__ __align__(16) bf16_t As[2][BM * kPitch];
+    __shared__ __align__(16) bf16_t Bs[2][BN * kPitch];
+    __shared__ uint32_t ubits_lds[BN / 32 > 0 ? BN / 32 : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    int nlim = N, klim = K;
+    if (ncount) {
+        if (ncount_is_k) klim = min(K, *ncount);
+        else nlim = min(N, *ncount);
+    }
+    if (n0 >= nlim || m0 >= M) return;  // tile beyond the device-side size (uniform)
+    const int S = gridDim.z;
+    int kb = 0, ke = klim;
+    if (S > 1) {
+        const int steps = (klim + kBK - 1) / kBK;
+        kb = (int)(((long long)steps * blockIdx.z) / S) * kBK;
+        ke = min(klim, (int)(((long long)steps * (blockIdx.z + 1)) / S) * kBK);
+    }
+
+    // ---- global -> register staging ----
+    constexpr int ACH = BM * (kBK / 8);                  // 16-byte chunks of an A tile
+    constexpr int BCH = BN * (kBK / 8);                  // and of a B tile
+    constexpr int AIT = (ACH + NTHR - 1) / NTHR, BIT = (BCH + NTHR - 1) / NTHR;
+    uint4 ra[AIT], rb[BIT];
+    // B row pointers are fixed for the NT form (rows = output columns)
+    auto load = [&](int k) {
+#pragma unroll
+        for (int it = 0; it < AIT; ++it) {
+            const int c = tid + it * NTHR;
+            const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+            ra[it] = make_uint4(0, 0, 0, 0);
+            if (c < ACH && m0 + row < M && k + kc < ke)
+                ra[it] = *reinterpret_cast<const uint4 *>(A + (size_t)(m0 + row) * lda + k + kc);
+        }
+#pragma unroll
+        for (int it = 0; it < BIT; ++it) {
+            const int c = tid + it * NTHR;
+            rb[it] = make_uint4(0, 0, 0, 0);
+            if (c >= BCH) continue;
+            if constexpr (!BNN) {
+                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+                const int n = n0 + row;
+                if (n < nlim && k + kc < ke) {
+                    const int src = bidx ? bidx[n] : n;
+                    rb[it] = *reinterpret_cast<const uint4 *>(B + (size_t)src * ldb + k + kc);
+                }
+            } else {
+                const int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+                const int kk = k + krow;
+                if (kk < ke && n0 + nc < nlim) {
+                    const int src = bidx ? bidx[kk] : kk;
+                    rb[it] = *reinterpret_cast<const uint4 *>(B + (size_t)src * ldb + n0 + nc);
+                }
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < AIT; ++it) {
+            const int c = tid + it * NTHR;
+            if (c < ACH) {
+                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+                *reinterpret_cast<uint4 *>(&As[buf][row * kPitch + kc]) = ra[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < BIT; ++it) {
+            const int c = tid + it * NTHR;
+            if (c >= BCH) continue;
+            if constexpr (!BNN) {
+                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+                *reinterpret_cast<uint4 *>(&Bs[buf][row * kPitch + kc]) = rb[it];
+            } else {
+                // transpose: 8 consecutive columns of one k row -> column-major in LDS
+                const int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+                const uint32_t w[4] = {rb[it].x, rb[it].y, rb[it].z, rb[it].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    Bs[buf][(nc + e) * kPitch + krow] = (bf16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
+            }
+        }
+    };
+
+    accv acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < ACC; ++r) acc[i][j][r] = 0.f;
+
+    const int arow = wm * MF * TM, bcol = wn * MF * TN;
+    const int fr = lane % MF, fk = (lane / MF) * 8;
+    int buf = 0;
+    if (kb < ke) {
+        load(kb);
+        store(0);
+    }
+    __syncthreads();
+    for (int k = kb; k < ke; k += kBK) {
+        const bool more = k + kBK < ke;
+        if (more) load(k + kBK);
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += (MF == 32 ? 16 : 32)) {
+            bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t *>(&As[buf][(arow + i * MF + fr) * kPitch + kk + fk]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&Bs[buf][(bcol + j * MF + fr) * kPitch + kk + fk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    if constexpr (MF == 32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                }
+        }
+        if (more) store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+
+    // ---- epilogue ----
+    if (S > 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
+                    const int m = m0 + arow + i * MF + rr, n = n0 + bcol + j * MF + lane % MF;
+                    if (m < M && n < nlim)
+                        part[((size_t)blockIdx.z * M + m) * part_ld + n] = acc[i][j][r];
+                }
+        return;
+    }
+    const bool gate_union = epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD;
+    if (gate_union) {
+        for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
+        __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        bool col_any = false;
+        const int n = n0 + bcol + j * MF + lane % MF;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < ACC; ++r) {
+                const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
+                const int m = m0 + arow + i * MF + rr;
+                if (m < M && n < nlim) col_any |= epilogue(epi, m, n, acc[i][j][r]);
+                else if (epi.kind == EPI_UP && m < M && n < ((nlim + 7) & ~7))
+                    epi.H[(size_t)m * epi.hld + n] = 0;  // pad: the down GEMM reads H in 8-wide chunks
+            }
+        if (gate_union && col_any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
+    }
+    if (gate_union) {
+        __syncthreads();
+        for (int w = tid; w < BN / 32; w += NTHR)
+            if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
+    }
+}
+
+// Sum the split-K partials in order and apply the epilogue (gate: also the
+// union bits, one atomic per word and block).
+__global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict__ part, int S, int M, int N,
+                                                         int part_ld, const int *__restrict__ ncount, EpiArgs epi)
+{
+    __shared__ uint32_t ub[8];
+    const int nlim = ncount ? min(N, *ncount) : N;
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    if (threadIdx.x < 8) ub[threadIdx.x] = 0;
+    __syncthreads();
+    if (n < nlim) {
+        float v = 0.f;
+        for (int s = 0; s < S; ++s) v += part[((size_t)s * M + m) * part_ld + n];
+        if (epilogue(epi, m, n, v) && epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD)
+            atomicOr(&ub[threadIdx.x / 32], 1u << (n & 31));
+    } else if (epi.kind == EPI_UP && n < ((nlim + 7) & ~7)) {
+        epi.H[(size_t)m * epi.hld + n] = 0;
+    }
+    __syncthreads();
+    if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
+        atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
+}
+
+// Top-K union: bitmap word w = OR over tokens of the flags of channels
+// 32w..32w+31.
+__global__ __launch_bounds__(256) void k_union_from_flags(const uint8_t *__restrict__ act, int T, int F, int W,
+                                                          uint32_t *__restrict__ ubits)
+{
+    const int w = blockIdx.x * 256 + threadIdx.x;
+    if (w >= W) return;
+    uint32_t u = 0;
+    for (int t = 0; t < T; ++t)
+        for (int b = 0; b < 32; ++b) {
+            const int i = w * 32 + b;
+            if (i < F && act[(size_t)t * F + i]) u |= 1u << b;
+        }
+    ubits[w] = u;
+}
+
+// Union bitmap -> ascending list and its size (one workgroup); clears the
+// bitmap for the next forward. Dense modes: every channel.
+__global__ __launch_bounds__(1024) void k_union_compact(uint32_t *__restrict__ ubits, int W, int F, int dense,
+                                                        int32_t *__restrict__ uidx, int *__restrict__ ncount)
+{
+    __shared__ int scan_scratch[16];
+    const int tid = threadIdx.x;
+    const int seg = (W + blockDim.x - 1) / blockDim.x;
+    const int w0 = min(W, tid * seg), w1 = min(W, w0 + seg);
+    int local = 0;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t u = ubits[w];
+        if (dense) u = (F - w * 32 >= 32) ? 0xffffffffu : ((1u << (F - w * 32)) - 1u);
+        local += __popc(u);
+    }
+    const int incl = block_incl_scan(local, scan_scratch);
+    int pos = incl - local;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t u = ubits[w];
+        if (dense) u = (F - w * 32 >= 32) ? 0xffffffffu : ((1u << (F - w * 32)) - 1u);
+        while (u) {
+            const int b = __ffs(u) - 1;
+            u &= u - 1;
+            uidx[pos++] = w * 32 + b;
+        }
+        ubits[w] = 0;
+    }
+    if (tid == blockDim.x - 1) *ncount = incl;
+}
+
+// Optional outputs for a batch: token t's ascending active list and count;
+// block T writes the union size.
+__global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict__ G, const uint8_t *__restrict__ act,
+                                                      int T, int F, int mode, const int *__restrict__ ncount,
+                                                      int32_t *__restrict__ active_idx,
+                                                      int32_t *__restrict__ active_cnt, int32_t *__restrict__ union_cnt)
+{
+    __shared__ int scan_scratch[4];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    if (t == T) {
+        if (tid == 0 && union_cnt) *union_cnt = *ncount;
+        return;
+    }
+    const bool dense = mode == SFFN_DENSE || mode == SFFN_DENSE_SILU;
+    auto on = [&](int i) -> bool {
+        if (dense) return true;
+        if (mode == SFFN_TOPK) return act[(size_t)t * F + i] != 0;
+        return G[(size_t)t * F + i] != 0;
+    };
+    const int seg = (F + blockDim.x - 1) / blockDim.x;
+    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+    int local = 0;
+    for (int i = i0; i < i1; ++i) local += on(i);
+    const int incl = block_incl_scan(local, scan_scratch);
+    int pos = incl - local;
+    if (active_idx)
+        for (int i = i0; i < i1; ++i)
+            if (on(i)) active_idx[(size_t)t * F + pos++] = i;
+    if (tid == blockDim.x - 1 && active_cnt) active_cnt[t] = incl;
+}
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+struct Cfg {
+    int mf, tm, tn, wm, wn;
+    int bm() const { return mf * tm * wm; }
+    int bn() const { return mf * tn * wn; }
+    int threads() const { return 64 * wm * wn; }
+};
+
+// Tile shapes by batch size (M = tokens).
+static Cfg cfg_for(int M)
+{
+    if (M >= 512) return {32, 4, 2, 2, 4};  // 256 x 256, 8 wavefronts
+    if (M >= 128) return {32, 2, 2, 4, 1};  // 256 x 64
+    if (M > 32) return {16, 1, 2, 4, 2};    // 64 x 64
+    return {16, 1, 2, 2, 2};                // 32 x 64
+}
+
+template <int MF, int TM, int TN, int WM, int WN, bool BNN>
+static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
+                        int ldb, const int32_t *bidx, const int *ncount, int ncount_is_k, float *part, int part_ld,
+                        const EpiArgs &e)
+{
+    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B, ldb,
+                       bidx, ncount, ncount_is_k, part, part_ld, e);
+}
+
+template <bool BNN>
+static void dispatch_mfma(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
+                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
+                          int pld, const EpiArgs &e)
+{
+    if (c.mf == 32 && c.tm == 4)
+        launch_mfma<32, 4, 2, 2, 4, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else if (c.mf == 32)
+        launch_mfma<32, 2, 2, 4, 1, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else if (c.wm == 4)
+        launch_mfma<16, 1, 2, 4, 2, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else
+        launch_mfma<16, 1, 2, 2, 2, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+}
+
+// Split K so that the grid has at least ~2 workgroups per CU (at most 8
+// splits, and K steps of at least 8 tiles per split).
+static int split_for(const sffn_ctx &c, long long tiles, int K, int M)
+{
+    int S = 1;
+    if (M >= 512) return 1;  // large batches have tiles enough, and no partial buffer
+    while (S < 8 && tiles * S < 2LL * c.n_cu && (K / kBK) / (2 * S) >= 8) S *= 2;
+    return S;
+}
+
+hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
+{
+    const sffn_shape &S = c.shape;
+    const int T = a.n, d = S.d_model, F = S.d_ff, W = c.L.words;
+    char *ws = c.ws;
+    uint16_t *G = reinterpret_cast<uint16_t *>(ws + c.L.gsel);
+    uint16_t *H = reinterpret_cast<uint16_t *>(ws + c.L.hbuf);
+    float *keys = reinterpret_cast<float *>(ws + c.L.keys);
+    uint8_t *act = reinterpret_cast<uint8_t *>(ws + c.L.act);
+    uint32_t *ubits = reinterpret_cast<uint32_t *>(ws + c.L.ubits);
+    int32_t *uidx = reinterpret_cast<int32_t *>(ws + c.L.uidx);
+    int *ncount = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionSize;
+    float *part = reinterpret_cast<float *>(ws + c.L.bpart);
+    const bf16_t *x = static_cast<const bf16_t *>(a.x);
+    const bf16_t *wg = static_cast<const bf16_t *>(a.w.w_gate);
+    const bf16_t *wu = static_cast<const bf16_t *>(a.w.w_up);
+    const bf16_t *wdn = static_cast<const bf16_t *>(a.w.w_down);
+    hipStream_t st = a.stream;
+    const bool dense = a.mode == SFFN_DENSE || a.mode == SFFN_DENSE_SILU;
+    hipEvent_t ev0 = static_cast<hipEvent_t>(c.ev_start), ev1 = static_cast<hipEvent_t>(c.ev_stop);
+    hipError_t e;
+
+    EpiArgs ep{};
+    ep.mode = a.mode;
+    ep.tau = a.tau;
+    ep.T = T;
+    ep.F = F;
+    ep.d = d;
+    ep.G = G;
+    ep.keys = keys;
+    ep.act = act;
+    ep.debug_z = a.debug_z;
+    ep.ubits = ubits;
+    ep.uidx = uidx;
+    ep.H = H;
+    ep.hld = (F + 7) / 8 * 8;
+    ep.Y = a.y;
+
+    const Cfg cf = cfg_for(T);
+    const int mt = (T + cf.bm() - 1) / cf.bm();
+
+    // ---- 1. gate GEMM ----
+    {
+        ep.kind = EPI_GATE;
+        const int nt = (F + cf.bn() - 1) / cf.bn();
+        const int sk = split_for(c, (long long)mt * nt, d, T);
+        if (ev0) hipEventRecord(ev0, st);
+        dispatch_mfma<false>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1) {
+            hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
+                               nullptr, ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (ev1) hipEventRecord(ev1, st);
+    }
+    // ---- Top-K: per-token select, then the union of the flags ----
+    if (a.mode == SFFN_TOPK) {
+        if ((e = launch_topk(keys, T, F, a.k, act, st)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_union_from_flags, dim3((W + 255) / 256), dim3(256), 0, st, act, T, F, W, ubits);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // ---- 2. union list ----
+    hipLaunchKernelGGL(k_union_compact, dim3(1), dim3(1024), 0, st, ubits, W, F, dense ? 1 : 0, uidx, ncount);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // ---- 3. up GEMM over the union rows ----
+    {
+        ep.kind = EPI_UP;
+        const int nt = (F + cf.bn() - 1) / cf.bn();
+        const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
+        dispatch_mfma<false>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1) {
+            hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
+                               ncount, ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    // ---- 4. down GEMM, K = union ----
+    {
+        ep.kind = EPI_DOWN;
+        const int nt = (d + cf.bn() - 1) / cf.bn();
+        const int sk = split_for(c, (long long)mt * nt, F / 2, T);
+        dispatch_mfma<true>(cf, dim3(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1) {
+            hipLaunchKernelGGL(k_splitk_epilogue, dim3((d + 255) / 256, T), dim3(256), 0, st, part, sk, T, d, d,
+                               nullptr, ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    // ---- optional outputs ----
+    if (a.active_idx || a.active_cnt || a.union_cnt) {
+        hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount, a.active_idx,
+                           a.active_cnt, a.union_cnt);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 }  // namespace sffn

@@ -620,6 +620,13 @@ bool decode_fits(const sffn_ctx &c, int, int) { return down_lds(c) <= c.lds_max;
 hipError_t launch_init(sffn_ctx &c, hipStream_t s)
 {
     hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
+    hipLaunchKernelGGL(k_zero_ints, dim3(16), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ubits), c.L.words);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *keys, int T, int F, int K, uint8_t *act, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_topk, dim3(T), dim3(1024), 0, st, keys, F, K, act);
     return hipGetLastError();
 }
 
@@ -694,8 +701,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
 
     // ---- Top-K: select, then the up rows ----
     if (a.mode == SFFN_TOPK) {
-        hipLaunchKernelGGL(k_topk, dim3(n), dim3(1024), 0, st, gsel, F, a.k, act);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_topk(gsel, n, F, a.k, act, st)) != hipSuccess) return e;
         const int lpr = lpr_for(d);
         const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
         if (lpr == 64)

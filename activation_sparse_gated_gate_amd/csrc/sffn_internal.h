@@ -17,6 +17,7 @@ constexpr int kDecodeMaxTokens = 8;
 // Control block (int32 slots) at the start of the workspace, zeroed by the
 // first forward on a handle; reserved for counters of the batched path.
 constexpr int kCtrlInts = 1024;
+constexpr int kCtrlUnionSize = 0;    // batched path: size of the union list
 
 constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
@@ -38,6 +39,7 @@ struct Layout {
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
+    size_t bpart;     // batched split-K partials: fp32 [8][T][max(d_ff, d_model)] when T < 512
     size_t total;
 };
 
@@ -78,6 +80,8 @@ hipError_t device_setup(sffn_ctx &c);
 hipError_t launch_init(sffn_ctx &c, hipStream_t s);
 hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a);
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
+// Per-token Top-K selection (decode.hip), shared by both regimes.
+hipError_t launch_topk(const float *keys, int T, int F, int K, uint8_t *act, hipStream_t st);
 // Host-side check that the decode kernels' LDS needs fit; false -> unsupported.
 bool decode_fits(const sffn_ctx &c, int n, int mode);
 }  // namespace sffn

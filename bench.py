@@ -22,6 +22,10 @@ Prints one JSON line. Besides the contract fields it carries:
                 W_down rows, y) over the step time, against 8 TB/s;
   sweep         every tau of the workload: sparsity, step time, tokens/s, HBM
                 fraction, and the speedup over this library's dense forward;
+  points        the other workloads (tiny fp32 layer, LoPA ranks, Mixture-of-Channels
+                Top-K at 1/16/64 tokens, 70B-shaped prefill at 256/2048 tokens):
+                tokens/s, HBM fraction on touched bytes or MFMA fraction on the
+                path's FLOPs, and the speedup over this library's dense forward;
   cpu_baseline  the CPU oracle (plain C, fp64, one thread) on a bounded sample.
 """
 from __future__ import annotations
@@ -38,6 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+PEAK_BF16 = 2.5e15  # MI355X dense bf16 MFMA, FLOP/s
+MALL_BYTES = 256 << 20  # Infinity Cache
 WORKLOAD = "llama7b_ffn_bf16_d4096_f11008"
 HEADLINE_TAU = 1.2816
 METRIC = "sparse FFN layer tokens/s + % HBM roofline at batch 1, 50–99% sparsity"
@@ -51,7 +57,8 @@ def parse():
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--copies", type=int, default=8, help="layer copies rotated to defeat the Infinity Cache")
-    p.add_argument("--no-sweep", action="store_true", help="headline point only")
+    p.add_argument("--no-sweep", action="store_true", help="headline point only (no tau sweep, no other workloads)")
+    p.add_argument("--no-points", action="store_true", help="skip the other workloads' points")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0 = skip)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
@@ -79,6 +86,149 @@ def read_traffic():
         return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def timed(ffn, xt, wlist, mode, y, steps, warmup, tau=0.0, k=0):
+    """Seconds per forward, rotating over the weight copies in wlist."""
+    import torch
+
+    L = len(wlist)
+    for s in range(warmup):
+        ffn.forward(xt, wlist[s % L], mode, y, tau=tau, k=k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ffn.forward(xt, wlist[s % L], mode, y, tau=tau, k=k)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def copies_for(layer_bytes, touched_bytes):
+    """Layer copies so that > 2x the Infinity Cache is read between reuses."""
+    return max(2, min(32, int(math.ceil(2 * MALL_BYTES / max(1, touched_bytes))) + 1))
+
+
+def measure_points(args, dev, S, inputs, np, torch):
+    W = inputs.WORKLOADS
+    out = []
+    es = 2
+
+    def union(ffn, xt, w, mode, y, tau=0.0, k=0):
+        u = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ffn.forward(xt, w, mode, y, tau=tau, k=k, union_cnt=u)
+        torch.cuda.synchronize()
+        return int(u.item())
+
+    def replicate(tensors, L):
+        return [tensors] + [{k: (v.clone() if v is not None else None) for k, v in tensors.items()}
+                            for _ in range(L - 1)]
+
+    # dense denominators on the Llama-7B-shaped layer (also the LoPA shape)
+    wl2 = W["llama7b_ffn_bf16_d4096_f11008"]
+    d2, f2 = wl2.d_model, wl2.d_ff
+    lay2 = inputs.make_layer(0, d2, f2, "bf16")
+    t2 = {"w_gate": dev(lay2.w_gate), "w_up": dev(lay2.w_up), "w_down": dev(lay2.w_down)}
+    c2 = replicate(t2, 4)
+    w2 = [S.SparseFFN.weights(**c) for c in c2]
+    dense2 = {}
+    for n in (1, 4):
+        ffn = S.SparseFFN(d2, f2, n, "bf16")
+        xt = dev(inputs.make_x(0, n, d2, "bf16"))
+        y = torch.empty(n, d2, dtype=torch.float32, device="cuda")
+        dense2[n] = timed(ffn, xt, w2, "dense_relu", y, 100, 10)
+    del c2, w2, t2
+
+    # tiny fp32 layer: cache-resident, latency and tokens/s only
+    wl = W["tiny_swiglu_fp32_d256_f1024"]
+    lay = inputs.make_layer(0, wl.d_model, wl.d_ff, "f32")
+    tt = {"w_gate": torch.from_numpy(lay.w_gate).cuda(), "w_up": torch.from_numpy(lay.w_up).cuda(),
+          "w_down": torch.from_numpy(lay.w_down).cuda()}
+    w = [S.SparseFFN.weights(**tt)]
+    for n in wl.tokens:
+        ffn = S.SparseFFN(wl.d_model, wl.d_ff, n, "f32")
+        xt = torch.from_numpy(inputs.make_x(0, n, wl.d_model, "f32")).cuda()
+        y = torch.empty(n, wl.d_model, dtype=torch.float32, device="cuda")
+        na = union(ffn, xt, w[0], "threshold", y, tau=1.2816)
+        sp = timed(ffn, xt, w, "threshold", y, 300, 30, tau=1.2816)
+        de = timed(ffn, xt, w, "dense_relu", y, 300, 30)
+        out.append({"workload": wl.name, "tokens": n, "mode": "threshold", "tau": 1.2816, "union": na,
+                    "us_per_step": round(sp * 1e6, 2), "tokens_per_s": round(n / sp, 1),
+                    "speedup_vs_dense": round(de / sp, 3), "note": "cache-resident (3 MB): no HBM fraction"})
+
+    # LoPA low-rank gate
+    wl = W["lopa_gate_bf16_d4096_f11008"]
+    d, f = wl.d_model, wl.d_ff
+    for r in wl.ranks:
+        lay = inputs.make_layer(0, d, f, "bf16", rank=r, with_gate=False)
+        base = {"lopa_a": dev(lay.lopa_a), "lopa_b": dev(lay.lopa_b), "w_up": dev(lay.w_up),
+                "w_down": dev(lay.w_down)}
+        for n in wl.tokens:
+            ffn = S.SparseFFN(d, f, n, "bf16", rank=r)
+            xt = dev(inputs.make_x(0, n, d, "bf16"))
+            y = torch.empty(n, d, dtype=torch.float32, device="cuda")
+            na = union(ffn, xt, S.SparseFFN.weights(**base), "lopa", y, tau=1.2816)
+            touched = n * d * es + r * d * es + f * r * es + 2 * na * d * es + n * d * 4
+            cl = replicate(base, copies_for(0, touched))
+            wlist = [S.SparseFFN.weights(**c) for c in cl]
+            sp = timed(ffn, xt, wlist, "lopa", y, 200, 20, tau=1.2816)
+            out.append({"workload": wl.name, "tokens": n, "mode": "lopa", "rank": r, "tau": 1.2816, "union": na,
+                        "us_per_step": round(sp * 1e6, 2), "tokens_per_s": round(n / sp, 1),
+                        "touched_bytes": touched, "hbm_frac": round(touched / sp / PEAK_HBM, 4),
+                        "speedup_vs_dense": round(dense2[n] / sp, 3), "layer_copies": len(wlist)})
+            del cl, wlist
+        del base
+        torch.cuda.empty_cache()
+
+    # Mixture-of-Channels Top-K (decode and batched)
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    d, f = wl.d_model, wl.d_ff
+    lay = inputs.make_layer(0, d, f, "bf16")
+    base = {"w_gate": dev(lay.w_gate), "w_up": dev(lay.w_up), "w_down": dev(lay.w_down)}
+    cl = replicate(base, copies_for(0, 3 * f * d * es // 2))
+    wlist = [S.SparseFFN.weights(**c) for c in cl]
+    for n in wl.tokens:
+        ffn = S.SparseFFN(d, f, n, "bf16")
+        xt = dev(inputs.make_x(0, n, d, "bf16"))
+        y = torch.empty(n, d, dtype=torch.float32, device="cuda")
+        de = timed(ffn, xt, wlist, "dense_silu", y, 100, 10)
+        for k in wl.ks:
+            na = union(ffn, xt, wlist[0], "topk", y, k=k)
+            touched = n * d * es + f * d * es + 2 * na * d * es + n * d * 4
+            sp = timed(ffn, xt, wlist, "topk", y, 200, 20, k=k)
+            out.append({"workload": wl.name, "tokens": n, "mode": "topk", "k": k, "union": na,
+                        "union_frac": round(na / f, 4), "us_per_step": round(sp * 1e6, 2),
+                        "tokens_per_s": round(n / sp, 1), "touched_bytes": touched,
+                        "hbm_frac": round(touched / sp / PEAK_HBM, 4), "speedup_vs_dense": round(de / sp, 3),
+                        "layer_copies": len(wlist)})
+    del cl, wlist, base
+    torch.cuda.empty_cache()
+
+    # 70B-shaped prefill layer on the MFMA union path
+    wl = W["prefill70b_ffn_bf16_d8192_f28672"]
+    d, f = wl.d_model, wl.d_ff
+    lay = inputs.make_layer(0, d, f, "bf16")
+    base = {"w_gate": dev(lay.w_gate), "w_up": dev(lay.w_up), "w_down": dev(lay.w_down)}
+    del lay
+    wlist = [S.SparseFFN.weights(**c) for c in replicate(base, 2)]
+    tau = wl.taus[0]
+    for n in wl.tokens:
+        ffn = S.SparseFFN(d, f, n, "bf16")
+        xt = dev(inputs.make_x(0, n, d, "bf16", correlated=True))
+        y = torch.empty(n, d, dtype=torch.float32, device="cuda")
+        na = union(ffn, xt, wlist[0], "threshold", y, tau=tau)
+        steps = 20 if n >= 1024 else 50
+        sp = timed(ffn, xt, wlist, "threshold", y, steps, 5, tau=tau)
+        de = timed(ffn, xt, wlist, "dense_relu", y, max(5, steps // 2), 3)
+        flops = 2 * n * d * (f + 2 * na)
+        out.append({"workload": wl.name, "tokens": n, "mode": "threshold", "tau": tau, "union": na,
+                    "union_frac": round(na / f, 4), "us_per_step": round(sp * 1e6, 2),
+                    "tokens_per_s": round(n / sp, 1), "flops": flops,
+                    "tflops": round(flops / sp / 1e12, 1), "mfma_frac": round(flops / sp / PEAK_BF16, 4),
+                    "dense_us_per_step": round(de * 1e6, 2), "speedup_vs_dense": round(de / sp, 3),
+                    "flop_ratio_vs_dense": round(3 * f / (f + 2 * na), 3)})
+    del wlist, base
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -194,6 +344,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # ---- the other workloads ----
+    pts = []
+    n_copies = len(weights)
+    if not args.no_sweep and not args.no_points:
+        del weights, copies, base
+        torch.cuda.empty_cache()
+        pts = measure_points(args, dev, S, inputs, np, torch)
+
     # ---- CPU oracle baseline (bounded sample) ----
     cpu = None
     if args.cpu_seconds > 0:
@@ -226,7 +384,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) token, N(0,1/d_in) weights, random init)",
         "config": {"workload": WORKLOAD, "d_model": d, "d_ff": f, "tokens": n, "mode": "threshold",
-                   "tau": HEADLINE_TAU, "sparsity": round(1 - n_act / f, 4), "layer_copies": len(weights)},
+                   "tau": HEADLINE_TAU, "sparsity": round(1 - n_act / f, 4), "layer_copies": n_copies},
         "roofline": roofline,
         "step_roofline": step_roofline,
         "ms_per_step_with_kernel_events": round(ev_sec * 1e3, 5),
@@ -234,6 +392,7 @@ def main():
         "dense_ms_per_step": round(dense_sec * 1e3, 5),
         "speedup_vs_dense": round(dense_sec / sec, 3),
         "sweep": sweep,
+        "points": pts,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -107,7 +107,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
 // Split-K: blockIdx.z takes K range [klim z / S, klim (z+1) / S) rounded to
 // the K step; with S > 1 the fp32 tile goes to part[z][m][n].
 // ---------------------------------------------------------------------------
-template <int MF, int TM, int TN, int WM, int WN, bool BNN>
+template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK>
 __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
                                                      const bf16_t *__restrict__ B, int ldb,
                                                      const int32_t *__restrict__ bidx, const int *__restrict__ ncount,
@@ -261,31 +261,91 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
                 }
         return;
     }
-    const bool gate_union = epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD;
-    if (gate_union) {
-        for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
+    // Element (i, j, r) of this lane: row rowof(i, r), column colof(j). The
+    // epilogue kind is a template parameter and the mode branch sits outside
+    // the unrolled element loops, so the accumulators stay in AGPRs.
+    auto rowof = [&](int i, int r) {
+        const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
+        return m0 + arow + i * MF + rr;
+    };
+    auto colof = [&](int j) { return n0 + bcol + j * MF + lane % MF; };
+    if constexpr (EK == EPI_DOWN) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= nlim) continue;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m < M) epi.Y[(size_t)m * epi.d + n] = acc[i][j][r];
+                }
+        }
+    } else if constexpr (EK == EPI_UP) {
+        const int padlim = (nlim + 7) & ~7;
+        const bool topk = epi.mode == SFFN_TOPK;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= padlim) continue;
+            const bool live = n < nlim;
+            const int src = live ? epi.uidx[n] : 0;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m >= M) continue;
+                    uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
+                    if (live) {
+                        const size_t o = (size_t)m * epi.F + src;
+                        const float g = topk ? (epi.act[o] ? epi.keys[o] : 0.f) : bf2f(epi.G[o]);
+                        h = f2bf(g * acc[i][j][r]);
+                    }
+                    epi.H[(size_t)m * epi.hld + n] = h;
+                }
+        }
+    } else {
+        const int mode = epi.mode;
+        const float tau = epi.tau;
+        float *dz = epi.debug_z;
+        if (mode == SFFN_THRESHOLD)
+            for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
         __syncthreads();
-    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        bool col_any = false;
-        const int n = n0 + bcol + j * MF + lane % MF;
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= nlim) continue;
+            bool any = false;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int r = 0; r < ACC; ++r) {
-                const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
-                const int m = m0 + arow + i * MF + rr;
-                if (m < M && n < nlim) col_any |= epilogue(epi, m, n, acc[i][j][r]);
-                else if (epi.kind == EPI_UP && m < M && n < ((nlim + 7) & ~7))
-                    epi.H[(size_t)m * epi.hld + n] = 0;  // pad: the down GEMM reads H in 8-wide chunks
-            }
-        if (gate_union && col_any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
-    }
-    if (gate_union) {
-        __syncthreads();
-        for (int w = tid; w < BN / 32; w += NTHR)
-            if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m >= M) continue;
+                    const float v = acc[i][j][r];
+                    const size_t o = (size_t)m * epi.F + n;
+                    if (dz) dz[o] = v;
+                    if (mode == SFFN_THRESHOLD) {
+                        const bool a = v > tau;
+                        epi.G[o] = a ? f2bf(v - tau) : (uint16_t)0;
+                        any |= a;
+                    } else if (mode == SFFN_TOPK) {
+                        epi.keys[o] = silu(v);
+                    } else if (mode == SFFN_DENSE) {
+                        epi.G[o] = f2bf(fmaxf(v - tau, 0.f));
+                    } else {
+                        epi.G[o] = f2bf(silu(v));
+                    }
+                }
+            if (any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
+        }
+        if (mode == SFFN_THRESHOLD) {
+            __syncthreads();
+            for (int w = tid; w < BN / 32; w += NTHR)
+                if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
+        }
     }
 }
 
@@ -313,20 +373,18 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
 }
 
-// Top-K union: bitmap word w = OR over tokens of the flags of channels
-// 32w..32w+31.
+// Top-K union: one thread per channel ORs the tokens' flags (consecutive
+// threads read consecutive bytes); a ballot packs 64 channels into two words.
 __global__ __launch_bounds__(256) void k_union_from_flags(const uint8_t *__restrict__ act, int T, int F, int W,
                                                           uint32_t *__restrict__ ubits)
 {
-    const int w = blockIdx.x * 256 + threadIdx.x;
-    if (w >= W) return;
-    uint32_t u = 0;
-    for (int t = 0; t < T; ++t)
-        for (int b = 0; b < 32; ++b) {
-            const int i = w * 32 + b;
-            if (i < F && act[(size_t)t * F + i]) u |= 1u << b;
-        }
-    ubits[w] = u;
+    const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
+    bool any = false;
+    if (i < F)
+        for (int t = 0; t < T && !any; ++t) any = act[(size_t)t * F + i] != 0;
+    const unsigned long long m = __ballot(any);
+    const int w = i >> 5;
+    if ((lane & 31) == 0 && w < W) ubits[w] = (uint32_t)(m >> (lane & 32));
 }
 
 // Union bitmap -> ascending list and its size (one workgroup); clears the
@@ -403,34 +461,34 @@ struct Cfg {
 // Tile shapes by batch size (M = tokens).
 static Cfg cfg_for(int M)
 {
-    if (M >= 512) return {32, 4, 2, 2, 4};  // 256 x 256, 8 wavefronts
+    if (M >= 512) return {32, 4, 2, 2, 2};  // 256 x 128, 4 wavefronts
     if (M >= 128) return {32, 2, 2, 4, 1};  // 256 x 64
     if (M > 32) return {16, 1, 2, 4, 2};    // 64 x 64
     return {16, 1, 2, 2, 2};                // 32 x 64
 }
 
-template <int MF, int TM, int TN, int WM, int WN, bool BNN>
+template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK>
 static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
                         int ldb, const int32_t *bidx, const int *ncount, int ncount_is_k, float *part, int part_ld,
                         const EpiArgs &e)
 {
-    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B, ldb,
-                       bidx, ncount, ncount_is_k, part, part_ld, e);
+    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN, EK>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
+                       ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
 }
 
-template <bool BNN>
+template <bool BNN, int EK>
 static void dispatch_mfma(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
                           const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
                           int pld, const EpiArgs &e)
 {
     if (c.mf == 32 && c.tm == 4)
-        launch_mfma<32, 4, 2, 2, 4, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+        launch_mfma<32, 4, 2, 2, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
     else if (c.mf == 32)
-        launch_mfma<32, 2, 2, 4, 1, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+        launch_mfma<32, 2, 2, 4, 1, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
     else if (c.wm == 4)
-        launch_mfma<16, 1, 2, 4, 2, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+        launch_mfma<16, 1, 2, 4, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
     else
-        launch_mfma<16, 1, 2, 2, 2, BNN>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+        launch_mfma<16, 1, 2, 2, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
 }
 
 // Split K so that the grid has at least ~2 workgroups per CU (at most 8
@@ -490,7 +548,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
-        dispatch_mfma<false>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
+        dispatch_mfma<false, EPI_GATE>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
@@ -502,7 +560,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- Top-K: per-token select, then the union of the flags ----
     if (a.mode == SFFN_TOPK) {
         if ((e = launch_topk(keys, T, F, a.k, act, st)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_union_from_flags, dim3((W + 255) / 256), dim3(256), 0, st, act, T, F, W, ubits);
+        hipLaunchKernelGGL(k_union_from_flags, dim3((F + 255) / 256), dim3(256), 0, st, act, T, F, W, ubits);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // ---- 2. union list ----
@@ -513,7 +571,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_UP;
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-        dispatch_mfma<false>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
+        dispatch_mfma<false, EPI_UP>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
@@ -526,7 +584,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_DOWN;
         const int nt = (d + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt, F / 2, T);
-        dispatch_mfma<true>(cf, dim3(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
+        dispatch_mfma<true, EPI_DOWN>(cf, dim3(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((d + 255) / 256, T), dim3(256), 0, st, part, sk, T, d, d,

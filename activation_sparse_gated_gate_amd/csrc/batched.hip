@@ -107,7 +107,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
 // Split-K: blockIdx.z takes K range [klim z / S, klim (z+1) / S) rounded to
 // the K step; with S > 1 the fp32 tile goes to part[z][m][n].
 // ---------------------------------------------------------------------------
-template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK>
+template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
 __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
                                                      const bf16_t *__restrict__ B, int ldb,
                                                      const int32_t *__restrict__ bidx, const int *__restrict__ ncount,
@@ -124,7 +124,15 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    // Tile order: workgroups are dealt round-robin over the 8 XCDs. Block b
+    // runs on XCD b % 8; on each XCD the M tiles of one N tile follow each
+    // other, so a weight panel is fetched into that XCD's L2 once and used by
+    // every M tile, and the N tiles are interleaved over the XCDs.
+    const int MT = (M + BM - 1) / BM, NTT = (N + BN - 1) / BN;
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int mi = j % MT, ni = (j / MT) * 8 + xcd;
+    if (ni >= NTT) return;
+    const int m0 = mi * BM, n0 = ni * BN;
     int nlim = N, klim = K;
     if (ncount) {
         if (ncount_is_k) klim = min(K, *ncount);
@@ -305,14 +313,19 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
                     }
                     epi.H[(size_t)m * epi.hld + n] = h;
                 }
+            // keep each sub-tile's gathered G loads from being hoisted over the
+            // whole tile (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        const int mode = epi.mode;
+        // gate; GM is the mode, a template parameter so each instantiation
+        // carries one straight-line epilogue
         const float tau = epi.tau;
         float *dz = epi.debug_z;
-        if (mode == SFFN_THRESHOLD)
+        if constexpr (GM == SFFN_THRESHOLD) {
             for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
-        __syncthreads();
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = colof(j);
@@ -327,21 +340,22 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
                     const float v = acc[i][j][r];
                     const size_t o = (size_t)m * epi.F + n;
                     if (dz) dz[o] = v;
-                    if (mode == SFFN_THRESHOLD) {
+                    if constexpr (GM == SFFN_THRESHOLD) {
                         const bool a = v > tau;
                         epi.G[o] = a ? f2bf(v - tau) : (uint16_t)0;
                         any |= a;
-                    } else if (mode == SFFN_TOPK) {
+                    } else if constexpr (GM == SFFN_TOPK) {
                         epi.keys[o] = silu(v);
-                    } else if (mode == SFFN_DENSE) {
+                    } else if constexpr (GM == SFFN_DENSE) {
                         epi.G[o] = f2bf(fmaxf(v - tau, 0.f));
                     } else {
                         epi.G[o] = f2bf(silu(v));
                     }
                 }
-            if (any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
+            if constexpr (GM == SFFN_THRESHOLD)
+                if (any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
         }
-        if (mode == SFFN_THRESHOLD) {
+        if constexpr (GM == SFFN_THRESHOLD) {
             __syncthreads();
             for (int w = tid; w < BN / 32; w += NTHR)
                 if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
@@ -461,19 +475,34 @@ struct Cfg {
 // Tile shapes by batch size (M = tokens).
 static Cfg cfg_for(int M)
 {
-    if (M >= 512) return {32, 4, 2, 2, 2};  // 256 x 128, 4 wavefronts
+    if (M >= 512) return {32, 4, 2, 2, 2};  // 256 x 128, 4 wavefronts of 128 x 64
     if (M >= 128) return {32, 2, 2, 4, 1};  // 256 x 64
     if (M > 32) return {16, 1, 2, 4, 2};    // 64 x 64
     return {16, 1, 2, 2, 2};                // 32 x 64
 }
 
-template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK>
+template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
 static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
                         int ldb, const int32_t *bidx, const int *ncount, int ncount_is_k, float *part, int part_ld,
                         const EpiArgs &e)
 {
-    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN, EK>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
+    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
                        ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
+}
+
+template <bool BNN, int EK, int GM>
+static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
+                         const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
+                         int pld, const EpiArgs &e)
+{
+    if (c.mf == 32 && c.tm == 4)
+        launch_mfma<32, 4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else if (c.mf == 32)
+        launch_mfma<32, 2, 2, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else if (c.wm == 4)
+        launch_mfma<16, 1, 2, 4, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    else
+        launch_mfma<16, 1, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
 }
 
 template <bool BNN, int EK>
@@ -481,15 +510,29 @@ static void dispatch_mfma(const Cfg &c, dim3 grid, hipStream_t st, int M, int N,
                           const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
                           int pld, const EpiArgs &e)
 {
-    if (c.mf == 32 && c.tm == 4)
-        launch_mfma<32, 4, 2, 2, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else if (c.mf == 32)
-        launch_mfma<32, 2, 2, 4, 1, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else if (c.wm == 4)
-        launch_mfma<16, 1, 2, 4, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else
-        launch_mfma<16, 1, 2, 2, 2, BNN, EK>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    if constexpr (EK != EPI_GATE) {
+        dispatch_cfg<BNN, EK, 0>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+    } else {
+        switch (e.mode) {
+        case SFFN_THRESHOLD:
+            dispatch_cfg<BNN, EK, SFFN_THRESHOLD>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            break;
+        case SFFN_TOPK:
+            dispatch_cfg<BNN, EK, SFFN_TOPK>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            break;
+        case SFFN_DENSE:
+            dispatch_cfg<BNN, EK, SFFN_DENSE>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            break;
+        default:
+            dispatch_cfg<BNN, EK, SFFN_DENSE_SILU>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld,
+                                                   e);
+            break;
+        }
+    }
 }
+
+// One block per (M tile, N tile), padded so the N tiles split evenly over 8 XCDs.
+static dim3 tile_grid(int nt, int mt, int sk) { return dim3(8 * ((nt + 7) / 8) * mt, 1, sk); }
 
 // Split K so that the grid has at least ~2 workgroups per CU (at most 8
 // splits, and K steps of at least 8 tiles per split).
@@ -548,7 +591,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
-        dispatch_mfma<false, EPI_GATE>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
+        dispatch_mfma<false, EPI_GATE>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
@@ -571,7 +614,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_UP;
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-        dispatch_mfma<false, EPI_UP>(cf, dim3(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
+        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
@@ -584,7 +627,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_DOWN;
         const int nt = (d + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt, F / 2, T);
-        dispatch_mfma<true, EPI_DOWN>(cf, dim3(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
+        dispatch_mfma<true, EPI_DOWN>(cf, tile_grid(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((d + 255) / 256, T), dim3(256), 0, st, part, sk, T, d, d,

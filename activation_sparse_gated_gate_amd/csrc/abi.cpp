@@ -50,6 +50,7 @@ Layout make_layout(const sffn_shape &s)
     L.keys = take(batched ? T * F * 4 : 0);
     L.ubits = take((size_t)L.words * 4);
     L.bpart = take(batched && T < 512 ? 8 * T * (F > d ? F : d) * 4 : 0);
+    L.thr = take(rows * 8);
     L.total = off;
     return L;
 }

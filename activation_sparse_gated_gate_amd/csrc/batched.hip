@@ -4,7 +4,8 @@
 //   1. gate GEMM   Z = X . W_gate^T (fp32 accumulate); epilogue: select from
 //                  the fp32 value, store the gate value G (bf16, 0 when the
 //                  channel is off for that token) and OR the union bitmap
-//                  (Top-K: store the SiLU keys; k_topk selects per token)
+//                  (Top-K: store the SiLU keys; each token's K-th key is
+//                  found next and the flags follow from it)
 //   2. compaction  union bitmap -> ascending union list U, its size N
 //   3. up GEMM     Uu = X . W_up[U]^T over the gathered rows; epilogue
 //                  H[t][j] = bf16(g[t][U[j]] * Uu[t][j])
@@ -387,20 +388,6 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
 }
 
-// Top-K union: one thread per channel ORs the tokens' flags (consecutive
-// threads read consecutive bytes); a ballot packs 64 channels into two words.
-__global__ __launch_bounds__(256) void k_union_from_flags(const uint8_t *__restrict__ act, int T, int F, int W,
-                                                          uint32_t *__restrict__ ubits)
-{
-    const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
-    bool any = false;
-    if (i < F)
-        for (int t = 0; t < T && !any; ++t) any = act[(size_t)t * F + i] != 0;
-    const unsigned long long m = __ballot(any);
-    const int w = i >> 5;
-    if ((lane & 31) == 0 && w < W) ubits[w] = (uint32_t)(m >> (lane & 32));
-}
-
 // Union bitmap -> ascending list and its size (one workgroup); clears the
 // bitmap for the next forward. Dense modes: every channel.
 __global__ __launch_bounds__(1024) void k_union_compact(uint32_t *__restrict__ ubits, int W, int F, int dense,
@@ -602,9 +589,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     }
     // ---- Top-K: per-token select, then the union of the flags ----
     if (a.mode == SFFN_TOPK) {
-        if ((e = launch_topk(keys, T, F, a.k, act, st)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k_union_from_flags, dim3((F + 255) / 256), dim3(256), 0, st, act, T, F, W, ubits);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        int2 *thr = reinterpret_cast<int2 *>(c.ws + c.L.thr);
+        if ((e = launch_topk_thr(keys, T, F, a.k, thr, st)) != hipSuccess) return e;
+        if ((e = launch_topk_flags(keys, T, F, thr, act, W, ubits, st)) != hipSuccess) return e;
     }
     // ---- 2. union list ----
     hipLaunchKernelGGL(k_union_compact, dim3(1), dim3(1024), 0, st, ubits, W, F, dense ? 1 : 0, uidx, ncount);

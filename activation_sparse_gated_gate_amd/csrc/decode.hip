@@ -6,8 +6,8 @@
 //              rows of the channels just found active -> k_down -> k_reduce
 //   LoPA       k_lopa_xa (x.A partials) -> k_gate<SELECT_UP> on B with t = x.A
 //              -> k_down -> k_reduce
-//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk (radix select) -> k_up
-//              -> k_down -> k_reduce
+//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (radix select of each
+//              token's K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
 //              -> k_reduce
 //
@@ -220,88 +220,15 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 }
 
 // ---------------------------------------------------------------------------
-// Per-token Top-K of the SiLU keys (one workgroup per token). MSD radix select
-// over order-preserving 32-bit keys, 8 bits per pass with a 256-bin LDS
-// histogram (radix k-selection as in Alabi, Blanchard, Gordon & Steinbach,
-// "Fast k-Selection Algorithms for Graphics Processing Units", 2012). After
-// four passes the K-th largest key is known exactly, together with how many
-// keys equal to it still belong to the set; those are taken in ascending
-// channel order, so ties go to the lower index. Output: act[t][i].
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_topk(const float *__restrict__ gsel, int F, int K,
-                                               uint8_t *__restrict__ act)
-{
-    __shared__ int hist[256];
-    __shared__ int sh_digit, sh_need;
-    __shared__ int scan_scratch[16];
-    const int t = blockIdx.x;
-    const float *s = gsel + (size_t)t * F;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    uint32_t prefix = 0, pmask = 0;
-    int need = K;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < F; i += blockDim.x) {
-            const uint32_t key = f2key(s[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane l owns bins 255-4l .. 252-4l (descending)
-            int c[4], tot = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c[e] = hist[255 - (lane * 4 + e)];
-                tot += c[e];
-            }
-            int run = wave_incl_scan(tot) - tot;  // keys in higher bins
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (run < need && need <= run + c[e]) {
-                    sh_digit = 255 - (lane * 4 + e);
-                    sh_need = need - run;
-                }
-                run += c[e];
-            }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)sh_digit << shift;
-        pmask |= 0xffu << shift;
-        need = sh_need;
-        __syncthreads();
-    }
-    const uint32_t kth = prefix;
-
-    // Contiguous channel segments per thread: the count of keys equal to the
-    // K-th before a channel is an exclusive block scan.
-    const int seg = (F + blockDim.x - 1) / blockDim.x;
-    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
-    int eq_local = 0;
-    for (int i = i0; i < i1; ++i) eq_local += f2key(s[i]) == kth;
-    int eq_before = block_incl_scan(eq_local, scan_scratch) - eq_local;
-    uint8_t *a = act + (size_t)t * F;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = f2key(s[i]);
-        uint8_t on = key > kth;
-        if (key == kth) {
-            on = eq_before < need;
-            ++eq_before;
-        }
-        a[i] = on;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Up kernel (Top-K): the gate kernel's row partition; each lane group reads
-// the W_up rows of its channels that some token selected.
-// h[i][t] = g[t][i] * (x_t . W_up[i]) if token t selected i, else 0.
+// Up kernel (Top-K): the gate kernel's row partition. Each lane group applies
+// the tokens' Top-K thresholds to its channels' keys (topk_on), writes the
+// flags act[t][i], and reads the W_up rows of its channels that some token
+// selected. h[i][t] = g[t][i] * (x_t . W_up[i]) if token t selected i, else 0.
 // ---------------------------------------------------------------------------
 template <typename TW, int NT, int LPR>
 __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int d,
                                             const TW *__restrict__ wu, int F,
-                                            const uint8_t *__restrict__ act,
+                                            const int2 *__restrict__ thr, uint8_t *__restrict__ act,
                                             const float *__restrict__ gsel, float *__restrict__ hbuf)
 {
     constexpr int SUB = 64 / LPR;
@@ -317,9 +244,15 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             gv[r][t] = 0.f;
-            if (r < nv && t < n && act[(size_t)t * F + row0 + r]) {
-                gv[r][t] = gsel[(size_t)t * F + row0 + r];
-                amask |= 1u << r;
+            if (r < nv && t < n) {
+                const size_t o = (size_t)t * F + row0 + r;
+                const float g = gsel[o];
+                const bool on = topk_on(g, row0 + r, thr[t]);
+                if (li == ((r * NT + t) & (LPR - 1))) act[o] = on;
+                if (on) {
+                    gv[r][t] = g;
+                    amask |= 1u << r;
+                }
             }
         }
     if (__ballot(amask != 0) == 0) return;
@@ -624,12 +557,6 @@ hipError_t launch_init(sffn_ctx &c, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *keys, int T, int F, int K, uint8_t *act, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_topk, dim3(T), dim3(1024), 0, st, keys, F, K, act);
-    return hipGetLastError();
-}
-
 // The gate kernel; with profiling events set, they take the kernel's own
 // begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
 template <typename TW, typename TX, int NT, int KIND>
@@ -701,15 +628,16 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
 
     // ---- Top-K: select, then the up rows ----
     if (a.mode == SFFN_TOPK) {
-        if ((e = launch_topk(gsel, n, F, a.k, act, st)) != hipSuccess) return e;
+        int2 *thr = reinterpret_cast<int2 *>(ws + c.L.thr);
+        if ((e = launch_topk_thr(gsel, n, F, a.k, thr, st)) != hipSuccess) return e;
         const int lpr = lpr_for(d);
         const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
         if (lpr == 64)
-            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
         else if (lpr == 32)
-            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
         else
-            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 

@@ -174,6 +174,15 @@ __device__ __forceinline__ uint32_t f2key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Top-K membership of channel i from its token's threshold: thr.x is the
+// K-th largest key (f2key encoding), thr.y the last channel index kept among
+// the keys equal to it.
+__device__ __forceinline__ bool topk_on(float g, int i, int2 thr)
+{
+    const uint32_t k = f2key(g), kth = (uint32_t)thr.x;
+    return k > kth || (k == kth && i <= thr.y);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
 }  // namespace sffn

@@ -40,6 +40,7 @@ struct Layout {
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
     size_t bpart;     // batched split-K partials: fp32 [8][T][max(d_ff, d_model)] when T < 512
+    size_t thr;       // Top-K: int2 [max(ntp, max_tokens)] per-token K-th key and tie cutoff
     size_t total;
 };
 
@@ -80,8 +81,12 @@ hipError_t device_setup(sffn_ctx &c);
 hipError_t launch_init(sffn_ctx &c, hipStream_t s);
 hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a);
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
-// Per-token Top-K selection (decode.hip), shared by both regimes.
-hipError_t launch_topk(const float *keys, int T, int F, int K, uint8_t *act, hipStream_t st);
+// Per-token Top-K (topk.hip), shared by both regimes: thr[t] = {K-th largest
+// key in the f2key encoding, last channel index kept among keys equal to it}.
+hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st);
+// Batched: act[t][i] from the thresholds, and the union bitmap words.
+hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, uint8_t *act, int W, uint32_t *ubits,
+                             hipStream_t st);
 // Host-side check that the decode kernels' LDS needs fit; false -> unsupported.
 bool decode_fits(const sffn_ctx &c, int n, int mode);
 }  // namespace sffn

@@ -168,6 +168,90 @@ def test_topk_k1_and_ties():
         compare(lay, x, "topk", ref, got, tol=1e-5)
 
 
+@pytest.mark.parametrize("f", [4096, 4097, 8193, 16385, 32769])
+@pytest.mark.parametrize("n", [3, 12])
+def test_topk_select_sizes_and_tie_cut(f, n):
+    """Every register-cache size of the per-token select (and the uncached one
+    above 16384 channels), decode (n=3) and batched (n=12), with K chosen so
+    that token 0's cut falls inside a group of four exactly tied channels
+    spread over the channel range."""
+    d = 64
+    say(f"case topk select F={f} n={n} ties cut inside the tied group")
+    lay = inputs.make_layer(30, d, f, "bf16")
+    tied = [7, f // 3, f // 2, f - 1]
+    for i in tied[1:]:
+        lay.w_gate[i] = lay.w_gate[tied[0]]
+    x = inputs.make_x(30, n, d, "bf16")
+    z0 = oracle_forward(lay, x[:1], "dense_silu").z[0]
+    key0 = z0 / (1.0 + np.exp(-z0))
+    k = int((key0 > key0[tied[0]]).sum()) + 2
+    ref = oracle_forward(lay, x, "topk", k=k)
+    got = run_gpu(lay, x, "topk", k=k, max_tokens=n)
+    compare(lay, x, "topk", ref, got)
+    assert (got.cnt[:n] == k).all()
+    for t in range(n):
+        sel = got.sets[t, tied]
+        assert not np.any(~sel[:-1] & sel[1:]), f"token {t}: tied channels kept out of index order"
+    others = np.ones(f, dtype=bool)
+    others[tied] = False
+    if np.min(np.abs(key0[others] - key0[tied[0]])) > 1e-6:
+        assert list(got.sets[0, tied]) == [True, True, False, False]
+
+
+@pytest.mark.parametrize("n", [2, 12])
+def test_topk_select_crowded_bin(n):
+    """More than 64 keys in the bin of the K-th value: 100 exactly tied
+    channels at the cut, and a layer whose one huge gate row stretches the
+    key range so that nearly every key shares the lowest value bin."""
+    d, f = 64, 3000
+    lay = inputs.make_layer(31, d, f, "bf16")
+    tied = list(range(11, 3000, 29))[:100]
+    for i in tied[1:]:
+        lay.w_gate[i] = lay.w_gate[tied[0]]
+    x = inputs.make_x(31, n, d, "bf16")
+    z0 = oracle_forward(lay, x[:1], "dense_silu").z[0]
+    key0 = z0 / (1.0 + np.exp(-z0))
+    k = int((key0 > key0[tied[0]]).sum()) + 37
+    say(f"case topk crowded bin: 100 ties, n={n} K={k}")
+    ref = oracle_forward(lay, x, "topk", k=k)
+    got = run_gpu(lay, x, "topk", k=k, max_tokens=n)
+    compare(lay, x, "topk", ref, got)
+    assert (got.cnt[:n] == k).all()
+    for t in range(n):
+        sel = got.sets[t, tied]
+        assert not np.any(~sel[:-1] & sel[1:]), f"token {t}: tied channels kept out of index order"
+    others = np.ones(f, dtype=bool)
+    others[tied] = False
+    if np.min(np.abs(key0[others] - key0[tied[0]])) > 1e-6:
+        assert int(got.sets[0, tied].sum()) == 37
+
+    lay = inputs.make_layer(32, d, f, "bf16")
+    lay.w_gate[5] = inputs.bf16_bits(inputs.bf16_bits_to_f32(lay.w_gate[5]) * 4096.0)
+    x = inputs.make_x(32, n, d, "bf16")
+    say(f"case topk crowded bin: one huge gate row, n={n}")
+    ref = oracle_forward(lay, x, "topk", k=400)
+    got = run_gpu(lay, x, "topk", k=400, max_tokens=n)
+    compare(lay, x, "topk", ref, got)
+    assert (got.cnt[:n] == 400).all()
+
+
+@pytest.mark.parametrize("n", [2, 12])
+def test_topk_all_keys_equal_takes_first_k(n):
+    """A zero gate makes every key SiLU(0) = 0: the set is channels 0..K-1."""
+    d, f, k = 64, 700, 123
+    say(f"case topk all keys equal n={n}")
+    lay = inputs.make_layer(33, d, f, "bf16")
+    lay.w_gate[:] = 0
+    x = inputs.make_x(33, n, d, "bf16")
+    ref = oracle_forward(lay, x, "topk", k=k)
+    got = run_gpu(lay, x, "topk", k=k, max_tokens=n)
+    expect = np.zeros(f, dtype=bool)
+    expect[:k] = True
+    assert np.array_equal(ref.mask.astype(bool), np.tile(expect, (n, 1)))
+    assert np.array_equal(got.sets, np.tile(expect, (n, 1)))
+    compare(lay, x, "topk", ref, got)
+
+
 def test_exact_dyadic_case_is_bit_exact():
     """Inputs on a coarse dyadic grid make every fp32 partial sum exact, so the
     GPU must equal the oracle bit for bit in any summation order."""

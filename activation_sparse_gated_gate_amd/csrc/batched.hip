@@ -26,6 +26,8 @@
 // row-major W_down rows are transposed on their way in. When the grid would be
 // too small, K is split and the fp32 partials are summed in order by a second
 // kernel that applies the same epilogue.
+#include <type_traits>
+
 #include "device_common.h"
 #include "sffn_internal.h"
 
@@ -96,6 +98,124 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
     e.Y[(size_t)m * e.d + n] = v;
     return false;
 }
+
+// ---------------------------------------------------------------------------
+// Tile epilogue shared by the GEMM kernels. Element (i, j, r) of lane `lane`
+// is row rowof(i, r), column colof(j) of the tile (MFMA accumulator layout).
+// With S > 1 (split K) the fp32 tile goes to part[z][m][n]; otherwise the
+// epilogue kind EK (and for the gate the mode GM) is applied. Both are
+// template parameters, and the branches sit outside the unrolled element
+// loops, so the accumulators stay in registers.
+// ---------------------------------------------------------------------------
+template <int MF, int TM, int TN, int NTHR, int BN, int EK, int GM, typename AccT>
+__device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int lane, int m0, int n0, int arow,
+                                              int bcol, int M, int nlim, int S, float *__restrict__ part,
+                                              int part_ld, const EpiArgs &epi, uint32_t *ubits_lds)
+{
+    constexpr int ACC = MF == 32 ? 16 : 4;
+    auto rowof = [&](int i, int r) {
+        const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
+        return m0 + arow + i * MF + rr;
+    };
+    auto colof = [&](int j) { return n0 + bcol + j * MF + lane % MF; };
+    if (S > 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r), n = colof(j);
+                    if (m < M && n < nlim) part[((size_t)blockIdx.z * M + m) * part_ld + n] = acc[i][j][r];
+                }
+        return;
+    }
+    if constexpr (EK == EPI_DOWN) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= nlim) continue;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m < M) epi.Y[(size_t)m * epi.d + n] = acc[i][j][r];
+                }
+        }
+    } else if constexpr (EK == EPI_UP) {
+        const int padlim = (nlim + 7) & ~7;
+        const bool topk = epi.mode == SFFN_TOPK;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= padlim) continue;
+            const bool live = n < nlim;
+            const int src = live ? epi.uidx[n] : 0;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m >= M) continue;
+                    uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
+                    if (live) {
+                        const size_t o = (size_t)m * epi.F + src;
+                        const float g = topk ? (epi.act[o] ? epi.keys[o] : 0.f) : bf2f(epi.G[o]);
+                        h = f2bf(g * acc[i][j][r]);
+                    }
+                    epi.H[(size_t)m * epi.hld + n] = h;
+                }
+            // keep each sub-tile's gathered G loads from being hoisted over the
+            // whole tile (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        // gate; GM is the mode, a template parameter so each instantiation
+        // carries one straight-line epilogue
+        const float tau = epi.tau;
+        float *dz = epi.debug_z;
+        if constexpr (GM == SFFN_THRESHOLD) {
+            for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= nlim) continue;
+            bool any = false;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m >= M) continue;
+                    const float v = acc[i][j][r];
+                    const size_t o = (size_t)m * epi.F + n;
+                    if (dz) dz[o] = v;
+                    if constexpr (GM == SFFN_THRESHOLD) {
+                        const bool a = v > tau;
+                        epi.G[o] = a ? f2bf(v - tau) : (uint16_t)0;
+                        any |= a;
+                    } else if constexpr (GM == SFFN_TOPK) {
+                        epi.keys[o] = silu(v);
+                    } else if constexpr (GM == SFFN_DENSE) {
+                        epi.G[o] = f2bf(fmaxf(v - tau, 0.f));
+                    } else {
+                        epi.G[o] = f2bf(silu(v));
+                    }
+                }
+            if constexpr (GM == SFFN_THRESHOLD)
+                if (any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
+        }
+        if constexpr (GM == SFFN_THRESHOLD) {
+            __syncthreads();
+            for (int w = tid; w < BN / 32; w += NTHR)
+                if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
+        }
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // GEMM  C[M x N] = A[M x K] . B, A row-major (K contiguous, leading dim lda).
@@ -255,113 +375,173 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
         buf ^= 1;
     }
 
-    // ---- epilogue ----
+    tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
+                                                ubits_lds);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined GEMM for the NT form (gate and up: both operands K-contiguous,
+// B rows gathered through bidx), v_mfma_f32_32x32x16_bf16, K step 64.
+//
+// Tiles move from global memory straight into LDS (16-byte direct-to-LDS
+// loads, no register staging) through a ring of three stages, so the loads
+// of K steps i+1 and i+2 are in flight while step i is multiplied. Each
+// stage is its own LDS array and the stage index is a compile-time constant
+// (the main loop is unrolled by three): the compiler can then tell the
+// stages apart and does not wait for every outstanding load before each LDS
+// read; the only waits are the explicit ones below.
+//
+// One load instruction of a wavefront fills 8 tile rows (1 KB): lane l
+// takes row l/8 and K chunk (l%8) ^ (l/8) of it, written to slot l%8, so LDS
+// element (row, 8p) holds chunk p ^ (row % 8). A fragment read (32 rows, one
+// chunk) then touches 8 distinct slots per 8 consecutive rows: no bank
+// conflicts. Chunks outside the operands (rows past M or past the union, K
+// past the end) are loaded from a zero block.
+// ---------------------------------------------------------------------------
+constexpr int kDmaBK = 64;
+
+// Source of the chunks outside the operands; never written.
+static __device__ __align__(16) uint4 g_zero16[1] = {};
+
+typedef __attribute__((address_space(1))) const void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
+
+// s_waitcnt: at most N vector-memory operations of this wavefront in flight,
+// and every LDS operation done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int TM, int TN, int WM, int WN, int EK, int GM>
+__global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
+                                                         const bf16_t *__restrict__ B, int ldb,
+                                                         const int32_t *__restrict__ bidx,
+                                                         const int *__restrict__ ncount, float *__restrict__ part,
+                                                         int part_ld, EpiArgs epi)
+{
+    constexpr int MF = 32, NW = WM * WN, NTHR = 64 * NW;
+    constexpr int BM = MF * TM * WM, BN = MF * TN * WN, BK = kDmaBK;
+    constexpr int APW = BM * (BK / 8) / 64 / NW;  // load instructions per wavefront and stage: A
+    constexpr int BPW = BN * (BK / 8) / 64 / NW;  // and B
+    constexpr int LPS = APW + BPW;
+    static_assert(APW * 64 * NW == BM * (BK / 8) && BPW * 64 * NW == BN * (BK / 8), "rows split over wavefronts");
+    typedef __attribute__((ext_vector_type(16))) float accv;
+    __shared__ __align__(16) bf16_t As0[BM * BK], As1[BM * BK], As2[BM * BK];
+    __shared__ __align__(16) bf16_t Bs0[BN * BK], Bs1[BN * BK], Bs2[BN * BK];
+    __shared__ uint32_t ubits_lds[BN / 32];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    // XCD-aware tile order (as k_mfma): the M tiles of one N tile run on one XCD
+    const int MT = (M + BM - 1) / BM, NTT = (N + BN - 1) / BN;
+    const int xcd = blockIdx.x % 8, jt = blockIdx.x / 8;
+    const int mi = jt % MT, ni = (jt / MT) * 8 + xcd;
+    if (ni >= NTT) return;
+    const int m0 = mi * BM, n0 = ni * BN;
+    const int nlim = ncount ? min(N, *ncount) : N;
+    if (n0 >= nlim || m0 >= M) return;
+    const int S = gridDim.z;
+    int kb = 0, ke = K;
     if (S > 1) {
+        const int steps = (K + BK - 1) / BK;
+        kb = (int)(((long long)steps * blockIdx.z) / S) * BK;
+        ke = min(K, (int)(((long long)steps * (blockIdx.z + 1)) / S) * BK);
+    }
+    const int nsteps = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+
+    // per-lane sources of this wavefront's load instructions
+    const int lr = lane >> 3, lc = ((lane & 7) ^ lr) * 8;
+    const bf16_t *asrc[APW];
+    const bf16_t *bsrc[BPW];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < APW; ++j) {
+        const int m = m0 + (wave * APW + j) * 8 + lr;
+        asrc[j] = m < M ? A + (size_t)m * lda + lc : nullptr;
+    }
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+        const int n = n0 + (wave * BPW + j) * 8 + lr;
+        bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + lc : nullptr;
+    }
+    const bf16_t *zero = reinterpret_cast<const bf16_t *>(g_zero16);
+
+    auto issue = [&](auto stage, int step) {
+        constexpr int SI = decltype(stage)::value;
+        bf16_t *la = SI == 0 ? As0 : SI == 1 ? As1 : As2;
+        bf16_t *lb = SI == 0 ? Bs0 : SI == 1 ? Bs1 : Bs2;
+        const int k = kb + step * BK;
+        const bool kin = k + lc < ke;
+#pragma unroll
+        for (int j = 0; j < APW; ++j) {
+            const bf16_t *src = (asrc[j] && kin) ? asrc[j] + k : zero;
+            __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(la + (wave * APW + j) * 512), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            const bf16_t *src = (bsrc[j] && kin) ? bsrc[j] + k : zero;
+            __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(lb + (wave * BPW + j) * 512), 16, 0, 0);
+        }
+    };
+
+    accv acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int arow = wm * MF * TM, bcol = wn * MF * TN;
+    auto compute = [&](auto stage) {
+        constexpr int SI = decltype(stage)::value;
+        const bf16_t *sa = SI == 0 ? As0 : SI == 1 ? As1 : As2;
+        const bf16_t *sb = SI == 0 ? Bs0 : SI == 1 ? Bs1 : Bs2;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int sw = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8;
+            bf16x8_t af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (arow + i * MF + (lane & 31)) * BK + sw);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (bcol + j * MF + (lane & 31)) * BK + sw);
 #pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
-                    const int m = m0 + arow + i * MF + rr, n = n0 + bcol + j * MF + lane % MF;
-                    if (m < M && n < nlim)
-                        part[((size_t)blockIdx.z * M + m) * part_ld + n] = acc[i][j][r];
-                }
-        return;
-    }
-    // Element (i, j, r) of this lane: row rowof(i, r), column colof(j). The
-    // epilogue kind is a template parameter and the mode branch sits outside
-    // the unrolled element loops, so the accumulators stay in AGPRs.
-    auto rowof = [&](int i, int r) {
-        const int rr = MF == 32 ? (r / 4) * 8 + (lane / 32) * 4 + (r % 4) : (lane / 16) * 4 + r;
-        return m0 + arow + i * MF + rr;
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
     };
-    auto colof = [&](int j) { return n0 + bcol + j * MF + lane % MF; };
-    if constexpr (EK == EPI_DOWN) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = colof(j);
-            if (n >= nlim) continue;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m < M) epi.Y[(size_t)m * epi.d + n] = acc[i][j][r];
-                }
-        }
-    } else if constexpr (EK == EPI_UP) {
-        const int padlim = (nlim + 7) & ~7;
-        const bool topk = epi.mode == SFFN_TOPK;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = colof(j);
-            if (n >= padlim) continue;
-            const bool live = n < nlim;
-            const int src = live ? epi.uidx[n] : 0;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m >= M) continue;
-                    uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
-                    if (live) {
-                        const size_t o = (size_t)m * epi.F + src;
-                        const float g = topk ? (epi.act[o] ? epi.keys[o] : 0.f) : bf2f(epi.G[o]);
-                        h = f2bf(g * acc[i][j][r]);
-                    }
-                    epi.H[(size_t)m * epi.hld + n] = h;
-                }
-            // keep each sub-tile's gathered G loads from being hoisted over the
-            // whole tile (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-        // gate; GM is the mode, a template parameter so each instantiation
-        // carries one straight-line epilogue
-        const float tau = epi.tau;
-        float *dz = epi.debug_z;
-        if constexpr (GM == SFFN_THRESHOLD) {
-            for (int w = tid; w < BN / 32; w += NTHR) ubits_lds[w] = 0;
-            __syncthreads();
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = colof(j);
-            if (n >= nlim) continue;
-            bool any = false;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m >= M) continue;
-                    const float v = acc[i][j][r];
-                    const size_t o = (size_t)m * epi.F + n;
-                    if (dz) dz[o] = v;
-                    if constexpr (GM == SFFN_THRESHOLD) {
-                        const bool a = v > tau;
-                        epi.G[o] = a ? f2bf(v - tau) : (uint16_t)0;
-                        any |= a;
-                    } else if constexpr (GM == SFFN_TOPK) {
-                        epi.keys[o] = silu(v);
-                    } else if constexpr (GM == SFFN_DENSE) {
-                        epi.G[o] = f2bf(fmaxf(v - tau, 0.f));
-                    } else {
-                        epi.G[o] = f2bf(silu(v));
-                    }
-                }
-            if constexpr (GM == SFFN_THRESHOLD)
-                if (any) atomicOr(&ubits_lds[(bcol + j * MF + lane % MF) / 32], 1u << (n & 31));
-        }
-        if constexpr (GM == SFFN_THRESHOLD) {
-            __syncthreads();
-            for (int w = tid; w < BN / 32; w += NTHR)
-                if (ubits_lds[w]) atomicOr(&epi.ubits[n0 / 32 + w], ubits_lds[w]);
-        }
+    // K step i: its loads (issued two steps earlier) have landed in every
+    // wavefront once each has waited for all but the next step's loads and
+    // passed the barrier; the barrier also ends every read of the stage that
+    // step i+2 refills (last read in step i-1). Every step issues and waits
+    // the same way: the step count is padded to a multiple of three, and
+    // steps past the end load the zero block (kin is false there), so every
+    // path through the loop has the same loads in flight.
+    auto step = [&](auto stage, int i) {
+        constexpr int SI = decltype(stage)::value;
+        wait_vm_lgkm<LPS>();
+        __builtin_amdgcn_s_barrier();
+        issue(std::integral_constant<int, (SI + 2) % 3>{}, i + 2);
+        compute(stage);
+    };
+    const int nst3 = (nsteps + 2) / 3 * 3;
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    for (int i = 0; i < nst3; i += 3) {
+        step(std::integral_constant<int, 0>{}, i);
+        step(std::integral_constant<int, 1>{}, i + 1);
+        step(std::integral_constant<int, 2>{}, i + 2);
     }
+    wait_vm_lgkm<0>();  // the last two (zero) stages land before the LDS is given up
+    tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
+                                                ubits_lds);
 }
 
 // Sum the split-K partials in order and apply the epilogue (gate: also the
@@ -454,6 +634,7 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // ===========================================================================
 struct Cfg {
     int mf, tm, tn, wm, wn;
+    bool dma;  // NT-form GEMMs (gate, up) use the pipelined direct-to-LDS kernel
     int bm() const { return mf * tm * wm; }
     int bn() const { return mf * tn * wn; }
     int threads() const { return 64 * wm * wn; }
@@ -462,10 +643,10 @@ struct Cfg {
 // Tile shapes by batch size (M = tokens).
 static Cfg cfg_for(int M)
 {
-    if (M >= 512) return {32, 4, 2, 2, 2};  // 256 x 128, 4 wavefronts of 128 x 64
-    if (M >= 128) return {32, 2, 2, 4, 1};  // 256 x 64
-    if (M > 32) return {16, 1, 2, 4, 2};    // 64 x 64
-    return {16, 1, 2, 2, 2};                // 32 x 64
+    if (M >= 512) return {32, 4, 2, 2, 2, true};  // 256 x 128, 4 wavefronts of 128 x 64
+    if (M >= 128) return {32, 2, 2, 4, 1, true};  // 256 x 64
+    if (M > 32) return {16, 1, 2, 4, 2, false};   // 64 x 64
+    return {16, 1, 2, 2, 2, false};               // 32 x 64
 }
 
 template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
@@ -477,11 +658,26 @@ static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf
                        ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
 }
 
+template <int TM, int TN, int WM, int WN, int EK, int GM>
+static void launch_dma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
+                       int ldb, const int32_t *bidx, const int *ncount, float *part, int part_ld, const EpiArgs &e)
+{
+    hipLaunchKernelGGL((k_mfma_dma<TM, TN, WM, WN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B, ldb,
+                       bidx, ncount, part, part_ld, e);
+}
+
 template <bool BNN, int EK, int GM>
 static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
                          int pld, const EpiArgs &e)
 {
+    if constexpr (!BNN) {
+        if (c.dma && nk == 0) {
+            if (c.tm == 4) launch_dma<4, 2, 2, 2, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
+            else launch_dma<2, 2, 4, 1, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
+            return;
+        }
+    }
     if (c.mf == 32 && c.tm == 4)
         launch_mfma<32, 4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
     else if (c.mf == 32)

@@ -34,6 +34,8 @@
 namespace sffn {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x4_t lbf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t_;
 
@@ -380,23 +382,38 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined GEMM for the NT form (gate and up: both operands K-contiguous,
-// B rows gathered through bidx), v_mfma_f32_32x32x16_bf16, K step 64.
+// Pipelined GEMM, v_mfma_f32_32x32x16_bf16, K step 64.
+//   BNN = false (gate, up): B rows are the N outputs, K contiguous, gathered
+//                through bidx (or identity); N limited by *ncount if set.
+//   BNN = true  (down):     B rows are the K inputs, N contiguous, gathered
+//                through bidx; K limited by *ncount.
 //
-// Tiles move from global memory straight into LDS (16-byte direct-to-LDS
-// loads, no register staging) through a ring of three stages, so the loads
-// of K steps i+1 and i+2 are in flight while step i is multiplied. Each
-// stage is its own LDS array and the stage index is a compile-time constant
-// (the main loop is unrolled by three): the compiler can then tell the
-// stages apart and does not wait for every outstanding load before each LDS
-// read; the only waits are the explicit ones below.
+// Tiles move from global memory straight into LDS (direct-to-LDS loads, no
+// register staging) through a ring of three stages, so the loads of K steps
+// i+1 and i+2 are in flight while step i is multiplied. Each stage is its
+// own LDS array and the stage index is a compile-time constant (the main
+// loop is unrolled by three): the compiler can then tell the stages apart
+// and does not wait for every outstanding load before each LDS read; the
+// only waits are the explicit ones below (it tells at most eight such
+// targets apart, so A and B of a stage share one array).
 //
-// One load instruction of a wavefront fills 8 tile rows (1 KB): lane l
-// takes row l/8 and K chunk (l%8) ^ (l/8) of it, written to slot l%8, so LDS
-// element (row, 8p) holds chunk p ^ (row % 8). A fragment read (32 rows, one
-// chunk) then touches 8 distinct slots per 8 consecutive rows: no bank
-// conflicts. Chunks outside the operands (rows past M or past the union, K
-// past the end) are loaded from a zero block.
+// K-contiguous tiles (A; B when BNN = false): one 16-byte load instruction
+// of a wavefront fills 8 tile rows (1 KB); lane l takes row l/8 and K chunk
+// (l%8) ^ (l/8) of it, written to slot l%8, so LDS element (row, 8p) holds
+// chunk p ^ (row % 8) and a fragment read (32 rows, one chunk) touches 8
+// distinct slots per 8 consecutive rows: no bank conflicts.
+//
+// N-contiguous B (BNN = true): one instruction fills 64/CPR K rows of CPR =
+// BN/8 chunks; K row r holds N chunk p at slot p ^ 2 (r % 4). A fragment (8
+// consecutive K values of one column per lane) is two LDS transpose reads;
+// each 16-lane group of such a read covers 4 K rows x 32 bytes, and the
+// swizzle puts those 4 rows on distinct banks.
+// The gathered row indices of K step s travel with the loads of step s-2
+// (one 4-byte load per lane into a three-slot LDS ring), so they are in LDS
+// when step s's loads are issued.
+//
+// Chunks outside the operands (rows past M or past the union, K past the
+// end) are loaded from a zero block.
 // ---------------------------------------------------------------------------
 constexpr int kDmaBK = 64;
 
@@ -415,7 +432,7 @@ __device__ __forceinline__ void wait_vm_lgkm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TM, int TN, int WM, int WN, int EK, int GM>
+template <int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
 __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
                                                          const bf16_t *__restrict__ B, int ldb,
                                                          const int32_t *__restrict__ bidx,
@@ -424,13 +441,17 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
 {
     constexpr int MF = 32, NW = WM * WN, NTHR = 64 * NW;
     constexpr int BM = MF * TM * WM, BN = MF * TN * WN, BK = kDmaBK;
-    constexpr int APW = BM * (BK / 8) / 64 / NW;  // load instructions per wavefront and stage: A
-    constexpr int BPW = BN * (BK / 8) / 64 / NW;  // and B
-    constexpr int LPS = APW + BPW;
+    constexpr int CPR = BN / 8, RPI = 64 / CPR;     // BNN: chunks per K row, K rows per instruction
+    constexpr int APW = BM * (BK / 8) / 64 / NW;    // 16-byte load instructions per wavefront and stage: A
+    constexpr int BPW = BN * (BK / 8) / 64 / NW;    // and B
+    constexpr int LPS = APW + BPW + (BNN ? 1 : 0);  // vector-memory operations per wavefront and stage
     static_assert(APW * 64 * NW == BM * (BK / 8) && BPW * 64 * NW == BN * (BK / 8), "rows split over wavefronts");
+    static_assert(!BNN || (CPR <= 64 && BPW * RPI * NW == BK), "K rows split over wavefronts");
     typedef __attribute__((ext_vector_type(16))) float accv;
-    __shared__ __align__(16) bf16_t As0[BM * BK], As1[BM * BK], As2[BM * BK];
-    __shared__ __align__(16) bf16_t Bs0[BN * BK], Bs1[BN * BK], Bs2[BN * BK];
+    // stage s: A tile at 0, B tile at BM * BK (one array per stage: the
+    // compiler tells at most eight direct-to-LDS targets apart)
+    __shared__ __align__(16) bf16_t St0[(BM + BN) * BK], St1[(BM + BN) * BK], St2[(BM + BN) * BK];
+    __shared__ __align__(16) int Is0[BNN ? BK : 1], Is1[BNN ? BK : 1], Is2[BNN ? BK : 1];
     __shared__ uint32_t ubits_lds[BN / 32];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -442,37 +463,66 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     const int mi = jt % MT, ni = (jt / MT) * 8 + xcd;
     if (ni >= NTT) return;
     const int m0 = mi * BM, n0 = ni * BN;
-    const int nlim = ncount ? min(N, *ncount) : N;
+    int nlim = N, klim = K;
+    if (ncount) {
+        if constexpr (BNN) klim = min(K, *ncount);
+        else nlim = min(N, *ncount);
+    }
     if (n0 >= nlim || m0 >= M) return;
     const int S = gridDim.z;
-    int kb = 0, ke = K;
+    int kb = 0, ke = klim;
     if (S > 1) {
-        const int steps = (K + BK - 1) / BK;
+        const int steps = (klim + BK - 1) / BK;
         kb = (int)(((long long)steps * blockIdx.z) / S) * BK;
-        ke = min(K, (int)(((long long)steps * (blockIdx.z + 1)) / S) * BK);
+        ke = min(klim, (int)(((long long)steps * (blockIdx.z + 1)) / S) * BK);
     }
     const int nsteps = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+    const bf16_t *zero = reinterpret_cast<const bf16_t *>(g_zero16);
 
-    // per-lane sources of this wavefront's load instructions
+    // ---- per-lane sources ----
     const int lr = lane >> 3, lc = ((lane & 7) ^ lr) * 8;
     const bf16_t *asrc[APW];
-    const bf16_t *bsrc[BPW];
 #pragma unroll
     for (int j = 0; j < APW; ++j) {
         const int m = m0 + (wave * APW + j) * 8 + lr;
         asrc[j] = m < M ? A + (size_t)m * lda + lc : nullptr;
     }
+    const bf16_t *bsrc[BNN ? 1 : BPW];
+    int bkr[BNN ? BPW : 1];  // BNN: local K row of each B instruction
+    int bnc[BNN ? BPW : 1];  // and the first column of the chunk this lane loads into it
+    if constexpr (!BNN) {
 #pragma unroll
-    for (int j = 0; j < BPW; ++j) {
-        const int n = n0 + (wave * BPW + j) * 8 + lr;
-        bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + lc : nullptr;
+        for (int j = 0; j < BPW; ++j) {
+            const int n = n0 + (wave * BPW + j) * 8 + lr;
+            bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + lc : nullptr;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+            bkr[j] = (wave * BPW + j) * RPI + lane / CPR;
+            bnc[j] = n0 + ((lane % CPR) ^ (2 * (bkr[j] & 3))) * 8;
+        }
     }
-    const bf16_t *zero = reinterpret_cast<const bf16_t *>(g_zero16);
 
-    auto issue = [&](auto stage, int step) {
+    auto As = [&](auto stage) -> bf16_t * {
         constexpr int SI = decltype(stage)::value;
-        bf16_t *la = SI == 0 ? As0 : SI == 1 ? As1 : As2;
-        bf16_t *lb = SI == 0 ? Bs0 : SI == 1 ? Bs1 : Bs2;
+        return SI == 0 ? St0 : SI == 1 ? St1 : St2;
+    };
+    auto Bs = [&](auto stage) -> bf16_t * { return As(stage) + BM * BK; };
+    auto Is = [&](auto stage) -> int * {
+        constexpr int SI = decltype(stage)::value;
+        return SI == 0 ? Is0 : SI == 1 ? Is1 : Is2;
+    };
+    // BNN: the row indices of K step `step` into index slot `stage`
+    auto issue_idx = [&](auto stage, int step) {
+        const int k = kb + step * BK + lane;
+        const int32_t *src = k < ke ? bidx + k : reinterpret_cast<const int32_t *>(g_zero16);
+        __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)Is(stage), 4, 0, 0);
+    };
+    // the tiles of K step `step` into stage `stage`; BNN: their row indices
+    // are in index slot `stage`
+    auto issue = [&](auto stage, int step) {
+        bf16_t *la = As(stage), *lb = Bs(stage);
         const int k = kb + step * BK;
         const bool kin = k + lc < ke;
 #pragma unroll
@@ -480,10 +530,20 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
             const bf16_t *src = (asrc[j] && kin) ? asrc[j] + k : zero;
             __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(la + (wave * APW + j) * 512), 16, 0, 0);
         }
+        if constexpr (!BNN) {
 #pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-            const bf16_t *src = (bsrc[j] && kin) ? bsrc[j] + k : zero;
-            __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(lb + (wave * BPW + j) * 512), 16, 0, 0);
+            for (int j = 0; j < BPW; ++j) {
+                const bf16_t *src = (bsrc[j] && kin) ? bsrc[j] + k : zero;
+                __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(lb + (wave * BPW + j) * 512), 16, 0, 0);
+            }
+        } else {
+            const int *is = Is(stage);
+#pragma unroll
+            for (int j = 0; j < BPW; ++j) {
+                const bool ok = k + bkr[j] < ke && bnc[j] < nlim;
+                const bf16_t *src = ok ? B + (size_t)is[bkr[j]] * ldb + bnc[j] : zero;
+                __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(lb + (wave * BPW + j) * 512), 16, 0, 0);
+            }
         }
     };
 
@@ -496,20 +556,46 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int arow = wm * MF * TM, bcol = wn * MF * TN;
+    // BNN: element offsets (K substep 0) of this lane's two transpose reads
+    // per B fragment. ds_read_b64_tr_b16: in each group of 16 lanes, lane
+    // 4a+b receives element b of the 8-byte reads of lanes 4e+a, e = 0..3.
+    // Lane s therefore points at K row 8 (s/32) + 4 half + (s%16)/4, columns
+    // 16 ((s/16)%2) + 4 (s%4) .. +3 of its fragment; lane l then holds
+    // K values 8 (l/32) + 4 half + 0..3 of column l%32, the operand layout.
+    int btr[BNN ? TN : 1][2];
+    if constexpr (BNN) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kr = 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
+                const int n = bcol + j * MF + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                btr[j][h] = kr * BN + ((((n >> 3) ^ (2 * (kr & 3))) << 3) | (n & 7));
+            }
+    }
     auto compute = [&](auto stage) {
-        constexpr int SI = decltype(stage)::value;
-        const bf16_t *sa = SI == 0 ? As0 : SI == 1 ? As1 : As2;
-        const bf16_t *sb = SI == 0 ? Bs0 : SI == 1 ? Bs1 : Bs2;
+        const bf16_t *sa = As(stage), *sb = Bs(stage);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int sw = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8;
             bf16x8_t af[TM], bfr[TN];
+            const int sw = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
                 af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (arow + i * MF + (lane & 31)) * BK + sw);
+            if constexpr (!BNN) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (bcol + j * MF + (lane & 31)) * BK + sw);
+                for (int j = 0; j < TN; ++j)
+                    bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (bcol + j * MF + (lane & 31)) * BK + sw);
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lbf16x4_t *)(sb + ks * 16 * BN + btr[j][0]));
+                    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lbf16x4_t *)(sb + ks * 16 * BN + btr[j][1]));
+                    bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -518,28 +604,43 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
         }
     };
     // K step i: its loads (issued two steps earlier) have landed in every
-    // wavefront once each has waited for all but the next step's loads and
-    // passed the barrier; the barrier also ends every read of the stage that
-    // step i+2 refills (last read in step i-1). Every step issues and waits
-    // the same way: the step count is padded to a multiple of three, and
-    // steps past the end load the zero block (kin is false there), so every
-    // path through the loop has the same loads in flight.
+    // wavefront once each has waited for all but the next step's group of
+    // loads and passed the barrier; the barrier also ends every read of the
+    // stage (and index slot) that this step refills, last read in step i-1.
+    // Every step issues and waits the same way: the step count is padded to
+    // a multiple of three, and steps past the end load the zero block, so
+    // every path through the loop has the same loads in flight.
     auto step = [&](auto stage, int i) {
         constexpr int SI = decltype(stage)::value;
         wait_vm_lgkm<LPS>();
         __builtin_amdgcn_s_barrier();
         issue(std::integral_constant<int, (SI + 2) % 3>{}, i + 2);
+        if constexpr (BNN) issue_idx(std::integral_constant<int, (SI + 1) % 3>{}, i + 4);
         compute(stage);
     };
+    if constexpr (BNN) {
+        // indices of steps 0..2, then the tiles of steps 0 and 1 with the
+        // indices of step 3 (slot 0, after every wavefront has read step 0's)
+        issue_idx(std::integral_constant<int, 0>{}, 0);
+        issue_idx(std::integral_constant<int, 1>{}, 1);
+        issue_idx(std::integral_constant<int, 2>{}, 2);
+        wait_vm_lgkm<0>();
+        issue(std::integral_constant<int, 0>{}, 0);
+        issue(std::integral_constant<int, 1>{}, 1);
+        wait_vm_lgkm<2 * (APW + BPW)>();  // no vector-memory wait: only the index reads above
+        __builtin_amdgcn_s_barrier();
+        issue_idx(std::integral_constant<int, 0>{}, 3);
+    } else {
+        issue(std::integral_constant<int, 0>{}, 0);
+        issue(std::integral_constant<int, 1>{}, 1);
+    }
     const int nst3 = (nsteps + 2) / 3 * 3;
-    issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, 1);
     for (int i = 0; i < nst3; i += 3) {
         step(std::integral_constant<int, 0>{}, i);
         step(std::integral_constant<int, 1>{}, i + 1);
         step(std::integral_constant<int, 2>{}, i + 2);
     }
-    wait_vm_lgkm<0>();  // the last two (zero) stages land before the LDS is given up
+    wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
     tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
                                                 ubits_lds);
 }
@@ -658,12 +759,12 @@ static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf
                        ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
 }
 
-template <int TM, int TN, int WM, int WN, int EK, int GM>
+template <int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
 static void launch_dma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
                        int ldb, const int32_t *bidx, const int *ncount, float *part, int part_ld, const EpiArgs &e)
 {
-    hipLaunchKernelGGL((k_mfma_dma<TM, TN, WM, WN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B, ldb,
-                       bidx, ncount, part, part_ld, e);
+    hipLaunchKernelGGL((k_mfma_dma<TM, TN, WM, WN, BNN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
+                       ldb, bidx, ncount, part, part_ld, e);
 }
 
 template <bool BNN, int EK, int GM>
@@ -671,12 +772,10 @@ static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, 
                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
                          int pld, const EpiArgs &e)
 {
-    if constexpr (!BNN) {
-        if (c.dma && nk == 0) {
-            if (c.tm == 4) launch_dma<4, 2, 2, 2, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
-            else launch_dma<2, 2, 4, 1, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
-            return;
-        }
+    if (c.dma && nk == (BNN ? 1 : 0)) {
+        if (c.tm == 4) launch_dma<4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
+        else launch_dma<2, 2, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
+        return;
     }
     if (c.mf == 32 && c.tm == 4)
         launch_mfma<32, 4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);

@@ -397,17 +397,18 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
 // only waits are the explicit ones below (it tells at most eight such
 // targets apart, so A and B of a stage share one array).
 //
-// K-contiguous tiles (A; B when BNN = false): one 16-byte load instruction
-// of a wavefront fills 8 tile rows (1 KB); lane l takes row l/8 and K chunk
-// (l%8) ^ (l/8) of it, written to slot l%8, so LDS element (row, 8p) holds
-// chunk p ^ (row % 8) and a fragment read (32 rows, one chunk) touches 8
-// distinct slots per 8 consecutive rows: no bank conflicts.
+// LDS serves a 128-bit read 16 lanes at a time, from a 256-byte bank window
+// (two 128-byte tile rows). K-contiguous tiles (A; B when BNN = false): one
+// 16-byte load instruction of a wavefront fills 8 tile rows (1 KB); lane l
+// writes slot l%8 of row l/8, loading the K chunk that belongs there: row r
+// keeps chunk p at slot p ^ ((r >> 1) & 7). A fragment read (32 rows, one
+// chunk) then puts each 16 consecutive rows on 16 distinct bank slots.
 //
 // N-contiguous B (BNN = true): one instruction fills 64/CPR K rows of CPR =
-// BN/8 chunks; K row r holds N chunk p at slot p ^ 2 (r % 4). A fragment (8
+// BN/8 chunks; K row r holds N chunk p at slot p ^ nswz(r). A fragment (8
 // consecutive K values of one column per lane) is two LDS transpose reads;
-// each 16-lane group of such a read covers 4 K rows x 32 bytes, and the
-// swizzle puts those 4 rows on distinct banks.
+// 32 lanes of such a read cover 4 K rows x 64 bytes, and the swizzle puts
+// those 16 pieces on distinct bank slots.
 // The gathered row indices of K step s travel with the loads of step s-2
 // (one 4-byte load per lane into a three-slot LDS ring), so they are in LDS
 // when step s's loads are issued.
@@ -478,29 +479,37 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     }
     const int nsteps = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const bf16_t *zero = reinterpret_cast<const bf16_t *>(g_zero16);
+    // BNN: K row r keeps N chunk p at slot p ^ nswz(r)
+    auto nswz = [](int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
 
     // ---- per-lane sources ----
-    const int lr = lane >> 3, lc = ((lane & 7) ^ lr) * 8;
+    // K-major tiles: tile row r keeps K chunk p at slot p ^ ((r >> 1) & 7)
+    const int lr = lane >> 3;
+    auto kchunk = [&](int row) { return ((lane & 7) ^ ((row >> 1) & 7)) * 8; };
     const bf16_t *asrc[APW];
+    int alc[APW];
 #pragma unroll
     for (int j = 0; j < APW; ++j) {
-        const int m = m0 + (wave * APW + j) * 8 + lr;
-        asrc[j] = m < M ? A + (size_t)m * lda + lc : nullptr;
+        const int r = (wave * APW + j) * 8 + lr, m = m0 + r;
+        alc[j] = kchunk(r);
+        asrc[j] = m < M ? A + (size_t)m * lda + alc[j] : nullptr;
     }
     const bf16_t *bsrc[BNN ? 1 : BPW];
+    int blc[BNN ? 1 : BPW];
     int bkr[BNN ? BPW : 1];  // BNN: local K row of each B instruction
     int bnc[BNN ? BPW : 1];  // and the first column of the chunk this lane loads into it
     if constexpr (!BNN) {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
-            const int n = n0 + (wave * BPW + j) * 8 + lr;
-            bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + lc : nullptr;
+            const int r = (wave * BPW + j) * 8 + lr, n = n0 + r;
+            blc[j] = kchunk(r);
+            bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + blc[j] : nullptr;
         }
     } else {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
             bkr[j] = (wave * BPW + j) * RPI + lane / CPR;
-            bnc[j] = n0 + ((lane % CPR) ^ (2 * (bkr[j] & 3))) * 8;
+            bnc[j] = n0 + ((lane % CPR) ^ nswz(bkr[j])) * 8;
         }
     }
 
@@ -524,16 +533,15 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     auto issue = [&](auto stage, int step) {
         bf16_t *la = As(stage), *lb = Bs(stage);
         const int k = kb + step * BK;
-        const bool kin = k + lc < ke;
 #pragma unroll
         for (int j = 0; j < APW; ++j) {
-            const bf16_t *src = (asrc[j] && kin) ? asrc[j] + k : zero;
+            const bf16_t *src = (asrc[j] && k + alc[j] < ke) ? asrc[j] + k : zero;
             __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(la + (wave * APW + j) * 512), 16, 0, 0);
         }
         if constexpr (!BNN) {
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
-                const bf16_t *src = (bsrc[j] && kin) ? bsrc[j] + k : zero;
+                const bf16_t *src = (bsrc[j] && k + blc[j] < ke) ? bsrc[j] + k : zero;
                 __builtin_amdgcn_global_load_lds((gmem_t *)src, (lmem_t *)(lb + (wave * BPW + j) * 512), 16, 0, 0);
             }
         } else {
@@ -570,37 +578,47 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
             for (int h = 0; h < 2; ++h) {
                 const int kr = 8 * (lane >> 5) + 4 * h + ((lane & 15) >> 2);
                 const int n = bcol + j * MF + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                btr[j][h] = kr * BN + ((((n >> 3) ^ (2 * (kr & 3))) << 3) | (n & 7));
+                btr[j][h] = kr * BN + ((((n >> 3) ^ nswz(kr)) << 3) | (n & 7));
             }
     }
+    // Fragments of K substep ks of a stage.
+    auto frags = [&](const bf16_t *sa, const bf16_t *sb, int ks, bf16x8_t (&af)[TM], bf16x8_t (&bfr)[TN]) {
+        const int sw = ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 8;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (arow + i * MF + (lane & 31)) * BK + sw);
+        if constexpr (!BNN) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (bcol + j * MF + (lane & 31)) * BK + sw);
+        } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(sb + ks * 16 * BN + btr[j][0]));
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4_t *)(sb + ks * 16 * BN + btr[j][1]));
+                bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+    auto mma = [&](const bf16x8_t (&af)[TM], const bf16x8_t (&bfr)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    };
+    // The fragments of substep ks+1 are read while substep ks is multiplied
+    // (two register sets), so LDS latency hides behind the MFMAs.
     auto compute = [&](auto stage) {
         const bf16_t *sa = As(stage), *sb = Bs(stage);
+        bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+        frags(sa, sb, 0, a0, b0);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8_t af[TM], bfr[TN];
-            const int sw = ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 8;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (arow + i * MF + (lane & 31)) * BK + sw);
-            if constexpr (!BNN) {
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    bfr[j] = *reinterpret_cast<const bf16x8_t *>(sb + (bcol + j * MF + (lane & 31)) * BK + sw);
-            } else {
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lbf16x4_t *)(sb + ks * 16 * BN + btr[j][0]));
-                    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lbf16x4_t *)(sb + ks * 16 * BN + btr[j][1]));
-                    bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int ks = 0; ks < BK / 16; ks += 2) {
+            frags(sa, sb, ks + 1, a1, b1);
+            mma(a0, b0);
+            if (ks + 2 < BK / 16) frags(sa, sb, ks + 2, a0, b0);
+            mma(a1, b1);
         }
     };
     // K step i: its loads (issued two steps earlier) have landed in every

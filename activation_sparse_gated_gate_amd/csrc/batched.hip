@@ -724,28 +724,25 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
                                                       int32_t *__restrict__ active_idx,
                                                       int32_t *__restrict__ active_cnt, int32_t *__restrict__ union_cnt)
 {
-    __shared__ int scan_scratch[4];
-    const int t = blockIdx.x, tid = threadIdx.x;
+    __shared__ int scratch[5];
+    const int t = blockIdx.x;
     if (t == T) {
-        if (tid == 0 && union_cnt) *union_cnt = *ncount;
+        if (threadIdx.x == 0 && union_cnt) *union_cnt = *ncount;
         return;
     }
     const bool dense = mode == SFFN_DENSE || mode == SFFN_DENSE_SILU;
-    auto on = [&](int i) -> bool {
-        if (dense) return true;
-        if (mode == SFFN_TOPK) return act[(size_t)t * F + i] != 0;
-        return G[(size_t)t * F + i] != 0;
+    const bool topk = mode == SFFN_TOPK;
+    const uint16_t *g = G + (size_t)t * F;
+    const uint8_t *a = act + (size_t)t * F;
+    auto on8 = [&](int i0, bool f[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = i0 + e;
+            f[e] = i < F && (dense || (topk ? a[i] != 0 : g[i] != 0));
+        }
     };
-    const int seg = (F + blockDim.x - 1) / blockDim.x;
-    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
-    int local = 0;
-    for (int i = i0; i < i1; ++i) local += on(i);
-    const int incl = block_incl_scan(local, scan_scratch);
-    int pos = incl - local;
-    if (active_idx)
-        for (int i = i0; i < i1; ++i)
-            if (on(i)) active_idx[(size_t)t * F + pos++] = i;
-    if (tid == blockDim.x - 1 && active_cnt) active_cnt[t] = incl;
+    const int c = emit_ordered(F, on8, active_idx ? active_idx + (size_t)t * F : nullptr, scratch);
+    if (threadIdx.x == 0 && active_cnt) active_cnt[t] = c;
 }
 
 // ===========================================================================

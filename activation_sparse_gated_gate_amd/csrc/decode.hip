@@ -22,202 +22,9 @@
 // Active channels are byte flags act[t][i] with one writer each, so any row
 // partition works without atomics. No kernel waits on another workgroup:
 // cross-workgroup results go through global memory and the next kernel.
-#include <hip/hip_ext.h>
-
-#include "device_common.h"
-#include "sffn_internal.h"
+#include "rowdot.h"
 
 namespace sffn {
-
-enum GateKind { KEYS = 0, SELECT_UP = 1, DENSE = 2 };
-
-// ---------------------------------------------------------------------------
-// Row-dot engine. A lane group of LPR lanes owns R rows; lane li covers the
-// 8-element chunks j = 8*li + s*8*LPR of every row. Each batch issues all its
-// weight loads (128-bit, non-temporal: weights are read once per forward) and
-// the matching x chunks of the NT tokens (small and cache-resident) before any
-// arithmetic; rows whose bit is clear in `valid` are not read. Products
-// accumulate in fp32 per lane (packed bf16 dot2 when both sides are bf16) and
-// are summed over the lane group, so every lane of a group ends with all
-// R x NT results.
-// ---------------------------------------------------------------------------
-template <typename TW, typename TX, int NT, int R, int LPR, int MAXS>
-struct RowDot {
-    static constexpr int STEP = LPR * 8;
-    float acc[R][NT];
-
-    // x: token t starts at x + t*ldx; tokens >= n read as zero. With tpart
-    // (LoPA, TX = float) the chunk is the in-order sum of ks partial slices
-    // tpart[s][t][.] of stride ps floats.
-    __device__ __forceinline__ void run(const TW *const rows[R], uint32_t valid, int len, int li, const TX *x,
-                                        int ldx, int n, const float *tpart = nullptr, int ks = 0, size_t ps = 0)
-    {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[r][t] = 0.f;
-        for (int jb = li * 8; jb < len; jb += MAXS * STEP) {
-            typename Ld8<TW>::raw w[MAXS][R];
-            typename Ld8<TX>::raw xv[MAXS][NT];
-#pragma unroll
-            for (int s = 0; s < MAXS; ++s)
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int j = jb + s * STEP;
-                    w[s][r] = (((valid >> r) & 1u) && j < len) ? Ld8<TW>::load_nt(rows[r] + j) : Ld8<TW>::zero();
-                }
-#pragma unroll
-            for (int s = 0; s < MAXS; ++s)
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int j = jb + s * STEP;
-                    xv[s][t] = Ld8<TX>::zero();
-                    if (t < n && j < len) {
-                        if constexpr (sizeof(TX) == 4) {
-                            if (tpart) {
-                                for (int p = 0; p < ks; ++p)
-                                    Ld8<TX>::add(xv[s][t], Ld8<TX>::load(reinterpret_cast<const TX *>(
-                                                               tpart + (size_t)p * ps + (size_t)t * ldx + j)));
-                                continue;
-                            }
-                        }
-                        xv[s][t] = Ld8<TX>::load(x + (size_t)t * ldx + j);
-                    }
-                }
-#pragma unroll
-            for (int s = 0; s < MAXS; ++s)
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[r][t] = dot8<TW, TX>(w[s][r], xv[s][t], acc[r][t]);
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[r][t] = group_sum<LPR>(acc[r][t]);
-    }
-};
-
-// Rows per lane group by token count: x chunks are reused over the rows.
-template <int NT>
-struct RowsPer {
-    static constexpr int v = NT <= 2 ? 1 : NT / 2;
-};
-
-// Chunks per batch, keeping the weight and x registers of a batch near 96.
-template <typename TW, typename TX, int NT, int R>
-struct Batch {
-    static constexpr int per = R * (sizeof(TW) == 2 ? 4 : 8) + NT * (sizeof(TX) == 2 ? 4 : 8);
-    static constexpr int raw = 96 / per;
-    static constexpr int v = raw >= 8 ? 8 : raw >= 4 ? 4 : raw >= 2 ? 2 : 1;
-};
-
-// ---------------------------------------------------------------------------
-// Gate kernel. Lane group q of wavefront gw (4 wavefronts per workgroup, LPR
-// lanes per group) owns rows (gw * 64/LPR + q) * R .. + R-1: every wavefront
-// gets the same small share, and there are many wavefronts per CU.
-//   z = x . W_gate[i]   (or t . B[i] for LoPA, t = x.A in fp32)
-//   KEYS:      g = SiLU(z) for the Top-K select that follows
-//   SELECT_UP: active = z > tau, g = z - tau; then the group reads the W_up
-//              rows of its channels that some token selected and writes
-//              h[i][t] = g * (x_t . W_up[i]) for the selecting tokens, else 0
-//   DENSE:     every channel; gate and up rows are read together,
-//              g = max(z - tau, 0) or SiLU(z), h = g * u
-// h is stored channel-major, hbuf[i][t] (8 token slots per channel).
-// ---------------------------------------------------------------------------
-template <typename TW, typename TX, int NT, int LPR, int KIND>
-__global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
-                                              const TW *__restrict__ xu, int d,
-                                              const float *__restrict__ tpart, int ks,
-                                              const TW *__restrict__ wg, const TW *__restrict__ wu,
-                                              int F, int mode, float tau,
-                                              float *__restrict__ gsel, uint8_t *__restrict__ act,
-                                              float *__restrict__ hbuf, float *__restrict__ debug_z)
-{
-    constexpr int SUB = 64 / LPR;
-    constexpr int R = RowsPer<NT>::v;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int q = lane / LPR, li = lane % LPR;
-    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
-    const int nv = max(0, min(R, F - row0));
-    const uint32_t vmask = (1u << nv) - 1u;
-
-    float zz[R][NT], uu[R][NT];
-    if constexpr (KIND == DENSE) {
-        const TW *rows[2 * R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            rows[r] = wg + (size_t)(row0 + r) * L;
-            rows[R + r] = wu + (size_t)(row0 + r) * L;
-        }
-        RowDot<TW, TX, NT, 2 * R, LPR, Batch<TW, TX, NT, 2 * R>::v> dot;
-        dot.run(rows, vmask | (vmask << R), L, li, xg, L, n);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                zz[r][t] = dot.acc[r][t];
-                uu[r][t] = dot.acc[R + r][t];
-            }
-    } else {
-        const TW *rows[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) rows[r] = wg + (size_t)(row0 + r) * L;
-        RowDot<TW, TX, NT, R, LPR, Batch<TW, TX, NT, R>::v> dot;
-        dot.run(rows, vmask, L, li, xg, L, n, tpart, ks, (size_t)kDecodeMaxTokens * L);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) zz[r][t] = dot.acc[r][t];
-    }
-
-    // ---- activation and selection (every lane of the group has every z) ----
-    float gv[R][NT];      // gate value of a selected (row, token), else 0
-    uint32_t amask = 0;   // rows some token selected
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int i = row0 + r;
-            const float z = zz[r][t];
-            float g;
-            bool a;
-            if constexpr (KIND == SELECT_UP) {
-                a = z > tau;
-                g = z - tau;
-            } else if constexpr (KIND == KEYS) {
-                a = false;
-                g = silu(z);
-            } else {
-                a = true;
-                g = mode == SFFN_DENSE ? fmaxf(z - tau, 0.f) : silu(z);
-            }
-            const bool live = r < nv && t < n;
-            a = a && live;
-            gv[r][t] = a ? g : 0.f;
-            if (a) amask |= 1u << r;
-            if (live && li == ((r * NT + t) & (LPR - 1))) {
-                gsel[(size_t)t * F + i] = g;
-                if (debug_z) debug_z[(size_t)t * F + i] = z;
-                if constexpr (KIND == SELECT_UP) act[(size_t)t * F + i] = a ? 1 : 0;
-                if constexpr (KIND == DENSE) hbuf[(size_t)i * kDecodeMaxTokens + t] = g * uu[r][t];
-            }
-        }
-    if constexpr (KIND == SELECT_UP) {
-        if (__ballot(amask != 0) == 0) return;  // nothing selected in this wavefront
-        const TW *urows[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) urows[r] = wu + (size_t)(row0 + r) * d;
-        RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
-        up.run(urows, amask, d, li, xu, d, n);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
-                    hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Up kernel (Top-K): the gate kernel's row partition. Each lane group applies
@@ -438,40 +245,31 @@ __global__ __launch_bounds__(256) void k_emit_lists(const uint8_t *__restrict__ 
                                                     int32_t *__restrict__ active_cnt,
                                                     int32_t *__restrict__ union_cnt)
 {
-    __shared__ int scan_scratch[4];
-    const int b = blockIdx.x, tid = threadIdx.x;
-    if (dense) {
-        if (b < n) {
-            if (active_idx)
-                for (int i = tid; i < F; i += blockDim.x) active_idx[(size_t)b * F + i] = i;
-            if (tid == 0 && active_cnt) active_cnt[b] = F;
-        } else if (tid == 0 && union_cnt) {
-            *union_cnt = F;
-        }
-        return;
-    }
-    const int seg = (F + blockDim.x - 1) / blockDim.x;
-    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
-    if (b == n) {
-        int local = 0;
-        for (int i = i0; i < i1; ++i) {
-            bool any = false;
-            for (int t = 0; t < n && !any; ++t) any = act[(size_t)t * F + i] != 0;
-            local += any;
-        }
-        const int incl = block_incl_scan(local, scan_scratch);
-        if (tid == blockDim.x - 1 && union_cnt) *union_cnt = incl;
-        return;
-    }
+    __shared__ int scratch[5];
+    const int b = blockIdx.x;
     const uint8_t *a = act + (size_t)b * F;
-    int local = 0;
-    for (int i = i0; i < i1; ++i) local += a[i] != 0;
-    const int incl = block_incl_scan(local, scan_scratch);
-    int pos = incl - local;
-    if (active_idx)
-        for (int i = i0; i < i1; ++i)
-            if (a[i]) active_idx[(size_t)b * F + pos++] = i;
-    if (tid == blockDim.x - 1 && active_cnt) active_cnt[b] = incl;
+    auto token = [&](int i0, bool f[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = i0 + e < F && (dense || a[i0 + e] != 0);
+    };
+    auto any = [&](int i0, bool f[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bool v = i0 + e < F && (dense || n > 0);
+            if (v && !dense) {
+                v = false;
+                for (int t = 0; t < n; ++t) v |= act[(size_t)t * F + i0 + e] != 0;
+            }
+            f[e] = v;
+        }
+    };
+    if (b < n) {
+        const int c = emit_ordered(F, token, active_idx ? active_idx + (size_t)b * F : nullptr, scratch);
+        if (threadIdx.x == 0 && active_cnt) active_cnt[b] = c;
+    } else {
+        const int c = emit_ordered(F, any, nullptr, scratch);
+        if (threadIdx.x == 0 && union_cnt) *union_cnt = c;
+    }
 }
 
 __global__ void k_zero_ints(int *__restrict__ p, int count)
@@ -490,15 +288,6 @@ static int lpr_for(int len)
 }
 
 static int nt_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
-
-// Workgroups (4 wavefronts) for a row partition of `rows` rows in groups of
-// R rows per LPR lanes.
-static int row_blocks(int rows, int lpr, int R)
-{
-    const int per_wave = (64 / lpr) * R;
-    const int waves = (rows + per_wave - 1) / per_wave;
-    return max(1, (waves + 3) / 4);
-}
 
 // 16 channel groups, more for very wide layers so that a thread of the list
 // prologue scans at most 32 channels of its group.
@@ -557,29 +346,6 @@ hipError_t launch_init(sffn_ctx &c, hipStream_t s)
     return hipGetLastError();
 }
 
-// The gate kernel; with profiling events set, they take the kernel's own
-// begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
-template <typename TW, typename TX, int NT, int KIND>
-static void launch_gate(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
-                        const TW *xu, int d, const float *tpart, int ks, const TW *wg, const TW *wu, int F, int mode,
-                        float tau, float *gsel, uint8_t *act, float *hbuf, float *dz)
-{
-    const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
-#define SFFN_G(LP)                                                                                               \
-    do {                                                                                                         \
-        if (ev0)                                                                                                 \
-            hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
-                                  xu, d, tpart, ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                 \
-        else                                                                                                     \
-            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart,   \
-                               ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                                   \
-    } while (0)
-    if (lpr == 64) SFFN_G(64);
-    else if (lpr == 32) SFFN_G(32);
-    else SFFN_G(16);
-#undef SFFN_G
-}
-
 template <typename TW, int NT>
 static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
 {
@@ -596,10 +362,31 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     const TW *wdn = static_cast<const TW *>(a.w.w_down);
     hipStream_t st = a.stream;
     const bool dense = a.mode == SFFN_DENSE || a.mode == SFFN_DENSE_SILU;
-    hipEvent_t ev0 = static_cast<hipEvent_t>(c.ev_start), ev1 = static_cast<hipEvent_t>(c.ev_stop);
     hipError_t e;
 
     // ---- gate (+ select, + up for threshold / LoPA / dense) ----
+    GateArgs g{};
+    g.dtype = S.dtype;
+    g.nt = NT;
+    g.n = n;
+    g.xg = x;
+    g.L = d;
+    g.xu = x;
+    g.d = d;
+    g.wg = wg;
+    g.wu = wu;
+    g.F = F;
+    g.mode = a.mode;
+    g.tau = a.tau;
+    g.gsel = gsel;
+    g.act = act;
+    g.hbuf = hbuf;
+    g.debug_z = a.debug_z;
+    g.stream = st;
+    g.ev_start = c.ev_start;
+    g.ev_stop = c.ev_stop;
+    g.lpr = lpr_for(d);
+    g.kind = dense ? DENSE : a.mode == SFFN_TOPK ? KEYS : SELECT_UP;
     if (a.mode == SFFN_LOPA) {
         const int r = S.rank;
         float *tpart = reinterpret_cast<float *>(ws + c.L.tpart);
@@ -608,23 +395,17 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
         hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(blocks, ks), dim3(256), 0, st, x, n, d,
                            static_cast<const TW *>(a.w.lopa_a), r, chunk, tpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        const TW *bt = static_cast<const TW *>(a.w.lopa_b);
-        // the gate rows (length r) and the up rows (length d) share the lane
-        // groups, sized for the shorter of the two
-        launch_gate<TW, float, NT, SELECT_UP>(st, ev0, ev1, lpr_for(min(r, d)), nullptr, n, r, x, d, tpart, ks, bt, wu, F,
-                                              a.mode, a.tau, gsel, act, hbuf, a.debug_z);
-    } else {
-        if (dense)
-            launch_gate<TW, TW, NT, DENSE>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
-                                           act, hbuf, a.debug_z);
-        else if (a.mode == SFFN_TOPK)
-            launch_gate<TW, TW, NT, KEYS>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau, gsel,
-                                          act, hbuf, a.debug_z);
-        else
-            launch_gate<TW, TW, NT, SELECT_UP>(st, ev0, ev1, lpr_for(d), x, n, d, x, d, nullptr, 0, wg, wu, F, a.mode, a.tau,
-                                               gsel, act, hbuf, a.debug_z);
+        // gate rows are B (length r) dotted with t = x.A; the gate rows and
+        // the up rows (length d) share the lane groups, sized for the shorter
+        g.lopa = true;
+        g.xg = nullptr;
+        g.L = r;
+        g.tpart = tpart;
+        g.ks = ks;
+        g.wg = a.w.lopa_b;
+        g.lpr = lpr_for(min(r, d));
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_gate(g)) != hipSuccess) return e;
 
     // ---- Top-K: select, then the up rows ----
     if (a.mode == SFFN_TOPK) {

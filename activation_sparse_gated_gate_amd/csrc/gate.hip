@@ -1,0 +1,187 @@
+// Gate kernel of the decode regime (1..8 tokens): gate GEMV fused with the
+// activation, the threshold select and the up rows of the channels just found
+// active ("Model Casting and Low-Parameter Gating", Abstract: the gate is
+// computed first and only the channels it leaves active read their W_up and
+// W_down rows). Launched through launch_gate (sffn_internal.h).
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
+#include "rowdot.h"
+
+namespace sffn {
+
+// ---------------------------------------------------------------------------
+// Gate kernel. Lane group q of wavefront gw (4 wavefronts per workgroup, LPR
+// lanes per group) owns rows (gw * 64/LPR + q) * R .. + R-1: every wavefront
+// gets the same small share, and there are many wavefronts per CU.
+//   z = x . W_gate[i]   (or t . B[i] for LoPA, t = x.A in fp32)
+//   KEYS:      g = SiLU(z) for the Top-K select that follows
+//   SELECT_UP: active = z > tau, g = z - tau; then the group reads the W_up
+//              rows of its channels that some token selected and writes
+//              h[i][t] = g * (x_t . W_up[i]) for the selecting tokens, else 0
+//   DENSE:     every channel; gate and up rows are read together,
+//              g = max(z - tau, 0) or SiLU(z), h = g * u
+// h is stored channel-major, hbuf[i][t] (8 token slots per channel).
+// ---------------------------------------------------------------------------
+template <typename TW, typename TX, int NT, int LPR, int KIND>
+__global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
+                                              const TW *__restrict__ xu, int d,
+                                              const float *__restrict__ tpart, int ks,
+                                              const TW *__restrict__ wg, const TW *__restrict__ wu,
+                                              int F, int mode, float tau,
+                                              float *__restrict__ gsel, uint8_t *__restrict__ act,
+                                              float *__restrict__ hbuf, float *__restrict__ debug_z)
+{
+    constexpr int SUB = 64 / LPR;
+    constexpr int R = RowsPer<NT>::v;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = lane / LPR, li = lane % LPR;
+    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
+    const int nv = max(0, min(R, F - row0));
+    const uint32_t vmask = (1u << nv) - 1u;
+
+    float zz[R][NT], uu[R][NT];
+    if constexpr (KIND == DENSE) {
+        const TW *rows[2 * R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rows[r] = wg + (size_t)(row0 + r) * L;
+            rows[R + r] = wu + (size_t)(row0 + r) * L;
+        }
+        RowDot<TW, TX, NT, 2 * R, LPR, Batch<TW, TX, NT, 2 * R>::v> dot;
+        dot.run(rows, vmask | (vmask << R), L, li, xg, L, n);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                zz[r][t] = dot.acc[r][t];
+                uu[r][t] = dot.acc[R + r][t];
+            }
+    } else {
+        const TW *rows[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) rows[r] = wg + (size_t)(row0 + r) * L;
+        RowDot<TW, TX, NT, R, LPR, Batch<TW, TX, NT, R>::v> dot;
+        dot.run(rows, vmask, L, li, xg, L, n, tpart, ks, (size_t)kDecodeMaxTokens * L);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) zz[r][t] = dot.acc[r][t];
+    }
+
+    // ---- activation and selection (every lane of the group has every z) ----
+    float gv[R][NT];      // gate value of a selected (row, token), else 0
+    uint32_t amask = 0;   // rows some token selected
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int i = row0 + r;
+            const float z = zz[r][t];
+            float g;
+            bool a;
+            if constexpr (KIND == SELECT_UP) {
+                a = z > tau;
+                g = z - tau;
+            } else if constexpr (KIND == KEYS) {
+                a = false;
+                g = silu(z);
+            } else {
+                a = true;
+                g = mode == SFFN_DENSE ? fmaxf(z - tau, 0.f) : silu(z);
+            }
+            const bool live = r < nv && t < n;
+            a = a && live;
+            gv[r][t] = a ? g : 0.f;
+            if (a) amask |= 1u << r;
+            if (live && li == ((r * NT + t) & (LPR - 1))) {
+                gsel[(size_t)t * F + i] = g;
+                if (debug_z) debug_z[(size_t)t * F + i] = z;
+                if constexpr (KIND == SELECT_UP) act[(size_t)t * F + i] = a ? 1 : 0;
+                if constexpr (KIND == DENSE) hbuf[(size_t)i * kDecodeMaxTokens + t] = g * uu[r][t];
+            }
+        }
+    if constexpr (KIND == SELECT_UP) {
+        if (__ballot(amask != 0) == 0) return;  // nothing selected in this wavefront
+        const TW *urows[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) urows[r] = wu + (size_t)(row0 + r) * d;
+        RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+        up.run(urows, amask, d, li, xu, d, n);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
+                    hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
+    }
+}
+
+// The gate kernel; with profiling events set, they take the kernel's own
+// begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
+template <typename TW, typename TX, int NT, int KIND>
+static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
+                        const TW *xu, int d, const float *tpart, int ks, const TW *wg, const TW *wu, int F, int mode,
+                        float tau, float *gsel, uint8_t *act, float *hbuf, float *dz)
+{
+    const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
+#define SFFN_G(LP)                                                                                               \
+    do {                                                                                                         \
+        if (ev0)                                                                                                 \
+            hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
+                                  xu, d, tpart, ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                 \
+        else                                                                                                     \
+            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart,   \
+                               ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                                   \
+    } while (0)
+    if (lpr == 64) SFFN_G(64);
+    else if (lpr == 32) SFFN_G(32);
+    else SFFN_G(16);
+#undef SFFN_G
+}
+
+hipError_t launch_gate(const GateArgs &g)
+{
+    hipStream_t st = g.stream;
+    hipEvent_t ev0 = static_cast<hipEvent_t>(g.ev_start), ev1 = static_cast<hipEvent_t>(g.ev_stop);
+    auto run = [&](auto tw, auto tx, auto nt) {
+        typedef decltype(tw) TW;
+        typedef decltype(tx) TX;
+        constexpr int NT = decltype(nt)::value;
+        const TX *xg = static_cast<const TX *>(g.xg);
+        const TW *xu = static_cast<const TW *>(g.xu), *wg = static_cast<const TW *>(g.wg);
+        const TW *wu = static_cast<const TW *>(g.wu);
+        switch (g.kind) {
+        case KEYS:
+            launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu, g.F,
+                                            g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+            break;
+        case DENSE:
+            launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu, g.F,
+                                             g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+            break;
+        default:
+            launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu,
+                                                 g.F, g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+            break;
+        }
+    };
+    auto by_nt = [&](auto tw, auto tx) {
+        switch (g.nt) {
+        case 1: run(tw, tx, std::integral_constant<int, 1>{}); break;
+        case 2: run(tw, tx, std::integral_constant<int, 2>{}); break;
+        case 4: run(tw, tx, std::integral_constant<int, 4>{}); break;
+        default: run(tw, tx, std::integral_constant<int, 8>{}); break;
+        }
+    };
+    if (g.dtype == SFFN_BF16) {
+        if (g.lopa) by_nt(bf16_t{}, float{});
+        else by_nt(bf16_t{}, bf16_t{});
+    } else {
+        by_nt(float{}, float{});
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sffn

@@ -87,6 +87,31 @@ hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hi
 // Batched: act[t][i] from the thresholds, and the union bitmap words.
 hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, uint8_t *act, int W, uint32_t *ubits,
                              hipStream_t st);
+// Decode gate kernel (gate.hip): gate GEMV + activation + select (+ the up
+// rows of the selected channels, or of every channel in the dense modes).
+struct GateArgs {
+    int dtype;            // sffn_dtype of weights and x
+    bool lopa;            // gate rows are B (length L) dotted with t = x.A from fp32 partials
+    int nt;               // padded token count: 1, 2, 4 or 8
+    int kind;             // GateKind (rowdot.h)
+    int lpr;              // lanes per row group: 16, 32 or 64
+    const void *xg;       // gate input x [n][L] (null for LoPA)
+    int n, L;
+    const void *xu;       // up input x [n][d]
+    int d;
+    const float *tpart;   // LoPA: x.A partials [ks][8][L]
+    int ks;
+    const void *wg, *wu;  // gate rows [F][L] (B for LoPA), up rows [F][d]
+    int F, mode;
+    float tau;
+    float *gsel;          // [8][F] gate values / Top-K keys
+    uint8_t *act;         // [8][F] selected flags (threshold)
+    float *hbuf;          // [F][8] h values of selected channels
+    float *debug_z;
+    hipStream_t stream;
+    void *ev_start, *ev_stop;  // optional: this kernel's own begin / end timestamps
+};
+hipError_t launch_gate(const GateArgs &g);
 // Host-side check that the decode kernels' LDS needs fit; false -> unsupported.
 bool decode_fits(const sffn_ctx &c, int n, int mode);
 }  // namespace sffn

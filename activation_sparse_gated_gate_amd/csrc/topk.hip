@@ -233,16 +233,18 @@ __global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ key
     }
 }
 
-// Batched: act[t][i] from the thresholds (thread per channel, loop over the
-// tokens) and the union bitmap word of each 32 channels.
+// Batched: act[t][i] from the thresholds, and the union bitmap. Block (x, y)
+// takes 256 channels and 8 tokens; the union words are ORed in (the bitmap
+// is all zero on entry: the compaction that reads it clears it).
 __global__ __launch_bounds__(256) void k_topk_flags(const float *__restrict__ keys, int T, int F,
                                                     const int2 *__restrict__ thr, uint8_t *__restrict__ act,
                                                     int W, uint32_t *__restrict__ ubits)
 {
     const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
+    const int t0 = blockIdx.y * 8, t1 = min(T, t0 + 8);
     bool any = false;
     if (i < F)
-        for (int t = 0; t < T; ++t) {
+        for (int t = t0; t < t1; ++t) {
             const size_t o = (size_t)t * F + i;
             const bool on = topk_on(keys[o], i, thr[t]);
             act[o] = on;
@@ -250,7 +252,8 @@ __global__ __launch_bounds__(256) void k_topk_flags(const float *__restrict__ ke
         }
     const unsigned long long m = __ballot(any);
     const int w = i >> 5;
-    if ((lane & 31) == 0 && w < W) ubits[w] = (uint32_t)(m >> (lane & 32));
+    const uint32_t bits = (uint32_t)(m >> (lane & 32));
+    if ((lane & 31) == 0 && w < W && bits) atomicOr(&ubits[w], bits);
 }
 
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st)
@@ -266,7 +269,8 @@ hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hi
 hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, uint8_t *act, int W, uint32_t *ubits,
                              hipStream_t st)
 {
-    hipLaunchKernelGGL(k_topk_flags, dim3((F + 255) / 256), dim3(256), 0, st, keys, T, F, thr, act, W, ubits);
+    hipLaunchKernelGGL(k_topk_flags, dim3((F + 255) / 256, (T + 7) / 8), dim3(256), 0, st, keys, T, F, thr, act, W,
+                       ubits);
     return hipGetLastError();
 }
 

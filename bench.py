@@ -47,7 +47,9 @@ MALL_BYTES = 256 << 20  # Infinity Cache
 WORKLOAD = "llama7b_ffn_bf16_d4096_f11008"
 HEADLINE_TAU = 1.2816
 METRIC = "sparse FFN layer tokens/s + % HBM roofline at batch 1, 50–99% sparsity"
-GATE_SRC = os.path.join(ROOT, "activation_sparse_gated_gate_amd", "csrc", "decode.hip")
+# sources of the gate kernel: its counters stay valid while these are unchanged
+GATE_SRC = [os.path.join(ROOT, "activation_sparse_gated_gate_amd", "csrc", f)
+            for f in ("gate.hip", "rowdot.h", "device_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_llama7b_bf16_pmc.md")
 
 
@@ -60,14 +62,20 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="headline point only (no tau sweep, no other workloads)")
     p.add_argument("--no-points", action="store_true", help="skip the other workloads' points")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0 = skip)")
+    p.add_argument("--only", default="",
+                   help="comma list of point families to measure (tiny, lopa, moc, prefill); runs them even "
+                        "with --no-sweep")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
 
 
-def sha256(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+def sha256(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def read_traffic():
@@ -109,36 +117,56 @@ def copies_for(layer_bytes, touched_bytes):
 
 
 def measure_points(args, dev, S, inputs, np, torch):
+    """The other workloads' points, by family (all, or those named by --only)."""
     W = inputs.WORKLOADS
     out = []
-    es = 2
+    fams = {f.strip() for f in args.only.split(",") if f.strip()}
 
-    def union(ffn, xt, w, mode, y, tau=0.0, k=0):
-        u = torch.zeros(1, dtype=torch.int32, device="cuda")
-        ffn.forward(xt, w, mode, y, tau=tau, k=k, union_cnt=u)
-        torch.cuda.synchronize()
-        return int(u.item())
+    def want(fam):
+        return not fams or fam in fams
 
     def replicate(tensors, L):
         return [tensors] + [{k: (v.clone() if v is not None else None) for k, v in tensors.items()}
                             for _ in range(L - 1)]
 
     # dense denominators on the Llama-7B-shaped layer (also the LoPA shape)
-    wl2 = W["llama7b_ffn_bf16_d4096_f11008"]
-    d2, f2 = wl2.d_model, wl2.d_ff
-    lay2 = inputs.make_layer(0, d2, f2, "bf16")
-    t2 = {"w_gate": dev(lay2.w_gate), "w_up": dev(lay2.w_up), "w_down": dev(lay2.w_down)}
-    c2 = replicate(t2, 4)
-    w2 = [S.SparseFFN.weights(**c) for c in c2]
     dense2 = {}
-    for n in (1, 4):
-        ffn = S.SparseFFN(d2, f2, n, "bf16")
-        xt = dev(inputs.make_x(0, n, d2, "bf16"))
-        y = torch.empty(n, d2, dtype=torch.float32, device="cuda")
-        dense2[n] = timed(ffn, xt, w2, "dense_relu", y, 100, 10)
-    del c2, w2, t2
+    if want("lopa"):
+        wl2 = W["llama7b_ffn_bf16_d4096_f11008"]
+        d2, f2 = wl2.d_model, wl2.d_ff
+        lay2 = inputs.make_layer(0, d2, f2, "bf16")
+        t2 = {"w_gate": dev(lay2.w_gate), "w_up": dev(lay2.w_up), "w_down": dev(lay2.w_down)}
+        c2 = replicate(t2, 4)
+        w2 = [S.SparseFFN.weights(**c) for c in c2]
+        for n in (1, 4):
+            ffn = S.SparseFFN(d2, f2, n, "bf16")
+            xt = dev(inputs.make_x(0, n, d2, "bf16"))
+            y = torch.empty(n, d2, dtype=torch.float32, device="cuda")
+            dense2[n] = timed(ffn, xt, w2, "dense_relu", y, 100, 10)
+        del c2, w2, t2
+    if want("tiny"):
+        out += points_tiny(W, S, inputs, torch, timed_union(torch))
+    if want("lopa"):
+        out += points_lopa(W, S, inputs, torch, dev, dense2, timed_union(torch), replicate)
+    if want("moc"):
+        out += points_moc(W, S, inputs, torch, dev, timed_union(torch), replicate)
+    if want("prefill"):
+        out += points_prefill(W, S, inputs, torch, dev, timed_union(torch), replicate)
+    return out
 
-    # tiny fp32 layer: cache-resident, latency and tokens/s only
+
+def timed_union(torch):
+    def union(ffn, xt, w, mode, y, tau=0.0, k=0):
+        u = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ffn.forward(xt, w, mode, y, tau=tau, k=k, union_cnt=u)
+        torch.cuda.synchronize()
+        return int(u.item())
+    return union
+
+
+def points_tiny(W, S, inputs, torch, union):
+    """Tiny fp32 layer: cache-resident, latency and tokens/s only."""
+    out = []
     wl = W["tiny_swiglu_fp32_d256_f1024"]
     lay = inputs.make_layer(0, wl.d_model, wl.d_ff, "f32")
     tt = {"w_gate": torch.from_numpy(lay.w_gate).cuda(), "w_up": torch.from_numpy(lay.w_up).cuda(),
@@ -154,8 +182,13 @@ def measure_points(args, dev, S, inputs, np, torch):
         out.append({"workload": wl.name, "tokens": n, "mode": "threshold", "tau": 1.2816, "union": na,
                     "us_per_step": round(sp * 1e6, 2), "tokens_per_s": round(n / sp, 1),
                     "speedup_vs_dense": round(de / sp, 3), "note": "cache-resident (3 MB): no HBM fraction"})
+    return out
 
-    # LoPA low-rank gate
+
+def points_lopa(W, S, inputs, torch, dev, dense2, union, replicate):
+    """LoPA low-rank gate, speedup against the dense Llama-7B-shaped layer."""
+    out = []
+    es = 2
     wl = W["lopa_gate_bf16_d4096_f11008"]
     d, f = wl.d_model, wl.d_ff
     for r in wl.ranks:
@@ -178,8 +211,13 @@ def measure_points(args, dev, S, inputs, np, torch):
             del cl, wlist
         del base
         torch.cuda.empty_cache()
+    return out
 
-    # Mixture-of-Channels Top-K (decode and batched)
+
+def points_moc(W, S, inputs, torch, dev, union, replicate):
+    """Mixture-of-Channels Top-K, decode and batched."""
+    out = []
+    es = 2
     wl = W["moc_topk_bf16_d2048_f5632"]
     d, f = wl.d_model, wl.d_ff
     lay = inputs.make_layer(0, d, f, "bf16")
@@ -202,8 +240,12 @@ def measure_points(args, dev, S, inputs, np, torch):
                         "layer_copies": len(wlist)})
     del cl, wlist, base
     torch.cuda.empty_cache()
+    return out
 
-    # 70B-shaped prefill layer on the MFMA union path
+
+def points_prefill(W, S, inputs, torch, dev, union, replicate):
+    """70B-shaped prefill layer on the MFMA union path."""
+    out = []
     wl = W["prefill70b_ffn_bf16_d8192_f28672"]
     d, f = wl.d_model, wl.d_ff
     lay = inputs.make_layer(0, d, f, "bf16")
@@ -347,7 +389,7 @@ def main():
     # ---- the other workloads ----
     pts = []
     n_copies = len(weights)
-    if not args.no_sweep and not args.no_points:
+    if not args.no_points and (args.only or not args.no_sweep):
         del weights, copies, base
         torch.cuda.empty_cache()
         pts = measure_points(args, dev, S, inputs, np, torch)

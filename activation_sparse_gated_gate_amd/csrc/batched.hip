@@ -28,6 +28,7 @@
 // kernel that applies the same epilogue.
 #include <type_traits>
 
+#include "compact.h"
 #include "device_common.h"
 #include "sffn_internal.h"
 

@@ -22,6 +22,7 @@
 // Active channels are byte flags act[t][i] with one writer each, so any row
 // partition works without atomics. No kernel waits on another workgroup:
 // cross-workgroup results go through global memory and the next kernel.
+#include "compact.h"
 #include "rowdot.h"
 
 namespace sffn {

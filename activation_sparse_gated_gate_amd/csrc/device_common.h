@@ -166,37 +166,6 @@ __device__ __forceinline__ int block_incl_scan(int v, int *scratch)
     return v + add;
 }
 
-// Ordered compaction of one row of flags, for a block of 256 threads: writes
-// the channels i < F whose flag is set to out[0 .. count) in ascending order
-// (out may be null) and returns count to every thread. Chunks of 2048
-// channels, 8 consecutive ones per thread (coalesced reads); a block scan of
-// the per-thread counts places them. on8(i0, f) sets f[e] for channel i0 + e
-// (false from F on). scratch holds 5 ints. Contains barriers.
-template <typename On8>
-__device__ __forceinline__ int emit_ordered(int F, On8 on8, int32_t *out, int *scratch)
-{
-    int base = 0;
-    for (int c0 = 0; c0 < F; c0 += 2048) {
-        const int i0 = c0 + 8 * (int)threadIdx.x;
-        bool f[8];
-        on8(i0, f);
-        int local = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) local += f[e];
-        const int incl = block_incl_scan(local, scratch);
-        int pos = base + incl - local;
-        if (out)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (f[e]) out[pos++] = i0 + e;
-        if (threadIdx.x == blockDim.x - 1) scratch[4] = incl;
-        __syncthreads();
-        base += scratch[4];
-        __syncthreads();
-    }
-    return base;
-}
-
 // Order-preserving map from fp32 to uint32 (larger float -> larger key).
 // -0 is folded onto +0 so that equal values get equal keys.
 __device__ __forceinline__ uint32_t f2key(float f)

@@ -417,7 +417,6 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const
 // Chunks outside the operands (rows past M or past the union, K past the
 // end) are loaded from a zero block.
 // ---------------------------------------------------------------------------
-constexpr int kDmaBK = 64;
 
 // Source of the chunks outside the operands; never written.
 static __device__ __align__(16) uint4 g_zero16[1] = {};
@@ -434,15 +433,20 @@ __device__ __forceinline__ void wait_vm_lgkm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-template <int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
-__global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
+template <int TM, int TN, int WM, int WN, int BKT, int NS, int OCC, bool BNN, int EK, int GM>
+__global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int K, const bf16_t *__restrict__ A,
+                                                              int lda,
                                                          const bf16_t *__restrict__ B, int ldb,
                                                          const int32_t *__restrict__ bidx,
                                                          const int *__restrict__ ncount, float *__restrict__ part,
                                                          int part_ld, EpiArgs epi)
 {
     constexpr int MF = 32, NW = WM * WN, NTHR = 64 * NW;
-    constexpr int BM = MF * TM * WM, BN = MF * TN * WN, BK = kDmaBK;
+    constexpr int BM = MF * TM * WM, BN = MF * TN * WN, BK = BKT;
+    static_assert(BK == 64 || (BK == 32 && !BNN), "K step 64, or 32 for the K-contiguous form");
+    static_assert(NS == 3 || ((NS == 2 || NS == 4) && !BNN), "three stages, or two / four for the K-contiguous form");
+    constexpr int CH = BK / 8;                      // K chunks per tile row
+    constexpr int SWS = BK == 64 ? 1 : 2;           // log2(tile rows per 256-byte bank window)
     constexpr int CPR = BN / 8, RPI = 64 / CPR;     // BNN: chunks per K row, K rows per instruction
     constexpr int APW = BM * (BK / 8) / 64 / NW;    // 16-byte load instructions per wavefront and stage: A
     constexpr int BPW = BN * (BK / 8) / 64 / NW;    // and B
@@ -452,7 +456,8 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     typedef __attribute__((ext_vector_type(16))) float accv;
     // stage s: A tile at 0, B tile at BM * BK (one array per stage: the
     // compiler tells at most eight direct-to-LDS targets apart)
-    __shared__ __align__(16) bf16_t St0[(BM + BN) * BK], St1[(BM + BN) * BK], St2[(BM + BN) * BK];
+    __shared__ __align__(16) bf16_t St0[(BM + BN) * BK], St1[(BM + BN) * BK], St2[NS > 2 ? (BM + BN) * BK : 8],
+        St3[NS > 3 ? (BM + BN) * BK : 8];
     __shared__ __align__(16) int Is0[BNN ? BK : 1], Is1[BNN ? BK : 1], Is2[BNN ? BK : 1];
     __shared__ uint32_t ubits_lds[BN / 32];
 
@@ -484,14 +489,14 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     auto nswz = [](int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
 
     // ---- per-lane sources ----
-    // K-major tiles: tile row r keeps K chunk p at slot p ^ ((r >> 1) & 7)
-    const int lr = lane >> 3;
-    auto kchunk = [&](int row) { return ((lane & 7) ^ ((row >> 1) & 7)) * 8; };
+    // K-major tiles: tile row r keeps K chunk p at slot p ^ ((r >> SWS) & (CH - 1))
+    const int lr = lane / CH;
+    auto kchunk = [&](int row) { return ((lane % CH) ^ ((row >> SWS) & (CH - 1))) * 8; };
     const bf16_t *asrc[APW];
     int alc[APW];
 #pragma unroll
     for (int j = 0; j < APW; ++j) {
-        const int r = (wave * APW + j) * 8 + lr, m = m0 + r;
+        const int r = (wave * APW + j) * (64 / CH) + lr, m = m0 + r;
         alc[j] = kchunk(r);
         asrc[j] = m < M ? A + (size_t)m * lda + alc[j] : nullptr;
     }
@@ -502,7 +507,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     if constexpr (!BNN) {
 #pragma unroll
         for (int j = 0; j < BPW; ++j) {
-            const int r = (wave * BPW + j) * 8 + lr, n = n0 + r;
+            const int r = (wave * BPW + j) * (64 / CH) + lr, n = n0 + r;
             blc[j] = kchunk(r);
             bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + blc[j] : nullptr;
         }
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
 
     auto As = [&](auto stage) -> bf16_t * {
         constexpr int SI = decltype(stage)::value;
-        return SI == 0 ? St0 : SI == 1 ? St1 : St2;
+        return SI == 0 ? St0 : SI == 1 ? St1 : SI == 2 ? St2 : St3;
     };
     auto Bs = [&](auto stage) -> bf16_t * { return As(stage) + BM * BK; };
     auto Is = [&](auto stage) -> int * {
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     }
     // Fragments of K substep ks of a stage.
     auto frags = [&](const bf16_t *sa, const bf16_t *sb, int ks, bf16x8_t (&af)[TM], bf16x8_t (&bfr)[TN]) {
-        const int sw = ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 8;
+        const int sw = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> SWS) & (CH - 1))) * 8;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
             af[i] = *reinterpret_cast<const bf16x8_t *>(sa + (arow + i * MF + (lane & 31)) * BK + sw);
@@ -612,18 +617,29 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     // (two register sets), so LDS latency hides behind the MFMAs.
     auto compute = [&](auto stage) {
         const bf16_t *sa = As(stage), *sb = Bs(stage);
-        bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
-        frags(sa, sb, 0, a0, b0);
+        if constexpr (OCC > 1 || BK / 16 < 2) {
+            // two workgroups per CU: the other one's wavefronts hide LDS
+            // latency, and one fragment set keeps the registers within half
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ks += 2) {
-            frags(sa, sb, ks + 1, a1, b1);
-            mma(a0, b0);
-            if (ks + 2 < BK / 16) frags(sa, sb, ks + 2, a0, b0);
-            mma(a1, b1);
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                bf16x8_t a0[TM], b0[TN];
+                frags(sa, sb, ks, a0, b0);
+                mma(a0, b0);
+            }
+        } else {
+            bf16x8_t a0[TM], b0[TN], a1[TM], b1[TN];
+            frags(sa, sb, 0, a0, b0);
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ks += 2) {
+                frags(sa, sb, ks + 1, a1, b1);
+                mma(a0, b0);
+                if (ks + 2 < BK / 16) frags(sa, sb, ks + 2, a0, b0);
+                mma(a1, b1);
+            }
         }
     };
-    // K step i: its loads (issued two steps earlier) have landed in every
-    // wavefront once each has waited for all but the next step's group of
+    // K step i: its loads (issued NS-1 steps earlier) have landed in every
+    // wavefront once each has waited for all but the later steps' groups of
     // loads and passed the barrier; the barrier also ends every read of the
     // stage (and index slot) that this step refills, last read in step i-1.
     // Every step issues and waits the same way: the step count is padded to
@@ -631,9 +647,9 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
     // every path through the loop has the same loads in flight.
     auto step = [&](auto stage, int i) {
         constexpr int SI = decltype(stage)::value;
-        wait_vm_lgkm<LPS>();
+        wait_vm_lgkm<LPS * (NS - 2)>();
         __builtin_amdgcn_s_barrier();
-        issue(std::integral_constant<int, (SI + 2) % 3>{}, i + 2);
+        issue(std::integral_constant<int, (SI + NS - 1) % NS>{}, i + NS - 1);
         if constexpr (BNN) issue_idx(std::integral_constant<int, (SI + 1) % 3>{}, i + 4);
         compute(stage);
     };
@@ -651,13 +667,15 @@ __global__ __launch_bounds__(64 * WM *WN) void k_mfma_dma(int M, int N, int K, c
         issue_idx(std::integral_constant<int, 0>{}, 3);
     } else {
         issue(std::integral_constant<int, 0>{}, 0);
-        issue(std::integral_constant<int, 1>{}, 1);
+        if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
+        if constexpr (NS > 3) issue(std::integral_constant<int, 2>{}, 2);
     }
-    const int nst3 = (nsteps + 2) / 3 * 3;
-    for (int i = 0; i < nst3; i += 3) {
+    const int nstp = (nsteps + NS - 1) / NS * NS;
+    for (int i = 0; i < nstp; i += NS) {
         step(std::integral_constant<int, 0>{}, i);
         step(std::integral_constant<int, 1>{}, i + 1);
-        step(std::integral_constant<int, 2>{}, i + 2);
+        if constexpr (NS > 2) step(std::integral_constant<int, 2>{}, i + 2);
+        if constexpr (NS > 3) step(std::integral_constant<int, 3>{}, i + 3);
     }
     wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
     tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
@@ -751,16 +769,19 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // ===========================================================================
 struct Cfg {
     int mf, tm, tn, wm, wn;
-    bool dma;  // NT-form GEMMs (gate, up) use the pipelined direct-to-LDS kernel
+    bool dma;  // pipelined direct-to-LDS kernel (k_mfma_dma), else k_mfma
     int bm() const { return mf * tm * wm; }
     int bn() const { return mf * tn * wn; }
-    int threads() const { return 64 * wm * wn; }
 };
 
-// Tile shapes by batch size (M = tokens).
-static Cfg cfg_for(int M)
+// Tile shapes by batch size (M = tokens) and B layout. Large batches: the
+// K-contiguous GEMMs (gate, up) take 256 x 256 tiles of 8 wavefronts (fewer
+// tile-fill bytes per FLOP: the loads from L2, not the MFMAs, bound the
+// loop), K step 32 through four stages; the down GEMM keeps 256 x 128 with K
+// step 64 (its gathered-row index ring is sized for it).
+static Cfg cfg_for(int M, bool bnn)
 {
-    if (M >= 512) return {32, 4, 2, 2, 2, true};  // 256 x 128, 4 wavefronts of 128 x 64
+    if (M >= 512) return bnn ? Cfg{32, 4, 2, 2, 2, true} : Cfg{32, 4, 2, 2, 4, true};
     if (M >= 128) return {32, 2, 2, 4, 1, true};  // 256 x 64
     if (M > 32) return {16, 1, 2, 4, 2, false};   // 64 x 64
     return {16, 1, 2, 2, 2, false};               // 32 x 64
@@ -775,12 +796,12 @@ static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf
                        ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
 }
 
-template <int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
+template <int TM, int TN, int WM, int WN, int BKT, int NS, int OCC, bool BNN, int EK, int GM>
 static void launch_dma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
                        int ldb, const int32_t *bidx, const int *ncount, float *part, int part_ld, const EpiArgs &e)
 {
-    hipLaunchKernelGGL((k_mfma_dma<TM, TN, WM, WN, BNN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
-                       ldb, bidx, ncount, part, part_ld, e);
+    hipLaunchKernelGGL((k_mfma_dma<TM, TN, WM, WN, BKT, NS, OCC, BNN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N,
+                       K, A, lda, B, ldb, bidx, ncount, part, part_ld, e);
 }
 
 template <bool BNN, int EK, int GM>
@@ -788,16 +809,25 @@ static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, 
                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
                          int pld, const EpiArgs &e)
 {
-    if (c.dma && nk == (BNN ? 1 : 0)) {
-        if (c.tm == 4) launch_dma<4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
-        else launch_dma<2, 2, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
+    if (c.dma) {
+        if constexpr (!BNN) {
+            if (c.wn == 4)
+                launch_dma<4, 2, 2, 4, 32, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
+                                                              e);
+            else
+                launch_dma<2, 2, 4, 1, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
+                                                              e);
+        } else {
+            if (c.tm == 4)
+                launch_dma<4, 2, 2, 2, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
+                                                              e);
+            else
+                launch_dma<2, 2, 4, 1, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
+                                                              e);
+        }
         return;
     }
-    if (c.mf == 32 && c.tm == 4)
-        launch_mfma<32, 4, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else if (c.mf == 32)
-        launch_mfma<32, 2, 2, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else if (c.wm == 4)
+    if (c.wm == 4)
         launch_mfma<16, 1, 2, 4, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
     else
         launch_mfma<16, 1, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
@@ -880,8 +910,8 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     ep.hld = (F + 7) / 8 * 8;
     ep.Y = a.y;
 
-    const Cfg cf = cfg_for(T);
-    const int mt = (T + cf.bm() - 1) / cf.bm();
+    const Cfg cf = cfg_for(T, false), cfd = cfg_for(T, true);
+    const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- 1. gate GEMM ----
     {
@@ -923,9 +953,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 4. down GEMM, K = union ----
     {
         ep.kind = EPI_DOWN;
-        const int nt = (d + cf.bn() - 1) / cf.bn();
-        const int sk = split_for(c, (long long)mt * nt, F / 2, T);
-        dispatch_mfma<true, EPI_DOWN>(cf, tile_grid(nt, mt, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part, d, ep);
+        const int nt = (d + cfd.bn() - 1) / cfd.bn();
+        const int sk = split_for(c, (long long)mtd * nt, F / 2, T);
+        dispatch_mfma<true, EPI_DOWN>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part,
+                                      d, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((d + 255) / 256, T), dim3(256), 0, st, part, sk, T, d, d,

@@ -6,8 +6,8 @@
 //              rows of the channels just found active -> k_down -> k_reduce
 //   LoPA       k_lopa_xa (x.A partials) -> k_gate<SELECT_UP> on B with t = x.A
 //              -> k_down -> k_reduce
-//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (radix select of each
-//              token's K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
+//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
+//              K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
 //              -> k_reduce
 //

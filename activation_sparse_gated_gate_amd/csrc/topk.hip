@@ -8,229 +8,21 @@
 // (topk_on), so ties at the K-th value go to the lower channel indices and
 // exactly K channels are selected. The consumer applies that rule where it
 // reads the keys anyway: the decode up kernel, or k_topk_flags for a batch.
-#include "device_common.h"
+#include "select.h"
 #include "sffn_internal.h"
 
 namespace sffn {
 
-// ---------------------------------------------------------------------------
-// One workgroup (1024 threads) per token.
-//
-// Stage 1 bins the keys by value: 2048 equal-width bins over the token's
-// [min, max]. The bin of a value is a non-decreasing function of it (a
-// subtraction and a scaling, both rounded monotonically, then a floor), so
-// every key of a higher bin is at least as large as every key of a lower one
-// and the K-th largest lies in the bin where the count from the top reaches
-// K. Equal keys share a bin. SiLU keys crowd into a few exponent values, so
-// value bins spread the histogram atomics where a radix digit of the leading
-// bits would pile them onto a handful of LDS words.
-//
-// Stage 2 resolves that bin exactly. Up to 64 candidates are gathered in LDS
-// and one wavefront ranks them by (key descending, channel ascending).
-// Larger bins go through an MSD radix select restricted to the bin: 8 bits
-// per pass over the order-preserving 32-bit keys with a 256-bin histogram
-// (radix k-selection as in Alabi, Blanchard, Gordon & Steinbach, "Fast
-// k-Selection Algorithms for Graphics Processing Units", 2012), then a block
-// scan of the keys equal to the K-th gives the tie cutoff.
-//
-// KPT > 0: thread j holds keys [KPT j, KPT j + KPT) in registers (F <= 1024
-// KPT) and the keys are read from memory once. KPT == 0: any F, the keys are
-// re-read at every stage.
-// ---------------------------------------------------------------------------
+// One workgroup (1024 threads) per token; the select itself is select_kth
+// (select.h).
 template <int KPT>
 __global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ keys, int F, int K,
                                                    int2 *__restrict__ thr)
 {
-    constexpr int NTHR = 1024, NB = 2048, CMAX = 64;
-    __shared__ __align__(16) int hist[NB];  // value bins, later 3 x 256 radix bins
-    __shared__ float red[2][16];
-    __shared__ uint32_t cand_key[CMAX];
-    __shared__ int cand_idx[CMAX];
-    __shared__ int sh[4];  // bin of the K-th, keys of it still needed, count in it, gathered
-    __shared__ int scan_scratch[16];
+    __shared__ SelectLds L;
     const int t = blockIdx.x;
-    const float *s = keys + (size_t)t * F;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    float kf[KPT > 0 ? KPT : 1];
-    if constexpr (KPT > 0) {
-        const int i0 = tid * KPT;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) kf[e] = (i0 + e < F) ? s[i0 + e] : 0.f;
-    }
-    // fn(i, v) over this thread's keys
-    auto for_keys = [&](auto &&fn) {
-        if constexpr (KPT > 0) {
-#pragma unroll
-            for (int e = 0; e < KPT; ++e)
-                if (tid * KPT + e < F) fn(tid * KPT + e, kf[e]);
-        } else {
-            for (int i = tid; i < F; i += NTHR) fn(i, s[i]);
-        }
-    };
-
-    // ---- range ----
-    float lo = INFINITY, hi = -INFINITY;
-    for_keys([&](int, float v) {
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-    });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o, 64));
-        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-    }
-    if (lane == 0) {
-        red[0][wave] = lo;
-        red[1][wave] = hi;
-    }
-    for (int b = tid; b < NB; b += NTHR) hist[b] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        lo = fminf(lo, red[0][w]);
-        hi = fmaxf(hi, red[1][w]);
-    }
-    if (!(hi > lo)) {  // every key equal: the first K channels
-        if (tid == 0) thr[t] = make_int2((int)f2key(lo), K - 1);
-        return;
-    }
-    float scale = (float)NB / (hi - lo);
-    if (!(scale < 1e30f)) scale = 0.f;  // range too narrow to scale: one bin, resolved below
-    auto bin_of = [&](float v) {
-        const float q = (v - lo) * scale;  // >= 0
-        return q >= (float)NB ? NB - 1 : (int)q;
-    };
-
-    // ---- stage 1: value histogram, bin of the K-th ----
-    for_keys([&](int, float v) { atomicAdd(&hist[bin_of(v)], 1); });
-    __syncthreads();
-    if (wave == 0) {
-        // lane l owns bins NB-1-32l .. NB-32-32l (descending); the counts
-        // are read twice (total, then the search) to keep registers low
-        const int4 *row = reinterpret_cast<const int4 *>(&hist[NB - 32 - 32 * lane]);
-        int tot = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int4 v = row[q];
-            tot += v.x + v.y + v.z + v.w;
-        }
-        int run = wave_incl_scan(tot) - tot;
-        const int need = K;
-#pragma unroll
-        for (int q = 7; q >= 0; --q) {
-            const int4 v = row[q];
-            const int c[4] = {v.w, v.z, v.y, v.x};  // bins NB-32-32l+4q+3 .. +0
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (run < need && need <= run + c[e]) {
-                    sh[0] = NB - 32 - 32 * lane + 4 * q + 3 - e;
-                    sh[1] = need - run;
-                    sh[2] = c[e];
-                    sh[3] = 0;
-                }
-                run += c[e];
-            }
-        }
-    }
-    __syncthreads();
-    const int bstar = sh[0], cnt = sh[2];
-    int need = sh[1];
-
-    // ---- stage 2a: few candidates, ranked by one wavefront ----
-    if (cnt <= CMAX) {
-        for_keys([&](int i, float v) {
-            if (bin_of(v) == bstar) {
-                const int slot = atomicAdd(&sh[3], 1);
-                cand_key[slot] = f2key(v);
-                cand_idx[slot] = i;
-            }
-        });
-        __syncthreads();
-        if (wave == 0 && lane < cnt) {
-            const uint32_t mk = cand_key[lane];
-            const int mi = cand_idx[lane];
-            int rank = 0;
-            for (int m = 0; m < cnt; ++m) {
-                const uint32_t ok = cand_key[m];
-                rank += ok > mk || (ok == mk && cand_idx[m] < mi);
-            }
-            if (rank == need - 1) thr[t] = make_int2((int)mk, mi);
-        }
-        return;
-    }
-
-    // ---- stage 2b: radix select within the bin ----
-    // Three buffers rotate so a pass needs one barrier: every wavefront scans
-    // the finished histogram itself, and pass p clears the buffer of pass
-    // p + 1, last read in pass p - 2.
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    uint32_t prefix = 0, pmask = 0;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int shift = 24 - 8 * p;
-        int *h = hist + 256 * (p % 3);
-        if (tid < 256) hist[256 * ((p + 1) % 3) + tid] = 0;
-        for_keys([&](int, float v) {
-            const uint32_t key = f2key(v);
-            if (bin_of(v) == bstar && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1);
-        });
-        __syncthreads();
-        // lane l owns bins 255-4l .. 252-4l (descending)
-        const int4 c4 = *reinterpret_cast<const int4 *>(&h[252 - 4 * lane]);
-        const int c[4] = {c4.w, c4.z, c4.y, c4.x};
-        const int tot = c[0] + c[1] + c[2] + c[3];
-        int run = wave_incl_scan(tot) - tot;
-        int my_digit = -1, my_need = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (run < need && need <= run + c[e]) {
-                my_digit = 255 - (lane * 4 + e);
-                my_need = need - run;
-            }
-            run += c[e];
-        }
-        const unsigned long long hit = __ballot(my_digit >= 0);
-        const int src = __ffsll((long long)hit) - 1;
-        const int digit = __shfl(my_digit, src, 64);
-        need = __shfl(my_need, src, 64);
-        prefix |= (uint32_t)digit << shift;
-        pmask |= 0xffu << shift;
-    }
-    const uint32_t kth = prefix;
-
-    // need = how many keys equal to the K-th belong to the set: the first
-    // `need` of them in channel order. Contiguous segments per thread make
-    // "equal keys before mine" an exclusive block scan.
-    const int seg = KPT > 0 ? KPT : (F + NTHR - 1) / NTHR;
-    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
-    int eq_local = 0;
-    if constexpr (KPT > 0) {
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) eq_local += (i0 + e < i1 && f2key(kf[e]) == kth);
-    } else {
-        for (int i = i0; i < i1; ++i) eq_local += f2key(s[i]) == kth;
-    }
-    const int eq_before = block_incl_scan(eq_local, scan_scratch) - eq_local;
-    if (eq_before < need && need <= eq_before + eq_local) {
-        int left = need - eq_before, cut = i0;
-        if constexpr (KPT > 0) {
-#pragma unroll
-            for (int e = 0; e < KPT; ++e)
-                if (i0 + e < i1 && f2key(kf[e]) == kth && left > 0) {
-                    cut = i0 + e;
-                    --left;
-                }
-        } else {
-            for (int i = i0; i < i1 && left > 0; ++i)
-                if (f2key(s[i]) == kth) {
-                    cut = i;
-                    --left;
-                }
-        }
-        thr[t] = make_int2((int)kth, cut);
-    }
+    const int2 r = select_kth<KPT>(keys + (size_t)t * F, F, K, L);
+    if (threadIdx.x == 0) thr[t] = r;
 }
 
 // Batched: act[t][i] from the thresholds, and the union bitmap. Block (x, y)

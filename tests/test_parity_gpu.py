@@ -169,10 +169,11 @@ def test_topk_k1_and_ties():
 
 
 @pytest.mark.parametrize("f", [4096, 4097, 8193, 16385, 32769])
-@pytest.mark.parametrize("n", [3, 12])
+@pytest.mark.parametrize("n", [1, 3, 12])
 def test_topk_select_sizes_and_tie_cut(f, n):
     """Every register-cache size of the per-token select (and the uncached one
-    above 16384 channels), decode (n=3) and batched (n=12), with K chosen so
+    above 16384 channels), one token (fused select + up kernel), decode (n=3)
+    and batched (n=12), with K chosen so
     that token 0's cut falls inside a group of four exactly tied channels
     spread over the channel range."""
     d = 64
@@ -198,7 +199,7 @@ def test_topk_select_sizes_and_tie_cut(f, n):
         assert list(got.sets[0, tied]) == [True, True, False, False]
 
 
-@pytest.mark.parametrize("n", [2, 12])
+@pytest.mark.parametrize("n", [1, 2, 12])
 def test_topk_select_crowded_bin(n):
     """More than 64 keys in the bin of the K-th value: 100 exactly tied
     channels at the cut, and a layer whose one huge gate row stretches the
@@ -235,7 +236,7 @@ def test_topk_select_crowded_bin(n):
     assert (got.cnt[:n] == 400).all()
 
 
-@pytest.mark.parametrize("n", [2, 12])
+@pytest.mark.parametrize("n", [1, 2, 12])
 def test_topk_all_keys_equal_takes_first_k(n):
     """A zero gate makes every key SiLU(0) = 0: the set is channels 0..K-1."""
     d, f, k = 64, 700, 123

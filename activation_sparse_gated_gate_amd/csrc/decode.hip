@@ -4,8 +4,8 @@
 // Pipeline per forward (modes as in include/sffn.h):
 //   threshold  k_gate<SELECT_UP>: gate GEMV, shifted-ReLU select, and the W_up
 //              rows of the channels just found active -> k_down -> k_reduce
-//   LoPA       k_lopa_xa (x.A partials) -> k_gate<SELECT_UP> on B with t = x.A
-//              -> k_down -> k_reduce
+//   LoPA       k_lopa_xa (x.A partials) -> k_lopa_t (their ordered sum t) ->
+//              k_gate<SELECT_UP> on B with t -> k_down -> k_reduce
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
 //              K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
@@ -236,6 +236,20 @@ __global__ __launch_bounds__(256) void k_lopa_xa(const TW *__restrict__ x, int n
                 tpart[((size_t)s * kDecodeMaxTokens + t) * r + row0 + q] = dot.acc[q][t];
 }
 
+// t[t][k] = sum over slices s (ascending, from zero) of tpart[s][t][k]: the
+// order the gate kernel would use summing the slices itself, done once here
+// instead of in every wavefront that reads t.
+__global__ __launch_bounds__(256) void k_lopa_t(const float *__restrict__ tpart, int ks, int n, int r,
+                                                float *__restrict__ tvec)
+{
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= n * r) return;
+    const int t = o / r, k = o - t * r;
+    float v = 0.f;
+    for (int s = 0; s < ks; ++s) v += tpart[((size_t)s * kDecodeMaxTokens + t) * r + k];
+    tvec[(size_t)t * r + k] = v;
+}
+
 // ---------------------------------------------------------------------------
 // Optional outputs: each token's ascending active list and count (every
 // channel in the dense modes), and the union size. Workgroup b < n handles
@@ -396,13 +410,16 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
         hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(blocks, ks), dim3(256), 0, st, x, n, d,
                            static_cast<const TW *>(a.w.lopa_a), r, chunk, tpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        float *tvec = reinterpret_cast<float *>(ws + c.L.tvec);
+        hipLaunchKernelGGL(k_lopa_t, dim3((n * r + 255) / 256), dim3(256), 0, st, tpart, ks, n, r, tvec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         // gate rows are B (length r) dotted with t = x.A; the gate rows and
         // the up rows (length d) share the lane groups, sized for the shorter
         g.lopa = true;
         g.xg = nullptr;
         g.L = r;
-        g.tpart = tpart;
-        g.ks = ks;
+        g.tpart = tvec;
+        g.ks = 1;
         g.wg = a.w.lopa_b;
         g.lpr = lpr_for(min(r, d));
     }

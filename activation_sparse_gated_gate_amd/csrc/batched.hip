@@ -444,7 +444,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     constexpr int MF = 32, NW = WM * WN, NTHR = 64 * NW;
     constexpr int BM = MF * TM * WM, BN = MF * TN * WN, BK = BKT;
     static_assert(BK == 64 || (BK == 32 && !BNN), "K step 64, or 32 for the K-contiguous form");
-    static_assert(NS == 3 || ((NS == 2 || NS == 4) && !BNN), "three stages, or two / four for the K-contiguous form");
+    static_assert(NS == 2 || NS == 3 || (NS == 4 && !BNN), "two or three stages, or four for the K-contiguous form");
     constexpr int CH = BK / 8;                      // K chunks per tile row
     constexpr int SWS = BK == 64 ? 1 : 2;           // log2(tile rows per 256-byte bank window)
     constexpr int CPR = BN / 8, RPI = 64 / CPR;     // BNN: chunks per K row, K rows per instruction
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     // compiler tells at most eight direct-to-LDS targets apart)
     __shared__ __align__(16) bf16_t St0[(BM + BN) * BK], St1[(BM + BN) * BK], St2[NS > 2 ? (BM + BN) * BK : 8],
         St3[NS > 3 ? (BM + BN) * BK : 8];
-    __shared__ __align__(16) int Is0[BNN ? BK : 1], Is1[BNN ? BK : 1], Is2[BNN ? BK : 1];
+    __shared__ __align__(16) int Is0[BNN ? BK : 1], Is1[BNN ? BK : 1], Is2[BNN && NS == 3 ? BK : 1];
     __shared__ uint32_t ubits_lds[BN / 32];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -650,10 +650,16 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         wait_vm_lgkm<LPS * (NS - 2)>();
         __builtin_amdgcn_s_barrier();
         issue(std::integral_constant<int, (SI + NS - 1) % NS>{}, i + NS - 1);
-        if constexpr (BNN) issue_idx(std::integral_constant<int, (SI + 1) % 3>{}, i + 4);
+        if constexpr (BNN) {
+            // three stages: indices two groups ahead of their tiles (slot
+            // (i+4) % 3, last read in step i-1); two stages: one group ahead
+            // (slot (i+2) % 2, last read before this step's barrier)
+            if constexpr (NS == 3) issue_idx(std::integral_constant<int, (SI + 1) % 3>{}, i + 4);
+            else issue_idx(std::integral_constant<int, SI>{}, i + 2);
+        }
         compute(stage);
     };
-    if constexpr (BNN) {
+    if constexpr (BNN && NS == 3) {
         // indices of steps 0..2, then the tiles of steps 0 and 1 with the
         // indices of step 3 (slot 0, after every wavefront has read step 0's)
         issue_idx(std::integral_constant<int, 0>{}, 0);
@@ -665,6 +671,13 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         wait_vm_lgkm<2 * (APW + BPW)>();  // no vector-memory wait: only the index reads above
         __builtin_amdgcn_s_barrier();
         issue_idx(std::integral_constant<int, 0>{}, 3);
+    } else if constexpr (BNN) {
+        // indices of steps 0 and 1, then the tiles of step 0 (each step then
+        // waits for everything in flight)
+        issue_idx(std::integral_constant<int, 0>{}, 0);
+        issue_idx(std::integral_constant<int, 1>{}, 1);
+        wait_vm_lgkm<0>();
+        issue(std::integral_constant<int, 0>{}, 0);
     } else {
         issue(std::integral_constant<int, 0>{}, 0);
         if constexpr (NS > 2) issue(std::integral_constant<int, 1>{}, 1);
@@ -774,14 +787,14 @@ struct Cfg {
     int bn() const { return mf * tn * wn; }
 };
 
-// Tile shapes by batch size (M = tokens) and B layout. Large batches: the
-// K-contiguous GEMMs (gate, up) take 256 x 256 tiles of 8 wavefronts (fewer
-// tile-fill bytes per FLOP: the loads from L2, not the MFMAs, bound the
-// loop), K step 32 through four stages; the down GEMM keeps 256 x 128 with K
-// step 64 (its gathered-row index ring is sized for it).
-static Cfg cfg_for(int M, bool bnn)
+// Tile shapes by batch size (M = tokens). Large batches take 256 x 256 tiles
+// of 8 wavefronts (fewer tile-fill bytes per FLOP: the loads from L2, not
+// the MFMAs, bound the loop): K step 32 through four stages for the
+// K-contiguous GEMMs (gate, up), K step 64 through two stages for the down
+// GEMM (its gathered-row index ring is sized for K step 64).
+static Cfg cfg_for(int M)
 {
-    if (M >= 512) return bnn ? Cfg{32, 4, 2, 2, 2, true} : Cfg{32, 4, 2, 2, 4, true};
+    if (M >= 512) return {32, 4, 2, 2, 4, true};  // 256 x 256, 8 wavefronts
     if (M >= 128) return {32, 2, 2, 4, 1, true};  // 256 x 64
     if (M > 32) return {16, 1, 2, 4, 2, false};   // 64 x 64
     return {16, 1, 2, 2, 2, false};               // 32 x 64
@@ -818,7 +831,10 @@ static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, 
                 launch_dma<2, 2, 4, 1, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
                                                               e);
         } else {
-            if (c.tm == 4)
+            if (c.wn == 4)
+                launch_dma<4, 2, 2, 4, 64, 2, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
+                                                              e);
+            else if (c.tm == 4)
                 launch_dma<4, 2, 2, 2, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
                                                               e);
             else
@@ -910,7 +926,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     ep.hld = (F + 7) / 8 * 8;
     ep.Y = a.y;
 
-    const Cfg cf = cfg_for(T, false), cfd = cfg_for(T, true);
+    const Cfg cf = cfg_for(T);
+    Cfg cfd = cf;
+    // the down GEMM's N is d_model: keep 256 x 256 tiles only while they
+    // still give every CU a workgroup, else 256 x 128 (twice the tiles)
+    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{32, 4, 2, 2, 2, true};
     const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- 1. gate GEMM ----

@@ -936,10 +936,16 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 1. gate GEMM ----
     {
         ep.kind = EPI_GATE;
-        const int nt = (F + cf.bn() - 1) / cf.bn();
-        const int sk = split_for(c, (long long)mt * nt, d, T);
+        // 256 <= T < 512: the gate GEMM reads every weight row once either
+        // way, but 256 x 64 tiles re-read the activation block for every
+        // 64 channels; 256 x 256 tiles split K in two instead
+        const bool wide = T >= 256 && T < 512;
+        const Cfg cg = wide ? Cfg{32, 4, 2, 2, 4, true} : cf;
+        const int nt = (F + cg.bn() - 1) / cg.bn(), mtg = (T + cg.bm() - 1) / cg.bm();
+        const int sk = wide ? 2 : split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
-        dispatch_mfma<false, EPI_GATE>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F, ep);
+        dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F,
+                                       ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,

@@ -49,7 +49,11 @@ Layout make_layout(const sffn_shape &s)
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(batched ? T * F * 4 : 0);
     L.ubits = take((size_t)L.words * 4);
-    L.bpart = take(batched && T < 512 ? 8 * T * (F > d ? F : d) * 4 : 0);
+    // room for every split a forward of up to T tokens takes, at least 16
+    // splits of 64 tokens (forwards smaller than the handle's maximum)
+    const size_t prow = T < 512 ? (size_t)splits_max((int)T) * T : 0, pmin = 16 * (T < 64 ? T : 64);
+    L.bpart_rows = batched ? (int)(prow > pmin ? prow : pmin) : 0;
+    L.bpart = take((size_t)L.bpart_rows * (F > d ? F : d) * 4);
     L.thr = take(rows * 8);
     L.total = off;
     return L;

@@ -20,12 +20,11 @@
 //
 // GEMM tiles use v_mfma_f32_32x32x16_bf16 (operand lane l: row l%32, k
 // 8*(l/32)..+7; accumulator register i: row 8*(i/4) + 4*(l/32) + i%4, column
-// l%32) or v_mfma_f32_16x16x32_bf16 (row l%16, k 8*(l/16)..+7; register i:
-// row 4*(l/16) + i, column l%16). Tiles of A and B are staged in LDS (double
-// buffered, K step 32); B is stored [n][k] in LDS, so the down projection's
-// row-major W_down rows are transposed on their way in. When the grid would be
-// too small, K is split and the fp32 partials are summed in order by a second
-// kernel that applies the same epilogue.
+// l%32). Tiles of A and B go straight from global memory to LDS through a
+// ring of stages; the down projection's N-contiguous W_down rows are read
+// out of LDS with transpose reads. When the grid would be too small, K is
+// split and the fp32 partials are summed in order by a second kernel that
+// applies the same epilogue.
 #include <type_traits>
 
 #include "compact.h"
@@ -40,8 +39,6 @@ typedef __attribute__((address_space(3))) bf16x4_t lbf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t_;
 
-constexpr int kBK = 32;           // K step of a tile
-constexpr int kPitch = kBK + 8;   // LDS row pitch in bf16 (80 bytes, 16-byte aligned rows)
 
 // fp32 -> bf16, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f2bf(float f)
@@ -221,173 +218,14 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
 
 
 // ---------------------------------------------------------------------------
-// GEMM  C[M x N] = A[M x K] . B, A row-major (K contiguous, leading dim lda).
-//   BNN = false: B rows are the N outputs, K contiguous: row n at
-//                B + rowmap(n) * ldb (rowmap = bidx or identity)
-//   BNN = true:  B rows are the K inputs, N contiguous: row k at
-//                B + rowmap(k) * ldb
-// Limits: rows m < M; columns n < nlim; k < klim. nlim / klim come from
-// *ncount when it is set (device-side union size), else from N / K.
-// Split-K: blockIdx.z takes K range [klim z / S, klim (z+1) / S) rounded to
-// the K step; with S > 1 the fp32 tile goes to part[z][m][n].
-// ---------------------------------------------------------------------------
-template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
-__global__ __launch_bounds__(64 * WM *WN) void k_mfma(int M, int N, int K, const bf16_t *__restrict__ A, int lda,
-                                                     const bf16_t *__restrict__ B, int ldb,
-                                                     const int32_t *__restrict__ bidx, const int *__restrict__ ncount,
-                                                     int ncount_is_k, float *__restrict__ part, int part_ld,
-                                                     EpiArgs epi)
-{
-    constexpr int NTHR = 64 * WM * WN;
-    constexpr int BM = MF * TM * WM, BN = MF * TN * WN;
-    constexpr int ACC = MF == 32 ? 16 : 4;
-    typedef __attribute__((ext_vector_type(ACC))) float accv;
-    __shared__ __align__(16) bf16_t As[2][BM * kPitch];
-    __shared__ __align__(16) bf16_t Bs[2][BN * kPitch];
-    __shared__ uint32_t ubits_lds[BN / 32 > 0 ? BN / 32 : 1];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    // Tile order: workgroups are dealt round-robin over the 8 XCDs. Block b
-    // runs on XCD b % 8; on each XCD the M tiles of one N tile follow each
-    // other, so a weight panel is fetched into that XCD's L2 once and used by
-    // every M tile, and the N tiles are interleaved over the XCDs.
-    const int MT = (M + BM - 1) / BM, NTT = (N + BN - 1) / BN;
-    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
-    const int mi = j % MT, ni = (j / MT) * 8 + xcd;
-    if (ni >= NTT) return;
-    const int m0 = mi * BM, n0 = ni * BN;
-    int nlim = N, klim = K;
-    if (ncount) {
-        if (ncount_is_k) klim = min(K, *ncount);
-        else nlim = min(N, *ncount);
-    }
-    if (n0 >= nlim || m0 >= M) return;  // tile beyond the device-side size (uniform)
-    const int S = gridDim.z;
-    int kb = 0, ke = klim;
-    if (S > 1) {
-        const int steps = (klim + kBK - 1) / kBK;
-        kb = (int)(((long long)steps * blockIdx.z) / S) * kBK;
-        ke = min(klim, (int)(((long long)steps * (blockIdx.z + 1)) / S) * kBK);
-    }
-
-    // ---- global -> register staging ----
-    constexpr int ACH = BM * (kBK / 8);                  // 16-byte chunks of an A tile
-    constexpr int BCH = BN * (kBK / 8);                  // and of a B tile
-    constexpr int AIT = (ACH + NTHR - 1) / NTHR, BIT = (BCH + NTHR - 1) / NTHR;
-    uint4 ra[AIT], rb[BIT];
-    // B row pointers are fixed for the NT form (rows = output columns)
-    auto load = [&](int k) {
-#pragma unroll
-        for (int it = 0; it < AIT; ++it) {
-            const int c = tid + it * NTHR;
-            const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-            ra[it] = make_uint4(0, 0, 0, 0);
-            if (c < ACH && m0 + row < M && k + kc < ke)
-                ra[it] = *reinterpret_cast<const uint4 *>(A + (size_t)(m0 + row) * lda + k + kc);
-        }
-#pragma unroll
-        for (int it = 0; it < BIT; ++it) {
-            const int c = tid + it * NTHR;
-            rb[it] = make_uint4(0, 0, 0, 0);
-            if (c >= BCH) continue;
-            if constexpr (!BNN) {
-                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-                const int n = n0 + row;
-                if (n < nlim && k + kc < ke) {
-                    const int src = bidx ? bidx[n] : n;
-                    rb[it] = *reinterpret_cast<const uint4 *>(B + (size_t)src * ldb + k + kc);
-                }
-            } else {
-                const int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
-                const int kk = k + krow;
-                if (kk < ke && n0 + nc < nlim) {
-                    const int src = bidx ? bidx[kk] : kk;
-                    rb[it] = *reinterpret_cast<const uint4 *>(B + (size_t)src * ldb + n0 + nc);
-                }
-            }
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < AIT; ++it) {
-            const int c = tid + it * NTHR;
-            if (c < ACH) {
-                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&As[buf][row * kPitch + kc]) = ra[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < BIT; ++it) {
-            const int c = tid + it * NTHR;
-            if (c >= BCH) continue;
-            if constexpr (!BNN) {
-                const int row = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-                *reinterpret_cast<uint4 *>(&Bs[buf][row * kPitch + kc]) = rb[it];
-            } else {
-                // transpose: 8 consecutive columns of one k row -> column-major in LDS
-                const int krow = c / (BN / 8), nc = (c % (BN / 8)) * 8;
-                const uint32_t w[4] = {rb[it].x, rb[it].y, rb[it].z, rb[it].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Bs[buf][(nc + e) * kPitch + krow] = (bf16_t)((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-            }
-        }
-    };
-
-    accv acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < ACC; ++r) acc[i][j][r] = 0.f;
-
-    const int arow = wm * MF * TM, bcol = wn * MF * TN;
-    const int fr = lane % MF, fk = (lane / MF) * 8;
-    int buf = 0;
-    if (kb < ke) {
-        load(kb);
-        store(0);
-    }
-    __syncthreads();
-    for (int k = kb; k < ke; k += kBK) {
-        const bool more = k + kBK < ke;
-        if (more) load(k + kBK);
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += (MF == 32 ? 16 : 32)) {
-            bf16x8_t af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t *>(&As[buf][(arow + i * MF + fr) * kPitch + kk + fk]);
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t *>(&Bs[buf][(bcol + j * MF + fr) * kPitch + kk + fk]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    if constexpr (MF == 32)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                }
-        }
-        if (more) store(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
-    }
-
-    tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
-                                                ubits_lds);
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined GEMM, v_mfma_f32_32x32x16_bf16, K step 64.
+// GEMM C[M x N] = A[M x K] . B on v_mfma_f32_32x32x16_bf16, A row-major (K
+// contiguous, leading dim lda):
 //   BNN = false (gate, up): B rows are the N outputs, K contiguous, gathered
 //                through bidx (or identity); N limited by *ncount if set.
 //   BNN = true  (down):     B rows are the K inputs, N contiguous, gathered
 //                through bidx; K limited by *ncount.
+// Rows m < M. Split-K: blockIdx.z takes K range [klim z / S, klim (z+1) / S)
+// rounded to the K step; with S > 1 the fp32 tile goes to part[z][m][n].
 //
 // Tiles move from global memory straight into LDS (direct-to-LDS loads, no
 // register staging) through a ring of three stages, so the loads of K steps
@@ -697,6 +535,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
 
 // Sum the split-K partials in order and apply the epilogue (gate: also the
 // union bits, one atomic per word and block).
+template <int SM>
 __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict__ part, int S, int M, int N,
                                                          int part_ld, const int *__restrict__ ncount, EpiArgs epi)
 {
@@ -707,8 +546,15 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     if (threadIdx.x < 8) ub[threadIdx.x] = 0;
     __syncthreads();
     if (n < nlim) {
+        // all S (<= SM) partial loads in flight at once, then summed in split
+        // order; splits past S re-read the last one and are not added
+        float p[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) p[s] = part[((size_t)min(s, S - 1) * M + m) * part_ld + n];
         float v = 0.f;
-        for (int s = 0; s < S; ++s) v += part[((size_t)s * M + m) * part_ld + n];
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
+            if (s < S) v += p[s];
         if (epilogue(epi, m, n, v) && epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD)
             atomicOr(&ub[threadIdx.x / 32], 1u << (n & 31));
     } else if (epi.kind == EPI_UP && n < ((nlim + 7) & ~7)) {
@@ -780,11 +626,12 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // ===========================================================================
 // Host side
 // ===========================================================================
+// Tile shape of k_mfma_dma: TM x TN 32 x 32 MFMA tiles per wavefront, WM x WN
+// wavefronts.
 struct Cfg {
-    int mf, tm, tn, wm, wn;
-    bool dma;  // pipelined direct-to-LDS kernel (k_mfma_dma), else k_mfma
-    int bm() const { return mf * tm * wm; }
-    int bn() const { return mf * tn * wn; }
+    int tm, tn, wm, wn;
+    int bm() const { return 32 * tm * wm; }
+    int bn() const { return 32 * tn * wn; }
 };
 
 // Tile shapes by batch size (M = tokens). Large batches take 256 x 256 tiles
@@ -794,19 +641,10 @@ struct Cfg {
 // GEMM (its gathered-row index ring is sized for K step 64).
 static Cfg cfg_for(int M)
 {
-    if (M >= 512) return {32, 4, 2, 2, 4, true};  // 256 x 256, 8 wavefronts
-    if (M >= 128) return {32, 2, 2, 4, 1, true};  // 256 x 64
-    if (M > 32) return {16, 1, 2, 4, 2, false};   // 64 x 64
-    return {16, 1, 2, 2, 2, false};               // 32 x 64
-}
-
-template <int MF, int TM, int TN, int WM, int WN, bool BNN, int EK, int GM>
-static void launch_mfma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
-                        int ldb, const int32_t *bidx, const int *ncount, int ncount_is_k, float *part, int part_ld,
-                        const EpiArgs &e)
-{
-    hipLaunchKernelGGL((k_mfma<MF, TM, TN, WM, WN, BNN, EK, GM>), grid, dim3(64 * WM * WN), 0, st, M, N, K, A, lda, B,
-                       ldb, bidx, ncount, ncount_is_k, part, part_ld, e);
+    if (M >= 512) return {4, 2, 2, 4};  // 256 x 256, 8 wavefronts
+    if (M >= 128) return {2, 2, 4, 1};  // 256 x 64
+    if (M > 64) return {2, 1, 2, 2};    // 128 x 64
+    return {1, 1, 1, 2};                // 32 x 64, 2 wavefronts (two M tiles above 32)
 }
 
 template <int TM, int TN, int WM, int WN, int BKT, int NS, int OCC, bool BNN, int EK, int GM>
@@ -819,72 +657,82 @@ static void launch_dma(dim3 grid, hipStream_t st, int M, int N, int K, const bf1
 
 template <bool BNN, int EK, int GM>
 static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
-                         const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
-                         int pld, const EpiArgs &e)
+                         const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, float *part, int pld,
+                         const EpiArgs &e)
 {
-    if (c.dma) {
-        if constexpr (!BNN) {
-            if (c.wn == 4)
-                launch_dma<4, 2, 2, 4, 32, 4, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
-                                                              e);
-            else
-                launch_dma<2, 2, 4, 1, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
-                                                              e);
-        } else {
-            if (c.wn == 4)
-                launch_dma<4, 2, 2, 4, 64, 2, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
-                                                              e);
-            else if (c.tm == 4)
-                launch_dma<4, 2, 2, 2, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
-                                                              e);
-            else
-                launch_dma<2, 2, 4, 1, 64, 3, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
-                                                              e);
-        }
-        return;
+#define SFFN_D(TM, TN, WM, WN, BK, NS) \
+    launch_dma<TM, TN, WM, WN, BK, NS, 1, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e)
+    // small batches (tn == 1): 32 or 128 x 64 tiles, K step 64, four stages
+    // (three for the gathered-row down GEMM)
+    constexpr int NSS = BNN ? 3 : 4;
+    if (c.tn == 1) {
+        if (c.wm == 2) SFFN_D(2, 1, 2, 2, 64, NSS);
+        else SFFN_D(1, 1, 1, 2, 64, NSS);
+    } else if constexpr (!BNN) {
+        if (c.wn == 4) SFFN_D(4, 2, 2, 4, 32, 4);
+        else SFFN_D(2, 2, 4, 1, 64, 3);
+    } else {
+        if (c.wn == 4) SFFN_D(4, 2, 2, 4, 64, 2);
+        else if (c.tm == 4) SFFN_D(4, 2, 2, 2, 64, 3);
+        else SFFN_D(2, 2, 4, 1, 64, 3);
     }
-    if (c.wm == 4)
-        launch_mfma<16, 1, 2, 4, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
-    else
-        launch_mfma<16, 1, 2, 2, 2, BNN, EK, GM>(grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+#undef SFFN_D
 }
 
 template <bool BNN, int EK>
 static void dispatch_mfma(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda,
-                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, int nk, float *part,
-                          int pld, const EpiArgs &e)
+                          const bf16_t *B, int ldb, const int32_t *bidx, const int *ncount, float *part, int pld,
+                          const EpiArgs &e)
 {
     if constexpr (EK != EPI_GATE) {
-        dispatch_cfg<BNN, EK, 0>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+        dispatch_cfg<BNN, EK, 0>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
     } else {
         switch (e.mode) {
         case SFFN_THRESHOLD:
-            dispatch_cfg<BNN, EK, SFFN_THRESHOLD>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            dispatch_cfg<BNN, EK, SFFN_THRESHOLD>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
             break;
         case SFFN_TOPK:
-            dispatch_cfg<BNN, EK, SFFN_TOPK>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            dispatch_cfg<BNN, EK, SFFN_TOPK>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
             break;
         case SFFN_DENSE:
-            dispatch_cfg<BNN, EK, SFFN_DENSE>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld, e);
+            dispatch_cfg<BNN, EK, SFFN_DENSE>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
             break;
         default:
-            dispatch_cfg<BNN, EK, SFFN_DENSE_SILU>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, nk, part, pld,
+            dispatch_cfg<BNN, EK, SFFN_DENSE_SILU>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld,
                                                    e);
             break;
         }
     }
 }
 
+// Sum of S split-K partial slices [S][M][part_ld] with the epilogue applied.
+static hipError_t launch_splitk_sum(hipStream_t st, const float *part, int S, int M, int N, int part_ld,
+                                    const int *ncount, const EpiArgs &e)
+{
+    const dim3 grid((N + 255) / 256, M), block(256);
+    if (S <= 2) hipLaunchKernelGGL(k_splitk_epilogue<2>, grid, block, 0, st, part, S, M, N, part_ld, ncount, e);
+    else if (S <= 4) hipLaunchKernelGGL(k_splitk_epilogue<4>, grid, block, 0, st, part, S, M, N, part_ld, ncount, e);
+    else if (S <= 8) hipLaunchKernelGGL(k_splitk_epilogue<8>, grid, block, 0, st, part, S, M, N, part_ld, ncount, e);
+    else hipLaunchKernelGGL(k_splitk_epilogue<16>, grid, block, 0, st, part, S, M, N, part_ld, ncount, e);
+    return hipGetLastError();
+}
+
 // One block per (M tile, N tile), padded so the N tiles split evenly over 8 XCDs.
 static dim3 tile_grid(int nt, int mt, int sk) { return dim3(8 * ((nt + 7) / 8) * mt, 1, sk); }
 
 // Split K so that the grid has at least ~2 workgroups per CU (at most 8
-// splits, and K steps of at least 8 tiles per split).
+// splits, and K steps of at least 8 tiles per split). Below 128 tokens the
+// weights stream once through many small workgroups: up to splits_max
+// splits, ~3 workgroups per CU, at least 4 K steps of 64 per split.
 static int split_for(const sffn_ctx &c, long long tiles, int K, int M)
 {
     int S = 1;
-    if (M >= 512) return 1;  // large batches have tiles enough, and no partial buffer
-    while (S < 8 && tiles * S < 2LL * c.n_cu && (K / kBK) / (2 * S) >= 8) S *= 2;
+    const int smax = min(splits_max(M), c.L.bpart_rows / M);  // and what the partial buffer holds
+    if (M < 128) {
+        while (2 * S <= smax && tiles * S < c.n_cu && (K / 64) / (2 * S) >= 4) S *= 2;
+        return S;
+    }
+    while (2 * S <= smax && tiles * S < 2LL * c.n_cu && (K / 32) / (2 * S) >= 8) S *= 2;
     return S;
 }
 
@@ -930,7 +778,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     Cfg cfd = cf;
     // the down GEMM's N is d_model: keep 256 x 256 tiles only while they
     // still give every CU a workgroup, else 256 x 128 (twice the tiles)
-    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{32, 4, 2, 2, 2, true};
+    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{4, 2, 2, 2};
     const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- 1. gate GEMM ----
@@ -939,18 +787,16 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         // 256 <= T < 512: the gate GEMM reads every weight row once either
         // way, but 256 x 64 tiles re-read the activation block for every
         // 64 channels; 256 x 256 tiles split K in two instead
-        const bool wide = T >= 256 && T < 512;
-        const Cfg cg = wide ? Cfg{32, 4, 2, 2, 4, true} : cf;
+        const bool wide = T >= 256 && T < 512 && c.L.bpart_rows >= 2 * T;
+        const Cfg cg = wide ? Cfg{4, 2, 2, 4} : cf;
         const int nt = (F + cg.bn() - 1) / cg.bn(), mtg = (T + cg.bm() - 1) / cg.bm();
         const int sk = wide ? 2 : split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
-        dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, 0, part, F,
+        dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, part, F,
                                        ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
-            hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
-                               nullptr, ep);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_splitk_sum(st, part, sk, T, F, F, nullptr, ep)) != hipSuccess) return e;
         }
         if (ev1) hipEventRecord(ev1, st);
     }
@@ -968,12 +814,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_UP;
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, 0, part, F, ep);
+        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, part, F, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
-            hipLaunchKernelGGL(k_splitk_epilogue, dim3((F + 255) / 256, T), dim3(256), 0, st, part, sk, T, F, F,
-                               ncount, ep);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_splitk_sum(st, part, sk, T, F, F, ncount, ep)) != hipSuccess) return e;
         }
     }
     // ---- 4. down GEMM, K = union ----
@@ -981,13 +825,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.kind = EPI_DOWN;
         const int nt = (d + cfd.bn() - 1) / cfd.bn();
         const int sk = split_for(c, (long long)mtd * nt, F / 2, T);
-        dispatch_mfma<true, EPI_DOWN>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, 1, part,
+        dispatch_mfma<true, EPI_DOWN>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, part,
                                       d, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
-            hipLaunchKernelGGL(k_splitk_epilogue, dim3((d + 255) / 256, T), dim3(256), 0, st, part, sk, T, d, d,
-                               nullptr, ep);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if ((e = launch_splitk_sum(st, part, sk, T, d, d, nullptr, ep)) != hipSuccess) return e;
         }
     }
     // ---- optional outputs ----

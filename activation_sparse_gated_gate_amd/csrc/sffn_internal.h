@@ -23,6 +23,10 @@ constexpr int kDownGroupsMax = 64;   // channel groups of the split down project
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
 constexpr int kLopaSplitMax = 16;    // split of d_model in the LoPA x.A kernel
 constexpr int kLopaRowsPerWG = 16;
+// K splits of a batched GEMM (partial slices): up to 16 below 65 tokens, 8 up
+// to 511 tokens, none from 512.
+constexpr int kSplitMax = 16;
+inline int splits_max(int T) { return T <= 64 ? 16 : T < 512 ? 8 : 1; }
 
 constexpr int kMaxDff = 262144;
 
@@ -39,7 +43,8 @@ struct Layout {
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
-    size_t bpart;     // batched split-K partials: fp32 [8][T][max(d_ff, d_model)] when T < 512
+    size_t bpart;     // batched split-K partials: fp32 [bpart_rows][max(d_ff, d_model)]
+    int bpart_rows;   // splits x tokens that fit in bpart
     size_t thr;       // Top-K: int2 [max(ntp, max_tokens)] per-token K-th key and tie cutoff
     size_t total;
 };

@@ -115,6 +115,21 @@ def test_batched_handle_mixes_decode_and_batched_forwards():
         compare(lay, x, mode, ref, got)
 
 
+def test_batched_handle_larger_than_batch_splits_within_its_buffer():
+    # A handle sized for 600 tokens serves smaller batches, whose GEMMs split
+    # K (up to 16 ways at 64 tokens and below, 8 below 512, and the two-way
+    # split gate from 256): every split must fit the handle's partial buffer.
+    say("case handle of 600 tokens serving 12..511-token batches")
+    d, f = 1024, 1500
+    lay = inputs.make_layer(27, d, f, "bf16")
+    ffn = S.SparseFFN(d, f, 600, "bf16")
+    for n, mode in ((12, "topk"), (64, "threshold"), (100, "dense_silu"), (300, "threshold"), (511, "topk")):
+        x = inputs.make_x(27 + n, n, d, "bf16", correlated=True)
+        ref = oracle_forward(lay, x, mode, tau=1.0, k=200)
+        got = run_gpu(lay, x, mode, tau=1.0, k=200, ffn=ffn)
+        compare(lay, x, mode, ref, got)
+
+
 # ---------------------------------------------------------------------------
 # 70B-shaped prefill layer at full size, sampled tokens
 # ---------------------------------------------------------------------------

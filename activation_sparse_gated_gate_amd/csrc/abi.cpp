@@ -45,7 +45,6 @@ Layout make_layout(const sffn_shape &s)
     L.uidx = take(F * 4);
     L.hbuf = take(batched ? (F * ntp * 4 > T * FP * 2 ? F * ntp * 4 : T * FP * 2) : F * ntp * 4);
     L.part = take((size_t)kDownGroupsMax * ntp * d * 4);
-    L.tpart = take(r ? (size_t)kLopaSplitMax * ntp * r * 4 : 0);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(batched ? T * F * 4 : 0);
     L.ubits = take((size_t)L.words * 4);

@@ -4,8 +4,8 @@
 // Pipeline per forward (modes as in include/sffn.h):
 //   threshold  k_gate<SELECT_UP>: gate GEMV, shifted-ReLU select, and the W_up
 //              rows of the channels just found active -> k_down -> k_reduce
-//   LoPA       k_lopa_xa (x.A partials) -> k_lopa_t (their ordered sum t) ->
-//              k_gate<SELECT_UP> on B with t -> k_down -> k_reduce
+//   LoPA       k_lopa_xa (t = x.A) -> k_gate<SELECT_UP> on B with t -> k_down
+//              -> k_reduce
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
 //              K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
@@ -209,45 +209,22 @@ __global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ part, 
 }
 
 // ---------------------------------------------------------------------------
-// LoPA first product, partials: workgroup (b, s) takes 16 rows of A^T (4 per
-// wavefront) and the d-slice s; tpart[s][t][k] = x_t[slice] . A^T[k][slice].
-// The gate kernel sums the slices in order.
+// LoPA first product t[t][k] = x_t . A[k] (fp32) for the r rows of A, stored
+// [r][d]: one row per wavefront, read once for all tokens; the gate kernel
+// then dots the rows of B with t.
 // ---------------------------------------------------------------------------
 template <typename TW, int NT>
-__global__ __launch_bounds__(256) void k_lopa_xa(const TW *__restrict__ x, int n, int d,
-                                                 const TW *__restrict__ at, int r, int chunk,
-                                                 float *__restrict__ tpart)
+__global__ __launch_bounds__(256) void k_lopa_xa(const TW *__restrict__ x, int n, int d, const TW *__restrict__ a,
+                                                 int r, float *__restrict__ tvec)
 {
-    const int b = blockIdx.x, s = blockIdx.y;
-    const int j0 = s * chunk, len = max(0, min(d - j0, chunk));
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row0 = b * kLopaRowsPerWG + wave * 4;
-    const int nv = max(0, min(4, r - row0));
-    const TW *rows[4];
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const TW *rows[1] = {a + (size_t)min(row, r - 1) * d};
+    RowDot<TW, TW, NT, 1, 64, Batch<TW, TW, NT, 1>::v> dot;
+    dot.run(rows, row < r ? 1u : 0u, d, lane, x, d, n);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) rows[q] = at + (size_t)(row0 + q) * d + j0;
-    RowDot<TW, TW, NT, 4, 64, Batch<TW, TW, NT, 4>::v> dot;
-    dot.run(rows, (1u << nv) - 1u, len, lane, x + j0, d, n);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (q < nv && t < n && lane == ((q * NT + t) & 63))
-                tpart[((size_t)s * kDecodeMaxTokens + t) * r + row0 + q] = dot.acc[q][t];
-}
-
-// t[t][k] = sum over slices s (ascending, from zero) of tpart[s][t][k]: the
-// order the gate kernel would use summing the slices itself, done once here
-// instead of in every wavefront that reads t.
-__global__ __launch_bounds__(256) void k_lopa_t(const float *__restrict__ tpart, int ks, int n, int r,
-                                                float *__restrict__ tvec)
-{
-    const int o = blockIdx.x * 256 + threadIdx.x;
-    if (o >= n * r) return;
-    const int t = o / r, k = o - t * r;
-    float v = 0.f;
-    for (int s = 0; s < ks; ++s) v += tpart[((size_t)s * kDecodeMaxTokens + t) * r + k];
-    tvec[(size_t)t * r + k] = v;
+    for (int t = 0; t < NT; ++t)
+        if (row < r && t < n && lane == t) tvec[(size_t)t * r + row] = dot.acc[0][t];
 }
 
 // ---------------------------------------------------------------------------
@@ -319,23 +296,6 @@ static size_t down_lds(const sffn_ctx &c)
     return (size_t)4 * ((F + G - 1) / G + 1);
 }
 
-static int lopa_split(const sffn_ctx &c)
-{
-    const int d = c.shape.d_model, r = c.shape.rank;
-    const int blocks = (r + kLopaRowsPerWG - 1) / kLopaRowsPerWG;
-    int ks = (2 * c.n_cu + blocks - 1) / blocks;
-    ks = min(ks, kLopaSplitMax);
-    ks = min(ks, max(1, d / 512));
-    return max(ks, 1);
-}
-
-static int lopa_chunk(const sffn_ctx &c, int ks)
-{
-    const int d = c.shape.d_model;
-    int chunk = (d + ks - 1) / ks;
-    return (chunk + 7) / 8 * 8;
-}
-
 hipError_t device_setup(sffn_ctx &c)
 {
     int dev = 0;
@@ -404,22 +364,15 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     g.kind = dense ? DENSE : a.mode == SFFN_TOPK ? KEYS : SELECT_UP;
     if (a.mode == SFFN_LOPA) {
         const int r = S.rank;
-        float *tpart = reinterpret_cast<float *>(ws + c.L.tpart);
-        const int ks = lopa_split(c), chunk = lopa_chunk(c, ks);
-        const int blocks = (r + kLopaRowsPerWG - 1) / kLopaRowsPerWG;
-        hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(blocks, ks), dim3(256), 0, st, x, n, d,
-                           static_cast<const TW *>(a.w.lopa_a), r, chunk, tpart);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
         float *tvec = reinterpret_cast<float *>(ws + c.L.tvec);
-        hipLaunchKernelGGL(k_lopa_t, dim3((n * r + 255) / 256), dim3(256), 0, st, tpart, ks, n, r, tvec);
+        hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3((r + 3) / 4), dim3(256), 0, st, x, n, d,
+                           static_cast<const TW *>(a.w.lopa_a), r, tvec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // gate rows are B (length r) dotted with t = x.A; the gate rows and
         // the up rows (length d) share the lane groups, sized for the shorter
         g.lopa = true;
-        g.xg = nullptr;
+        g.xg = tvec;
         g.L = r;
-        g.tpart = tvec;
-        g.ks = 1;
         g.wg = a.w.lopa_b;
         g.lpr = lpr_for(min(r, d));
     }

@@ -27,7 +27,6 @@ namespace sffn {
 template <typename TW, typename TX, int NT, int LPR, int KIND>
 __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
                                               const TW *__restrict__ xu, int d,
-                                              const float *__restrict__ tpart, int ks,
                                               const TW *__restrict__ wg, const TW *__restrict__ wu,
                                               int F, int mode, float tau,
                                               float *__restrict__ gsel, uint8_t *__restrict__ act,
@@ -63,7 +62,7 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 #pragma unroll
         for (int r = 0; r < R; ++r) rows[r] = wg + (size_t)(row0 + r) * L;
         RowDot<TW, TX, NT, R, LPR, Batch<TW, TX, NT, R>::v> dot;
-        dot.run(rows, vmask, L, li, xg, L, n, tpart, ks, (size_t)kDecodeMaxTokens * L);
+        dot.run(rows, vmask, L, li, xg, L, n);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -122,18 +121,18 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 // begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
 template <typename TW, typename TX, int NT, int KIND>
 static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
-                        const TW *xu, int d, const float *tpart, int ks, const TW *wg, const TW *wu, int F, int mode,
-                        float tau, float *gsel, uint8_t *act, float *hbuf, float *dz)
+                        const TW *xu, int d, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel,
+                        uint8_t *act, float *hbuf, float *dz)
 {
     const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
 #define SFFN_G(LP)                                                                                               \
     do {                                                                                                         \
         if (ev0)                                                                                                 \
             hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
-                                  xu, d, tpart, ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                 \
+                                  xu, d, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                            \
         else                                                                                                     \
-            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, tpart,   \
-                               ks, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                                   \
+            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
+                               F, mode, tau, gsel, act, hbuf, dz);                                               \
     } while (0)
     if (lpr == 64) SFFN_G(64);
     else if (lpr == 32) SFFN_G(32);
@@ -154,16 +153,16 @@ hipError_t launch_gate(const GateArgs &g)
         const TW *wu = static_cast<const TW *>(g.wu);
         switch (g.kind) {
         case KEYS:
-            launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu, g.F,
+            launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
                                             g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
             break;
         case DENSE:
-            launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu, g.F,
+            launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
                                              g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
             break;
         default:
-            launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, g.tpart, g.ks, wg, wu,
-                                                 g.F, g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+            launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                 g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
             break;
         }
     };

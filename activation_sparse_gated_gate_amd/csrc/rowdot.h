@@ -24,11 +24,9 @@ struct RowDot {
     static constexpr int STEP = LPR * 8;
     float acc[R][NT];
 
-    // x: token t starts at x + t*ldx; tokens >= n read as zero. With tpart
-    // (LoPA, TX = float) the chunk is the in-order sum of ks partial slices
-    // tpart[s][t][.] of stride ps floats.
+    // x: token t starts at x + t*ldx; tokens >= n read as zero.
     __device__ __forceinline__ void run(const TW *const rows[R], uint32_t valid, int len, int li, const TX *x,
-                                        int ldx, int n, const float *tpart = nullptr, int ks = 0, size_t ps = 0)
+                                        int ldx, int n)
     {
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -49,18 +47,7 @@ struct RowDot {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const int j = jb + s * STEP;
-                    xv[s][t] = Ld8<TX>::zero();
-                    if (t < n && j < len) {
-                        if constexpr (sizeof(TX) == 4) {
-                            if (tpart) {
-                                for (int p = 0; p < ks; ++p)
-                                    Ld8<TX>::add(xv[s][t], Ld8<TX>::load(reinterpret_cast<const TX *>(
-                                                               tpart + (size_t)p * ps + (size_t)t * ldx + j)));
-                                continue;
-                            }
-                        }
-                        xv[s][t] = Ld8<TX>::load(x + (size_t)t * ldx + j);
-                    }
+                    xv[s][t] = (t < n && j < len) ? Ld8<TX>::load(x + (size_t)t * ldx + j) : Ld8<TX>::zero();
                 }
 #pragma unroll
             for (int s = 0; s < MAXS; ++s)

@@ -21,8 +21,6 @@ constexpr int kCtrlUnionSize = 0;    // batched path: size of the union list
 
 constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
-constexpr int kLopaSplitMax = 16;    // split of d_model in the LoPA x.A kernel
-constexpr int kLopaRowsPerWG = 16;
 // K splits of a batched GEMM (partial slices): up to 16 below 65 tokens, 8 up
 // to 511 tokens, none from 512.
 constexpr int kSplitMax = 16;
@@ -39,7 +37,6 @@ struct Layout {
     size_t uidx;      // int32 [d_ff] ascending union list
     size_t hbuf;      // decode: fp32 [d_ff][ntp] gated up values; batched: bf16 [T][d_ff]
     size_t part;      // fp32 [kDownGroupsMax][ntp][d_model] down-projection partials
-    size_t tpart;     // fp32 [kLopaSplitMax][ntp][rank] LoPA partial x.A
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
@@ -96,16 +93,14 @@ hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, u
 // rows of the selected channels, or of every channel in the dense modes).
 struct GateArgs {
     int dtype;            // sffn_dtype of weights and x
-    bool lopa;            // gate rows are B (length L) dotted with t = x.A from fp32 partials
+    bool lopa;            // gate rows are B (length L) dotted with t = x.A (fp32, in xg)
     int nt;               // padded token count: 1, 2, 4 or 8
     int kind;             // GateKind (rowdot.h)
     int lpr;              // lanes per row group: 16, 32 or 64
-    const void *xg;       // gate input x [n][L] (null for LoPA)
+    const void *xg;       // gate input [n][L]: x, or t = x.A for LoPA
     int n, L;
     const void *xu;       // up input x [n][d]
     int d;
-    const float *tpart;   // LoPA: x.A partials [ks][8][L]
-    int ks;
     const void *wg, *wu;  // gate rows [F][L] (B for LoPA), up rows [F][d]
     int F, mode;
     float tau;

@@ -6,10 +6,13 @@
 //                  channel is off for that token) and OR the union bitmap
 //                  (Top-K: store the SiLU keys; each token's K-th key is
 //                  found next and the flags follow from it)
-//   2. compaction  union bitmap -> ascending union list U, its size N
-//   3. up GEMM     Uu = X . W_up[U]^T over the gathered rows; epilogue
+//   2. up GEMM     each workgroup reads the union bitmap and lists its own
+//                  tile's part of the ascending union list U (writing it,
+//                  and the union size, for what follows); Uu = X . W_up[U]^T
+//                  over the gathered rows; epilogue
 //                  H[t][j] = bf16(g[t][U[j]] * Uu[t][j])
-//   4. down GEMM   Y = H . W_down[U, :] (rows gathered by U, fp32 output)
+//   3. down GEMM   Y = H . W_down[U, :] (rows gathered by U, fp32 output);
+//                  it also clears the bitmap for the next forward
 //
 // A channel that no token selected reads neither W_up nor W_down: the gate is
 // computed first and the other two matrices only for what it kept ("Model
@@ -40,14 +43,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t_;
 
 
-// fp32 -> bf16, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f2bf(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 enum EpiKind { EPI_GATE = 0, EPI_UP = 1, EPI_DOWN = 2 };
 
@@ -56,12 +51,12 @@ struct EpiArgs {
     int mode;           // sffn_mode (gate)
     float tau;
     int T, F, d;
-    uint16_t *G;        // [T][F] bf16 gate values (gate writes, up reads)
-    float *keys;        // [T][F] fp32 SiLU keys (Top-K)
-    const uint8_t *act; // [T][F] Top-K flags (up reads)
+    uint16_t *G;        // [T][F] bf16 gate values, 0 where off (gate or Top-K flags write, up reads)
+    float *keys;        // [T][F] fp32 SiLU keys (Top-K gate writes)
     float *debug_z;     // [T][F] optional
-    uint32_t *ubits;    // union bitmap (gate)
-    const int32_t *uidx;  // union list (up)
+    uint32_t *ubits;    // union bitmap (gate and Top-K flags set it, up reads it, down clears it)
+    int32_t *uidx;      // union list (up writes, down and the split-K sum read)
+    int *ucount;        // union size (up writes)
     uint16_t *H;        // [T][hld] bf16 (up writes)
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
     float *Y;           // [T][d] fp32 (down writes)
@@ -88,11 +83,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
     }
     if (e.kind == EPI_UP) {
         const int i = e.uidx[n];
-        const size_t o = (size_t)m * e.F + i;
-        float g;
-        if (e.mode == SFFN_TOPK) g = e.act[o] ? e.keys[o] : 0.f;
-        else g = bf2f(e.G[o]);
-        e.H[(size_t)m * e.hld + n] = f2bf(g * v);
+        e.H[(size_t)m * e.hld + n] = f2bf(bf2f(e.G[(size_t)m * e.F + i]) * v);
         return false;
     }
     e.Y[(size_t)m * e.d + n] = v;
@@ -110,7 +101,8 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
 template <int MF, int TM, int TN, int NTHR, int BN, int EK, int GM, typename AccT>
 __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int lane, int m0, int n0, int arow,
                                               int bcol, int M, int nlim, int S, float *__restrict__ part,
-                                              int part_ld, const EpiArgs &epi, uint32_t *ubits_lds)
+                                              int part_ld, const EpiArgs &epi, uint32_t *ubits_lds,
+                                              const int *uloc)
 {
     constexpr int ACC = MF == 32 ? 16 : 4;
     auto rowof = [&](int i, int r) {
@@ -145,13 +137,12 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
         }
     } else if constexpr (EK == EPI_UP) {
         const int padlim = (nlim + 7) & ~7;
-        const bool topk = epi.mode == SFFN_TOPK;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = colof(j);
             if (n >= padlim) continue;
             const bool live = n < nlim;
-            const int src = live ? epi.uidx[n] : 0;
+            const int src = live ? uloc[n - n0] : 0;  // this tile's part of the union list (LDS)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -159,11 +150,7 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                     const int m = rowof(i, r);
                     if (m >= M) continue;
                     uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
-                    if (live) {
-                        const size_t o = (size_t)m * epi.F + src;
-                        const float g = topk ? (epi.act[o] ? epi.keys[o] : 0.f) : bf2f(epi.G[o]);
-                        h = f2bf(g * acc[i][j][r]);
-                    }
+                    if (live) h = f2bf(bf2f(epi.G[(size_t)m * epi.F + src]) * acc[i][j][r]);
                     epi.H[(size_t)m * epi.hld + n] = h;
                 }
             // keep each sub-tile's gathered G loads from being hoisted over the
@@ -298,6 +285,8 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         St3[NS > 3 ? (BM + BN) * BK : 8];
     __shared__ __align__(16) int Is0[BNN ? BK : 1], Is1[BNN ? BK : 1], Is2[BNN && NS == 3 ? BK : 1];
     __shared__ uint32_t ubits_lds[BN / 32];
+    __shared__ int uloc[EK == EPI_UP ? BN : 1];  // up: union entries n0 .. n0 + BN - 1
+    __shared__ int utot;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,9 +298,84 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     if (ni >= NTT) return;
     const int m0 = mi * BM, n0 = ni * BN;
     int nlim = N, klim = K;
-    if (ncount) {
+    if constexpr (EK == EPI_UP) {
+        // The union list, ascending: entry e is the e-th set bit of the
+        // bitmap (every channel in the dense modes). Wavefront 0 holds words
+        // w0 + 64 q + lane (up to 16 per lane in one batch of loads). First
+        // the total, so that tiles past the union leave at once; then round
+        // q by round q a wavefront scan of the popcounts plus the carry of
+        // the earlier rounds gives each word's first entry, and the lanes
+        // whose word meets entries [n0, n0 + BN) extract its bits (a tile's
+        // words lie on different lanes, so in parallel), up to the round
+        // that passes the tile.
+        const int F = epi.F, W = (F + 31) / 32;
+        if (epi.mode == SFFN_DENSE || epi.mode == SFFN_DENSE_SILU) {
+            for (int j = tid; j < BN; j += 64 * WM * WN) uloc[j] = n0 + j;
+            if (tid == 0) utot = F;
+        } else if (wave == 0) {
+            const uint32_t *ub = epi.ubits;
+            uint32_t u[16];
+            auto load = [&](int w0) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int w = w0 + 64 * q + lane;
+                    u[q] = w < W ? ub[w] : 0u;
+                }
+            };
+            load(0);
+            int tot = 0;
+            for (int w0 = 0;;) {
+                int c = 0;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) c += __popc(u[q]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+                tot += c;
+                w0 += 1024;
+                if (w0 >= W) break;
+                load(w0);
+            }
+            if (lane == 0) utot = tot;
+            if (n0 < tot) {
+                int carry = 0;
+                for (int w0 = 0; w0 < W && carry < n0 + BN; w0 += 1024) {
+                    if (W > 1024) load(w0);  // one batch: still in registers
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        if (w0 + 64 * q >= W || carry >= n0 + BN) break;
+                        const int pc = __popc(u[q]);
+                        const int incl = wave_incl_scan(pc);
+                        int rank = carry + incl - pc;
+                        if (rank < n0 + BN && rank + pc > n0) {
+                            const int w = w0 + 64 * q + lane;
+                            uint32_t v = u[q];
+                            while (v) {
+                                const int b = __ffs(v) - 1;
+                                v &= v - 1;
+                                if (rank >= n0 && rank < n0 + BN) uloc[rank - n0] = w * 32 + b;
+                                ++rank;
+                            }
+                        }
+                        carry += __shfl(incl, 63, 64);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        nlim = min(N, utot);
+        // one workgroup per N tile publishes its part; the first, the size
+        if (blockIdx.z == 0 && mi == 0) {
+            for (int j = tid; j < BN && n0 + j < nlim; j += 64 * WM * WN) epi.uidx[n0 + j] = uloc[j];
+            if (n0 == 0 && tid == 0) *epi.ucount = utot;
+        }
+    } else if (ncount) {
         if constexpr (BNN) klim = min(K, *ncount);
         else nlim = min(N, *ncount);
+    }
+    if constexpr (EK == EPI_DOWN) {
+        // the up GEMM has read the bitmap: clear it for the next forward
+        if (blockIdx.x == 0 && blockIdx.z == 0)
+            for (int w = tid; w < (epi.F + 31) / 32; w += 64 * WM * WN) epi.ubits[w] = 0;
     }
     if (n0 >= nlim || m0 >= M) return;
     const int S = gridDim.z;
@@ -347,7 +411,8 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         for (int j = 0; j < BPW; ++j) {
             const int r = (wave * BPW + j) * (64 / CH) + lr, n = n0 + r;
             blc[j] = kchunk(r);
-            bsrc[j] = n < nlim ? B + (size_t)(bidx ? bidx[n] : n) * ldb + blc[j] : nullptr;
+            const int row = EK == EPI_UP ? uloc[r] : bidx ? bidx[n] : n;
+            bsrc[j] = n < nlim ? B + (size_t)row * ldb + blc[j] : nullptr;
         }
     } else {
 #pragma unroll
@@ -530,7 +595,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     }
     wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
     tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
-                                                ubits_lds);
+                                                ubits_lds, uloc);
 }
 
 // Sum the split-K partials in order and apply the epilogue (gate: also the
@@ -563,36 +628,6 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     __syncthreads();
     if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
-}
-
-// Union bitmap -> ascending list and its size (one workgroup); clears the
-// bitmap for the next forward. Dense modes: every channel.
-__global__ __launch_bounds__(1024) void k_union_compact(uint32_t *__restrict__ ubits, int W, int F, int dense,
-                                                        int32_t *__restrict__ uidx, int *__restrict__ ncount)
-{
-    __shared__ int scan_scratch[16];
-    const int tid = threadIdx.x;
-    const int seg = (W + blockDim.x - 1) / blockDim.x;
-    const int w0 = min(W, tid * seg), w1 = min(W, w0 + seg);
-    int local = 0;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t u = ubits[w];
-        if (dense) u = (F - w * 32 >= 32) ? 0xffffffffu : ((1u << (F - w * 32)) - 1u);
-        local += __popc(u);
-    }
-    const int incl = block_incl_scan(local, scan_scratch);
-    int pos = incl - local;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t u = ubits[w];
-        if (dense) u = (F - w * 32 >= 32) ? 0xffffffffu : ((1u << (F - w * 32)) - 1u);
-        while (u) {
-            const int b = __ffs(u) - 1;
-            u &= u - 1;
-            uidx[pos++] = w * 32 + b;
-        }
-        ubits[w] = 0;
-    }
-    if (tid == blockDim.x - 1) *ncount = incl;
 }
 
 // Optional outputs for a batch: token t's ascending active list and count;
@@ -766,10 +801,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     ep.d = d;
     ep.G = G;
     ep.keys = keys;
-    ep.act = act;
     ep.debug_z = a.debug_z;
     ep.ubits = ubits;
     ep.uidx = uidx;
+    ep.ucount = ncount;
     ep.H = H;
     ep.hld = (F + 7) / 8 * 8;
     ep.Y = a.y;
@@ -804,23 +839,21 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     if (a.mode == SFFN_TOPK) {
         int2 *thr = reinterpret_cast<int2 *>(c.ws + c.L.thr);
         if ((e = launch_topk_thr(keys, T, F, a.k, thr, st)) != hipSuccess) return e;
-        if ((e = launch_topk_flags(keys, T, F, thr, act, W, ubits, st)) != hipSuccess) return e;
+        if ((e = launch_topk_flags(keys, T, F, thr, act, G, W, ubits, st)) != hipSuccess) return e;
     }
-    // ---- 2. union list ----
-    hipLaunchKernelGGL(k_union_compact, dim3(1), dim3(1024), 0, st, ubits, W, F, dense ? 1 : 0, uidx, ncount);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // ---- 3. up GEMM over the union rows ----
+    // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {
         ep.kind = EPI_UP;
         const int nt = (F + cf.bn() - 1) / cf.bn();
         const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, uidx, ncount, part, F, ep);
+        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, nullptr, nullptr, part, F,
+                                      ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1) {
             if ((e = launch_splitk_sum(st, part, sk, T, F, F, ncount, ep)) != hipSuccess) return e;
         }
     }
-    // ---- 4. down GEMM, K = union ----
+    // ---- 3. down GEMM, K = union ----
     {
         ep.kind = EPI_DOWN;
         const int nt = (d + cfd.bn() - 1) / cfd.bn();

@@ -185,4 +185,13 @@ __device__ __forceinline__ bool topk_on(float g, int i, int2 thr)
 
 __device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
 
+// fp32 -> bf16, round to nearest even (finite inputs), and back.
+__device__ __forceinline__ uint16_t f2bf(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
 }  // namespace sffn

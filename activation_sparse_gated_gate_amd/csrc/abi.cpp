@@ -44,7 +44,9 @@ Layout make_layout(const sffn_shape &s)
     L.gsel = take(batched ? (ntp * F * 4 > T * F * 2 ? ntp * F * 4 : T * F * 2) : ntp * F * 4);
     L.uidx = take(F * 4);
     L.hbuf = take(batched ? (F * ntp * 4 > T * FP * 2 ? F * ntp * 4 : T * FP * 2) : F * ntp * 4);
-    L.part = take((size_t)kDownGroupsMax * ntp * d * 4);
+    L.any = take(F);
+    L.part_words = (size_t)kDownGroupsMax * ntp * d;
+    L.part = take(L.part_words * 4);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(batched ? T * F * 4 : 0);
     L.ubits = take((size_t)L.words * 4);

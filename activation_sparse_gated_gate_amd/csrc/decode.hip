@@ -3,13 +3,11 @@
 //
 // Pipeline per forward (modes as in include/sffn.h):
 //   threshold  k_gate<SELECT_UP>: gate GEMV, shifted-ReLU select, and the W_up
-//              rows of the channels just found active -> k_down -> k_reduce
+//              rows of the channels just found active -> k_down
 //   LoPA       k_lopa_xa (t = x.A) -> k_gate<SELECT_UP> on B with t -> k_down
-//              -> k_reduce
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
-//              K-th key) -> k_up (flags + up rows) -> k_down -> k_reduce
+//              K-th key) -> k_up (flags + up rows) -> k_down
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
-//              -> k_reduce
 //
 // The gate is computed first and in full; only the channels it leaves active
 // read their W_up and W_down rows ("Model Casting and Low-Parameter Gating",
@@ -19,9 +17,11 @@
 //
 // Work is split evenly per compute unit: under full load a CU draws about
 // 1/256 of the HBM bandwidth, so a kernel lasts as long as its most loaded CU.
-// Active channels are byte flags act[t][i] with one writer each, so any row
-// partition works without atomics. No kernel waits on another workgroup:
-// cross-workgroup results go through global memory and the next kernel.
+// Active channels are byte flags act[t][i], and any[i] for the union over the
+// tokens, with one writer each, so any row partition works without atomics.
+// Only the down kernel's summing workgroups wait on other workgroups (for
+// their partial sums, see k_down); everything else passes through global
+// memory to the next kernel.
 #include "compact.h"
 #include "rowdot.h"
 
@@ -37,7 +37,8 @@ template <typename TW, int NT, int LPR>
 __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int d,
                                             const TW *__restrict__ wu, int F,
                                             const int2 *__restrict__ thr, uint8_t *__restrict__ act,
-                                            const float *__restrict__ gsel, float *__restrict__ hbuf)
+                                            uint8_t *__restrict__ any, const float *__restrict__ gsel,
+                                            float *__restrict__ hbuf)
 {
     constexpr int SUB = 64 / LPR;
     constexpr int R = RowsPer<NT>::v;
@@ -63,6 +64,9 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
                 }
             }
         }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
     if (__ballot(amask != 0) == 0) return;
     const TW *rows[R];
 #pragma unroll
@@ -78,18 +82,33 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
 }
 
 // ---------------------------------------------------------------------------
-// Down kernel: partial y over one channel group.
-// Workgroup (s, g) takes output columns [128 s, 128 s + 128) and channels
-// [F g / G, F (g+1) / G). It lists that range's channels selected by any token
-// (every channel in the dense modes) in LDS in ascending order, then its 16
-// row streams (4 per wavefront, 16 lanes x 8 columns each) read the 256-byte
-// segments of those W_down rows, UNR rows per stream in flight:
-//   part[g][t][c] = sum_i h[i][t] * W_down[i][c]   (fixed order).
+// Down kernel: the split-channel two-stage reduction in one launch.
+// Stage 1: workgroup (s, g) takes output columns [128 s, 128 s + 128) and
+// channels [F g / G, F (g+1) / G). It lists that range's channels some token
+// selected (any[i]; every channel in the dense modes) in LDS in ascending
+// order, then its 16 row streams (4 per wavefront, 16 lanes x 8 columns each)
+// read the 256-byte segments of those W_down rows, UNR rows per stream in
+// flight:  P[g][t][c] = sum_i h[i][t] * W_down[i][c]   (fixed order).
+// Stage 2: workgroup (s, G-1) sums P[0][t][c], ..., P[G-1][t][c] in that
+// order and writes y. The other groups publish their P with relaxed
+// device-scope atomic stores into slots that hold a marker (the all-ones NaN
+// pattern, which no sum of finite products produces) until written; the
+// summing workgroup polls each slot with device-scope atomic loads until the
+// marker is gone, then writes the marker back for the next forward. Each slot
+// carries its own readiness, so no counter or fence is needed (a device-scope
+// release fence writes back the whole L2 of an XCD). Only the G-1 groups'
+// summing workgroups wait, and only on workgroups that never wait, so every
+// wait ends; the poll count is bounded anyway (kDownSpinMax), after which the
+// slot's marker (a NaN) goes into y.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kDownMarker = 0xffffffffu;
+constexpr int kDownSpinMax = 1 << 18;
+
 template <typename TW, int NT, int UNR>
 __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, int d, int n,
-                                              const uint8_t *__restrict__ act, int dense,
-                                              const float *__restrict__ hbuf, float *__restrict__ part)
+                                              const uint8_t *__restrict__ any, int dense,
+                                              const float *__restrict__ hbuf, uint32_t *__restrict__ part,
+                                              float *__restrict__ y)
 {
     extern __shared__ __align__(16) char smem[];
     int *list = reinterpret_cast<int *>(smem);
@@ -105,11 +124,7 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
     const int seg = (len + blockDim.x - 1) / blockDim.x;  // <= 32, fixed on the host
     const int i0 = cb + min(len, tid * seg), i1 = cb + min(len, tid * seg + seg);
     uint32_t sel = 0;  // bit k: channel i0 + k
-    for (int i = i0; i < i1; ++i) {
-        bool any = dense != 0;
-        for (int t = 0; t < n && !any; ++t) any = act[(size_t)t * F + i] != 0;
-        sel |= (uint32_t)any << (i - i0);
-    }
+    for (int i = i0; i < i1; ++i) sel |= (uint32_t)(dense != 0 || any[i] != 0) << (i - i0);
     const int local = __popc(sel);
     const int incl = block_incl_scan(local, scan_scratch);
     int pos = incl - local;
@@ -178,34 +193,63 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
             for (int e = 0; e < 8; ++e) red[wave][t][c8 * 8 + e] = acc[t][e];
     }
     __syncthreads();
-    const int c0 = s * kDownSliceCols;
-    for (int e = tid; e < NT * kDownSliceCols; e += blockDim.x) {
-        const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
-        if (t < n && c0 + c < d)
-            part[((size_t)g * kDecodeMaxTokens + t) * d + c0 + c] =
-                ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
-    }
-}
 
-// y[t][c] = sum over groups g (ascending) of part[g][t][c]. Loads are issued
-// in batches of 16 so the group loop is not one round trip per group.
-__global__ __launch_bounds__(256) void k_reduce(const float *__restrict__ part, int G, int n, int d,
-                                                float *__restrict__ y)
-{
-    const int e = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= n * d) return;
-    const int t = e / d, c = e - t * d;
-    const float *p = part + (size_t)t * d + c;
-    const size_t gs = (size_t)kDecodeMaxTokens * d;
-    float v = 0.f;
-    for (int g0 = 0; g0 < G; g0 += 16) {
-        float b[16];
+    const int c0 = s * kDownSliceCols;
+    const size_t gs = (size_t)kDecodeMaxTokens * d;  // stride of one group's slab
+    constexpr int PER = (NT * kDownSliceCols + 255) / 256;  // elements per thread
+    if (g < G - 1) {
+        // ---- stage 1 only: publish this group's slice of P ----
 #pragma unroll
-        for (int u = 0; u < 16; ++u) b[u] = g0 + u < G ? p[(size_t)(g0 + u) * gs] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v += b[u];
+        for (int q = 0; q < PER; ++q) {
+            const int e = tid + 256 * q;
+            const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
+            if (t < n && c0 + c < d) {
+                const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
+                __hip_atomic_store(part + (size_t)g * gs + (size_t)t * d + c0 + c, __float_as_uint(v),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        return;
     }
-    y[e] = v;
+    // ---- stage 2: ordered sum over the groups ----
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = tid + 256 * q;
+        const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
+        if (t < n && c0 + c < d) {
+            const float own = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
+            uint32_t *p = part + (size_t)t * d + c0 + c;
+            float v = 0.f;
+            for (int g0 = 0; g0 < G - 1; g0 += 16) {
+                uint32_t b[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    b[u] = g0 + u < G - 1
+                               ? __hip_atomic_load(p + (size_t)(g0 + u) * gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0u;
+                for (int spin = 0; spin < kDownSpinMax; ++spin) {
+                    bool ready = true;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) ready = ready && b[u] != kDownMarker;
+                    if (ready) break;
+                    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        if (b[u] == kDownMarker)
+                            b[u] = __hip_atomic_load(p + (size_t)(g0 + u) * gs, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (g0 + u < G - 1) {
+                        v += __uint_as_float(b[u]);
+                        __hip_atomic_store(p + (size_t)(g0 + u) * gs, kDownMarker, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            }
+            y[(size_t)t * d + c0 + c] = v + own;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -314,8 +358,17 @@ hipError_t device_setup(sffn_ctx &c)
 
 bool decode_fits(const sffn_ctx &c, int, int) { return down_lds(c) <= c.lds_max; }
 
+__global__ void k_fill_u32(uint32_t *__restrict__ p, size_t count, uint32_t v)
+{
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
 hipError_t launch_init(sffn_ctx &c, hipStream_t s)
 {
+    // the down projection's group slots start out holding their marker
+    hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, s, reinterpret_cast<uint32_t *>(c.ws + c.L.part),
+                       c.L.part_words, kDownMarker);
     hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
     hipLaunchKernelGGL(k_zero_ints, dim3(16), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ubits), c.L.words);
     return hipGetLastError();
@@ -330,7 +383,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     uint8_t *act = reinterpret_cast<uint8_t *>(ws + c.L.act);
     float *gsel = reinterpret_cast<float *>(ws + c.L.gsel);
     float *hbuf = reinterpret_cast<float *>(ws + c.L.hbuf);
-    float *part = reinterpret_cast<float *>(ws + c.L.part);
+    uint8_t *any = reinterpret_cast<uint8_t *>(ws + c.L.any);
     const TW *x = static_cast<const TW *>(a.x);
     const TW *wg = static_cast<const TW *>(a.w.w_gate);
     const TW *wu = static_cast<const TW *>(a.w.w_up);
@@ -355,6 +408,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     g.tau = a.tau;
     g.gsel = gsel;
     g.act = act;
+    g.any = any;
     g.hbuf = hbuf;
     g.debug_z = a.debug_z;
     g.stream = st;
@@ -385,21 +439,23 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
         const int lpr = lpr_for(d);
         const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
         if (lpr == 64)
-            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
+                               hbuf);
         else if (lpr == 32)
-            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
+                               hbuf);
         else
-            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, gsel, hbuf);
+            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
+                               hbuf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 
-    // ---- down partials, then the ordered reduction ----
+    // ---- down projection: group partials and their ordered sum ----
+    uint32_t *part = reinterpret_cast<uint32_t *>(ws + c.L.part);
     const int slices = (d + kDownSliceCols - 1) / kDownSliceCols;
     const int G = down_groups(c);
-    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, G), dim3(256), down_lds(c), st, wdn, F, d, n, act,
-                       dense ? 1 : 0, hbuf, part);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_reduce, dim3((n * d + 255) / 256), dim3(256), 0, st, part, G, n, d, a.y);
+    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, G), dim3(256), down_lds(c), st, wdn, F, d, n, any,
+                       dense ? 1 : 0, hbuf, part, a.y);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // ---- optional outputs ----

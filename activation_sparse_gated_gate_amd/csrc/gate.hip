@@ -22,7 +22,8 @@ namespace sffn {
 //              h[i][t] = g * (x_t . W_up[i]) for the selecting tokens, else 0
 //   DENSE:     every channel; gate and up rows are read together,
 //              g = max(z - tau, 0) or SiLU(z), h = g * u
-// h is stored channel-major, hbuf[i][t] (8 token slots per channel).
+// h is stored channel-major, hbuf[i][t] (8 token slots per channel); SELECT_UP
+// also writes any[i], whether some token selected channel i.
 // ---------------------------------------------------------------------------
 template <typename TW, typename TX, int NT, int LPR, int KIND>
 __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
@@ -30,7 +31,8 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
                                               const TW *__restrict__ wg, const TW *__restrict__ wu,
                                               int F, int mode, float tau,
                                               float *__restrict__ gsel, uint8_t *__restrict__ act,
-                                              float *__restrict__ hbuf, float *__restrict__ debug_z)
+                                              uint8_t *__restrict__ any, float *__restrict__ hbuf,
+                                              float *__restrict__ debug_z)
 {
     constexpr int SUB = 64 / LPR;
     constexpr int R = RowsPer<NT>::v;
@@ -102,6 +104,9 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
             }
         }
     if constexpr (KIND == SELECT_UP) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
         if (__ballot(amask != 0) == 0) return;  // nothing selected in this wavefront
         const TW *urows[R];
 #pragma unroll
@@ -122,17 +127,17 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 template <typename TW, typename TX, int NT, int KIND>
 static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
                         const TW *xu, int d, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel,
-                        uint8_t *act, float *hbuf, float *dz)
+                        uint8_t *act, uint8_t *any, float *hbuf, float *dz)
 {
     const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
 #define SFFN_G(LP)                                                                                               \
     do {                                                                                                         \
         if (ev0)                                                                                                 \
             hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
-                                  xu, d, wg, wu, F, mode, tau, gsel, act, hbuf, dz);                            \
+                                  xu, d, wg, wu, F, mode, tau, gsel, act, any, hbuf, dz);                       \
         else                                                                                                     \
             hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
-                               F, mode, tau, gsel, act, hbuf, dz);                                               \
+                               F, mode, tau, gsel, act, any, hbuf, dz);                                          \
     } while (0)
     if (lpr == 64) SFFN_G(64);
     else if (lpr == 32) SFFN_G(32);
@@ -154,15 +159,15 @@ hipError_t launch_gate(const GateArgs &g)
         switch (g.kind) {
         case KEYS:
             launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                            g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+                                            g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
             break;
         case DENSE:
             launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                             g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+                                             g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
             break;
         default:
             launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                                 g.mode, g.tau, g.gsel, g.act, g.hbuf, g.debug_z);
+                                                 g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
             break;
         }
     };

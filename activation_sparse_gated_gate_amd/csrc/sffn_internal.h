@@ -19,12 +19,13 @@ constexpr int kDecodeMaxTokens = 8;
 constexpr int kCtrlInts = 1024;
 constexpr int kCtrlUnionSize = 0;    // batched path: size of the union list
 
-constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
-constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
 // K splits of a batched GEMM (partial slices): up to 16 below 65 tokens, 8 up
 // to 511 tokens, none from 512.
 constexpr int kSplitMax = 16;
 inline int splits_max(int T) { return T <= 64 ? 16 : T < 512 ? 8 : 1; }
+
+constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
+constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
 
 constexpr int kMaxDff = 262144;
 
@@ -36,7 +37,9 @@ struct Layout {
     size_t gsel;      // decode: fp32 [ntp][d_ff] gate values; batched: bf16 [T][d_ff]
     size_t uidx;      // int32 [d_ff] ascending union list
     size_t hbuf;      // decode: fp32 [d_ff][ntp] gated up values; batched: bf16 [T][d_ff]
-    size_t part;      // fp32 [kDownGroupsMax][ntp][d_model] down-projection partials
+    size_t any;       // decode: uint8 [d_ff] union of the tokens' active flags
+    size_t part;      // decode: fp32 bits [kDownGroupsMax][ntp][d_model] down-projection group slots
+    size_t part_words;
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
@@ -107,6 +110,7 @@ struct GateArgs {
     float tau;
     float *gsel;          // [8][F] gate values / Top-K keys
     uint8_t *act;         // [8][F] selected flags (threshold)
+    uint8_t *any;         // [F] union of the selected flags over the tokens
     float *hbuf;          // [F][8] h values of selected channels
     float *debug_z;
     hipStream_t stream;

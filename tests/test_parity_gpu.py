@@ -108,6 +108,23 @@ def test_ragged_shapes(dtype, d, f, n, mode):
     assert rep.rel_err <= (1e-5 if dtype == "f32" else DECODE_GUARD)
 
 
+@pytest.mark.parametrize("f", [8193, 16385, 24600])
+@pytest.mark.parametrize("n", [1, 5, 8])
+@pytest.mark.parametrize("mode", ["threshold", "dense_relu"])
+def test_down_channel_passes(f, n, mode):
+    """The down projection lists the selected channels in passes of 8192
+    (8 tokens) or 16384 channels: one, two and several passes, with ragged
+    output pieces (d = 136) and every token count class."""
+    d = 136
+    say(f"case down passes bf16 d={d} F={f} n={n} {mode}")
+    lay = inputs.make_layer(12, d, f, "bf16")
+    x = inputs.make_x(12, n, d, "bf16")
+    ref = oracle_forward(lay, x, mode, tau=1.0)
+    got = run_gpu(lay, x, mode, tau=1.0, max_tokens=8)
+    rep = compare(lay, x, mode, ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
 @pytest.mark.parametrize("rank", [8, 64, 264])
 @pytest.mark.parametrize("n", [1, 5])
 def test_lopa_ragged(rank, n):

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    // XCD-aware tile order (as k_mfma): the M tiles of one N tile run on one XCD
+    // XCD-aware tile order: the M tiles of one N tile run on one XCD
     const int MT = (M + BM - 1) / BM, NTT = (N + BN - 1) / BN;
     const int xcd = blockIdx.x % 8, jt = blockIdx.x / 8;
     const int mi = jt % MT, ni = (jt / MT) * 8 + xcd;
@@ -774,7 +774,7 @@ static int split_for(const sffn_ctx &c, long long tiles, int K, int M)
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
 {
     const sffn_shape &S = c.shape;
-    const int T = a.n, d = S.d_model, F = S.d_ff, W = c.L.words;
+    const int T = a.n, d = S.d_model, F = S.d_ff;
     char *ws = c.ws;
     uint16_t *G = reinterpret_cast<uint16_t *>(ws + c.L.gsel);
     uint16_t *H = reinterpret_cast<uint16_t *>(ws + c.L.hbuf);
@@ -835,11 +835,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         }
         if (ev1) hipEventRecord(ev1, st);
     }
-    // ---- Top-K: per-token select, then the union of the flags ----
+    // ---- Top-K: per-token select, its flags and the union of the flags ----
     if (a.mode == SFFN_TOPK) {
-        int2 *thr = reinterpret_cast<int2 *>(c.ws + c.L.thr);
-        if ((e = launch_topk_thr(keys, T, F, a.k, thr, st)) != hipSuccess) return e;
-        if ((e = launch_topk_flags(keys, T, F, thr, act, G, W, ubits, st)) != hipSuccess) return e;
+        if ((e = launch_topk_select_flags(keys, T, F, a.k, act, G, ubits, st)) != hipSuccess) return e;
     }
     // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {

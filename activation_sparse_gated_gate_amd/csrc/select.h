@@ -41,10 +41,23 @@ struct __align__(16) SelectLds {
     int scan_scratch[16];
 };
 
-// The select of one token's keys s[0 .. F) by a block of 1024 threads;
-// returns {K-th key, tie cutoff} in every thread. Contains barriers.
+// This thread's keys of the KPT > 0 form: kf[e] = s[KPT tid + e] (0 past F).
 template <int KPT>
-__device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, int K, SelectLds &L)
+__device__ __forceinline__ void load_keys(const float *__restrict__ s, int F, float (&kf)[KPT > 0 ? KPT : 1])
+{
+    if constexpr (KPT > 0) {
+        const int i0 = threadIdx.x * KPT;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) kf[e] = (i0 + e < F) ? s[i0 + e] : 0.f;
+    }
+}
+
+// The select of one token's keys s[0 .. F) by a block of 1024 threads, with
+// this thread's keys in kf (load_keys) when KPT > 0; returns {K-th key, tie
+// cutoff} in every thread. Contains barriers.
+template <int KPT>
+__device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, int K, SelectLds &L,
+                                           const float (&kf)[KPT > 0 ? KPT : 1])
 {
     constexpr int NTHR = 1024, NB = SelectLds::NB, CMAX = SelectLds::CMAX;
     int *hist = L.hist;
@@ -55,12 +68,6 @@ __device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, i
     int *scan_scratch = L.scan_scratch;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    float kf[KPT > 0 ? KPT : 1];
-    if constexpr (KPT > 0) {
-        const int i0 = tid * KPT;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) kf[e] = (i0 + e < F) ? s[i0 + e] : 0.f;
-    }
     // fn(i, v) over this thread's keys
     auto for_keys = [&](auto &&fn) {
         if constexpr (KPT > 0) {

@@ -89,10 +89,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
 // Per-token Top-K (topk.hip), shared by both regimes: thr[t] = {K-th largest
 // key in the f2key encoding, last channel index kept among keys equal to it}.
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st);
-// Batched: act[t][i] and bf16 gate values G[t][i] from the thresholds, and
-// the union bitmap words.
-hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, uint8_t *act, uint16_t *G, int W,
-                             uint32_t *ubits, hipStream_t st);
+// Batched: the per-token select, then act[t][i], the bf16 gate values
+// G[t][i] and the union bitmap words from it.
+hipError_t launch_topk_select_flags(const float *keys, int T, int F, int K, uint8_t *act, uint16_t *G,
+                                   uint32_t *ubits, hipStream_t st);
 // Decode gate kernel (gate.hip): gate GEMV + activation + select (+ the up
 // rows of the selected channels, or of every channel in the dense modes).
 struct GateArgs {

@@ -6,9 +6,10 @@
 // writes no per-channel output. Channel i of token t is then selected iff
 //   key > kth  or  (key == kth and i <= cut)
 // (topk_on), so ties at the K-th value go to the lower channel indices and
-// exactly K channels are selected. The consumer applies that rule where it
-// reads the keys anyway: the decode up kernel, or k_topk_flags for a batch
-// (which also writes the batch's gate values and union bitmap).
+// exactly K channels are selected. The decode up kernel applies that rule
+// where it reads the keys anyway; for a batch, k_topk_select_flags applies it
+// right after the select, to the keys the select holds, and writes the
+// batch's flags, gate values and union bitmap.
 #include "select.h"
 #include "sffn_internal.h"
 
@@ -22,34 +23,64 @@ __global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ key
 {
     __shared__ SelectLds L;
     const int t = blockIdx.x;
-    const int2 r = select_kth<KPT>(keys + (size_t)t * F, F, K, L);
+    const float *s = keys + (size_t)t * F;
+    float kf[KPT > 0 ? KPT : 1];
+    load_keys<KPT>(s, F, kf);
+    const int2 r = select_kth<KPT>(s, F, K, L, kf);
     if (threadIdx.x == 0) thr[t] = r;
 }
 
-// Batched: act[t][i] from the thresholds, the gate values the up GEMM reads
-// (G[t][i] = bf16 key where selected, else 0), and the union bitmap. Block
-// (x, y) takes 256 channels and 8 tokens; the union words are ORed in (the
-// bitmap is all zero on entry: the down GEMM clears it after use).
-__global__ __launch_bounds__(256) void k_topk_flags(const float *__restrict__ keys, int T, int F,
-                                                    const int2 *__restrict__ thr, uint8_t *__restrict__ act,
-                                                    uint16_t *__restrict__ G, int W, uint32_t *__restrict__ ubits)
+// Batched: the select of token t (one 1024-thread workgroup per token), then
+// token t's flags act[t][i], the gate values the up GEMM reads (G[t][i] =
+// bf16 key where selected, else 0) and its bits of the union bitmap, ORed
+// in with one atomic per 32-bit word and wavefront (the bitmap is all zero
+// on entry: the down GEMM clears it after use).
+template <int KPT>
+__global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restrict__ keys, int F, int K,
+                                                            uint8_t *__restrict__ act, uint16_t *__restrict__ G,
+                                                            uint32_t *__restrict__ ubits)
 {
-    const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
-    const int t0 = blockIdx.y * 8, t1 = min(T, t0 + 8);
-    bool any = false;
-    if (i < F)
-        for (int t = t0; t < t1; ++t) {
-            const size_t o = (size_t)t * F + i;
-            const float k = keys[o];
-            const bool on = topk_on(k, i, thr[t]);
-            act[o] = on;
-            G[o] = on ? f2bf(k) : (uint16_t)0;
-            any |= on;
+    __shared__ SelectLds L;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const float *s = keys + (size_t)t * F;
+    float kf[KPT > 0 ? KPT : 1];
+    load_keys<KPT>(s, F, kf);
+    const int2 r = select_kth<KPT>(s, F, K, L, kf);
+    uint8_t *a = act + (size_t)t * F;
+    uint16_t *g = G + (size_t)t * F;
+    if constexpr (KPT > 0) {
+        // channels KPT tid .. + KPT-1: one 32-bit word, shared by 32 / KPT lanes
+        const int i0 = tid * KPT;
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int i = i0 + e;
+            if (i < F) {
+                const bool on = topk_on(kf[e], i, r);
+                a[i] = on;
+                g[i] = on ? f2bf(kf[e]) : (uint16_t)0;
+                m |= (uint32_t)on << e;
+            }
         }
-    const unsigned long long m = __ballot(any);
-    const int w = i >> 5;
-    const uint32_t bits = (uint32_t)(m >> (lane & 32));
-    if ((lane & 31) == 0 && w < W && bits) atomicOr(&ubits[w], bits);
+        m <<= i0 & 31;
+#pragma unroll
+        for (int o = 1; o < 32 / KPT; o <<= 1) m |= __shfl_xor(m, o, 64);
+        if ((lane & (32 / KPT - 1)) == 0 && m) atomicOr(&ubits[i0 >> 5], m);
+    } else {
+        for (int i0 = tid - lane; i0 < F; i0 += 1024) {
+            const int i = i0 + lane;
+            bool on = false;
+            if (i < F) {
+                const float k = s[i];
+                on = topk_on(k, i, r);
+                a[i] = on;
+                g[i] = on ? f2bf(k) : (uint16_t)0;
+            }
+            const unsigned long long b = __ballot(on);
+            const uint32_t bits = (uint32_t)(b >> (lane & 32));
+            if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
+        }
+    }
 }
 
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st)
@@ -62,11 +93,15 @@ hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hi
     return hipGetLastError();
 }
 
-hipError_t launch_topk_flags(const float *keys, int T, int F, const int2 *thr, uint8_t *act, uint16_t *G, int W,
-                             uint32_t *ubits, hipStream_t st)
+hipError_t launch_topk_select_flags(const float *keys, int T, int F, int K, uint8_t *act, uint16_t *G,
+                                   uint32_t *ubits, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_topk_flags, dim3((F + 255) / 256, (T + 7) / 8), dim3(256), 0, st, keys, T, F, thr, act, G, W,
-                       ubits);
+    const dim3 grid(T), block(1024);
+    if (F <= 1024 * 4) hipLaunchKernelGGL(k_topk_select_flags<4>, grid, block, 0, st, keys, F, K, act, G, ubits);
+    else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topk_select_flags<8>, grid, block, 0, st, keys, F, K, act, G, ubits);
+    else if (F <= 1024 * 16)
+        hipLaunchKernelGGL(k_topk_select_flags<16>, grid, block, 0, st, keys, F, K, act, G, ubits);
+    else hipLaunchKernelGGL(k_topk_select_flags<0>, grid, block, 0, st, keys, F, K, act, G, ubits);
     return hipGetLastError();
 }
 

@@ -11,7 +11,8 @@ Sources: "Model Casting and Low-Parameter Gating: Towards More Sparsely
 Activated FFNs", Abstract (gate-first skipping, LoPA); "Mixture-of-Channels:
 Exploiting Sparse FFNs for Efficient LLMs Pre-Training and Inference" (blog
 summary), sections "Dentro il 'mixture'" and "'Dentro MoC'" (per-token Top-K of
-the SwiGLU gate, binary mask, loading only active rows).
+the SwiGLU gate, binary mask, loading only active rows; the 2:8 structured
+option).
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         _lib.oracle_select_threshold.argtypes = [I, I, P, D, P, P]
         _lib.oracle_select_topk.argtypes = [I, I, I, P, P, P, P]
         _lib.oracle_select_topk.restype = I
+        _lib.oracle_select_nm.argtypes = [I, I, I, I, P, P, P, P]
+        _lib.oracle_select_nm.restype = I
         _lib.oracle_select_dense.argtypes = [I, I, I, P, D, P, P]
         _lib.oracle_up.argtypes = [I, I, I, P, I, P, I, P, P, I, P]
         _lib.oracle_down.argtypes = [I, I, I, P, P, I, P, I, P]
@@ -142,6 +145,21 @@ def select_topk(z: np.ndarray, k: int):
     return mask, g, kth
 
 
+def select_nm(z: np.ndarray, n_keep: int = 2, group: int = 8):
+    """Structured n_keep:group selection of the SiLU gate (2:8 by default).
+    Returns the mask, the gate values and each channel's group bound (the
+    n_keep-th largest key of its group; -inf where the group keeps all)."""
+    z = _c(np.asarray(z, dtype=np.float64))
+    n, f = z.shape
+    mask = np.empty((n, f), dtype=np.uint8)
+    g = np.empty((n, f), dtype=np.float64)
+    bound = np.empty((n, f), dtype=np.float64)
+    rc = lib().oracle_select_nm(n, f, int(n_keep), int(group), _p(z), _p(mask), _p(g), _p(bound))
+    if rc != 0:
+        raise ValueError(f"{n_keep}:{group} selection")
+    return mask, g, bound
+
+
 def select_dense(z: np.ndarray, act: str, tau: float = 0.0):
     z = _c(np.asarray(z, dtype=np.float64))
     n, f = z.shape
@@ -202,7 +220,8 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
     """The whole forward: gate, selection, up, down.
 
     mode: "threshold" (full gate, shifted ReLU), "lopa" (low-rank gate, shifted
-    ReLU), "topk" (full gate, per-token Top-K of SiLU), "dense_relu" /
+    ReLU), "topk" (full gate, per-token Top-K of SiLU), "topk_2_8" (full gate,
+    per-token top 2 of every aligned group of 8 SiLU keys), "dense_relu" /
     "dense_silu" (every channel kept). tau is rounded to fp32 first when
     tau_f32 is set, so both sides compare against the same number.
     """
@@ -219,6 +238,9 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
     elif mode == "topk":
         mask, g, kth = select_topk(z, k)
         band = np.abs(g - kth[:, None]) <= BAND
+    elif mode == "topk_2_8":
+        mask, g, bound = select_nm(z, 2, 8)
+        band = np.abs(g - bound) <= BAND
     elif mode == "dense_relu":
         mask, g = select_dense(z, "relu", tau)
         band = np.zeros(z.shape, dtype=bool)

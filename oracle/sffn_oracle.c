@@ -17,7 +17,8 @@
  *   Pre-Training and Inference" (blog summary), sections "Dentro il
  *   'mixture'" and "'Dentro MoC'": per token only the Top-K channels of the
  *   SwiGLU gate stay active (a binary mask), and only the weight rows and
- *   columns of active channels are loaded.
+ *   columns of active channels are loaded; the same sections and "Kernel e
+ *   strutture" name a 2:8 structured-sparsity option.
  *
  * Readings where the pages leave a step open (each is listed in the design
  * notes of the repository):
@@ -25,6 +26,8 @@
  *     z > tau (strict), so z == tau is inactive;
  *   - the Top-K key is the signed SiLU value s = z / (1 + exp(-z)); ties go to
  *     the lower channel index; the gate value of an active channel is s;
+ *   - the 2:8 structured option keeps, per token, the 2 largest keys of every
+ *     aligned group of 8 consecutive channels, under the same order;
  *   - inputs are the exact values the GPU sees (fp32, or bf16 bit patterns
  *     widened exactly), and every sum runs in ascending index order in fp64.
  *
@@ -147,6 +150,45 @@ int oracle_select_topk(int n, int F, int K, const double *z, unsigned char *mask
         for (int q = 0; q < K; ++q)
             mt[order[q].i] = 1;
         kth[t] = order[K - 1].s;
+    }
+    free(order);
+    return 0;
+}
+
+/* Structured N:M selection of the SiLU gate (the MoC 2:8 option is N = 2,
+ * M = 8): g = SiLU(z) for every channel; the channels are split into aligned
+ * groups of M consecutive ones, [M q, M q + M) (the last group may be shorter),
+ * and within each group mask marks the N channels with the largest g under
+ * the same total order as the Top-K (key descending, then channel ascending);
+ * a group of at most N channels keeps them all. bound[t][i] receives the
+ * N-th largest key of channel i's group, or -INFINITY when its group keeps
+ * every channel. Returns 0, or -1 on bad N / M or no memory. */
+int oracle_select_nm(int n, int F, int N, int M, const double *z, unsigned char *mask, double *g,
+                     double *bound)
+{
+    if (N < 1 || M < N) return -1;
+    struct keyed *order = (struct keyed *)malloc(sizeof(struct keyed) * (size_t)M);
+    if (!order) return -1;
+    for (int t = 0; t < n; ++t) {
+        const double *zt = z + (long)t * F;
+        double *gt = g + (long)t * F, *bt = bound + (long)t * F;
+        unsigned char *mt = mask + (long)t * F;
+        for (int q0 = 0; q0 < F; q0 += M) {
+            const int len = F - q0 < M ? F - q0 : M;
+            for (int e = 0; e < len; ++e) {
+                gt[q0 + e] = silu(zt[q0 + e]);
+                order[e].s = gt[q0 + e];
+                order[e].i = q0 + e;
+                mt[q0 + e] = 0;
+            }
+            qsort(order, (size_t)len, sizeof(struct keyed), keyed_cmp);
+            const int keep = len < N ? len : N;
+            for (int e = 0; e < keep; ++e)
+                mt[order[e].i] = 1;
+            const double b = len > N ? order[N - 1].s : -INFINITY;
+            for (int e = 0; e < len; ++e)
+                bt[q0 + e] = b;
+        }
     }
     free(order);
     return 0;

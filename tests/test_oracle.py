@@ -72,7 +72,7 @@ def _rand_layer(seed, d, f, dtype, rank=0):
     return inputs.make_layer(seed, d, f, dtype, rank=rank, with_gate=True)
 
 
-@pytest.mark.parametrize("mode", ["threshold", "topk", "lopa", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "lopa", "dense_relu", "dense_silu"])
 @pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
 def test_masked_dense_equals_sparse_skip(mode, dtype):
     d, f, n = 64, 200, 3
@@ -235,6 +235,78 @@ def test_topk_rejects_bad_k():
         oracle.select_topk(np.zeros((1, 4)), 0)
     with pytest.raises(ValueError):
         oracle.select_topk(np.zeros((1, 4)), 5)
+
+
+# ---------------------------------------------------------------------------
+# 2:8 structured selection
+# ---------------------------------------------------------------------------
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def test_nm_brute_force_with_ties():
+    """In every aligned group of 8 channels (the last may be shorter) the kept
+    pair is, among all pairs of the group with the largest sum of keys, the
+    one with the lexicographically smallest sorted channel indices; groups of
+    at most 2 keep everything. Keys drawn from a few values, so ties are
+    common."""
+    rng = np.random.default_rng(21)
+    for f in (1, 2, 3, 8, 9, 13, 16, 21):
+        z = rng.integers(-3, 4, size=(4, f)).astype(np.float64) * 0.5
+        mask, g, _ = oracle.select_nm(z, 2, 8)
+        keys = _silu(z)
+        for t in range(z.shape[0]):
+            want = []
+            for q0 in range(0, f, 8):
+                grp = list(range(q0, min(f, q0 + 8)))
+                if len(grp) <= 2:
+                    want += grp
+                    continue
+                best = max(keys[t, list(c)].sum() for c in itertools.combinations(grp, 2))
+                cands = [c for c in itertools.combinations(grp, 2) if keys[t, list(c)].sum() == best]
+                want += list(min(cands))
+            assert list(np.nonzero(mask[t])[0]) == want, (f, t)
+            np.testing.assert_array_equal(g[t], keys[t])
+
+
+def test_nm_single_group_is_top2():
+    """With F = 8 there is one group, and 2:8 is the per-token Top-K with K = 2
+    (pinned separately)."""
+    z = np.random.default_rng(22).standard_normal((5, 8)) * 2.0
+    m_nm, g_nm, b_nm = oracle.select_nm(z, 2, 8)
+    m_tk, g_tk, kth = oracle.select_topk(z, 2)
+    assert np.array_equal(m_nm, m_tk)
+    assert np.array_equal(g_nm, g_tk)
+    assert np.array_equal(b_nm, np.repeat(kth[:, None], 8, axis=1))
+
+
+def test_nm_invariants_at_moc_shape():
+    """2 kept per group of 8; every kept key of a group is at least every
+    dropped one; the group bound is the smaller kept key."""
+    f = 5632
+    z = np.random.default_rng(23).standard_normal((3, f))
+    mask, g, bound = oracle.select_nm(z, 2, 8)
+    m = mask.reshape(3, f // 8, 8).astype(bool)
+    k = g.reshape(3, f // 8, 8)
+    assert (m.sum(axis=2) == 2).all()
+    kept_min = np.where(m, k, np.inf).min(axis=2)
+    dropped_max = np.where(m, -np.inf, k).max(axis=2)
+    assert (kept_min >= dropped_max).all()
+    assert np.array_equal(bound.reshape(3, f // 8, 8), np.repeat(kept_min[:, :, None], 8, axis=2))
+
+
+def test_nm_permutation_within_groups():
+    """Permuting channels inside their groups (distinct keys) permutes the set,
+    and leaves y unchanged up to rounding."""
+    d, f, n = 32, 40, 3
+    lay = _rand_layer(24, d, f, inputs.F32)
+    x = inputs.make_x(24, n, d, inputs.F32)
+    rng = np.random.default_rng(24)
+    perm = np.concatenate([q0 + rng.permutation(8) for q0 in range(0, f, 8)])
+    a = oracle.forward("topk_2_8", x, lay.w_up, lay.w_down, w_gate=lay.w_gate)
+    b = oracle.forward("topk_2_8", x, lay.w_up[perm], lay.w_down[perm], w_gate=lay.w_gate[perm])
+    assert np.array_equal(a.mask[:, perm], b.mask)
+    np.testing.assert_allclose(a.y, b.y, rtol=1e-13, atol=1e-14)
 
 
 # ---------------------------------------------------------------------------

@@ -38,6 +38,10 @@ MUTATIONS = {
     "topk_ties_to_higher_index": ("return (a->i > b->i) - (a->i < b->i);",
                                   "return (a->i < b->i) - (a->i > b->i);"),
     "topk_off_by_one": ("for (int q = 0; q < K; ++q)", "for (int q = 1; q < K; ++q)"),
+    "nm_keeps_three": ("const int keep = len < N ? len : N;", "const int keep = len < N + 1 ? len : N + 1;"),
+    "nm_groups_misaligned": ("for (int q0 = 0; q0 < F; q0 += M) {", "for (int q0 = 0; q0 < F; q0 += M - 1) {"),
+    "nm_bound_off_by_one": ("const double b = len > N ? order[N - 1].s : -INFINITY;",
+                            "const double b = len > N ? order[N].s : -INFINITY;"),
     "lopa_a_transposed": ("elem(at, w_dt, (long)k * d + j)", "elem(at, w_dt, (long)j * r + k)"),
     "lopa_b_transposed": ("elem(bt, w_dt, (long)i * r + k)", "elem(bt, w_dt, (long)k * F + i)"),
     "union_and": ("any |= mask[(long)t * F + i];", "any &= mask[(long)t * F + i];"),

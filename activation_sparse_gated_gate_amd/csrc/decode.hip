@@ -7,6 +7,9 @@
 //   LoPA       k_lopa_xa (t = x.A) -> k_gate<SELECT_UP> on B with t -> k_down
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
 //              K-th key) -> k_up (flags + up rows) -> k_down
+//   2:8        k_gate<SELECT_NM>: gate GEMV, SiLU keys ranked within each
+//              aligned group of 8 channels, and the W_up rows of the 2 kept
+//              per group -> k_down
 //   dense      k_gate<DENSE> (gate and up rows of every channel) -> k_down
 //
 // The gate is computed first and in full; only the channels it leaves active
@@ -415,7 +418,8 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     g.ev_start = c.ev_start;
     g.ev_stop = c.ev_stop;
     g.lpr = lpr_for(d);
-    g.kind = dense ? DENSE : a.mode == SFFN_TOPK ? KEYS : SELECT_UP;
+    g.kind = dense ? DENSE : a.mode == SFFN_TOPK ? KEYS : a.mode == SFFN_TOPK_2_8 ? SELECT_NM : SELECT_UP;
+    if (g.kind == SELECT_NM && g.lpr == 64 && RowsPer<NT>::v < 2) g.lpr = 32;  // whole 2:8 groups per workgroup
     if (a.mode == SFFN_LOPA) {
         const int r = S.rank;
         float *tvec = reinterpret_cast<float *>(ws + c.L.tvec);

@@ -22,8 +22,13 @@ namespace sffn {
 //              h[i][t] = g * (x_t . W_up[i]) for the selecting tokens, else 0
 //   DENSE:     every channel; gate and up rows are read together,
 //              g = max(z - tau, 0) or SiLU(z), h = g * u
+//   SELECT_NM: g = SiLU(z); the workgroup's rows are whole aligned groups of
+//              8 channels (LPR <= 32, or enough rows per lane group); the keys
+//              go through LDS and each (channel, token) is ranked within its
+//              group by (key descending, channel ascending); the 2 first are
+//              active. Then as SELECT_UP: flags, union flag, up rows.
 // h is stored channel-major, hbuf[i][t] (8 token slots per channel); SELECT_UP
-// also writes any[i], whether some token selected channel i.
+// and SELECT_NM also write any[i], whether some token selected channel i.
 // ---------------------------------------------------------------------------
 template <typename TW, typename TX, int NT, int LPR, int KIND>
 __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
@@ -71,6 +76,20 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
             for (int t = 0; t < NT; ++t) zz[r][t] = dot.acc[r][t];
     }
 
+    // ---- 2:8: every key of the workgroup's groups into LDS ----
+    constexpr int WGROWS = 4 * SUB * R;  // rows of one workgroup, a multiple of 8 for SELECT_NM
+    static_assert(KIND != SELECT_NM || WGROWS % kNmGroup == 0, "2:8 needs whole groups per workgroup");
+    __shared__ float nm_keys[KIND == SELECT_NM ? WGROWS : 1][NT];
+    const int wg_row0 = blockIdx.x * WGROWS;
+    if constexpr (KIND == SELECT_NM) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (li == ((r * NT + t) & (LPR - 1))) nm_keys[row0 + r - wg_row0][t] = silu(zz[r][t]);
+        __syncthreads();
+    }
+
     // ---- activation and selection (every lane of the group has every z) ----
     float gv[R][NT];      // gate value of a selected (row, token), else 0
     uint32_t amask = 0;   // rows some token selected
@@ -85,6 +104,17 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
             if constexpr (KIND == SELECT_UP) {
                 a = z > tau;
                 g = z - tau;
+            } else if constexpr (KIND == SELECT_NM) {
+                g = nm_keys[i - wg_row0][t];
+                const int b = (i & ~(kNmGroup - 1)) - wg_row0;
+                int rank = 0;
+#pragma unroll
+                for (int e = 0; e < kNmGroup; ++e) {
+                    const float o = nm_keys[b + e][t];
+                    const int j = wg_row0 + b + e;
+                    rank += j < F && (o > g || (o == g && j < i));
+                }
+                a = rank < kNmKeep;
             } else if constexpr (KIND == KEYS) {
                 a = false;
                 g = silu(z);
@@ -99,11 +129,11 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
             if (live && li == ((r * NT + t) & (LPR - 1))) {
                 gsel[(size_t)t * F + i] = g;
                 if (debug_z) debug_z[(size_t)t * F + i] = z;
-                if constexpr (KIND == SELECT_UP) act[(size_t)t * F + i] = a ? 1 : 0;
+                if constexpr (KIND == SELECT_UP || KIND == SELECT_NM) act[(size_t)t * F + i] = a ? 1 : 0;
                 if constexpr (KIND == DENSE) hbuf[(size_t)i * kDecodeMaxTokens + t] = g * uu[r][t];
             }
         }
-    if constexpr (KIND == SELECT_UP) {
+    if constexpr (KIND == SELECT_UP || KIND == SELECT_NM) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
@@ -139,8 +169,16 @@ static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lp
             hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
                                F, mode, tau, gsel, act, any, hbuf, dz);                                          \
     } while (0)
-    if (lpr == 64) SFFN_G(64);
-    else if (lpr == 32) SFFN_G(32);
+    // 2:8 needs whole groups of 8 rows per workgroup: 64 lanes per row only
+    // with at least two rows per lane group (the host picks 32 otherwise)
+    constexpr bool full64 = KIND != SELECT_NM || RowsPer<NT>::v >= 2;
+    if constexpr (full64) {
+        if (lpr == 64) {
+            SFFN_G(64);
+            return;
+        }
+    }
+    if (lpr == 32) SFFN_G(32);
     else SFFN_G(16);
 #undef SFFN_G
 }
@@ -164,6 +202,11 @@ hipError_t launch_gate(const GateArgs &g)
         case DENSE:
             launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
                                              g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
+            break;
+        case SELECT_NM:
+            if constexpr (std::is_same<TX, TW>::value)  // 2:8 takes the full gate
+                launch_gate_k<TW, TX, NT, SELECT_NM>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                     g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
             break;
         default:
             launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,

@@ -7,7 +7,11 @@
 
 namespace sffn {
 
-enum GateKind { KEYS = 0, SELECT_UP = 1, DENSE = 2 };
+enum GateKind { KEYS = 0, SELECT_UP = 1, DENSE = 2, SELECT_NM = 3 };
+
+// Rows of one 2:8 group: the SELECT_NM gate kernel needs whole groups in a
+// workgroup (it ranks each group's keys through LDS).
+constexpr int kNmGroup = 8, kNmKeep = 2;
 
 // ---------------------------------------------------------------------------
 // Row-dot engine. A lane group of LPR lanes owns R rows; lane li covers the

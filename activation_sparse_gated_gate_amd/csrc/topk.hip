@@ -1,6 +1,8 @@
 // Per-token Top-K selection over the SiLU gate keys, shared by the decode and
 // batched regimes ("Mixture-of-Channels" blog summary, "Dentro il 'mixture'":
-// each token keeps its K channels of largest SiLU(gate)).
+// each token keeps its K channels of largest SiLU(gate)), and the batched 2:8
+// structured selection (the same summary's 2:8 option: the top 2 of every
+// aligned group of 8 channels).
 //
 // k_topk_thr finds, per token, the K-th largest key and a tie cutoff; it
 // writes no per-channel output. Channel i of token t is then selected iff
@@ -81,6 +83,46 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
             if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
         }
     }
+}
+
+// Batched 2:8 structured selection: block (x, t) takes channels
+// [256 x, 256 x + 256) of token t (32 whole groups of 8). The keys go through
+// LDS; each channel is ranked within its group by (key descending, channel
+// ascending) and the first 2 are kept: act[t][i], G[t][i] = bf16 key where
+// kept, else 0, and the union bits (one atomic per 32-bit word).
+__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int F, uint8_t *__restrict__ act,
+                                                  uint16_t *__restrict__ G, uint32_t *__restrict__ ubits)
+{
+    constexpr int GROUP = 8, KEEP = 2;
+    __shared__ float kl[256];
+    const int t = blockIdx.y, i0 = blockIdx.x * 256, tid = threadIdx.x, lane = tid & 63;
+    const int i = i0 + tid;
+    const size_t o = (size_t)t * F + i;
+    const float k = i < F ? keys[o] : 0.f;
+    kl[tid] = k;
+    __syncthreads();
+    const int b = tid & ~(GROUP - 1);
+    int rank = 0;
+#pragma unroll
+    for (int e = 0; e < GROUP; ++e) {
+        const float v = kl[b + e];
+        rank += i0 + b + e < F && (v > k || (v == k && b + e < tid));
+    }
+    const bool on = i < F && rank < KEEP;
+    if (i < F) {
+        act[o] = on;
+        G[o] = on ? f2bf(k) : (uint16_t)0;
+    }
+    const unsigned long long m = __ballot(on);
+    const uint32_t bits = (uint32_t)(m >> (lane & 32));
+    if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
+}
+
+hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
+                           hipStream_t st)
+{
+    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, T), dim3(256), 0, st, keys, F, act, G, ubits);
+    return hipGetLastError();
 }
 
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st)

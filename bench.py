@@ -215,7 +215,7 @@ def points_lopa(W, S, inputs, torch, dev, dense2, union, replicate):
 
 
 def points_moc(W, S, inputs, torch, dev, union, replicate):
-    """Mixture-of-Channels Top-K, decode and batched."""
+    """Mixture-of-Channels Top-K and its 2:8 structured option, decode and batched."""
     out = []
     es = 2
     wl = W["moc_topk_bf16_d2048_f5632"]
@@ -238,6 +238,15 @@ def points_moc(W, S, inputs, torch, dev, union, replicate):
                         "tokens_per_s": round(n / sp, 1), "touched_bytes": touched,
                         "hbm_frac": round(touched / sp / PEAK_HBM, 4), "speedup_vs_dense": round(de / sp, 3),
                         "layer_copies": len(wlist)})
+        # the 2:8 structured option: 2 of every 8 channels per token (d_ff / 4)
+        na = union(ffn, xt, wlist[0], "topk_2_8", y)
+        touched = n * d * es + f * d * es + 2 * na * d * es + n * d * 4
+        sp = timed(ffn, xt, wlist, "topk_2_8", y, 200, 20)
+        out.append({"workload": wl.name, "tokens": n, "mode": "topk_2_8", "k": f // 4, "union": na,
+                    "union_frac": round(na / f, 4), "us_per_step": round(sp * 1e6, 2),
+                    "tokens_per_s": round(n / sp, 1), "touched_bytes": touched,
+                    "hbm_frac": round(touched / sp / PEAK_HBM, 4), "speedup_vs_dense": round(de / sp, 3),
+                    "layer_copies": len(wlist)})
     del cl, wlist, base
     torch.cuda.empty_cache()
     return out

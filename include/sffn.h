@@ -19,7 +19,9 @@
  * Efficient LLMs Pre-Training and Inference" (blog summary), sections "Dentro il
  * 'mixture'" and "'Dentro MoC'" -- per token keep the Top-K channels of the
  * SwiGLU gate as a binary mask and, at inference, load only the weight rows and
- * columns of the active channels.
+ * columns of the active channels; the same summary ("Kernel e strutture")
+ * names a 2:8 structured-sparsity option, read here as the top 2 of every
+ * aligned group of 8 channels.
  *
  * Layout (all row-major, element type = the shape's dtype unless stated):
  *   x        [n_tokens][d_model]
@@ -71,7 +73,11 @@ typedef enum {
                             ties go to the lower channel index                   */
     SFFN_LOPA = 2,       /* low-rank gate (x.A).B; active = z > tau; g = z - tau  */
     SFFN_DENSE = 3,      /* full gate; every channel computed, g = max(z - tau, 0) */
-    SFFN_DENSE_SILU = 4  /* full gate; every channel computed, g = SiLU(z) (SwiGLU) */
+    SFFN_DENSE_SILU = 4, /* full gate; every channel computed, g = SiLU(z) (SwiGLU) */
+    SFFN_TOPK_2_8 = 5    /* full gate; 2:8 structured: per token, within every aligned
+                            group of 8 consecutive channels [8q, 8q + 8), the 2 of
+                            largest SiLU(z) (ties to the lower index; a last group of
+                            at most 2 channels keeps them all); g = SiLU(z)       */
 } sffn_mode;
 
 /* Shape of a layer and the largest batch a handle serves.
@@ -118,7 +124,8 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
  *   w           host struct of device weight pointers
  *   mode        an sffn_mode
  *   tau         threshold for THRESHOLD, LOPA and DENSE (compared in fp32)
- *   k           Top-K size for TOPK, 1 <= k <= d_ff (ignored otherwise)
+ *   k           Top-K size for TOPK, 1 <= k <= d_ff (ignored otherwise; TOPK_2_8
+ *               keeps 2 of every 8 channels and takes no k)
  *   y           device, [n_tokens][d_model] fp32, written
  * Optional outputs (NULL to skip):
  *   active_idx  device int32 [n_tokens][d_ff]: row t holds token t's active
@@ -127,8 +134,8 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
  *   union_cnt   device int32 [1]: channels active for at least one token
  *   debug_z     device fp32 [n_tokens][d_ff]: the gate pre-activation z
  * A token with no active channel gets y = 0. n_tokens = 0 returns SFFN_OK and
- * enqueues nothing. LOPA needs a handle created with rank > 0; TOPK, THRESHOLD
- * and the dense modes need w_gate. */
+ * enqueues nothing. LOPA needs a handle created with rank > 0; TOPK, TOPK_2_8,
+ * THRESHOLD and the dense modes need w_gate. */
 sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const sffn_weights *w,
                          int mode, float tau, int k, float *y, int32_t *active_idx,
                          int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream);

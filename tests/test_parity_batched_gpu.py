@@ -48,11 +48,23 @@ def test_moc_topk_batched(moc_layer, n, k):
     say(f"    union fraction {rep.union / wl.d_ff:.3f}")
 
 
+@pytest.mark.parametrize("n", [16, 64])
+def test_moc_2_8_batched(moc_layer, n):
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    say(f"case moc 2:8 batched bf16 d=2048 F=5632 n={n}")
+    x = inputs.make_x(0, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(moc_layer, x, "topk_2_8")
+    got = run_gpu(moc_layer, x, "topk_2_8")
+    rep = compare(moc_layer, x, "topk_2_8", ref, got)
+    assert (got.sets.reshape(n, -1, 8).sum(axis=2) == 2).all()
+    say(f"    union fraction {rep.union / wl.d_ff:.3f}")
+
+
 # ---------------------------------------------------------------------------
 # Ragged batches through every tile configuration and mode
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n", [9, 33, 100, 300, 600])
-@pytest.mark.parametrize("mode", ["threshold", "topk", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "dense_relu", "dense_silu"])
 def test_batched_ragged(n, mode):
     d, f = 264, 1000
     say(f"case batched ragged bf16 d={d} F={f} n={n} {mode}")

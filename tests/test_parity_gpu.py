@@ -87,6 +87,42 @@ def test_moc_topk_decode(k):
     assert rep.rel_err <= DECODE_GUARD
 
 
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_moc_2_8_decode(n):
+    """The 2:8 structured option at the MoC shape: exactly 2 of every 8
+    channels per token (d_ff = 5632 is a multiple of 8)."""
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    say(f"case moc 2:8 bf16 d=2048 F=5632 n={n}")
+    lay = _layer(wl)
+    x = inputs.make_x(0, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, "topk_2_8")
+    got = run_gpu(lay, x, "topk_2_8", max_tokens=8)
+    rep = compare(lay, x, "topk_2_8", ref, got)
+    assert (got.sets.reshape(n, -1, 8).sum(axis=2) == 2).all()
+    assert rep.rel_err <= DECODE_GUARD
+
+
+@pytest.mark.parametrize("n", [1, 3, 12])
+def test_2_8_ties_go_to_lower_index(n):
+    """Gate rows duplicated inside a group of 8 give exactly tied keys: the
+    lower channel index is kept. Ragged d_ff (a last group of 3)."""
+    d, f = 64, 35
+    say(f"case 2:8 exact ties n={n}")
+    lay = inputs.make_layer(31, d, f, "bf16")
+    for q0 in range(0, 32, 8):
+        lay.w_gate[q0 + 5] = lay.w_gate[q0 + 2]
+        lay.w_gate[q0 + 7] = lay.w_gate[q0 + 2]
+    x = inputs.make_x(31, n, d, "bf16")
+    ref = oracle_forward(lay, x, "topk_2_8")
+    got = run_gpu(lay, x, "topk_2_8", max_tokens=n)
+    compare(lay, x, "topk_2_8", ref, got)
+    for t in range(n):
+        for q0 in range(0, 32, 8):
+            tied = got.sets[t, [q0 + 2, q0 + 5, q0 + 7]]
+            assert not np.any(~tied[:-1] & tied[1:]), f"token {t} group {q0 // 8}: tie kept out of index order"
+        assert got.sets[t, 32:].sum() == 2
+
+
 # ---------------------------------------------------------------------------
 # Shapes that span several tiles and ragged tails, every mode and dtype
 # ---------------------------------------------------------------------------
@@ -96,7 +132,7 @@ RAGGED = [(264, 1000), (64, 37), (136, 333), (1024, 2049)]
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d,f", RAGGED)
 @pytest.mark.parametrize("n", [1, 3, 8])
-@pytest.mark.parametrize("mode", ["threshold", "topk", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "dense_relu", "dense_silu"])
 def test_ragged_shapes(dtype, d, f, n, mode):
     say(f"case ragged {dtype} d={d} F={f} n={n} {mode}")
     lay = inputs.make_layer(3, d, f, dtype)

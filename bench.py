@@ -372,6 +372,35 @@ def main():
     }
     hot_sec = run("threshold", HEADLINE_TAU, args.steps, 5, rotate=False)
 
+    # ---- the same forwards replayed from a HIP graph (one capture of a
+    # forward per layer copy); each replay's y is checked against the eager
+    # forward of that copy, bit for bit ----
+    graph_sec = None
+    try:
+        y_eager = torch.empty_like(y)
+        ffn.forward(x, weights[-1], "threshold", y_eager, tau=HEADLINE_TAU)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for w in weights:
+                ffn.forward(x, w, "threshold", y, tau=HEADLINE_TAU)
+        reps = max(1, args.steps // len(weights))
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_eager), "graph replay differs from the eager forward"
+            ffn.forward(x, weights[0], "threshold", y_eager, tau=HEADLINE_TAU)  # eager work in between
+            ffn.forward(x, weights[-1], "threshold", y_eager, tau=HEADLINE_TAU)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_sec = (time.perf_counter() - t0) / (reps * len(weights))
+        del graph
+    except Exception as exc:  # reported, never hidden: the eager number stands
+        print(f"graph replay not measured: {exc}", file=sys.stderr)
+
     # ---- sweep over tau, with the dense forward as denominator ----
     sweep = []
     dense_sec = run("dense_relu", 0.0, max(50, args.steps // 4), 10)
@@ -440,6 +469,7 @@ def main():
         "step_roofline": step_roofline,
         "ms_per_step_with_kernel_events": round(ev_sec * 1e3, 5),
         "hot_cache_ms_per_step": round(hot_sec * 1e3, 5),
+        "graph_replay_ms_per_step": round(graph_sec * 1e3, 5) if graph_sec else None,
         "dense_ms_per_step": round(dense_sec * 1e3, 5),
         "speedup_vs_dense": round(dense_sec / sec, 3),
         "sweep": sweep,

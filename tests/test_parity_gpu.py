@@ -371,3 +371,42 @@ def test_handle_reuse_across_modes_and_batch_sizes():
         ref = oracle_forward(lay, x, mode, tau=1.0, k=100)
         got = run_gpu(lay, x, mode, tau=1.0, k=100, ffn=ffn)
         compare(lay, x, mode, ref, got)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: the forward enqueues only kernels (no allocation, no
+# memset, no synchronisation), so it can be captured and replayed
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode,n", [("threshold", 1), ("topk", 3), ("topk_2_8", 1), ("lopa", 4), ("threshold", 40)])
+def test_graph_replay_matches_eager(mode, n):
+    """Replays of a captured forward equal the eager forward bit for bit, with
+    eager forwards on other inputs between the replays."""
+    d, f = 512, 1536
+    say(f"case graph replay {mode} n={n}")
+    rank = 64 if mode == "lopa" else 0
+    lay = inputs.make_layer(40, d, f, "bf16", rank=rank, with_gate=(rank == 0))
+    from gpu_harness import dev
+    w = S.SparseFFN.weights(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down),
+                            lopa_a=dev(lay.lopa_a), lopa_b=dev(lay.lopa_b))
+    x = dev(inputs.make_x(40, n, d, "bf16"))
+    x_other = dev(inputs.make_x(41, n, d, "bf16"))
+    ffn = S.SparseFFN(d, f, n, "bf16", rank)
+    kw = dict(tau=0.7, k=200)
+    y_eager = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    y_other = torch.empty_like(y_eager)
+    y = torch.empty_like(y_eager)
+    ffn.forward(x, w, mode, y_eager, **kw)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ffn.forward(x, w, mode, y, **kw)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager)
+        ffn.forward(x_other, w, mode, y_other, **kw)
+        torch.cuda.synchronize()
+    ref = oracle_forward(lay, inputs.make_x(40, n, d, "bf16"), mode, tau=0.7, k=200)
+    scale = float(np.abs(ref.y).max())
+    assert float(np.abs(y.cpu().numpy() - ref.y).max()) / scale <= 2e-2

@@ -85,6 +85,31 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
 }
 
 // ---------------------------------------------------------------------------
+// Cross-workgroup slots inside one launch. A slot holds the marker, all ones
+// (a NaN bit pattern no sum of finite products has), until its producer
+// writes it with a relaxed device-scope atomic store (global_store ... sc1);
+// the consumer polls it with device-scope atomic loads (global_load ... sc1)
+// and writes the marker back after reading. Each slot carries its own
+// readiness, which per-location coherence alone makes sound: no counter, no
+// fence (a device-scope release fence writes back the whole L2 of an XCD). A
+// consumer only waits on workgroups of lower index that never wait;
+// workgroups are dispatched in index order on each XCD, so every wait ends.
+// The polls are bounded anyway (kSpinMax), after which the marker itself (a
+// NaN) is used.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSlotMarker = 0xffffffffu;
+constexpr int kSpinMax = 1 << 18;
+
+__device__ __forceinline__ uint32_t ld_slot(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_slot(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
 // Down kernel: the split-channel two-stage reduction in one launch.
 // Stage 1: workgroup (s, g) takes output columns [128 s, 128 s + 128) and
 // channels [F g / G, F (g+1) / G). It lists that range's channels some token
@@ -93,20 +118,10 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
 // read the 256-byte segments of those W_down rows, UNR rows per stream in
 // flight:  P[g][t][c] = sum_i h[i][t] * W_down[i][c]   (fixed order).
 // Stage 2: workgroup (s, G-1) sums P[0][t][c], ..., P[G-1][t][c] in that
-// order and writes y. The other groups publish their P with relaxed
-// device-scope atomic stores into slots that hold a marker (the all-ones NaN
-// pattern, which no sum of finite products produces) until written; the
-// summing workgroup polls each slot with device-scope atomic loads until the
-// marker is gone, then writes the marker back for the next forward. Each slot
-// carries its own readiness, so no counter or fence is needed (a device-scope
-// release fence writes back the whole L2 of an XCD). Only the G-1 groups'
-// summing workgroups wait, and only on workgroups that never wait, so every
-// wait ends; the poll count is bounded anyway (kDownSpinMax), after which the
-// slot's marker (a NaN) goes into y.
+// order and writes y. The other groups publish their P in marker-tagged slots
+// (above), which the summing workgroup polls, reads and re-marks.
+// Only the G-1 groups' summing workgroups wait, on workgroups that never wait.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kDownMarker = 0xffffffffu;
-constexpr int kDownSpinMax = 1 << 18;
-
 template <typename TW, int NT, int UNR>
 __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, int d, int n,
                                               const uint8_t *__restrict__ any, int dense,
@@ -208,8 +223,7 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
             const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
             if (t < n && c0 + c < d) {
                 const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
-                __hip_atomic_store(part + (size_t)g * gs + (size_t)t * d + c0 + c, __float_as_uint(v),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                st_slot(part + (size_t)g * gs + (size_t)t * d + c0 + c, __float_as_uint(v));
             }
         }
         return;
@@ -227,27 +241,23 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
                 uint32_t b[16];
 #pragma unroll
                 for (int u = 0; u < 16; ++u)
-                    b[u] = g0 + u < G - 1
-                               ? __hip_atomic_load(p + (size_t)(g0 + u) * gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : 0u;
-                for (int spin = 0; spin < kDownSpinMax; ++spin) {
+                    b[u] = g0 + u < G - 1 ? ld_slot(p + (size_t)(g0 + u) * gs) : 0u;
+                for (int spin = 0; spin < kSpinMax; ++spin) {
                     bool ready = true;
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) ready = ready && b[u] != kDownMarker;
+                    for (int u = 0; u < 16; ++u) ready = ready && b[u] != kSlotMarker;
                     if (ready) break;
                     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                     for (int u = 0; u < 16; ++u)
-                        if (b[u] == kDownMarker)
-                            b[u] = __hip_atomic_load(p + (size_t)(g0 + u) * gs, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
+                        if (b[u] == kSlotMarker)
+                            b[u] = ld_slot(p + (size_t)(g0 + u) * gs);
                 }
 #pragma unroll
                 for (int u = 0; u < 16; ++u)
                     if (g0 + u < G - 1) {
                         v += __uint_as_float(b[u]);
-                        __hip_atomic_store(p + (size_t)(g0 + u) * gs, kDownMarker, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                        st_slot(p + (size_t)(g0 + u) * gs, kSlotMarker);
                     }
             }
             y[(size_t)t * d + c0 + c] = v + own;
@@ -371,7 +381,7 @@ hipError_t launch_init(sffn_ctx &c, hipStream_t s)
 {
     // the down projection's group slots start out holding their marker
     hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, s, reinterpret_cast<uint32_t *>(c.ws + c.L.part),
-                       c.L.part_words, kDownMarker);
+                       c.L.part_words, kSlotMarker);
     hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
     hipLaunchKernelGGL(k_zero_ints, dim3(16), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ubits), c.L.words);
     return hipGetLastError();

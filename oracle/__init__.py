@@ -31,8 +31,9 @@ _SO = os.path.join(_HERE, "libsffn_oracle.so")
 DT = {"f32": 0, "bf16": 1, "f64": 2}
 
 # Band half-width around the decision boundary, from the stated parity rule:
-# channels whose oracle pre-activation (threshold) or key (Top-K) lies within
-# 1e-5 of the boundary may be decided either way.
+# channels whose oracle pre-activation lies within 1e-5 of tau (threshold), or
+# whose key lies within 1e-5 of the boundary between the last kept and the
+# first dropped key (Top-K; 2:8 within each group), may be decided either way.
 BAND = 1e-5
 
 
@@ -63,7 +64,7 @@ def lib() -> ctypes.CDLL:
         _lib.oracle_gate_full.argtypes = [I, I, I, P, I, P, I, P]
         _lib.oracle_gate_lopa.argtypes = [I, I, I, I, P, I, P, P, I, P, P]
         _lib.oracle_select_threshold.argtypes = [I, I, P, D, P, P]
-        _lib.oracle_select_topk.argtypes = [I, I, I, P, P, P, P]
+        _lib.oracle_select_topk.argtypes = [I, I, I, P, P, P, P, P]
         _lib.oracle_select_topk.restype = I
         _lib.oracle_select_nm.argtypes = [I, I, I, I, P, P, P, P]
         _lib.oracle_select_nm.restype = I
@@ -139,16 +140,18 @@ def select_topk(z: np.ndarray, k: int):
     mask = np.empty((n, f), dtype=np.uint8)
     g = np.empty((n, f), dtype=np.float64)
     kth = np.empty((n,), dtype=np.float64)
-    rc = lib().oracle_select_topk(n, f, int(k), _p(z), _p(mask), _p(g), _p(kth))
+    nxt = np.empty((n,), dtype=np.float64)
+    rc = lib().oracle_select_topk(n, f, int(k), _p(z), _p(mask), _p(g), _p(kth), _p(nxt))
     if rc != 0:
         raise ValueError(f"top-k with k={k} over {f} channels")
-    return mask, g, kth
+    return mask, g, kth, nxt
 
 
 def select_nm(z: np.ndarray, n_keep: int = 2, group: int = 8):
     """Structured n_keep:group selection of the SiLU gate (2:8 by default).
-    Returns the mask, the gate values and each channel's group bound (the
-    n_keep-th largest key of its group; -inf where the group keeps all)."""
+    Returns the mask, the gate values and each channel's group boundary
+    (midway between the group's n_keep-th and next largest keys; -inf where
+    the group keeps all)."""
     z = _c(np.asarray(z, dtype=np.float64))
     n, f = z.shape
     mask = np.empty((n, f), dtype=np.uint8)
@@ -236,8 +239,10 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
         mask, g = select_threshold(z, tau)
         band = np.abs(z - tau) <= BAND
     elif mode == "topk":
-        mask, g, kth = select_topk(z, k)
-        band = np.abs(g - kth[:, None]) <= BAND
+        mask, g, kth, nxt = select_topk(z, k)
+        # the decision boundary lies between the K-th and (K+1)-th keys
+        bnd = np.where(np.isfinite(nxt), 0.5 * (kth + nxt), -np.inf)
+        band = np.abs(g - bnd[:, None]) <= BAND
     elif mode == "topk_2_8":
         mask, g, bound = select_nm(z, 2, 8)
         band = np.abs(g - bound) <= BAND

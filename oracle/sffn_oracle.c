@@ -129,9 +129,10 @@ static int keyed_cmp(const void *pa, const void *pb)
 
 /* Per-token Top-K of the SiLU gate: g = SiLU(z) for every channel; mask marks
  * the K channels with the largest g (ties to the lower index). kth[t] receives
- * the K-th largest key of token t. Returns 0, or -1 on a bad K / no memory. */
+ * the K-th largest key of token t and nxt[t] the (K+1)-th (-INFINITY when
+ * K = F). Returns 0, or -1 on a bad K / no memory. */
 int oracle_select_topk(int n, int F, int K, const double *z, unsigned char *mask, double *g,
-                       double *kth)
+                       double *kth, double *nxt)
 {
     if (K < 1 || K > F) return -1;
     struct keyed *order = (struct keyed *)malloc(sizeof(struct keyed) * (size_t)F);
@@ -150,6 +151,7 @@ int oracle_select_topk(int n, int F, int K, const double *z, unsigned char *mask
         for (int q = 0; q < K; ++q)
             mt[order[q].i] = 1;
         kth[t] = order[K - 1].s;
+        nxt[t] = K < F ? order[K].s : -INFINITY;
     }
     free(order);
     return 0;
@@ -161,8 +163,9 @@ int oracle_select_topk(int n, int F, int K, const double *z, unsigned char *mask
  * and within each group mask marks the N channels with the largest g under
  * the same total order as the Top-K (key descending, then channel ascending);
  * a group of at most N channels keeps them all. bound[t][i] receives the
- * N-th largest key of channel i's group, or -INFINITY when its group keeps
- * every channel. Returns 0, or -1 on bad N / M or no memory. */
+ * decision boundary of channel i's group, midway between its N-th and
+ * (N+1)-th largest keys, or -INFINITY when the group keeps every channel.
+ * Returns 0, or -1 on bad N / M or no memory. */
 int oracle_select_nm(int n, int F, int N, int M, const double *z, unsigned char *mask, double *g,
                      double *bound)
 {
@@ -185,7 +188,7 @@ int oracle_select_nm(int n, int F, int N, int M, const double *z, unsigned char 
             const int keep = len < N ? len : N;
             for (int e = 0; e < keep; ++e)
                 mt[order[e].i] = 1;
-            const double b = len > N ? order[N - 1].s : -INFINITY;
+            const double b = len > N ? 0.5 * (order[N - 1].s + order[N].s) : -INFINITY;
             for (int e = 0; e < len; ++e)
                 bt[q0 + e] = b;
         }

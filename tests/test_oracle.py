@@ -207,18 +207,20 @@ def test_topk_set_brute_force():
         f = 10
         k = int(rng.integers(1, f + 1))
         z = rng.standard_normal((1, f)) * 2.0
-        mask, g, kth = oracle.select_topk(z, k)
+        mask, g, kth, nxt = oracle.select_topk(z, k)
         keys = z[0] / (1.0 + np.exp(-z[0]))
         best = max(itertools.combinations(range(f), k), key=lambda c: sum(keys[list(c)]))
         assert list(np.nonzero(mask[0])[0]) == sorted(best)
-        assert kth[0] == sorted(keys)[::-1][k - 1]
+        desc = sorted(keys)[::-1]
+        assert kth[0] == desc[k - 1]
+        assert nxt[0] == (desc[k] if k < f else -np.inf)
 
 
 def test_topk_ties_go_to_lower_index():
     z = np.array([[0.5, 2.0, 1.0, 2.0, 1.0, 2.0]])
-    mask, _, _ = oracle.select_topk(z, 2)
+    mask, _, _, _ = oracle.select_topk(z, 2)
     assert list(np.nonzero(mask[0])[0]) == [1, 3]
-    mask, _, _ = oracle.select_topk(z, 4)
+    mask, _, _, _ = oracle.select_topk(z, 4)
     assert list(np.nonzero(mask[0])[0]) == [1, 2, 3, 5]
 
 
@@ -226,8 +228,32 @@ def test_topk_negative_keys_rank_by_signed_silu():
     """SiLU has its minimum near z = -1.28: a large negative z has a key closer
     to 0 than z = -1.28, so it ranks above it."""
     z = np.array([[-1.28, -6.0, -0.1]])
-    mask, g, _ = oracle.select_topk(z, 2)
+    mask, g, _, _ = oracle.select_topk(z, 2)
     assert list(np.nonzero(mask[0])[0]) == [1, 2]
+
+
+def test_selection_bands_straddle_the_boundary():
+    """The parity band of Top-K and 2:8 holds the channels within 1e-5 of the
+    boundary between the last kept and the first dropped key: none when that
+    gap is wide, both sides of it when it is narrower than 2e-5."""
+    d, f = 4, 16
+    wg = np.zeros((f, d))
+    wg[:, 0] = np.linspace(-1.0, 2.0, f)  # z_i = x_0 * wg[i][0], distinct and well apart
+    x = np.array([[1.0, 0.0, 0.0, 0.0]])
+    wu = np.ones((f, d))
+    wd = np.ones((f, d))
+    r = oracle.forward("topk", x, wu, wd, w_gate=wg, k=5)
+    assert not r.band.any()
+    r = oracle.forward("topk_2_8", x, wu, wd, w_gate=wg)
+    assert not r.band.any()
+    wg[10, 0] = wg[11, 0] - 1e-6  # keys 10 and 11 (5th/6th largest, 2nd/3rd of group 1) nearly tie
+    r = oracle.forward("topk", x, wu, wd, w_gate=wg, k=5)
+    assert list(np.nonzero(r.band[0])[0]) == [10, 11]
+    r = oracle.forward("topk_2_8", x, wu, wd, w_gate=wg)
+    assert list(np.nonzero(r.band[0])[0]) == []  # in group 1 the 2nd/3rd largest are 14/13
+    wg[13, 0] = wg[14, 0] - 1e-6
+    r = oracle.forward("topk_2_8", x, wu, wd, w_gate=wg)
+    assert list(np.nonzero(r.band[0])[0]) == [13, 14]
 
 
 def test_topk_rejects_bad_k():
@@ -274,15 +300,16 @@ def test_nm_single_group_is_top2():
     (pinned separately)."""
     z = np.random.default_rng(22).standard_normal((5, 8)) * 2.0
     m_nm, g_nm, b_nm = oracle.select_nm(z, 2, 8)
-    m_tk, g_tk, kth = oracle.select_topk(z, 2)
+    m_tk, g_tk, kth, nxt = oracle.select_topk(z, 2)
     assert np.array_equal(m_nm, m_tk)
     assert np.array_equal(g_nm, g_tk)
-    assert np.array_equal(b_nm, np.repeat(kth[:, None], 8, axis=1))
+    assert np.array_equal(b_nm, np.repeat(0.5 * (kth + nxt)[:, None], 8, axis=1))
 
 
 def test_nm_invariants_at_moc_shape():
     """2 kept per group of 8; every kept key of a group is at least every
-    dropped one; the group bound is the smaller kept key."""
+    dropped one; the group boundary lies midway between the smaller kept key
+    and the largest dropped one."""
     f = 5632
     z = np.random.default_rng(23).standard_normal((3, f))
     mask, g, bound = oracle.select_nm(z, 2, 8)
@@ -292,7 +319,8 @@ def test_nm_invariants_at_moc_shape():
     kept_min = np.where(m, k, np.inf).min(axis=2)
     dropped_max = np.where(m, -np.inf, k).max(axis=2)
     assert (kept_min >= dropped_max).all()
-    assert np.array_equal(bound.reshape(3, f // 8, 8), np.repeat(kept_min[:, :, None], 8, axis=2))
+    mid = 0.5 * (kept_min + dropped_max)
+    assert np.array_equal(bound.reshape(3, f // 8, 8), np.repeat(mid[:, :, None], 8, axis=2))
 
 
 def test_nm_permutation_within_groups():

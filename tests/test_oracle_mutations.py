@@ -40,8 +40,9 @@ MUTATIONS = {
     "topk_off_by_one": ("for (int q = 0; q < K; ++q)", "for (int q = 1; q < K; ++q)"),
     "nm_keeps_three": ("const int keep = len < N ? len : N;", "const int keep = len < N + 1 ? len : N + 1;"),
     "nm_groups_misaligned": ("for (int q0 = 0; q0 < F; q0 += M) {", "for (int q0 = 0; q0 < F; q0 += M - 1) {"),
-    "nm_bound_off_by_one": ("const double b = len > N ? order[N - 1].s : -INFINITY;",
-                            "const double b = len > N ? order[N].s : -INFINITY;"),
+    "nm_bound_off_by_one": ("const double b = len > N ? 0.5 * (order[N - 1].s + order[N].s) : -INFINITY;",
+                            "const double b = len > N ? 0.5 * (order[N - 2].s + order[N - 1].s) : -INFINITY;"),
+    "topk_next_is_kth": ("nxt[t] = K < F ? order[K].s : -INFINITY;", "nxt[t] = order[K - 1].s;"),
     "lopa_a_transposed": ("elem(at, w_dt, (long)k * d + j)", "elem(at, w_dt, (long)j * r + k)"),
     "lopa_b_transposed": ("elem(bt, w_dt, (long)i * r + k)", "elem(bt, w_dt, (long)k * F + i)"),
     "union_and": ("any |= mask[(long)t * F + i];", "any &= mask[(long)t * F + i];"),

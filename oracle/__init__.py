@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         _lib.oracle_select_threshold.argtypes = [I, I, P, D, P, P]
         _lib.oracle_select_topk.argtypes = [I, I, I, P, P, P, P, P]
         _lib.oracle_select_topk.restype = I
+        _lib.oracle_select_topp.argtypes = [I, I, D, P, P, P, P, P, P]
+        _lib.oracle_select_topp.restype = I
         _lib.oracle_select_nm.argtypes = [I, I, I, I, P, P, P, P]
         _lib.oracle_select_nm.restype = I
         _lib.oracle_select_dense.argtypes = [I, I, I, P, D, P, P]
@@ -147,6 +149,23 @@ def select_topk(z: np.ndarray, k: int):
     return mask, g, kth, nxt
 
 
+def select_topp(z: np.ndarray, p: float):
+    """Top-p of the SiLU gate by cumulative softmax mass. Returns the mask, the
+    gate values, the prefix masses [n][2] (without / with the last kept
+    channel), and the last kept / first dropped keys."""
+    z = _c(np.asarray(z, dtype=np.float64))
+    n, f = z.shape
+    mask = np.empty((n, f), dtype=np.uint8)
+    g = np.empty((n, f), dtype=np.float64)
+    cum = np.empty((n, 2), dtype=np.float64)
+    kth = np.empty((n,), dtype=np.float64)
+    nxt = np.empty((n,), dtype=np.float64)
+    rc = lib().oracle_select_topp(n, f, float(p), _p(z), _p(mask), _p(g), _p(cum), _p(kth), _p(nxt))
+    if rc != 0:
+        raise ValueError(f"top-p with p={p}")
+    return mask, g, cum, kth, nxt
+
+
 def select_nm(z: np.ndarray, n_keep: int = 2, group: int = 8):
     """Structured n_keep:group selection of the SiLU gate (2:8 by default).
     Returns the mask, the gate values and each channel's group boundary
@@ -224,12 +243,14 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
 
     mode: "threshold" (full gate, shifted ReLU), "lopa" (low-rank gate, shifted
     ReLU), "topk" (full gate, per-token Top-K of SiLU), "topk_2_8" (full gate,
-    per-token top 2 of every aligned group of 8 SiLU keys), "dense_relu" /
-    "dense_silu" (every channel kept). tau is rounded to fp32 first when
+    per-token top 2 of every aligned group of 8 SiLU keys), "topp" (full
+    gate, per-token shortest prefix of the Top-K order whose softmax mass of
+    the keys reaches p, passed as tau), "dense_relu" / "dense_silu" (every
+    channel kept). tau is rounded to fp32 first when
     tau_f32 is set, so both sides compare against the same number.
     """
     if tau_f32:
-        tau = float(np.float32(tau))
+        tau = float(np.float32(tau))  # also p of the top-p mode, an fp32 on the device
     t = kth = None
     if mode == "lopa":
         t, z = gate_lopa(x, lopa_a, lopa_b)
@@ -243,6 +264,19 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
         # the decision boundary lies between the K-th and (K+1)-th keys
         bnd = np.where(np.isfinite(nxt), 0.5 * (kth + nxt), -np.inf)
         band = np.abs(g - bnd[:, None]) <= BAND
+    elif mode == "topp":
+        # tau carries p; the band: a key within 1e-5 of the boundary, or a
+        # boundary channel whose inclusion turns on a prefix mass within 1e-5
+        # of p (the last kept one if the mass without it is that close, the
+        # first dropped one if the mass with the last kept one is)
+        mask, g, cum, kth, nxt = select_topp(z, tau)
+        bnd = np.where(np.isfinite(nxt), 0.5 * (kth + nxt), -np.inf)
+        band = np.abs(g - bnd[:, None]) <= BAND
+        for t in range(z.shape[0]):
+            if tau - cum[t, 0] <= BAND:
+                band[t] |= mask[t].astype(bool) & (g[t] == kth[t])
+            if cum[t, 1] - tau <= BAND and np.isfinite(nxt[t]):
+                band[t] |= ~mask[t].astype(bool) & (g[t] == nxt[t])
     elif mode == "topk_2_8":
         mask, g, bound = select_nm(z, 2, 8)
         band = np.abs(g - bound) <= BAND

@@ -18,7 +18,11 @@
  *   'mixture'" and "'Dentro MoC'": per token only the Top-K channels of the
  *   SwiGLU gate stay active (a binary mask), and only the weight rows and
  *   columns of active channels are loaded; the same sections and "Kernel e
- *   strutture" name a 2:8 structured-sparsity option.
+ *   strutture" name a 2:8 structured-sparsity option. "Model Casting ...",
+ *   Abstract, names top-p as a competing sparsification, and the PrunePath
+ *   abstract activates units under a cumulative threshold on a
+ *   softmax-normalised distribution: the top-p mode reads these at channel
+ *   granularity.
  *
  * Readings where the pages leave a step open (each is listed in the design
  * notes of the repository):
@@ -28,6 +32,8 @@
  *     the lower channel index; the gate value of an active channel is s;
  *   - the 2:8 structured option keeps, per token, the 2 largest keys of every
  *     aligned group of 8 consecutive channels, under the same order;
+ *   - top-p keeps the shortest prefix of that order whose softmax mass over
+ *     the token's keys reaches p;
  *   - inputs are the exact values the GPU sees (fp32, or bf16 bit patterns
  *     widened exactly), and every sum runs in ascending index order in fp64.
  *
@@ -150,6 +156,54 @@ int oracle_select_topk(int n, int F, int K, const double *z, unsigned char *mask
         qsort(order, (size_t)F, sizeof(struct keyed), keyed_cmp);
         for (int q = 0; q < K; ++q)
             mt[order[q].i] = 1;
+        kth[t] = order[K - 1].s;
+        nxt[t] = K < F ? order[K].s : -INFINITY;
+    }
+    free(order);
+    return 0;
+}
+
+/* Top-p (cumulative-mass) selection of the SiLU gate: g = SiLU(z) for every
+ * channel; each channel's mass is the softmax of the keys over the token,
+ * w_i = exp(g_i - max g) / sum_j exp(g_j - max g); in the Top-K order (key
+ * descending, then channel ascending) mask keeps the shortest prefix whose
+ * mass reaches p (0 < p <= 1). For the parity band: cum[t] = {mass of the
+ * prefix without its last channel, mass of the prefix}, and kth[t] / nxt[t]
+ * = the last kept and the first dropped key (-INFINITY when none is dropped).
+ * Returns 0, or -1 on a bad p / no memory. */
+int oracle_select_topp(int n, int F, double p, const double *z, unsigned char *mask, double *g,
+                       double *cum, double *kth, double *nxt)
+{
+    if (!(p > 0.0 && p <= 1.0)) return -1;
+    struct keyed *order = (struct keyed *)malloc(sizeof(struct keyed) * (size_t)F);
+    if (!order) return -1;
+    for (int t = 0; t < n; ++t) {
+        const double *zt = z + (long)t * F;
+        double *gt = g + (long)t * F;
+        unsigned char *mt = mask + (long)t * F;
+        double top = -INFINITY;
+        for (int i = 0; i < F; ++i) {
+            gt[i] = silu(zt[i]);
+            order[i].s = gt[i];
+            order[i].i = i;
+            mt[i] = 0;
+            if (gt[i] > top) top = gt[i];
+        }
+        qsort(order, (size_t)F, sizeof(struct keyed), keyed_cmp);
+        double zsum = 0.0;
+        for (int q = 0; q < F; ++q)
+            zsum += exp(order[q].s - top);
+        double c = 0.0, before = 0.0;
+        int K = 0;
+        while (K < F) {
+            before = c;
+            c += exp(order[K].s - top) / zsum;
+            mt[order[K].i] = 1;
+            ++K;
+            if (c >= p) break;
+        }
+        cum[2 * t] = before;
+        cum[2 * t + 1] = c;
         kth[t] = order[K - 1].s;
         nxt[t] = K < F ? order[K].s : -INFINITY;
     }

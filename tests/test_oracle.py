@@ -72,13 +72,13 @@ def _rand_layer(seed, d, f, dtype, rank=0):
     return inputs.make_layer(seed, d, f, dtype, rank=rank, with_gate=True)
 
 
-@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "lopa", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "topp", "lopa", "dense_relu", "dense_silu"])
 @pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
 def test_masked_dense_equals_sparse_skip(mode, dtype):
     d, f, n = 64, 200, 3
     lay = _rand_layer(1, d, f, dtype, rank=16)
     x = inputs.make_x(1, n, d, dtype)
-    kw = dict(w_gate=lay.w_gate, lopa_a=lay.lopa_a, lopa_b=lay.lopa_b, tau=0.8, k=37)
+    kw = dict(w_gate=lay.w_gate, lopa_a=lay.lopa_a, lopa_b=lay.lopa_b, tau=0.8 if mode != "topp" else 0.3, k=37)
     dense = oracle.forward(mode, x, lay.w_up, lay.w_down, skip=False, **kw)
     sparse = oracle.forward(mode, x, lay.w_up, lay.w_down, skip=True, **kw)
     assert np.array_equal(dense.mask, sparse.mask)
@@ -261,6 +261,57 @@ def test_topk_rejects_bad_k():
         oracle.select_topk(np.zeros((1, 4)), 0)
     with pytest.raises(ValueError):
         oracle.select_topk(np.zeros((1, 4)), 5)
+
+
+# ---------------------------------------------------------------------------
+# Top-p (cumulative softmax mass) selection
+# ---------------------------------------------------------------------------
+def test_topp_brute_force():
+    """The top-p set is the smallest set of channels whose softmax mass of the
+    keys reaches p, the one of largest mass among sets of that size (keys
+    distinct); check against every subset."""
+    rng = np.random.default_rng(31)
+    for trial in range(20):
+        f = 9
+        z = rng.standard_normal((1, f)) * 2.0
+        p = float(rng.uniform(0.05, 0.99))
+        mask, g, cum, kth, nxt = oracle.select_topp(z, p)
+        keys = z[0] / (1.0 + np.exp(-z[0]))
+        w = np.exp(keys - keys.max())
+        w /= w.sum()
+        best = None
+        for k in range(1, f + 1):
+            c = max(itertools.combinations(range(f), k), key=lambda c: w[list(c)].sum())
+            if w[list(c)].sum() >= p:
+                best = sorted(c)
+                break
+        assert list(np.nonzero(mask[0])[0]) == best
+        assert cum[0, 0] < p <= cum[0, 1]
+        np.testing.assert_allclose(cum[0, 1], w[best].sum(), rtol=1e-12)
+
+
+def test_topp_is_topk_with_its_count():
+    """Top-p keeps exactly the Top-K set for K = its own count (the Top-K
+    order is pinned separately); p = 1 keeps every channel, a tiny p the
+    largest key only."""
+    z = np.random.default_rng(32).standard_normal((4, 300))
+    for p in (0.1, 0.5, 0.9):
+        mask, g, cum, kth, nxt = oracle.select_topp(z, p)
+        for t in range(4):
+            k = int(mask[t].sum())
+            m_tk, _, kth_tk, nxt_tk = oracle.select_topk(z[t:t + 1], k)
+            assert np.array_equal(mask[t], m_tk[0])
+            assert kth[t] == kth_tk[0] and nxt[t] == nxt_tk[0]
+    mask, _, _, _, nxt = oracle.select_topp(z, 1.0)
+    assert mask.all() and np.isneginf(nxt).all()
+    mask, g, _, _, _ = oracle.select_topp(z, 1e-9)
+    assert (mask.sum(axis=1) == 1).all() and all(mask[t, np.argmax(g[t])] for t in range(4))
+
+
+def test_topp_rejects_bad_p():
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.select_topp(np.zeros((1, 4)), p)
 
 
 # ---------------------------------------------------------------------------

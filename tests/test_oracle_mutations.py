@@ -42,7 +42,10 @@ MUTATIONS = {
     "nm_groups_misaligned": ("for (int q0 = 0; q0 < F; q0 += M) {", "for (int q0 = 0; q0 < F; q0 += M - 1) {"),
     "nm_bound_off_by_one": ("const double b = len > N ? 0.5 * (order[N - 1].s + order[N].s) : -INFINITY;",
                             "const double b = len > N ? 0.5 * (order[N - 2].s + order[N - 1].s) : -INFINITY;"),
-    "topk_next_is_kth": ("nxt[t] = K < F ? order[K].s : -INFINITY;", "nxt[t] = order[K - 1].s;"),
+    "topk_next_is_kth": ("        kth[t] = order[K - 1].s;\n        nxt[t] = K < F ? order[K].s : -INFINITY;\n    }\n    free(order);\n    return 0;\n}\n\n/* Top-p",
+                         "        kth[t] = order[K - 1].s;\n        nxt[t] = order[K - 1].s;\n    }\n    free(order);\n    return 0;\n}\n\n/* Top-p"),
+    "topp_unnormalised": ("c += exp(order[K].s - top) / zsum;", "c += exp(order[K].s - top);"),
+    "topp_one_short": ("            if (c >= p) break;", "            if (c + exp(order[K - 1].s - top) / zsum >= p) break;"),
     "lopa_a_transposed": ("elem(at, w_dt, (long)k * d + j)", "elem(at, w_dt, (long)j * r + k)"),
     "lopa_b_transposed": ("elem(bt, w_dt, (long)i * r + k)", "elem(bt, w_dt, (long)k * F + i)"),
     "union_and": ("any |= mask[(long)t * F + i];", "any &= mask[(long)t * F + i];"),

@@ -134,7 +134,7 @@ sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const 
     if (!handle || !w) return SFFN_ERR_INVALID_ARG;
     const sffn_shape &s = handle->shape;
     if (n_tokens < 0 || n_tokens > s.max_tokens) return SFFN_ERR_INVALID_ARG;
-    if (mode < SFFN_THRESHOLD || mode > SFFN_TOPK_2_8) return SFFN_ERR_INVALID_ARG;
+    if (mode < SFFN_THRESHOLD || mode > SFFN_TOPP) return SFFN_ERR_INVALID_ARG;
     if (!x || !y || !aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID_ARG;
     if (!w->w_up || !w->w_down || !aligned16(w->w_up) || !aligned16(w->w_down))
         return SFFN_ERR_INVALID_ARG;
@@ -147,6 +147,7 @@ sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const 
     }
     if (mode == SFFN_TOPK && (k < 1 || k > s.d_ff)) return SFFN_ERR_INVALID_ARG;
     if (mode != SFFN_TOPK && mode != SFFN_TOPK_2_8 && std::isnan(tau)) return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_TOPP && !(tau > 0.f && tau <= 1.f)) return SFFN_ERR_INVALID_ARG;
     if ((active_idx && !aligned4(active_idx)) || (active_cnt && !aligned4(active_cnt)) ||
         (union_cnt && !aligned4(union_cnt)) || (debug_z && !aligned4(debug_z)))
         return SFFN_ERR_INVALID_ARG;

@@ -70,7 +70,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
     if (e.kind == EPI_GATE) {
         const size_t o = (size_t)m * e.F + n;
         if (e.debug_z) e.debug_z[o] = v;
-        if (e.mode == SFFN_TOPK || e.mode == SFFN_TOPK_2_8) {
+        if (e.mode == SFFN_TOPK || e.mode == SFFN_TOPK_2_8 || e.mode == SFFN_TOPP) {
             e.keys[o] = silu(v);
             return false;
         }
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
         return;
     }
     const bool dense = mode == SFFN_DENSE || mode == SFFN_DENSE_SILU;
-    const bool topk = mode == SFFN_TOPK || mode == SFFN_TOPK_2_8;
+    const bool topk = mode == SFFN_TOPK || mode == SFFN_TOPK_2_8 || mode == SFFN_TOPP;
     const uint16_t *g = G + (size_t)t * F;
     const uint8_t *a = act + (size_t)t * F;
     auto on8 = [&](int i0, bool f[8]) {
@@ -728,7 +728,8 @@ static void dispatch_mfma(const Cfg &c, dim3 grid, hipStream_t st, int M, int N,
             dispatch_cfg<BNN, EK, SFFN_THRESHOLD>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
             break;
         case SFFN_TOPK:
-        case SFFN_TOPK_2_8:  // both write the SiLU keys; the selection follows
+        case SFFN_TOPK_2_8:
+        case SFFN_TOPP:  // these write the SiLU keys; the selection follows
             dispatch_cfg<BNN, EK, SFFN_TOPK>(c, grid, st, M, N, K, A, lda, B, ldb, bidx, ncount, part, pld, e);
             break;
         case SFFN_DENSE:
@@ -840,6 +841,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- Top-K: per-token select, its flags and the union of the flags ----
     if (a.mode == SFFN_TOPK) {
         if ((e = launch_topk_select_flags(keys, T, F, a.k, act, G, ubits, st)) != hipSuccess) return e;
+    }
+    // ---- top-p: per-token select by cumulative mass, flags and union ----
+    if (a.mode == SFFN_TOPP) {
+        if ((e = launch_topp_select_flags(keys, T, F, a.tau, act, G, ubits, st)) != hipSuccess) return e;
     }
     // ---- 2:8: the top 2 of each group of 8 keys, its flags and the union ----
     if (a.mode == SFFN_TOPK_2_8) {

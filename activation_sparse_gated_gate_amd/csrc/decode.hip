@@ -7,6 +7,8 @@
 //   LoPA       k_lopa_xa (t = x.A) -> k_gate<SELECT_UP> on B with t -> k_down
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
 //              K-th key) -> k_up (flags + up rows) -> k_down
+//   top-p      as Top-K, with k_topp_thr (the boundary of the cumulative
+//              softmax mass p) in place of k_topk_thr
 //   2:8        k_gate<SELECT_NM>: gate GEMV, SiLU keys ranked within each
 //              aligned group of 8 channels, and the W_up rows of the 2 kept
 //              per group -> k_down
@@ -428,7 +430,8 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     g.ev_start = c.ev_start;
     g.ev_stop = c.ev_stop;
     g.lpr = lpr_for(d);
-    g.kind = dense ? DENSE : a.mode == SFFN_TOPK ? KEYS : a.mode == SFFN_TOPK_2_8 ? SELECT_NM : SELECT_UP;
+    const bool ranked = a.mode == SFFN_TOPK || a.mode == SFFN_TOPP;  // keys, then a per-token select
+    g.kind = dense ? DENSE : ranked ? KEYS : a.mode == SFFN_TOPK_2_8 ? SELECT_NM : SELECT_UP;
     if (g.kind == SELECT_NM && g.lpr == 64 && RowsPer<NT>::v < 2) g.lpr = 32;  // whole 2:8 groups per workgroup
     if (a.mode == SFFN_LOPA) {
         const int r = S.rank;
@@ -446,10 +449,12 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     }
     if ((e = launch_gate(g)) != hipSuccess) return e;
 
-    // ---- Top-K: select, then the up rows ----
-    if (a.mode == SFFN_TOPK) {
+    // ---- Top-K / top-p: select, then the up rows ----
+    if (ranked) {
         int2 *thr = reinterpret_cast<int2 *>(ws + c.L.thr);
-        if ((e = launch_topk_thr(gsel, n, F, a.k, thr, st)) != hipSuccess) return e;
+        e = a.mode == SFFN_TOPK ? launch_topk_thr(gsel, n, F, a.k, thr, st)
+                                : launch_topp_thr(gsel, n, F, a.tau, thr, st);
+        if (e != hipSuccess) return e;
         const int lpr = lpr_for(d);
         const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
         if (lpr == 64)

@@ -254,3 +254,275 @@ __device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, i
 }
 
 }  // namespace sffn
+
+namespace sffn {
+
+// ---------------------------------------------------------------------------
+// Top-p: the shortest prefix of the Top-K order (key descending, channel
+// ascending) whose softmax mass of the token's keys reaches p. One workgroup
+// (1024 threads) per token; the result is the same {boundary key, tie cutoff}
+// pair as select_kth, so the Top-K flag rule (topk_on) applies it.
+//
+// Masses are fixed-point integers, u = round(exp(v - max) * 2^44) (24
+// significant bits, as exp is computed in fp32), so every sum is exact and
+// independent of order: Z = sum u (< 2^62 for d_ff <= 2^18) and the target
+// T = ceil(p * Z). The search is select_kth's with masses in place of counts:
+// 2048 value bins carrying a count and a mass each, and a wavefront finds the
+// bin where the mass from the top reaches T. Up to 64 candidates in that bin
+// are ranked by one wavefront, each summing the masses of the candidates
+// ahead of it; the boundary channel is the one whose prefix mass falls short
+// of T and reaches it with its own. A larger bin goes through four 8-bit
+// radix passes over the order-preserving keys with a mass per digit, which
+// fixes the boundary key exactly; the channels equal to it that are needed
+// (ceil(mass still needed / their mass)) are taken in channel order.
+// ---------------------------------------------------------------------------
+struct __align__(16) SelectMassLds {
+    static constexpr int NB = 2048, CMAX = 64;
+    unsigned long long mass[NB];  // value bins, later 3 x 256 radix digits
+    int hist[NB];
+    unsigned long long cand_w[CMAX];
+    uint32_t cand_key[CMAX];
+    int cand_idx[CMAX];
+    unsigned long long zred[16];
+    unsigned long long shm[2];  // mass above the crossing bin
+    float red[2][16];
+    int sh[4];  // crossing bin, its count, gathered; then the result
+    int scan_scratch[16];
+};
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// inverse of f2key (for the keys f2key produces)
+__device__ __forceinline__ float key2f(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+template <int KPT>
+__device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, float p, SelectMassLds &L,
+                                            const float (&kf)[KPT > 0 ? KPT : 1])
+{
+    constexpr int NTHR = 1024, NB = SelectMassLds::NB, CMAX = SelectMassLds::CMAX;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto for_keys = [&](auto &&fn) {
+        if constexpr (KPT > 0) {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e)
+                if (tid * KPT + e < F) fn(tid * KPT + e, kf[e]);
+        } else {
+            for (int i = tid; i < F; i += NTHR) fn(i, s[i]);
+        }
+    };
+
+    // ---- range, total mass, target ----
+    float lo = INFINITY, hi = -INFINITY;
+    for_keys([&](int, float v) {
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    if (lane == 0) {
+        L.red[0][wave] = lo;
+        L.red[1][wave] = hi;
+    }
+    for (int b = tid; b < NB; b += NTHR) {
+        L.hist[b] = 0;
+        L.mass[b] = 0ull;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        lo = fminf(lo, L.red[0][w]);
+        hi = fmaxf(hi, L.red[1][w]);
+    }
+    const float top = hi;
+    auto mass_of = [&](float v) -> unsigned long long {
+        return (unsigned long long)(expf(v - top) * 17592186044416.0f + 0.5f);  // 2^44
+    };
+    unsigned long long zl = 0;
+    for_keys([&](int, float v) { zl += mass_of(v); });
+    zl = wave_sum_u64(zl);
+    if (lane == 0) L.zred[wave] = zl;
+    __syncthreads();
+    unsigned long long Z = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) Z += L.zred[w];
+    unsigned long long T = (unsigned long long)ceil((double)p * (double)Z);
+    T = T < 1ull ? 1ull : T > Z ? Z : T;
+
+    // The channels equal to the key kth that the prefix needs, given the
+    // mass `need` still missing, are the first ceil(need / u) of them in
+    // channel order; returns {kth, last of them}. Contiguous segments per
+    // thread make "equal keys before mine" an exclusive block scan.
+    auto take_ties = [&](uint32_t kth, unsigned long long need) -> int2 {
+        const unsigned long long u = mass_of(key2f(kth));
+        const unsigned long long want = u > 0 ? (need + u - 1) / u : 1ull;
+        const int seg = KPT > 0 ? KPT : (F + NTHR - 1) / NTHR;
+        const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+        int eq_local = 0;
+        if constexpr (KPT > 0) {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) eq_local += (i0 + e < i1 && f2key(kf[e]) == kth);
+        } else {
+            for (int i = i0; i < i1; ++i) eq_local += f2key(s[i]) == kth;
+        }
+        const int eq_incl = block_incl_scan(eq_local, L.scan_scratch), eq_before = eq_incl - eq_local;
+        if (tid == NTHR - 1) L.sh[3] = eq_incl;  // equal channels in all
+        __syncthreads();
+        const int n_eq = L.sh[3];
+        const int take = (int)min(want, (unsigned long long)max(1, n_eq));
+        __syncthreads();  // sh carries the result now
+        if (eq_before < take && take <= eq_before + eq_local) {
+            int left = take - eq_before, cut = i0;
+            if constexpr (KPT > 0) {
+#pragma unroll
+                for (int e = 0; e < KPT; ++e)
+                    if (i0 + e < i1 && f2key(kf[e]) == kth && left > 0) {
+                        cut = i0 + e;
+                        --left;
+                    }
+            } else {
+                for (int i = i0; i < i1 && left > 0; ++i)
+                    if (f2key(s[i]) == kth) {
+                        cut = i;
+                        --left;
+                    }
+            }
+            L.sh[0] = (int)kth;
+            L.sh[1] = cut;
+        }
+        __syncthreads();
+        const int2 r = make_int2(L.sh[0], L.sh[1]);
+        __syncthreads();
+        return r;
+    };
+
+    if (!(hi > lo)) return take_ties(f2key(hi), T);  // every key equal
+    float scale = (float)NB / (hi - lo);
+    if (!(scale < 1e30f)) scale = 0.f;  // range too narrow to scale: one bin, resolved below
+    auto bin_of = [&](float v) {
+        const float q = (v - lo) * scale;  // >= 0
+        return q >= (float)NB ? NB - 1 : (int)q;
+    };
+
+    // ---- stage 1: count and mass per value bin, bin where the mass from the top reaches T ----
+    for_keys([&](int, float v) {
+        const int b = bin_of(v);
+        atomicAdd(&L.hist[b], 1);
+        atomicAdd(&L.mass[b], mass_of(v));
+    });
+    __syncthreads();
+    if (wave == 0) {
+        // lane l owns bins NB-1-32l .. NB-32-32l (descending)
+        const int b0 = NB - 32 - 32 * lane;
+        unsigned long long tot = 0;
+        for (int q = 0; q < 32; ++q) tot += L.mass[b0 + q];
+        unsigned long long run = wave_incl_scan_u64(tot) - tot;
+        for (int q = 31; q >= 0; --q) {
+            const unsigned long long m = L.mass[b0 + q];
+            if (run < T && T <= run + m) {
+                L.sh[0] = b0 + q;
+                L.sh[1] = L.hist[b0 + q];
+                L.sh[2] = 0;
+                L.shm[0] = run;
+            }
+            run += m;
+        }
+    }
+    __syncthreads();
+    const int bstar = L.sh[0], cnt = L.sh[1];
+    unsigned long long need = T - L.shm[0];  // in (0, mass of bin bstar]
+
+    // ---- stage 2a: few candidates, ranked by one wavefront ----
+    if (cnt <= CMAX) {
+        for_keys([&](int i, float v) {
+            if (bin_of(v) == bstar) {
+                const int slot = atomicAdd(&L.sh[2], 1);
+                L.cand_key[slot] = f2key(v);
+                L.cand_idx[slot] = i;
+                L.cand_w[slot] = mass_of(v);
+            }
+        });
+        __syncthreads();
+        if (wave == 0 && lane < cnt) {
+            const uint32_t mk = L.cand_key[lane];
+            const int mi = L.cand_idx[lane];
+            unsigned long long ahead = 0;
+            for (int m = 0; m < cnt; ++m) {
+                const uint32_t ok = L.cand_key[m];
+                if (ok > mk || (ok == mk && L.cand_idx[m] < mi)) ahead += L.cand_w[m];
+            }
+            if (ahead < need && need <= ahead + L.cand_w[lane]) {
+                L.sh[0] = (int)mk;
+                L.sh[1] = mi;
+            }
+        }
+        __syncthreads();
+        const int2 r = make_int2(L.sh[0], L.sh[1]);
+        __syncthreads();
+        return r;
+    }
+
+    // ---- stage 2b: radix passes within the bin, a mass per digit ----
+    // Three buffers rotate so a pass needs one barrier (as in select_kth).
+    unsigned long long *dm = L.mass;
+    if (tid < 256) dm[tid] = 0ull;
+    __syncthreads();
+    uint32_t prefix = 0, pmask = 0;
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+        const int shift = 24 - 8 * ps;
+        unsigned long long *h = dm + 256 * (ps % 3);
+        if (tid < 256) dm[256 * ((ps + 1) % 3) + tid] = 0ull;
+        for_keys([&](int, float v) {
+            const uint32_t key = f2key(v);
+            if (bin_of(v) == bstar && (key & pmask) == prefix) atomicAdd(&h[(key >> shift) & 255u], mass_of(v));
+        });
+        __syncthreads();
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        unsigned long long c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = h[255 - 4 * lane - e];
+        const unsigned long long tot = c[0] + c[1] + c[2] + c[3];
+        unsigned long long run = wave_incl_scan_u64(tot) - tot;
+        int my_digit = -1;
+        unsigned long long my_need = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (run < need && need <= run + c[e]) {
+                my_digit = 255 - (lane * 4 + e);
+                my_need = need - run;
+            }
+            run += c[e];
+        }
+        const unsigned long long hit = __ballot(my_digit >= 0);
+        const int src = __ffsll((long long)hit) - 1;
+        const int digit = __shfl(my_digit, src, 64);
+        need = __shfl(my_need, src, 64);
+        prefix |= (uint32_t)digit << shift;
+        pmask |= 0xffu << shift;
+    }
+    return take_ties(prefix, need);
+}
+
+}  // namespace sffn

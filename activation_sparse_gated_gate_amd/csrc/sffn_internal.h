@@ -89,6 +89,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
 // Per-token Top-K (topk.hip), shared by both regimes: thr[t] = {K-th largest
 // key in the f2key encoding, last channel index kept among keys equal to it}.
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st);
+// Top-p: the same per-token pair, found by cumulative softmax mass p
+// (decode), and the batched select + flags.
+hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st);
+hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, uint8_t *act, uint16_t *G,
+                                   uint32_t *ubits, hipStream_t st);
 // Batched 2:8: act[t][i], bf16 gate values G[t][i] and the union bitmap from
 // the keys, keeping the top 2 of every aligned group of 8 channels.
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,

@@ -11,7 +11,8 @@
 // exactly K channels are selected. The decode up kernel applies that rule
 // where it reads the keys anyway; for a batch, k_topk_select_flags applies it
 // right after the select, to the keys the select holds, and writes the
-// batch's flags, gate values and union bitmap.
+// batch's flags, gate values and union bitmap. Top-p (k_topp_*) finds the
+// same pair by cumulative softmax mass instead of a count (select_mass).
 #include "select.h"
 #include "sffn_internal.h"
 
@@ -32,24 +33,17 @@ __global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ key
     if (threadIdx.x == 0) thr[t] = r;
 }
 
-// Batched: the select of token t (one 1024-thread workgroup per token), then
-// token t's flags act[t][i], the gate values the up GEMM reads (G[t][i] =
-// bf16 key where selected, else 0) and its bits of the union bitmap, ORed
-// in with one atomic per 32-bit word and wavefront (the bitmap is all zero
-// on entry: the down GEMM clears it after use).
+// Batched: token t's flags act[t][i], the gate values the up GEMM reads
+// (G[t][i] = bf16 key where selected, else 0) and its bits of the union
+// bitmap, ORed in with one atomic per 32-bit word and wavefront (the bitmap is
+// all zero on entry: the down GEMM clears it after use), from the boundary r
+// of a select; the keys are kf (KPT > 0) or re-read from s.
 template <int KPT>
-__global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restrict__ keys, int F, int K,
-                                                            uint8_t *__restrict__ act, uint16_t *__restrict__ G,
-                                                            uint32_t *__restrict__ ubits)
+__device__ __forceinline__ void write_flags(const float *__restrict__ s, int F, int2 r,
+                                            const float (&kf)[KPT > 0 ? KPT : 1], uint8_t *__restrict__ a,
+                                            uint16_t *__restrict__ g, uint32_t *__restrict__ ubits)
 {
-    __shared__ SelectLds L;
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-    const float *s = keys + (size_t)t * F;
-    float kf[KPT > 0 ? KPT : 1];
-    load_keys<KPT>(s, F, kf);
-    const int2 r = select_kth<KPT>(s, F, K, L, kf);
-    uint8_t *a = act + (size_t)t * F;
-    uint16_t *g = G + (size_t)t * F;
+    const int tid = threadIdx.x, lane = tid & 63;
     if constexpr (KPT > 0) {
         // channels KPT tid .. + KPT-1: one 32-bit word, shared by 32 / KPT lanes
         const int i0 = tid * KPT;
@@ -83,6 +77,51 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
             if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
         }
     }
+}
+
+// Batched Top-K: the select of token t (one 1024-thread workgroup per token),
+// then its flags.
+template <int KPT>
+__global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restrict__ keys, int F, int K,
+                                                            uint8_t *__restrict__ act, uint16_t *__restrict__ G,
+                                                            uint32_t *__restrict__ ubits)
+{
+    __shared__ SelectLds L;
+    const int t = blockIdx.x;
+    const float *s = keys + (size_t)t * F;
+    float kf[KPT > 0 ? KPT : 1];
+    load_keys<KPT>(s, F, kf);
+    const int2 r = select_kth<KPT>(s, F, K, L, kf);
+    write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
+}
+
+// Top-p (decode): each token's boundary key and tie cutoff, as k_topk_thr.
+template <int KPT>
+__global__ __launch_bounds__(1024) void k_topp_thr(const float *__restrict__ keys, int F, float p,
+                                                   int2 *__restrict__ thr)
+{
+    __shared__ SelectMassLds L;
+    const int t = blockIdx.x;
+    const float *s = keys + (size_t)t * F;
+    float kf[KPT > 0 ? KPT : 1];
+    load_keys<KPT>(s, F, kf);
+    const int2 r = select_mass<KPT>(s, F, p, L, kf);
+    if (threadIdx.x == 0) thr[t] = r;
+}
+
+// Batched top-p: the select of token t, then its flags.
+template <int KPT>
+__global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restrict__ keys, int F, float p,
+                                                            uint8_t *__restrict__ act, uint16_t *__restrict__ G,
+                                                            uint32_t *__restrict__ ubits)
+{
+    __shared__ SelectMassLds L;
+    const int t = blockIdx.x;
+    const float *s = keys + (size_t)t * F;
+    float kf[KPT > 0 ? KPT : 1];
+    load_keys<KPT>(s, F, kf);
+    const int2 r = select_mass<KPT>(s, F, p, L, kf);
+    write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
 }
 
 // Batched 2:8 structured selection: block (x, t) takes channels
@@ -132,6 +171,28 @@ hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hi
     else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topk_thr<8>, grid, block, 0, st, keys, F, K, thr);
     else if (F <= 1024 * 16) hipLaunchKernelGGL(k_topk_thr<16>, grid, block, 0, st, keys, F, K, thr);
     else hipLaunchKernelGGL(k_topk_thr<0>, grid, block, 0, st, keys, F, K, thr);
+    return hipGetLastError();
+}
+
+hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st)
+{
+    const dim3 grid(T), block(1024);
+    if (F <= 1024 * 4) hipLaunchKernelGGL(k_topp_thr<4>, grid, block, 0, st, keys, F, p, thr);
+    else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topp_thr<8>, grid, block, 0, st, keys, F, p, thr);
+    else if (F <= 1024 * 16) hipLaunchKernelGGL(k_topp_thr<16>, grid, block, 0, st, keys, F, p, thr);
+    else hipLaunchKernelGGL(k_topp_thr<0>, grid, block, 0, st, keys, F, p, thr);
+    return hipGetLastError();
+}
+
+hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, uint8_t *act, uint16_t *G,
+                                   uint32_t *ubits, hipStream_t st)
+{
+    const dim3 grid(T), block(1024);
+    if (F <= 1024 * 4) hipLaunchKernelGGL(k_topp_select_flags<4>, grid, block, 0, st, keys, F, p, act, G, ubits);
+    else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topp_select_flags<8>, grid, block, 0, st, keys, F, p, act, G, ubits);
+    else if (F <= 1024 * 16)
+        hipLaunchKernelGGL(k_topp_select_flags<16>, grid, block, 0, st, keys, F, p, act, G, ubits);
+    else hipLaunchKernelGGL(k_topp_select_flags<0>, grid, block, 0, st, keys, F, p, act, G, ubits);
     return hipGetLastError();
 }
 

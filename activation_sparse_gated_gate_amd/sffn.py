@@ -32,10 +32,11 @@ SFFN_LOPA = 2
 SFFN_DENSE = 3
 SFFN_DENSE_SILU = 4
 SFFN_TOPK_2_8 = 5
+SFFN_TOPP = 6
 
 MODES = {"threshold": SFFN_THRESHOLD, "topk": SFFN_TOPK, "lopa": SFFN_LOPA,
          "dense": SFFN_DENSE, "dense_relu": SFFN_DENSE, "dense_silu": SFFN_DENSE_SILU,
-         "topk_2_8": SFFN_TOPK_2_8}
+         "topk_2_8": SFFN_TOPK_2_8, "topp": SFFN_TOPP}
 DTYPES = {"f32": SFFN_F32, "bf16": SFFN_BF16}
 
 # Names exported by the library, as declared in include/sffn.h.

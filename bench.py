@@ -214,8 +214,11 @@ def points_lopa(W, S, inputs, torch, dev, dense2, union, replicate):
     return out
 
 
+TOPP_PS = (0.3, 0.5)
+
+
 def points_moc(W, S, inputs, torch, dev, union, replicate):
-    """Mixture-of-Channels Top-K and its 2:8 structured option, decode and batched."""
+    """Mixture-of-Channels Top-K, its 2:8 structured option and top-p, decode and batched."""
     out = []
     es = 2
     wl = W["moc_topk_bf16_d2048_f5632"]
@@ -247,6 +250,17 @@ def points_moc(W, S, inputs, torch, dev, union, replicate):
                     "tokens_per_s": round(n / sp, 1), "touched_bytes": touched,
                     "hbm_frac": round(touched / sp / PEAK_HBM, 4), "speedup_vs_dense": round(de / sp, 3),
                     "layer_copies": len(wlist)})
+        # top-p: the shortest Top-K-order prefix holding a p share of the
+        # softmax mass of the SiLU keys (p = 0.3 / 0.5 keep ~8.5 % / ~22.5 %)
+        for pp in TOPP_PS:
+            na = union(ffn, xt, wlist[0], "topp", y, tau=pp)
+            touched = n * d * es + f * d * es + 2 * na * d * es + n * d * 4
+            sp = timed(ffn, xt, wlist, "topp", y, 200, 20, tau=pp)
+            out.append({"workload": wl.name, "tokens": n, "mode": "topp", "p": pp, "union": na,
+                        "union_frac": round(na / f, 4), "us_per_step": round(sp * 1e6, 2),
+                        "tokens_per_s": round(n / sp, 1), "touched_bytes": touched,
+                        "hbm_frac": round(touched / sp / PEAK_HBM, 4), "speedup_vs_dense": round(de / sp, 3),
+                        "layer_copies": len(wlist)})
     del cl, wlist, base
     torch.cuda.empty_cache()
     return out

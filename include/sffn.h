@@ -21,7 +21,10 @@
  * SwiGLU gate as a binary mask and, at inference, load only the weight rows and
  * columns of the active channels; the same summary ("Kernel e strutture")
  * names a 2:8 structured-sparsity option, read here as the top 2 of every
- * aligned group of 8 channels.
+ * aligned group of 8 channels. "Model Casting ..." names top-p as a competing
+ * sparsification and the PrunePath abstract activates units under a
+ * cumulative-mass threshold on a softmax-normalised distribution: TOPP reads
+ * these at channel granularity.
  *
  * Layout (all row-major, element type = the shape's dtype unless stated):
  *   x        [n_tokens][d_model]
@@ -74,10 +77,14 @@ typedef enum {
     SFFN_LOPA = 2,       /* low-rank gate (x.A).B; active = z > tau; g = z - tau  */
     SFFN_DENSE = 3,      /* full gate; every channel computed, g = max(z - tau, 0) */
     SFFN_DENSE_SILU = 4, /* full gate; every channel computed, g = SiLU(z) (SwiGLU) */
-    SFFN_TOPK_2_8 = 5    /* full gate; 2:8 structured: per token, within every aligned
+    SFFN_TOPK_2_8 = 5,   /* full gate; 2:8 structured: per token, within every aligned
                             group of 8 consecutive channels [8q, 8q + 8), the 2 of
                             largest SiLU(z) (ties to the lower index; a last group of
                             at most 2 channels keeps them all); g = SiLU(z)       */
+    SFFN_TOPP = 6        /* full gate; top-p: per token, in the Top-K order of the keys
+                            s = SiLU(z), the shortest prefix whose softmax mass
+                            (exp(s_i) / sum_j exp(s_j)) reaches p, passed as tau,
+                            0 < p <= 1; g = SiLU(z)                               */
 } sffn_mode;
 
 /* Shape of a layer and the largest batch a handle serves.
@@ -123,7 +130,8 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
  *   x           device, [n_tokens][d_model], shape dtype
  *   w           host struct of device weight pointers
  *   mode        an sffn_mode
- *   tau         threshold for THRESHOLD, LOPA and DENSE (compared in fp32)
+ *   tau         threshold for THRESHOLD, LOPA and DENSE (compared in fp32); the
+ *               mass p of TOPP, 0 < p <= 1
  *   k           Top-K size for TOPK, 1 <= k <= d_ff (ignored otherwise; TOPK_2_8
  *               keeps 2 of every 8 channels and takes no k)
  *   y           device, [n_tokens][d_model] fp32, written
@@ -135,7 +143,7 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
  *   debug_z     device fp32 [n_tokens][d_ff]: the gate pre-activation z
  * A token with no active channel gets y = 0. n_tokens = 0 returns SFFN_OK and
  * enqueues nothing. LOPA needs a handle created with rank > 0; TOPK, TOPK_2_8,
- * THRESHOLD and the dense modes need w_gate. */
+ * TOPP, THRESHOLD and the dense modes need w_gate. */
 sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const sffn_weights *w,
                          int mode, float tau, int k, float *y, int32_t *active_idx,
                          int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream);

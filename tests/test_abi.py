@@ -118,7 +118,10 @@ def test_forward_rejects_bad_arguments(fake):
     assert fake.fwd(y=0x70004) == E                     # y not 16-byte aligned
     assert fake.fwd(n=-1) == E
     assert fake.fwd(n=9) == E                           # above max_tokens
-    assert fake.fwd(mode=6) == E
+    assert fake.fwd(mode=7) == E
+    assert fake.fwd(mode=S.SFFN_TOPP, tau=0.0) == E      # p outside (0, 1]
+    assert fake.fwd(mode=S.SFFN_TOPP, tau=1.5) == E
+    assert fake.fwd(mode=S.SFFN_TOPP, tau=math.nan) == E
     assert fake.fwd(mode=-1) == E
     assert fake.fwd(mode=S.SFFN_TOPK_2_8, w=S.sffn_weights(None, 0x20000, 0x30000, 0x40000, 0x50000)) == E
     assert fake.fwd(tau=math.nan) == E

@@ -60,11 +60,22 @@ def test_moc_2_8_batched(moc_layer, n):
     say(f"    union fraction {rep.union / wl.d_ff:.3f}")
 
 
+@pytest.mark.parametrize("n", [16, 64])
+def test_moc_topp_batched(moc_layer, n):
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    say(f"case moc top-p batched bf16 d=2048 F=5632 n={n} p=0.5")
+    x = inputs.make_x(0, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(moc_layer, x, "topp", tau=0.5)
+    got = run_gpu(moc_layer, x, "topp", tau=0.5)
+    rep = compare(moc_layer, x, "topp", ref, got)
+    say(f"    union fraction {rep.union / wl.d_ff:.3f}")
+
+
 # ---------------------------------------------------------------------------
 # Ragged batches through every tile configuration and mode
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("n", [9, 33, 100, 300, 600])
-@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "topp", "dense_relu", "dense_silu"])
 def test_batched_ragged(n, mode):
     d, f = 264, 1000
     say(f"case batched ragged bf16 d={d} F={f} n={n} {mode}")

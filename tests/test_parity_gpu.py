@@ -102,6 +102,56 @@ def test_moc_2_8_decode(n):
     assert rep.rel_err <= DECODE_GUARD
 
 
+@pytest.mark.parametrize("p", [0.3, 0.5])
+def test_moc_topp_decode(p):
+    """Top-p at the MoC shape: p = 0.3 / 0.5 keep ~8.5 % / ~22.5 % of the
+    channels of these keys."""
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    say(f"case moc top-p bf16 d=2048 F=5632 n=1 p={p}")
+    lay = _layer(wl)
+    x = inputs.make_x(0, 1, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, "topp", tau=p)
+    got = run_gpu(lay, x, "topp", tau=p)
+    rep = compare(lay, x, "topp", ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
+@pytest.mark.parametrize("f", [4096, 4097, 8193, 16385, 32769])
+@pytest.mark.parametrize("n", [1, 3, 12])
+@pytest.mark.parametrize("tied", [False, True])
+def test_topp_select_sizes_and_ties(f, n, tied):
+    """Every register-cache size of the top-p select (and the uncached one
+    above 16384 channels), decode and batched. tied: the gate rows repeat 5
+    distinct rows, so each token's keys take 5 values, each shared by about
+    F/5 channels; the boundary then falls inside a large group of exact ties
+    (the radix path), of which the lowest channel indices are kept."""
+    d = 64
+    say(f"case top-p select F={f} n={n} tied={tied}")
+    lay = inputs.make_layer(33, d, f, "bf16")
+    if tied:
+        lay.w_gate[:] = lay.w_gate[np.arange(f) % 5]
+    x = inputs.make_x(33, n, d, "bf16")
+    for p in (0.2, 0.6):
+        ref = oracle_forward(lay, x, "topp", tau=p)
+        got = run_gpu(lay, x, "topp", tau=p, max_tokens=n)
+        compare(lay, x, "topp", ref, got)
+        if tied:
+            for t in range(n):
+                for r in range(5):
+                    kept = got.sets[t, r::5]
+                    assert not np.any(~kept[:-1] & kept[1:]), f"token {t}: tie kept out of index order"
+
+
+def test_topp_one_keeps_every_channel():
+    say("case top-p p=1 == dense SiLU")
+    lay = inputs.make_layer(34, 256, 700, "bf16")
+    x = inputs.make_x(34, 2, 256, "bf16")
+    got = run_gpu(lay, x, "topp", tau=1.0)
+    assert got.sets.all()
+    ref = oracle_forward(lay, x, "dense_silu")
+    compare(lay, x, "dense_silu", ref, got)
+
+
 @pytest.mark.parametrize("n", [1, 3, 12])
 def test_2_8_ties_go_to_lower_index(n):
     """Gate rows duplicated inside a group of 8 give exactly tied keys: the
@@ -132,7 +182,7 @@ RAGGED = [(264, 1000), (64, 37), (136, 333), (1024, 2049)]
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d,f", RAGGED)
 @pytest.mark.parametrize("n", [1, 3, 8])
-@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "dense_relu", "dense_silu"])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "topp", "dense_relu", "dense_silu"])
 def test_ragged_shapes(dtype, d, f, n, mode):
     say(f"case ragged {dtype} d={d} F={f} n={n} {mode}")
     lay = inputs.make_layer(3, d, f, dtype)
@@ -377,7 +427,8 @@ def test_handle_reuse_across_modes_and_batch_sizes():
 # HIP graph capture: the forward enqueues only kernels (no allocation, no
 # memset, no synchronisation), so it can be captured and replayed
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("mode,n", [("threshold", 1), ("topk", 3), ("topk_2_8", 1), ("lopa", 4), ("threshold", 40)])
+@pytest.mark.parametrize("mode,n", [("threshold", 1), ("topk", 3), ("topk_2_8", 1), ("topp", 2), ("lopa", 4),
+                                    ("threshold", 40), ("topp", 20)])
 def test_graph_replay_matches_eager(mode, n):
     """Replays of a captured forward equal the eager forward bit for bit, with
     eager forwards on other inputs between the replays."""

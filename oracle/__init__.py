@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
         _lib.oracle_up.argtypes = [I, I, I, P, I, P, I, P, P, I, P]
         _lib.oracle_down.argtypes = [I, I, I, P, P, I, P, I, P]
         _lib.oracle_union.argtypes = [I, I, P, P]
+        _lib.oracle_backward.argtypes = [I, I, I, I, D, P, I, P, I, P, P, P, I, P, P, P, P, P]
         _lib.oracle_union.restype = I
     return _lib
 
@@ -291,6 +292,40 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
     h = up(x, w_up, mask, g, skip)
     y = down(h, w_down, mask, skip)
     return Result(z=z, mask=mask, g=g, h=h, y=y, band=band, kth=kth, t=t)
+
+
+# Backward activation kind of each mode: 0 = shifted ReLU on its active branch
+# (g = z - tau, g' = 1), 1 = SiLU.
+BWD_KIND = {"threshold": 0, "dense_relu": 0, "topk": 1, "topk_2_8": 1, "topp": 1, "dense_silu": 1}
+
+
+def saved_set(mode: str, res: "Result", tau: float) -> np.ndarray:
+    """The channels whose activations a training forward keeps for the
+    backward: the active set, except that the dense shifted ReLU keeps only
+    the channels it leaves nonzero (z > tau): the others pass no gradient."""
+    if mode == "dense_relu":
+        return (res.z > tau).astype(np.uint8)
+    return res.mask.astype(np.uint8)
+
+
+def backward(mode: str, x: np.ndarray, dy: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+             w_down: np.ndarray, mask: np.ndarray, tau: float = 0.0) -> dict:
+    """Gradients of sum(dy * y) over a fixed active set `mask` [n][F]: dx
+    [n][d], dw_gate, dw_up, dw_down [F][d], all fp64 (oracle_backward)."""
+    x, dy = _c(x), _c(dy)
+    w_gate, w_up, w_down = _c(w_gate), _c(w_up), _c(w_down)
+    assert w_gate.dtype == w_up.dtype == w_down.dtype
+    mask = _c(np.asarray(mask, dtype=np.uint8))
+    n, d = x.shape
+    f = w_up.shape[0]
+    assert dy.shape == (n, d) and mask.shape == (n, f)
+    assert w_gate.shape == w_up.shape == w_down.shape == (f, d)
+    out = {k: np.empty(s, dtype=np.float64) for k, s in
+           (("dx", (n, d)), ("dw_gate", (f, d)), ("dw_up", (f, d)), ("dw_down", (f, d)))}
+    lib().oracle_backward(n, d, f, BWD_KIND[mode], float(tau), _p(x), _dt(x), _p(dy), _dt(dy), _p(w_gate),
+                          _p(w_up), _p(w_down), _dt(w_up), _p(mask), _p(out["dx"]), _p(out["dw_gate"]),
+                          _p(out["dw_up"]), _p(out["dw_down"]))
+    return out
 
 
 def forward_with_mask(x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, g: np.ndarray,

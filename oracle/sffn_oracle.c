@@ -34,6 +34,9 @@
  *     aligned group of 8 consecutive channels, under the same order;
  *   - top-p keeps the shortest prefix of that order whose softmax mass over
  *     the token's keys reaches p;
+ *   - the backward runs over the stored active set: the selection passes no
+ *     gradient, the shifted ReLU's derivative is 1 on that set, SiLU's is
+ *     sigma(z) (1 + z (1 - sigma(z)));
  *   - inputs are the exact values the GPU sees (fp32, or bf16 bit patterns
  *     widened exactly), and every sum runs in ascending index order in fp64.
  *
@@ -316,4 +319,58 @@ int oracle_union(int n, int F, const unsigned char *mask, unsigned char *un)
         count += un[i];
     }
     return count;
+}
+
+/* Backward of the layer over a fixed set of active channels ("Mixture-of-
+ * Channels" blog summary, "Dentro il 'mixture'": in training only the masked
+ * parts are stored and the rest is rebuilt when the backward needs it). With
+ * y[t] = sum over active i of g(z[t][i]) u[t][i] Wd[i], z = x.Wg[i],
+ * u = x.Wu[i], and dy the gradient of the loss with respect to y, for every
+ * active (t, i):
+ *   dh = dy[t] . Wd[i]         du = dh g(z)         dz = dh u g'(z)
+ *   dWd[i] += g(z) u dy[t]     dWu[i] += du x[t]    dWg[i] += dz x[t]
+ *   dx[t]  += du Wu[i] + dz Wg[i]
+ * kind 0: g = z - tau, g' = 1 (the shifted ReLU on its active branch; the set
+ * says which channels are on); kind 1: g = SiLU(z),
+ * g' = sigma(z) (1 + z (1 - sigma(z))). The selection itself is a step
+ * function of z and passes no gradient. Every output is overwritten; sums run
+ * in ascending token, then channel order, in fp64. */
+void oracle_backward(int n, int d, int F, int kind, double tau, const void *x, int x_dt, const void *dy,
+                     int dy_dt, const void *wg, const void *wu, const void *wd, int w_dt,
+                     const unsigned char *mask, double *dx, double *dwg, double *dwu, double *dwd)
+{
+    memset(dx, 0, sizeof(double) * (size_t)n * d);
+    memset(dwg, 0, sizeof(double) * (size_t)F * d);
+    memset(dwu, 0, sizeof(double) * (size_t)F * d);
+    memset(dwd, 0, sizeof(double) * (size_t)F * d);
+    for (int t = 0; t < n; ++t) {
+        for (int i = 0; i < F; ++i) {
+            if (!mask[(long)t * F + i])
+                continue;
+            double z = 0.0, u = 0.0, dh = 0.0;
+            for (int k = 0; k < d; ++k) {
+                double xv = elem(x, x_dt, (long)t * d + k);
+                z += xv * elem(wg, w_dt, (long)i * d + k);
+                u += xv * elem(wu, w_dt, (long)i * d + k);
+                dh += elem(dy, dy_dt, (long)t * d + k) * elem(wd, w_dt, (long)i * d + k);
+            }
+            double g, gp;
+            if (kind == 0) {
+                g = z - tau;
+                gp = 1.0;
+            } else {
+                double sg = 1.0 / (1.0 + exp(-z));
+                g = z * sg;
+                gp = sg * (1.0 + z * (1.0 - sg));
+            }
+            double du = dh * g, dz = dh * u * gp, h = g * u;
+            for (int k = 0; k < d; ++k) {
+                double xv = elem(x, x_dt, (long)t * d + k);
+                dwd[(long)i * d + k] += h * elem(dy, dy_dt, (long)t * d + k);
+                dwu[(long)i * d + k] += du * xv;
+                dwg[(long)i * d + k] += dz * xv;
+                dx[(long)t * d + k] += du * elem(wu, w_dt, (long)i * d + k) + dz * elem(wg, w_dt, (long)i * d + k);
+            }
+        }
+    }
 }

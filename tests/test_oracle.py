@@ -488,3 +488,96 @@ def test_sparsity_matches_normal_quantile():
         p = 1.0 - _phi(tau * math.sqrt(w.d_model) / xn)
         sigma = math.sqrt(p * (1 - p) / w.d_ff)
         assert abs(mask.mean() - p) < 4 * sigma + 1e-3, (tau, mask.mean(), p)
+
+
+# ---------------------------------------------------------------------------
+# Backward over a fixed active set ("Mixture-of-Channels" blog summary,
+# "Dentro il 'mixture'": training keeps only the masked activations and
+# rebuilds the rest in the backward). The set is an input: any 0/1 mask.
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, n=4, d=12, f=10):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d))
+    dy = rng.standard_normal((n, d))
+    wg, wu, wd = (rng.standard_normal((f, d)) / math.sqrt(d) for _ in range(3))
+    mask = (rng.random((n, f)) < 0.5).astype(np.uint8)
+    return x, dy, wg, wu, wd, mask
+
+
+def _gate_act(mode, z, tau):
+    return z - tau if oracle.BWD_KIND[mode] == 0 else z / (1.0 + np.exp(-z))
+
+
+def _loss(mode, x, dy, wg, wu, wd, mask, tau):
+    """sum(dy * y) over the fixed set, through the oracle's forward steps."""
+    g = _gate_act(mode, oracle.gate_full(x, wg), tau)
+    return float(np.sum(dy * oracle.forward_with_mask(x, wu, wd, g, mask)))
+
+
+@pytest.mark.parametrize("mode,tau", [("threshold", 0.3), ("topk", 0.0), ("dense_silu", 0.0)])
+def test_backward_finite_differences(mode, tau):
+    """Central differences of sum(dy * y) with the set held fixed agree with
+    every gradient at sampled entries (the loss is a polynomial in each entry
+    for the shifted ReLU and smooth for SiLU: the difference error is ~1e-10)."""
+    x, dy, wg, wu, wd, mask = _bwd_case(41)
+    gr = oracle.backward(mode, x, dy, wg, wu, wd, mask, tau)
+    rng = np.random.default_rng(42)
+    h = 1e-5
+    for name, arr in (("dx", x), ("dw_gate", wg), ("dw_up", wu), ("dw_down", wd)):
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = _loss(mode, x, dy, wg, wu, wd, mask, tau)
+            arr[idx] = keep - h
+            lm = _loss(mode, x, dy, wg, wu, wd, mask, tau)
+            arr[idx] = keep
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gr[name][idx]) <= 1e-7 * (1 + abs(fd)), (name, idx, fd, gr[name][idx])
+
+
+@pytest.mark.parametrize("mode,tau", [("threshold", -0.4), ("topk_2_8", 0.0)])
+def test_backward_matches_autograd(mode, tau):
+    """torch's fp64 reverse mode on the CPU, through the same masked formula."""
+    torch = pytest.importorskip("torch")
+    x, dy, wg, wu, wd, mask = _bwd_case(43, n=5, d=16, f=24)
+    gr = oracle.backward(mode, x, dy, wg, wu, wd, mask, tau)
+    X, WG, WU, WD = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, wg, wu, wd))
+    Z = X @ WG.T
+    G = Z - tau if oracle.BWD_KIND[mode] == 0 else Z * torch.sigmoid(Z)
+    Y = (G * (X @ WU.T) * torch.tensor(mask, dtype=torch.float64)) @ WD
+    (Y * torch.tensor(dy)).sum().backward()
+    for name, t in (("dx", X), ("dw_gate", WG), ("dw_up", WU), ("dw_down", WD)):
+        np.testing.assert_allclose(gr[name], t.grad.numpy(), rtol=1e-12, atol=1e-13, err_msg=name)
+
+
+def test_backward_homogeneity():
+    """Exact scaling identities over a fixed set: y is linear in W_down and in
+    W_up, so <dW_down, W_down> = <dW_up, W_up> = <dy, y>; with the shifted
+    ReLU at tau = 0 it is linear in W_gate and of degree 2 in x, so
+    <dW_gate, W_gate> = <dy, y> and <dx, x> = 2 <dy, y>."""
+    for mode in ("threshold", "topk"):
+        x, dy, wg, wu, wd, mask = _bwd_case(44, n=6, d=20, f=30)
+        gr = oracle.backward(mode, x, dy, wg, wu, wd, mask, 0.0)
+        L = _loss(mode, x, dy, wg, wu, wd, mask, 0.0)
+        assert np.sum(gr["dw_down"] * wd) == pytest.approx(L, rel=1e-12, abs=1e-12)
+        assert np.sum(gr["dw_up"] * wu) == pytest.approx(L, rel=1e-12, abs=1e-12)
+        if mode == "threshold":
+            assert np.sum(gr["dw_gate"] * wg) == pytest.approx(L, rel=1e-12, abs=1e-12)
+            assert np.sum(gr["dx"] * x) == pytest.approx(2 * L, rel=1e-12, abs=1e-12)
+
+
+def test_backward_empty_set_and_bf16_widening():
+    """An empty set gives zero gradients; a token with no active channel gets
+    dx = 0; bf16 inputs give exactly what their widened values give."""
+    x, dy, wg, wu, wd, mask = _bwd_case(45)
+    gr = oracle.backward("topk", x, dy, wg, wu, wd, np.zeros_like(mask))
+    assert all(not np.any(v) for v in gr.values())
+    mask[2] = 0
+    gr = oracle.backward("topk", x, dy, wg, wu, wd, mask)
+    assert not np.any(gr["dx"][2]) and np.any(gr["dx"][1])
+    b = [inputs.bf16_bits(a.astype(np.float32)) for a in (x, dy, wg, wu, wd)]
+    g16 = oracle.backward("threshold", *b, mask, 0.25)
+    g64 = oracle.backward("threshold", *[oracle.widen(a) for a in b], mask, 0.25)
+    for k in g16:
+        assert np.array_equal(g16[k], g64[k]), k

@@ -50,6 +50,14 @@ MUTATIONS = {
     "lopa_b_transposed": ("elem(bt, w_dt, (long)i * r + k)", "elem(bt, w_dt, (long)k * F + i)"),
     "union_and": ("any |= mask[(long)t * F + i];", "any &= mask[(long)t * F + i];"),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "bwd_silu_prime_drops_term": ("gp = sg * (1.0 + z * (1.0 - sg));", "gp = sg;"),
+    "bwd_shift_sign": ("g = z - tau;\n                gp = 1.0;", "g = z + tau;\n                gp = 1.0;"),
+    "bwd_dz_uses_g": ("dz = dh * u * gp", "dz = dh * g * gp"),
+    "bwd_dwd_drops_gate": ("h = g * u;", "h = u;"),
+    "bwd_dx_drops_gate_term": (" + dz * elem(wg, w_dt, (long)i * d + k);", ";"),
+    "bwd_dwu_wrong_token": ("dwu[(long)i * d + k] += du * xv;", "dwu[(long)i * d + k] += du * elem(x, x_dt, k);"),
+    "bwd_dh_transposed": ("dh += elem(dy, dy_dt, (long)t * d + k) * elem(wd, w_dt, (long)i * d + k);",
+                          "dh += elem(dy, dy_dt, (long)t * d + k) * elem(wd, w_dt, (long)(k % F) * d + i % d);"),
 }
 
 

@@ -48,7 +48,7 @@ Layout make_layout(const sffn_shape &s)
     L.part_words = (size_t)kDownGroupsMax * ntp * d;
     L.part = take(L.part_words * 4);
     L.tvec = take(r ? ntp * r * 4 : 0);
-    L.keys = take(batched ? T * F * 4 : 0);
+    L.keys = take(rows * F * 4);  // also for a training forward of <= 8 tokens (union path)
     L.ubits = take((size_t)L.words * 4);
     // room for every split a forward of up to T tokens takes, at least 16
     // splits of 64 tokens (forwards smaller than the handle's maximum)
@@ -58,6 +58,45 @@ Layout make_layout(const sffn_shape &s)
     L.thr = take(rows * 8);
     L.total = off;
     return L;
+}
+
+TrainLayout make_train_layout(const sffn_shape &s)
+{
+    TrainLayout L{};
+    const size_t F = (size_t)s.d_ff, d = (size_t)s.d_model, T = (size_t)s.max_tokens;
+    const size_t FP = (F + 7) / 8 * 8, TP = (T + 7) / 8 * 8;
+    L.tp_max = (int)TP;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align256(off + bytes + 256);  // 256 bytes of slack after every buffer
+        return at;
+    };
+    L.zu = take(T * FP * 8);
+    L.du = take(T * FP * 2);
+    L.dz = take(T * FP * 2);
+    L.dut = take(FP * TP * 2);
+    L.dzt = take(FP * TP * 2);
+    L.ht = take(FP * TP * 2);
+    L.xt = take(d * TP * 2);
+    L.dyt = take(d * TP * 2);
+    L.ubits = take((F + 31) / 32 * 4);
+    L.uidx = take(F * 4);
+    L.ctrl = take(64 * 4);
+    const size_t prow = T < 512 ? (size_t)splits_max((int)T) * T : 0, pmin = 16 * (T < 64 ? T : 64);
+    L.part_rows = (int)(prow > pmin ? prow : pmin);
+    L.part = take((size_t)L.part_rows * (F > d ? F : d) * 4);
+    L.total = off;
+    return L;
+}
+
+// Most channels a mode can keep per token: the Top-K size, the 2:8 count,
+// or d_ff (threshold, top-p and the dense modes).
+static int max_kept(int mode, int F, int k)
+{
+    if (mode == SFFN_TOPK) return k;
+    if (mode == SFFN_TOPK_2_8) return (F / 8) * 2 + (F % 8 < 2 ? F % 8 : 2);
+    return F;
 }
 
 }  // namespace sffn
@@ -188,6 +227,108 @@ sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const 
         return e == hipErrorNotSupported ? SFFN_ERR_UNSUPPORTED : SFFN_ERR_HIP;
     }
     return SFFN_OK;
+}
+
+size_t sffn_train_workspace_bytes(const sffn_shape *shape)
+{
+    if (!shape || !shape_ok(*shape)) return 0;
+    return make_train_layout(*shape).total;
+}
+
+// Checks shared by the training forward and the backward; SFFN_OK or the
+// status to return.
+static sffn_status train_checks(sffn_handle handle, int n_tokens, const sffn_weights *w, int mode, float tau, int k,
+                                const sffn_saved *saved, void *train_ws, size_t train_ws_bytes)
+{
+    if (!handle || !w || !saved) return SFFN_ERR_INVALID_ARG;
+    const sffn_shape &s = handle->shape;
+    if (n_tokens < 0 || n_tokens > s.max_tokens) return SFFN_ERR_INVALID_ARG;
+    if (mode < SFFN_THRESHOLD || mode > SFFN_TOPP) return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_LOPA || s.dtype != SFFN_BF16) return SFFN_ERR_UNSUPPORTED;
+    if (!w->w_gate || !w->w_up || !w->w_down || !aligned16(w->w_gate) || !aligned16(w->w_up) ||
+        !aligned16(w->w_down))
+        return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_TOPK && (k < 1 || k > s.d_ff)) return SFFN_ERR_INVALID_ARG;
+    if (mode != SFFN_TOPK && mode != SFFN_TOPK_2_8 && std::isnan(tau)) return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_TOPP && !(tau > 0.f && tau <= 1.f)) return SFFN_ERR_INVALID_ARG;
+    if (saved->cap < 1 || saved->cap > s.d_ff) return SFFN_ERR_INVALID_ARG;
+    if ((mode == SFFN_TOPK || mode == SFFN_TOPK_2_8 || mode == SFFN_DENSE_SILU) &&
+        saved->cap < max_kept(mode, s.d_ff, k))
+        return SFFN_ERR_INVALID_ARG;
+    if (!saved->cnt || !saved->idx || !saved->z || !saved->u || !aligned4(saved->cnt) || !aligned4(saved->idx) ||
+        !aligned4(saved->z) || !aligned4(saved->u))
+        return SFFN_ERR_INVALID_ARG;
+    if (!train_ws || ((uintptr_t)train_ws & 255u) != 0 || train_ws_bytes < make_train_layout(s).total)
+        return SFFN_ERR_WORKSPACE;
+    return SFFN_OK;
+}
+
+static Saved to_saved(const sffn_saved *v) { return Saved{v->cap, v->cnt, v->idx, v->z, v->u}; }
+
+sffn_status sffn_forward_train(sffn_handle handle, const void *x, int n_tokens, const sffn_weights *w, int mode,
+                               float tau, int k, float *y, const sffn_saved *saved, void *train_ws,
+                               size_t train_ws_bytes, void *stream)
+{
+    const sffn_status v = train_checks(handle, n_tokens, w, mode, tau, k, saved, train_ws, train_ws_bytes);
+    if (v != SFFN_OK) return v;
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID_ARG;
+    if (n_tokens == 0) return SFFN_OK;
+    if (handle->n_cu == 0) {
+        if (device_setup(*handle) != hipSuccess) return SFFN_ERR_HIP;
+    }
+    FwdArgs a;
+    a.x = x;
+    a.n = n_tokens;
+    a.w = *w;
+    a.mode = mode;
+    a.tau = tau;
+    a.k = k;
+    a.y = y;
+    a.active_idx = nullptr;
+    a.active_cnt = nullptr;
+    a.union_cnt = nullptr;
+    a.debug_z = nullptr;
+    a.stream = static_cast<hipStream_t>(stream);
+    if (!handle->inited) {
+        if (launch_init(*handle, a.stream) != hipSuccess) return SFFN_ERR_HIP;
+        handle->inited = true;
+    }
+    const hipError_t e = launch_forward_train(*handle, a, to_saved(saved), static_cast<char *>(train_ws));
+    if (e != hipSuccess) {
+        handle->inited = false;
+        return e == hipErrorNotSupported ? SFFN_ERR_UNSUPPORTED : SFFN_ERR_HIP;
+    }
+    return SFFN_OK;
+}
+
+sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int n_tokens, const sffn_weights *w,
+                          int mode, float tau, int k, const sffn_saved *saved, float *dx, float *dw_gate,
+                          float *dw_up, float *dw_down, void *train_ws, size_t train_ws_bytes, void *stream)
+{
+    const sffn_status v = train_checks(handle, n_tokens, w, mode, tau, k, saved, train_ws, train_ws_bytes);
+    if (v != SFFN_OK) return v;
+    if (!x || !dy || !dx || !dw_gate || !dw_up || !dw_down || !aligned16(x) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dw_gate) || !aligned16(dw_up) || !aligned16(dw_down))
+        return SFFN_ERR_INVALID_ARG;
+    if (n_tokens == 0) return SFFN_OK;
+    if (handle->n_cu == 0) {
+        if (device_setup(*handle) != hipSuccess) return SFFN_ERR_HIP;
+    }
+    BwdArgs a;
+    a.x = x;
+    a.dy = dy;
+    a.n = n_tokens;
+    a.w = *w;
+    a.mode = mode;
+    a.tau = tau;
+    a.sv = to_saved(saved);
+    a.dx = dx;
+    a.dwg = dw_gate;
+    a.dwu = dw_up;
+    a.dwd = dw_down;
+    a.tws = static_cast<char *>(train_ws);
+    a.stream = static_cast<hipStream_t>(stream);
+    return launch_backward(*handle, a) == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
 }
 
 }  // extern "C"

@@ -45,7 +45,11 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t_;
 
 
 
-enum EpiKind { EPI_GATE = 0, EPI_UP = 1, EPI_DOWN = 2 };
+// Forward: gate, up, down. Backward (train.hip): BWD = the product
+// dH = dY . W_down[U]^T with the gate derivative applied (dU, dZ and H, token
+// major and transposed), DOWN_ACC = the down form adding into Y, WGRAD =
+// C[m][n] added into row U[n] of a weight gradient (M = d_model).
+enum EpiKind { EPI_GATE = 0, EPI_UP = 1, EPI_DOWN = 2, EPI_BWD = 3, EPI_DOWN_ACC = 4, EPI_WGRAD = 5 };
 
 struct EpiArgs {
     int kind;
@@ -60,8 +64,38 @@ struct EpiArgs {
     int *ucount;        // union size (up writes)
     uint16_t *H;        // [T][hld] bf16 (up writes)
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
-    float *Y;           // [T][d] fp32 (down writes)
+    float *Y;           // [T][d] fp32 (down writes; WGRAD: the gradient [F][d], added into)
+    float *usave;       // optional [T][F] fp32: the up values x . W_up[i] (up writes, training forward)
+    // backward (EPI_BWD): mode is the derivative kind (0: g = z - tau,
+    // g' = 1; 1: SiLU), ZU[t][i] the stored (z, u) of channel i (z NaN where
+    // channel i is off for token t); writes dU into H and dZ into H2 (token
+    // major, row stride hld) and dU, dZ, g(z) u transposed into DUT, DZT, HT
+    // ([union position][token], row stride tp)
+    const float2 *ZU;
+    uint16_t *H2, *DUT, *DZT, *HT;
+    int tp;
 };
+
+// Backward values of one (token, channel) from the product v = dy . W_down[i]:
+// du = v g(z), dz = v u g'(z), h = g(z) u; zero where the channel is off.
+__device__ __forceinline__ void bwd_values(const EpiArgs &e, int m, int ch, float v, float &du, float &dz, float &h)
+{
+    du = dz = h = 0.f;
+    const float2 zu = e.ZU[(size_t)m * e.F + ch];
+    if (zu.x != zu.x) return;  // off
+    float g, gp;
+    if (e.mode == 0) {
+        g = zu.x - e.tau;
+        gp = 1.f;
+    } else {
+        const float sg = 1.f / (1.f + expf(-zu.x));
+        g = zu.x * sg;
+        gp = sg * (1.f + zu.x * (1.f - sg));
+    }
+    du = v * g;
+    dz = v * zu.y * gp;
+    h = g * zu.y;
+}
 
 // One output element. Returns the union bit for the gate (1 if the channel is
 // kept for this token).
@@ -85,6 +119,26 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
     if (e.kind == EPI_UP) {
         const int i = e.uidx[n];
         e.H[(size_t)m * e.hld + n] = f2bf(bf2f(e.G[(size_t)m * e.F + i]) * v);
+        if (e.usave) e.usave[(size_t)m * e.F + i] = v;
+        return false;
+    }
+    if (e.kind == EPI_BWD) {
+        float du, dz, h;
+        bwd_values(e, m, e.uidx[n], v, du, dz, h);
+        e.H[(size_t)m * e.hld + n] = f2bf(du);
+        e.H2[(size_t)m * e.hld + n] = f2bf(dz);
+        const size_t o = (size_t)n * e.tp + m;
+        e.DUT[o] = f2bf(du);
+        e.DZT[o] = f2bf(dz);
+        e.HT[o] = f2bf(h);
+        return false;
+    }
+    if (e.kind == EPI_DOWN_ACC) {
+        e.Y[(size_t)m * e.d + n] += v;
+        return false;
+    }
+    if (e.kind == EPI_WGRAD) {
+        e.Y[(size_t)e.uidx[n] * e.d + m] += v;
         return false;
     }
     e.Y[(size_t)m * e.d + n] = v;
@@ -123,7 +177,7 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                 }
         return;
     }
-    if constexpr (EK == EPI_DOWN) {
+    if constexpr (EK == EPI_DOWN || EK == EPI_DOWN_ACC) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int n = colof(j);
@@ -133,8 +187,57 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
 #pragma unroll
                 for (int r = 0; r < ACC; ++r) {
                     const int m = rowof(i, r);
-                    if (m < M) epi.Y[(size_t)m * epi.d + n] = acc[i][j][r];
+                    if (m >= M) continue;
+                    float *o = epi.Y + (size_t)m * epi.d + n;
+                    if constexpr (EK == EPI_DOWN_ACC) *o += acc[i][j][r];
+                    else *o = acc[i][j][r];
                 }
+        }
+    } else if constexpr (EK == EPI_WGRAD) {
+        // column n is union entry n: row U[n] of the gradient; rows m are
+        // model dimensions, four consecutive ones per lane and register group
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= nlim) continue;
+            float *row = epi.Y + (size_t)epi.uidx[n] * epi.d;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m < M) row[m] += acc[i][j][r];
+                }
+        }
+    } else if constexpr (EK == EPI_BWD) {
+        // rows m are tokens, column n union entry n (channel U[n]); pad
+        // columns up to a multiple of 8 get zeros (the dx products read dU
+        // and dZ in 8-wide chunks)
+        const int padlim = (nlim + 7) & ~7;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = colof(j);
+            if (n >= padlim) continue;
+            const bool live = n < nlim;
+            const int ch = live ? epi.uidx[n] : 0;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < ACC; ++r) {
+                    const int m = rowof(i, r);
+                    if (m >= M) continue;
+                    float du = 0.f, dz = 0.f, h = 0.f;
+                    if (live) bwd_values(epi, m, ch, acc[i][j][r], du, dz, h);
+                    epi.H[(size_t)m * epi.hld + n] = f2bf(du);
+                    epi.H2[(size_t)m * epi.hld + n] = f2bf(dz);
+                    if (live) {
+                        const size_t o = (size_t)n * epi.tp + m;
+                        epi.DUT[o] = f2bf(du);
+                        epi.DZT[o] = f2bf(dz);
+                        epi.HT[o] = f2bf(h);
+                    }
+                }
+            __builtin_amdgcn_sched_barrier(0);
         }
     } else if constexpr (EK == EPI_UP) {
         const int padlim = (nlim + 7) & ~7;
@@ -151,7 +254,10 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                     const int m = rowof(i, r);
                     if (m >= M) continue;
                     uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
-                    if (live) h = f2bf(bf2f(epi.G[(size_t)m * epi.F + src]) * acc[i][j][r]);
+                    if (live) {
+                        h = f2bf(bf2f(epi.G[(size_t)m * epi.F + src]) * acc[i][j][r]);
+                        if (epi.usave) epi.usave[(size_t)m * epi.F + src] = acc[i][j][r];
+                    }
                     epi.H[(size_t)m * epi.hld + n] = h;
                 }
             // keep each sub-tile's gathered G loads from being hoisted over the
@@ -412,7 +518,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         for (int j = 0; j < BPW; ++j) {
             const int r = (wave * BPW + j) * (64 / CH) + lr, n = n0 + r;
             blc[j] = kchunk(r);
-            const int row = EK == EPI_UP ? uloc[r] : bidx ? bidx[n] : n;
+            const int row = EK == EPI_UP ? uloc[r] : (bidx && n < nlim) ? bidx[n] : n;
             bsrc[j] = n < nlim ? B + (size_t)row * ldb + blc[j] : nullptr;
         }
     } else {
@@ -623,8 +729,9 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
             if (s < S) v += p[s];
         if (epilogue(epi, m, n, v) && epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD)
             atomicOr(&ub[threadIdx.x / 32], 1u << (n & 31));
-    } else if (epi.kind == EPI_UP && n < ((nlim + 7) & ~7)) {
+    } else if ((epi.kind == EPI_UP || epi.kind == EPI_BWD) && n < ((nlim + 7) & ~7)) {
         epi.H[(size_t)m * epi.hld + n] = 0;
+        if (epi.kind == EPI_BWD) epi.H2[(size_t)m * epi.hld + n] = 0;
     }
     __syncthreads();
     if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
@@ -762,10 +869,11 @@ static dim3 tile_grid(int nt, int mt, int sk) { return dim3(8 * ((nt + 7) / 8) *
 // splits, and K steps of at least 8 tiles per split). Below 128 tokens the
 // weights stream once through many small workgroups: up to splits_max
 // splits, ~3 workgroups per CU, at least 4 K steps of 64 per split.
-static int split_for(const sffn_ctx &c, long long tiles, int K, int M)
+static int split_for(const sffn_ctx &c, long long tiles, int K, int M, int part_rows = -1)
 {
     int S = 1;
-    const int smax = min(splits_max(M), c.L.bpart_rows / M);  // and what the partial buffer holds
+    if (part_rows < 0) part_rows = c.L.bpart_rows;
+    const int smax = min(splits_max(M), part_rows / M);  // and what the partial buffer holds
     if (M < 128) {
         while (2 * S <= smax && tiles * S < c.n_cu && (K / 64) / (2 * S) >= 4) S *= 2;
         return S;
@@ -811,6 +919,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     ep.H = H;
     ep.hld = (F + 7) / 8 * 8;
     ep.Y = a.y;
+    ep.usave = a.usave;
 
     const Cfg cf = cfg_for(T);
     Cfg cfd = cf;
@@ -879,6 +988,129 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount, a.active_idx,
                            a.active_cnt, a.union_cnt);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// ===========================================================================
+// Training
+// ===========================================================================
+// The forward on the union path with the dense z and the union's up values
+// kept in the training workspace, then each token's stored rows.
+hipError_t launch_forward_train(sffn_ctx &c, FwdArgs a, const Saved &sv, char *tws)
+{
+    const sffn_shape &S = c.shape;
+    const TrainLayout TL = make_train_layout(S);
+    const size_t TF = (size_t)S.max_tokens * S.d_ff;
+    float *zd = reinterpret_cast<float *>(tws + TL.zu);
+    float *ud = zd + TF;
+    a.debug_z = zd;
+    a.usave = ud;
+    hipError_t e = launch_batched(c, a);
+    if (e != hipSuccess) return e;
+    const uint8_t *act = reinterpret_cast<const uint8_t *>(c.ws + c.L.act);
+    return launch_save(zd, ud, act, a.n, S.d_ff, a.mode, a.tau, sv, a.stream);
+}
+
+// Backward over the stored rows, on the union U of the stored channels:
+//   dH  = dY . W_down[U]^T        (T x |U|); epilogue: du = dh g(z),
+//                                 dz = dh u g'(z), h = g(z) u, zero where off
+//   dX  = dU . W_up[U] + dZ . W_gate[U]   (two down-form products, the second adds)
+//   dW_down[U] += H^T dY,  dW_up[U] += dU^T X,  dW_gate[U] += dZ^T X
+// The weight gradients are C = X^T . dU (M = d_model, N = |U|, K = tokens)
+// with both operands token-contiguous, written into row U[n].
+hipError_t launch_backward(sffn_ctx &c, const BwdArgs &a)
+{
+    const sffn_shape &S = c.shape;
+    const TrainLayout TL = make_train_layout(S);
+    const int T = a.n, d = S.d_model, F = S.d_ff;
+    const int FP = (F + 7) / 8 * 8, tp = (T + 7) / 8 * 8;
+    char *tws = a.tws;
+    float2 *ZU = reinterpret_cast<float2 *>(tws + TL.zu);
+    uint16_t *dU = reinterpret_cast<uint16_t *>(tws + TL.du), *dZ = reinterpret_cast<uint16_t *>(tws + TL.dz);
+    uint16_t *DUT = reinterpret_cast<uint16_t *>(tws + TL.dut), *DZT = reinterpret_cast<uint16_t *>(tws + TL.dzt);
+    uint16_t *HT = reinterpret_cast<uint16_t *>(tws + TL.ht);
+    uint16_t *XT = reinterpret_cast<uint16_t *>(tws + TL.xt), *DYT = reinterpret_cast<uint16_t *>(tws + TL.dyt);
+    uint32_t *ubits = reinterpret_cast<uint32_t *>(tws + TL.ubits);
+    int32_t *uidx = reinterpret_cast<int32_t *>(tws + TL.uidx);
+    int *ucount = reinterpret_cast<int *>(tws + TL.ctrl);
+    float *part = reinterpret_cast<float *>(tws + TL.part);
+    const bf16_t *x = static_cast<const bf16_t *>(a.x), *dy = static_cast<const bf16_t *>(a.dy);
+    const bf16_t *wg = static_cast<const bf16_t *>(a.w.w_gate), *wu = static_cast<const bf16_t *>(a.w.w_up);
+    const bf16_t *wdn = static_cast<const bf16_t *>(a.w.w_down);
+    hipStream_t st = a.stream;
+    hipError_t e;
+
+    e = launch_bwd_setup(a.sv, T, F, d, tp, ZU, ubits, uidx, ucount, DUT, DZT, HT,
+                         reinterpret_cast<const uint16_t *>(x), reinterpret_cast<const uint16_t *>(dy),
+                         XT, DYT, st);
+    if (e != hipSuccess) return e;
+
+    EpiArgs ep{};
+    ep.mode = (a.mode == SFFN_THRESHOLD || a.mode == SFFN_DENSE) ? 0 : 1;  // derivative kind
+    ep.tau = a.tau;
+    ep.T = T;
+    ep.F = F;
+    ep.d = d;
+    ep.ubits = ubits;
+    ep.uidx = uidx;
+    ep.ucount = ucount;
+    ep.H = dU;
+    ep.H2 = dZ;
+    ep.hld = FP;
+    ep.ZU = ZU;
+    ep.DUT = DUT;
+    ep.DZT = DZT;
+    ep.HT = HT;
+    ep.tp = tp;
+
+    const Cfg cf = cfg_for(T);
+    Cfg cfd = cf;
+    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{4, 2, 2, 2};
+    const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
+
+    // ---- dH = dY . W_down[U]^T, with the derivative epilogue ----
+    {
+        ep.kind = EPI_BWD;
+        const int nt = (F + cf.bn() - 1) / cf.bn();
+        const int sk = split_for(c, (long long)mt * nt / 2, d, T, TL.part_rows);
+        dispatch_mfma<false, EPI_BWD>(cf, tile_grid(nt, mt, sk), st, T, F, d, dy, d, wdn, d, uidx, ucount, part, F,
+                                      ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1 && (e = launch_splitk_sum(st, part, sk, T, F, F, ucount, ep)) != hipSuccess) return e;
+    }
+    // ---- dX = dU . W_up[U], then += dZ . W_gate[U] ----
+    {
+        const int nt = (d + cfd.bn() - 1) / cfd.bn();
+        const int sk = split_for(c, (long long)mtd * nt, F / 2, T, TL.part_rows);
+        ep.Y = a.dx;
+        ep.kind = EPI_DOWN;
+        dispatch_mfma<true, EPI_DOWN>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, dU, FP, wu, d, uidx, ucount, part, d,
+                                      ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1 && (e = launch_splitk_sum(st, part, sk, T, d, d, nullptr, ep)) != hipSuccess) return e;
+        ep.kind = EPI_DOWN_ACC;
+        dispatch_mfma<true, EPI_DOWN_ACC>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, dZ, FP, wg, d, uidx, ucount, part,
+                                          d, ep);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (sk > 1 && (e = launch_splitk_sum(st, part, sk, T, d, d, nullptr, ep)) != hipSuccess) return e;
+    }
+    // ---- weight gradients: C[d][|U|] over K = tokens, added into rows U[n] ----
+    {
+        const Cfg cw = cfg_for(d);
+        const int nt = (F + cw.bn() - 1) / cw.bn(), mw = (d + cw.bm() - 1) / cw.bm();
+        ep.kind = EPI_WGRAD;
+        const struct {
+            const uint16_t *a, *b;
+            float *out;
+        } prods[3] = {{DYT, HT, a.dwd}, {XT, DUT, a.dwu}, {XT, DZT, a.dwg}};
+        for (const auto &p : prods) {
+            ep.Y = p.out;
+            dispatch_mfma<false, EPI_WGRAD>(cw, tile_grid(nt, mw, 1), st, d, F, tp, reinterpret_cast<const bf16_t *>(p.a),
+                                            tp, reinterpret_cast<const bf16_t *>(p.b), tp, nullptr, ucount, part, F,
+                                            ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -65,6 +65,44 @@ struct FwdArgs {
     int32_t *union_cnt;
     float *debug_z;
     hipStream_t stream;
+    float *usave = nullptr;  // training forward: fp32 [n][d_ff] up values of the union's channels
+};
+
+// Training workspace (sffn_train_workspace_bytes): buffers of the training
+// forward's save step and of the backward, for up to T = max_tokens tokens.
+struct TrainLayout {
+    int tp_max;       // max_tokens rounded up to 8
+    size_t zu;        // backward: float2 [T][d_ff] stored (z, u), z = NaN where off;
+                      // forward: fp32 [T][d_ff] z, then fp32 [T][d_ff] u
+    size_t du, dz;    // bf16 [T][FP] dU, dZ (token major; FP = d_ff rounded up to 8)
+    size_t dut, dzt, ht;  // bf16 [FP][tp] dU, dZ, g(z) u transposed (union position major)
+    size_t xt, dyt;   // bf16 [d_model][tp] x and dy transposed
+    size_t ubits;     // uint32 [words] union of the stored sets
+    size_t uidx;      // int32 [d_ff] ascending union list
+    size_t ctrl;      // int32 [64]: union size
+    size_t part;      // fp32 [part_rows][max(d_ff, d_model)] split-K partials
+    int part_rows;
+    size_t total;
+};
+TrainLayout make_train_layout(const sffn_shape &s);
+
+// Stored activations of a training forward (per token, ascending channels).
+struct Saved {
+    int cap;
+    int32_t *cnt, *idx;
+    float *z, *u;
+};
+
+struct BwdArgs {
+    const void *x, *dy;
+    int n;
+    sffn_weights w;
+    int mode;
+    float tau;
+    Saved sv;
+    float *dx, *dwg, *dwu, *dwd;
+    char *tws;  // training workspace
+    hipStream_t stream;
 };
 
 }  // namespace sffn
@@ -86,6 +124,23 @@ hipError_t device_setup(sffn_ctx &c);
 hipError_t launch_init(sffn_ctx &c, hipStream_t s);
 hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a);
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a);
+// Training (batched.hip): the forward on the union path plus the stored
+// activations, and the backward over them.
+hipError_t launch_forward_train(sffn_ctx &c, FwdArgs a, const Saved &sv, char *tws);
+hipError_t launch_backward(sffn_ctx &c, const BwdArgs &a);
+// Training helper kernels (train.hip).
+// The saved rows of each token from the forward's dense z [T][F], up values
+// [T][F] and flags: the channels the mode keeps, ascending, the first cap of
+// them stored; cnt[t] = how many there are.
+hipError_t launch_save(const float *zd, const float *ud, const uint8_t *act, int T, int F, int mode, float tau,
+                       const Saved &sv, hipStream_t st);
+// Backward set-up: (z, u) of the stored channels into ZU [T][F] (NaN z
+// elsewhere), the union bitmap and ascending list of the stored channels
+// (uidx, *ucount), zeroed token padding [T, tp) of the transposed buffers'
+// rows, and x, dy transposed into xt, dyt [d][tp] (zero past T).
+hipError_t launch_bwd_setup(const Saved &sv, int T, int F, int d, int tp, float2 *ZU, uint32_t *ubits,
+                            int32_t *uidx, int *ucount, uint16_t *dut, uint16_t *dzt, uint16_t *ht,
+                            const uint16_t *x, const uint16_t *dy, uint16_t *xt, uint16_t *dyt, hipStream_t st);
 // Per-token Top-K (topk.hip), shared by both regimes: thr[t] = {K-th largest
 // key in the f2key encoding, last channel index kept among keys equal to it}.
 hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st);

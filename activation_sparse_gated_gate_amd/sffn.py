@@ -41,7 +41,8 @@ DTYPES = {"f32": SFFN_F32, "bf16": SFFN_BF16}
 
 # Names exported by the library, as declared in include/sffn.h.
 EXPORTS = ("sffn_workspace_bytes", "sffn_create", "sffn_forward", "sffn_set_profile_events",
-           "sffn_destroy", "sffn_status_string")
+           "sffn_destroy", "sffn_status_string", "sffn_train_workspace_bytes", "sffn_forward_train",
+           "sffn_backward")
 
 
 class sffn_shape(ctypes.Structure):
@@ -52,6 +53,11 @@ class sffn_shape(ctypes.Structure):
 class sffn_weights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("lopa_a", ctypes.c_void_p), ("lopa_b", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p)]
+
+
+class sffn_saved(ctypes.Structure):
+    _fields_ = [("cap", ctypes.c_int), ("cnt", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("z", ctypes.c_void_p), ("u", ctypes.c_void_p)]
 
 
 class SffnError(RuntimeError):
@@ -84,6 +90,13 @@ def lib() -> ctypes.CDLL:
             L.sffn_set_profile_events.restype = I
             L.sffn_destroy.argtypes = [P]
             L.sffn_destroy.restype = I
+            L.sffn_train_workspace_bytes.argtypes = [ctypes.POINTER(sffn_shape)]
+            L.sffn_train_workspace_bytes.restype = Z
+            SV = ctypes.POINTER(sffn_saved)
+            L.sffn_forward_train.argtypes = [P, P, I, ctypes.POINTER(sffn_weights), I, F, I, P, SV, P, Z, P]
+            L.sffn_forward_train.restype = I
+            L.sffn_backward.argtypes = [P, P, P, I, ctypes.POINTER(sffn_weights), I, F, I, SV, P, P, P, P, P, Z, P]
+            L.sffn_backward.restype = I
             L.sffn_status_string.argtypes = [I]
             L.sffn_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -123,6 +136,28 @@ def sffn_forward(handle: int, x: int, n_tokens: int, weights: sffn_weights, mode
                               float(tau), int(k), P(y), P(active_idx or None), P(active_cnt or None),
                               P(union_cnt or None), P(debug_z or None), P(stream or None)),
            "sffn_forward")
+
+
+def sffn_train_workspace_bytes(shape: sffn_shape) -> int:
+    return int(lib().sffn_train_workspace_bytes(ctypes.byref(shape)))
+
+
+def sffn_forward_train(handle: int, x: int, n_tokens: int, weights: sffn_weights, mode: int, tau: float,
+                       k: int, y: int, saved: sffn_saved, train_ws: int, train_ws_bytes: int,
+                       stream: int = 0) -> None:
+    P = ctypes.c_void_p
+    _check(lib().sffn_forward_train(P(handle), P(x), int(n_tokens), ctypes.byref(weights), int(mode),
+                                    float(tau), int(k), P(y), ctypes.byref(saved), P(train_ws),
+                                    int(train_ws_bytes), P(stream or None)), "sffn_forward_train")
+
+
+def sffn_backward(handle: int, x: int, dy: int, n_tokens: int, weights: sffn_weights, mode: int, tau: float,
+                  k: int, saved: sffn_saved, dx: int, dw_gate: int, dw_up: int, dw_down: int, train_ws: int,
+                  train_ws_bytes: int, stream: int = 0) -> None:
+    P = ctypes.c_void_p
+    _check(lib().sffn_backward(P(handle), P(x), P(dy), int(n_tokens), ctypes.byref(weights), int(mode),
+                               float(tau), int(k), ctypes.byref(saved), P(dx), P(dw_gate), P(dw_up), P(dw_down),
+                               P(train_ws), int(train_ws_bytes), P(stream or None)), "sffn_backward")
 
 
 def sffn_set_profile_events(handle: int, ev_start: int, ev_stop: int) -> None:
@@ -175,6 +210,46 @@ class SparseFFN:
         ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
         sffn_forward(self.handle, x.data_ptr(), x.shape[0], weights, m, tau, k, y.data_ptr(),
                      ptr(active_idx), ptr(active_cnt), ptr(union_cnt), ptr(debug_z), stream)
+
+    # ---- training ----
+    def _train_ws(self):
+        import torch
+
+        if getattr(self, "train_workspace", None) is None:
+            nbytes = sffn_train_workspace_bytes(self.shape)
+            self.train_workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.workspace.device)
+            self._train_bytes = nbytes
+        return (self.train_workspace.data_ptr() + 255) & ~255, self._train_bytes
+
+    @staticmethod
+    def saved(cap: int, cnt, idx, z, u) -> sffn_saved:
+        """Pointer struct of the stored activations (cnt int32 [n], idx int32
+        [n][cap], z and u fp32 [n][cap]); keeps the tensors alive."""
+        v = sffn_saved(int(cap), cnt.data_ptr(), idx.data_ptr(), z.data_ptr(), u.data_ptr())
+        v._keep = (cnt, idx, z, u)
+        return v
+
+    def forward_train(self, x, weights: sffn_weights, mode, y, saved: sffn_saved, tau: float = 0.0, k: int = 0,
+                      stream: Optional[int] = None) -> None:
+        import torch
+
+        m = MODES[mode] if isinstance(mode, str) else int(mode)
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        ws, nb = self._train_ws()
+        sffn_forward_train(self.handle, x.data_ptr(), x.shape[0], weights, m, tau, k, y.data_ptr(), saved, ws, nb,
+                           stream)
+
+    def backward(self, x, dy, weights: sffn_weights, mode, saved: sffn_saved, dx, dw_gate, dw_up, dw_down,
+                 tau: float = 0.0, k: int = 0, stream: Optional[int] = None) -> None:
+        import torch
+
+        m = MODES[mode] if isinstance(mode, str) else int(mode)
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        ws, nb = self._train_ws()
+        sffn_backward(self.handle, x.data_ptr(), dy.data_ptr(), x.shape[0], weights, m, tau, k, saved,
+                      dx.data_ptr(), dw_gate.data_ptr(), dw_up.data_ptr(), dw_down.data_ptr(), ws, nb, stream)
 
     def set_profile_events(self, start_event, stop_event) -> None:
         sffn_set_profile_events(self.handle, start_event.cuda_event if start_event is not None else 0,

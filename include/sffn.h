@@ -148,6 +148,70 @@ sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const 
                          int mode, float tau, int k, float *y, int32_t *active_idx,
                          int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Training: the forward with its activations stored in masked form, and the
+ * backward over them. "Mixture-of-Channels" (blog summary), "Dentro il
+ * 'mixture'": in training only the masked parts of the FFN activations are
+ * kept for the backward, and the rest is rebuilt when the backward needs it.
+ * Per token the stored rows hold the channels the mode keeps, ascending, with
+ * their gate pre-activation z and up value u = x . W_up[i]; the backward
+ * rebuilds g(z), g'(z) and h = g(z) u from them. With y as above and dy the
+ * gradient of a loss with respect to y, over the stored channels:
+ *   dh = dy . W_down[i],  du = dh g(z),  dz = dh u g'(z)
+ *   dx = sum du W_up[i] + dz W_gate[i];  dW_down[i] += g(z) u dy,
+ *   dW_up[i] += du x,  dW_gate[i] += dz x   (summed over tokens)
+ * g' is 1 for THRESHOLD and DENSE (the shifted ReLU on its active branch;
+ * DENSE stores only the channels with z > tau, the others carry no gradient)
+ * and sigma(z) (1 + z (1 - sigma(z))) for the SiLU modes. The selection passes
+ * no gradient. Both calls run the bf16 union path for any n_tokens (bf16
+ * shapes only; LOPA is not supported: SFFN_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------- */
+
+/* Stored activations, caller-owned device memory (4-byte aligned):
+ *   cap   slots per token, 1 <= cap <= d_ff; at least k for TOPK, the 2:8
+ *         count (2 per full group of 8, min(2, rest) for a last short group)
+ *         for TOPK_2_8, d_ff for DENSE_SILU
+ *   cnt   int32 [n_tokens]: channels the mode keeps for token t (written by
+ *         the training forward); when it exceeds cap only the first cap are
+ *         stored and the backward uses those
+ *   idx   int32 [n_tokens][cap]: their channel indices, ascending
+ *   z, u  fp32 [n_tokens][cap]: their gate pre-activation and up value */
+typedef struct {
+    int cap;
+    int32_t *cnt;
+    int32_t *idx;
+    float *z;
+    float *u;
+} sffn_saved;
+
+/* Bytes of the training workspace (caller-owned device memory, 256-byte
+ * aligned) that sffn_forward_train and sffn_backward use for up to
+ * shape->max_tokens tokens; 0 for an invalid shape. Pure host arithmetic. */
+size_t sffn_train_workspace_bytes(const sffn_shape *shape);
+
+/* A forward as sffn_forward (same x, w, mode, tau, k, y), always on the bf16
+ * union path, that also writes the stored activations `saved`. Uses the
+ * handle's workspace and train_ws (>= sffn_train_workspace_bytes). Errors as
+ * sffn_forward, plus SFFN_ERR_INVALID_ARG for a bad `saved` and
+ * SFFN_ERR_WORKSPACE for a bad train_ws. */
+sffn_status sffn_forward_train(sffn_handle handle, const void *x, int n_tokens, const sffn_weights *w, int mode,
+                               float tau, int k, float *y, const sffn_saved *saved, void *train_ws,
+                               size_t train_ws_bytes, void *stream);
+
+/* Backward over the stored activations of a training forward with the same
+ * x, weights, mode, tau and k.
+ *   dy       device, [n_tokens][d_model], bf16 (the shape's dtype)
+ *   dx       device, [n_tokens][d_model] fp32, written
+ *   dw_gate, dw_up, dw_down  device, [d_ff][d_model] fp32 (16-byte aligned),
+ *            ADDED INTO: rows of channels no token stored are not touched;
+ *            zero them before the first backward of an accumulation
+ * x, dy, dx and the weight pointers 16-byte aligned. Uses train_ws (its
+ * contents from the forward are not needed). Stored channel indices outside
+ * [0, d_ff) are skipped. n_tokens = 0 returns SFFN_OK and enqueues nothing. */
+sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int n_tokens, const sffn_weights *w,
+                          int mode, float tau, int k, const sffn_saved *saved, float *dx, float *dw_gate,
+                          float *dw_up, float *dw_down, void *train_ws, size_t train_ws_bytes, void *stream);
+
 /* Record two caller-created hipEvent_t (passed as void*) around the dominant
  * kernel of every later forward on this handle (the gate kernel, or the gate
  * GEMM on the batched path): ev_start before it, ev_stop after it, on the

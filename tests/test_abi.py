@@ -179,3 +179,66 @@ def test_valid_call_without_a_gpu_reports_hip_error(fake):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; this checks the no-device path")
     assert fake.fwd() == S.SFFN_ERR_HIP
+
+
+# ---------------------------------------------------------------------------
+# Training entry points
+# ---------------------------------------------------------------------------
+TRAIN_WS = 0x7E0000000000  # never dereferenced
+
+
+def test_train_workspace_bytes():
+    assert S.sffn_train_workspace_bytes(S.sffn_shape(0, 100, 0, 4, 1)) == 0
+    a = S.sffn_train_workspace_bytes(S.make_shape(64, 100, 0, 4, "bf16"))
+    b = S.sffn_train_workspace_bytes(S.make_shape(2048, 5632, 0, 64, "bf16"))
+    assert 0 < a < b and a % 256 == 0
+
+
+def _train_calls(fake, mode=S.SFFN_TOPK, k=5, tau=0.5, n=2, cap=8, sv=None, ws=TRAIN_WS, wsb=None, x=0x60000,
+                 y=0x70000, dy=0x90000, dx=0xA0000, dws=(0xB0000, 0xC0000, 0xD0000), w=None):
+    P = ctypes.c_void_p
+    if wsb is None:
+        wsb = S.sffn_train_workspace_bytes(fake.sh)
+    if sv is None:
+        sv = S.sffn_saved(cap, 0xE0000, 0xE1000, 0xE2000, 0xE3000)
+    w = w or fake.w
+    f = S.lib().sffn_forward_train(P(fake.h), P(x), n, ctypes.byref(w), mode, tau, k, P(y), ctypes.byref(sv),
+                                   P(ws), wsb, None)
+    b = S.lib().sffn_backward(P(fake.h), P(x), P(dy), n, ctypes.byref(w), mode, tau, k, ctypes.byref(sv), P(dx),
+                              P(dws[0]), P(dws[1]), P(dws[2]), P(ws), wsb, None)
+    return f, b
+
+
+def test_train_entry_points_reject_bad_arguments(fake):
+    E, W, U = S.SFFN_ERR_INVALID_ARG, S.SFFN_ERR_WORKSPACE, S.SFFN_ERR_UNSUPPORTED
+    assert _train_calls(fake, cap=4) == (E, E)              # Top-K needs cap >= k
+    assert _train_calls(fake, cap=0) == (E, E)
+    assert _train_calls(fake, cap=101) == (E, E)            # above d_ff
+    assert _train_calls(fake, mode=S.SFFN_TOPK_2_8, cap=25) == (E, E)   # 2:8 keeps 12 x 2 + 2 = 26 of 100
+    assert _train_calls(fake, mode=S.SFFN_TOPK_2_8, cap=26, n=0) == (S.SFFN_OK, S.SFFN_OK)
+    assert _train_calls(fake, mode=S.SFFN_DENSE_SILU, cap=99) == (E, E)
+    assert _train_calls(fake, mode=S.SFFN_THRESHOLD, tau=math.nan) == (E, E)
+    assert _train_calls(fake, mode=S.SFFN_TOPP, tau=1.5) == (E, E)
+    assert _train_calls(fake, mode=7) == (E, E)
+    assert _train_calls(fake, mode=S.SFFN_LOPA) == (U, U)
+    assert _train_calls(fake, n=9) == (E, E)
+    assert _train_calls(fake, sv=S.sffn_saved(8, 0xE0000, 0, 0xE2000, 0xE3000)) == (E, E)
+    assert _train_calls(fake, sv=S.sffn_saved(8, 0xE0001, 0xE1000, 0xE2000, 0xE3000)) == (E, E)
+    assert _train_calls(fake, w=S.sffn_weights(None, 0x20000, 0x30000, 0x40000, 0x50000)) == (E, E)
+    assert _train_calls(fake, ws=0) == (W, W)
+    assert _train_calls(fake, ws=TRAIN_WS + 16) == (W, W)
+    assert _train_calls(fake, wsb=S.sffn_train_workspace_bytes(fake.sh) - 1) == (W, W)
+    assert _train_calls(fake, x=0x60008) == (E, E)
+    assert _train_calls(fake, y=0)[0] == E
+    assert _train_calls(fake, dy=0)[1] == E
+    assert _train_calls(fake, dx=0xA0004)[1] == E
+    assert _train_calls(fake, dws=(0xB0000, 0, 0xD0000))[1] == E
+    assert _train_calls(fake, n=0) == (S.SFFN_OK, S.SFFN_OK)
+
+
+def test_train_entry_points_need_bf16():
+    f = _Fake(dtype="f32")
+    try:
+        assert _train_calls(f) == (S.SFFN_ERR_UNSUPPORTED, S.SFFN_ERR_UNSUPPORTED)
+    finally:
+        S.sffn_destroy(f.h)

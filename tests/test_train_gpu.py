@@ -1,0 +1,246 @@
+"""Training forward (stored activations) and backward on the GPU, through the
+C ABI, against the oracle (MoC's masked activation storage: "Mixture-of-
+Channels" blog summary, "Dentro il 'mixture'").
+
+Parity rule:
+  * stored sets: each token's stored channels equal the oracle's kept set
+    outside the band of the forward's parity rule (the dense shifted ReLU
+    stores the channels with z > tau, band |z - tau| <= 1e-5); listed
+    ascending, in range, cnt = list length;
+  * stored z and u: within 1e-4 of max(1, max |value|) of the oracle's fp64
+    values (fp32 accumulation of exact bf16 products);
+  * y, dx, dW_gate, dW_up, dW_down: max-abs error over max-abs value at most
+    2e-2 (bf16 operands of the MFMA products, as on the batched forward),
+    against the oracle evaluated on the GPU's own stored set.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_gated_gate_amd import inputs
+from activation_sparse_gated_gate_amd import sffn as S
+from gpu_harness import dev, oracle_forward, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+NAMES = ("dx", "dw_gate", "dw_up", "dw_down")
+
+
+def cap_for(mode, f, k):
+    if mode == "topk":
+        return k
+    if mode == "topk_2_8":
+        return (f // 8) * 2 + min(f % 8, 2)
+    return f
+
+
+def run_train(lay, x, dy, mode, tau=0.0, k=0, cap=None, dw_init=0.0, backward_calls=1):
+    n, d = x.shape
+    f = lay.d_ff
+    cap = cap or cap_for(mode, f, k)
+    ffn = S.SparseFFN(d, f, max(n, 1), "bf16")
+    w = S.SparseFFN.weights(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down))
+    xt, dyt = dev(x), dev(dy)
+    nan = float("nan")
+    y = torch.full((n, d), nan, dtype=torch.float32, device="cuda")
+    cnt = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    idx = torch.full((n, cap), -7, dtype=torch.int32, device="cuda")
+    z = torch.full((n, cap), nan, dtype=torch.float32, device="cuda")
+    u = torch.full((n, cap), nan, dtype=torch.float32, device="cuda")
+    sv = S.SparseFFN.saved(cap, cnt, idx, z, u)
+    ffn.forward_train(xt, w, mode, y, sv, tau=tau, k=k)
+    dx = torch.full((n, d), nan, dtype=torch.float32, device="cuda")
+    dws = [torch.full((f, d), dw_init, dtype=torch.float32, device="cuda") for _ in range(3)]
+    for _ in range(backward_calls):
+        ffn.backward(xt, dyt, w, mode, sv, dx, *dws, tau=tau, k=k)
+    torch.cuda.synchronize()
+    out = dict(y=y, cnt=cnt, idx=idx, z=z, u=u, dx=dx, dw_gate=dws[0], dw_up=dws[1], dw_down=dws[2])
+    out = {key: v.cpu().numpy() for key, v in out.items()}
+    out["cap"] = cap
+    return out
+
+
+def stored_sets(got, n, f):
+    sets = np.zeros((n, f), dtype=bool)
+    for t in range(n):
+        c = int(got["cnt"][t])
+        assert 0 <= c <= got["cap"], f"token {t}: count {c} (cap {got['cap']})"
+        row = got["idx"][t, :c]
+        assert np.all((row >= 0) & (row < f)), f"token {t}: stored index out of range"
+        assert np.all(np.diff(row) > 0), f"token {t}: stored list not strictly ascending"
+        sets[t, row] = True
+    return sets
+
+
+def rel_err(a, b):
+    scale = float(np.max(np.abs(b))) if b.size else 0.0
+    err = float(np.max(np.abs(a - b))) if b.size else 0.0
+    return err / scale if scale > 0 else err
+
+
+def check_forward(lay, x, mode, tau, k, got, tokens=None):
+    """Stored sets, z, u and y of the tokens `tokens` (all by default)."""
+    n = x.shape[0]
+    tokens = np.arange(n) if tokens is None else np.asarray(tokens)
+    xs = x[tokens]
+    ref = oracle_forward(lay, xs, mode, tau=tau, k=k)
+    kept = oracle.saved_set(mode, ref, tau).astype(bool)
+    band = np.abs(ref.z - tau) <= oracle.BAND if mode == "dense_relu" else ref.band
+    sets = stored_sets(got, n, lay.d_ff)[tokens]
+    outside = (sets ^ kept) & ~band
+    assert not outside.any(), f"{int(outside.sum())} stored-set mismatches outside the band"
+    u_ref = oracle.up(xs, lay.w_up, np.ones_like(kept, dtype=np.uint8), np.ones(kept.shape), False)
+    for j, t in enumerate(tokens):
+        c = int(got["cnt"][t])
+        row = got["idx"][t, :c]
+        for name, ref_v in (("z", ref.z), ("u", u_ref)):
+            if c == 0:
+                continue
+            err = np.max(np.abs(got[name][t, :c] - ref_v[j, row]))
+            scale = max(1.0, float(np.max(np.abs(ref_v[j]))))
+            assert err <= 1e-4 * scale, f"token {t}: stored {name} error {err:.3e}"
+    y_ref = oracle.forward_with_mask(xs, lay.w_up, lay.w_down, ref.g, sets.astype(np.uint8))
+    assert np.all(np.isfinite(got["y"][tokens]))
+    ry = rel_err(got["y"][tokens], y_ref)
+    assert ry <= TOL, f"y rel err {ry:.3e}"
+    return sets, int((sets ^ kept).sum()), int(band.sum()), ry
+
+
+def check_backward(lay, x, dy, mode, tau, sets, got, dw_init=0.0, calls=1):
+    gr = oracle.backward(mode, x, dy, lay.w_gate, lay.w_up, lay.w_down, sets.astype(np.uint8), tau)
+    errs = {}
+    for name in NAMES:
+        g = got[name]
+        assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+        if name != "dx":
+            g = (g - dw_init) / calls
+        errs[name] = rel_err(g, gr[name])
+        assert errs[name] <= TOL, f"{name} rel err {errs[name]:.3e}"
+    return errs
+
+
+MODES = [("threshold", 0.9, 0), ("topk", 0.0, 150), ("topk_2_8", 0.0, 0), ("topp", 0.5, 0),
+         ("dense_relu", 0.3, 0), ("dense_silu", 0.0, 0)]
+
+
+@pytest.mark.parametrize("mode,tau,k", MODES)
+@pytest.mark.parametrize("n", [1, 7, 12, 40, 130])
+def test_train_ragged(mode, tau, k, n):
+    """Every mode through every tile configuration of the small and middle
+    batch sizes, with ragged d_model (264) and d_ff (1000) and a token count
+    that is not a multiple of 8."""
+    d, f = 264, 1000
+    say(f"case train ragged d={d} F={f} n={n} {mode}")
+    lay = inputs.make_layer(5, d, f, "bf16")
+    x = inputs.make_x(5, n, d, "bf16")
+    dy = inputs.make_x(6, n, d, "bf16")
+    got = run_train(lay, x, dy, mode, tau=tau, k=k)
+    sets, flips, band, ry = check_forward(lay, x, mode, tau, k, got)
+    errs = check_backward(lay, x, dy, mode, tau, sets, got)
+    say(f"    band={band} flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+
+
+def test_train_moc_topk():
+    """The MoC layer (d 2048, d_ff 5632) with K = 704 over 64 tokens."""
+    wl = inputs.WORKLOADS["moc_topk_bf16_d2048_f5632"]
+    n, k = 64, 704
+    say(f"case train moc topk d={wl.d_model} F={wl.d_ff} n={n} K={k}")
+    lay = inputs.make_layer(0, wl.d_model, wl.d_ff, "bf16")
+    x = inputs.make_x(0, n, wl.d_model, "bf16")
+    dy = inputs.make_x(7, n, wl.d_model, "bf16")
+    got = run_train(lay, x, dy, "topk", k=k)
+    sets, flips, band, ry = check_forward(lay, x, "topk", 0.0, k, got)
+    errs = check_backward(lay, x, dy, "topk", 0.0, sets, got)
+    say(f"    band={band} flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+
+
+def test_train_large_batch_sampled():
+    """2048 tokens on the MoC layer (256 x 256 tiles, weight gradients over
+    K = 2048): y and dx checked on sampled tokens (a token's own forward and
+    dx depend on no other token), the weight gradients on sampled channels
+    (the gradient row of channel i depends only on the (t, i) entries of the
+    stored set), all against the oracle."""
+    wl = inputs.WORKLOADS["moc_topk_bf16_d2048_f5632"]
+    n, k = 2048, 704
+    d, f = wl.d_model, wl.d_ff
+    say(f"case train moc topk sampled d={d} F={f} n={n} K={k}")
+    lay = inputs.make_layer(0, d, f, "bf16")
+    x = inputs.make_x(0, n, d, "bf16")
+    dy = inputs.make_x(8, n, d, "bf16")
+    got = run_train(lay, x, dy, "topk", k=k)
+    toks = np.array([0, 1, 777, 1500, 2047])
+    sets_s, flips, band, ry = check_forward(lay, x, "topk", 0.0, k, got, tokens=toks)
+    sets = stored_sets(got, n, f)
+    for j, t in enumerate(toks):
+        gr = oracle.backward("topk", x[t:t + 1], dy[t:t + 1], lay.w_gate, lay.w_up, lay.w_down,
+                             sets[t:t + 1].astype(np.uint8))
+        e = rel_err(got["dx"][t:t + 1], gr["dx"])
+        assert e <= TOL, f"dx token {t}: {e:.3e}"
+    chans = np.array([0, 3, 1000, 2817, 5631])
+    sub = sets[:, chans].astype(np.uint8)
+    gr = oracle.backward("topk", x, dy, lay.w_gate[chans], lay.w_up[chans], lay.w_down[chans], sub)
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        e = rel_err(got[name][chans], gr[name])
+        assert e <= TOL, f"{name} sampled rows: {e:.3e}"
+    say(f"    sampled: flips={flips} y={ry:.2e}")
+
+
+def test_weight_gradients_accumulate():
+    """dW is added into: two backward calls over a buffer holding 0.25 give
+    0.25 + 2 dW on the stored channels' rows and leave every other row at
+    0.25 exactly."""
+    d, f, n, k = 136, 333, 20, 9
+    say(f"case train accumulate d={d} F={f} n={n} K={k}")
+    lay = inputs.make_layer(9, d, f, "bf16")
+    x = inputs.make_x(9, n, d, "bf16")
+    dy = inputs.make_x(10, n, d, "bf16")
+    got = run_train(lay, x, dy, "topk", k=k, dw_init=0.25, backward_calls=2)
+    sets, _, _, _ = check_forward(lay, x, "topk", 0.0, k, got)
+    check_backward(lay, x, dy, "topk", 0.0, sets, got, dw_init=0.25, calls=2)
+    untouched = ~sets.any(axis=0)
+    assert untouched.any()
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(got[name][untouched] == np.float32(0.25)), name
+
+
+def test_no_channel_kept():
+    """A threshold above every z keeps nothing: cnt = 0, y = 0, dx = 0 and
+    the weight gradients untouched."""
+    d, f, n = 64, 100, 10
+    say("case train empty set")
+    lay = inputs.make_layer(11, d, f, "bf16")
+    x = inputs.make_x(11, n, d, "bf16")
+    dy = inputs.make_x(12, n, d, "bf16")
+    got = run_train(lay, x, dy, "threshold", tau=1e3, dw_init=-1.5)
+    assert np.all(got["cnt"] == 0)
+    assert np.all(got["y"] == 0) and np.all(got["dx"] == 0)
+    for name in ("dw_gate", "dw_up", "dw_down"):
+        assert np.all(got[name] == np.float32(-1.5)), name
+
+
+def test_small_cap_truncates_and_counts():
+    """A threshold forward whose tokens keep more channels than cap reports
+    the true count and stores the first cap channels; the backward then runs
+    over the stored ones."""
+    d, f, n, cap = 64, 300, 9, 20
+    say(f"case train cap {cap}")
+    lay = inputs.make_layer(13, d, f, "bf16")
+    x = inputs.make_x(13, n, d, "bf16")
+    dy = inputs.make_x(14, n, d, "bf16")
+    tau = 0.0
+    got = run_train(lay, x, dy, "threshold", tau=tau, cap=cap)
+    ref = oracle_forward(lay, x, "threshold", tau=tau)
+    counts = ref.mask.sum(axis=1)
+    assert np.all(counts > cap)
+    outside = ~ref.band.any(axis=1)
+    assert np.array_equal(got["cnt"][outside], counts[outside])
+    stored = np.zeros((n, f), dtype=np.uint8)
+    for t in range(n):
+        row = got["idx"][t, :cap]
+        assert np.all(np.diff(row) > 0)
+        stored[t, row] = 1
+    check_backward(lay, x, dy, "threshold", tau, stored.astype(bool), dict(got, cap=cap))

@@ -212,7 +212,11 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
     } else if constexpr (EK == EPI_BWD) {
         // rows m are tokens, column n union entry n (channel U[n]); pad
         // columns up to a multiple of 8 get zeros (the dx products read dU
-        // and dZ in 8-wide chunks)
+        // and dZ in 8-wide chunks). Registers 4q .. 4q+3 of a lane hold four
+        // consecutive tokens of one column (32 x 32 tiles): their transposed
+        // values go out as one 8-byte store (tokens past M are zeros there,
+        // inside the row's padding to tp, a multiple of 8).
+        static_assert(MF == 32, "the packed transposed stores assume 32 x 32 tiles");
         const int padlim = (nlim + 7) & ~7;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -223,18 +227,29 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m >= M) continue;
-                    float du = 0.f, dz = 0.f, h = 0.f;
-                    if (live) bwd_values(epi, m, ch, acc[i][j][r], du, dz, h);
-                    epi.H[(size_t)m * epi.hld + n] = f2bf(du);
-                    epi.H2[(size_t)m * epi.hld + n] = f2bf(dz);
+                for (int q = 0; q < ACC / 4; ++q) {
+                    const int mb = rowof(i, 4 * q);  // multiple of 4
+                    if (mb >= M) continue;
+                    uint32_t pu[2] = {0u, 0u}, pz[2] = {0u, 0u}, ph[2] = {0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = mb + e;
+                        float du = 0.f, dz = 0.f, h = 0.f;
+                        if (live && m < M) bwd_values(epi, m, ch, acc[i][j][4 * q + e], du, dz, h);
+                        const uint16_t bu = f2bf(du), bz = f2bf(dz), bh = f2bf(h);
+                        if (m < M) {
+                            epi.H[(size_t)m * epi.hld + n] = bu;
+                            epi.H2[(size_t)m * epi.hld + n] = bz;
+                        }
+                        pu[e / 2] |= (uint32_t)bu << (16 * (e & 1));
+                        pz[e / 2] |= (uint32_t)bz << (16 * (e & 1));
+                        ph[e / 2] |= (uint32_t)bh << (16 * (e & 1));
+                    }
                     if (live) {
-                        const size_t o = (size_t)n * epi.tp + m;
-                        epi.DUT[o] = f2bf(du);
-                        epi.DZT[o] = f2bf(dz);
-                        epi.HT[o] = f2bf(h);
+                        const size_t o = (size_t)n * epi.tp + mb;
+                        *reinterpret_cast<uint2 *>(epi.DUT + o) = make_uint2(pu[0], pu[1]);
+                        *reinterpret_cast<uint2 *>(epi.DZT + o) = make_uint2(pz[0], pz[1]);
+                        *reinterpret_cast<uint2 *>(epi.HT + o) = make_uint2(ph[0], ph[1]);
                     }
                 }
             __builtin_amdgcn_sched_barrier(0);
@@ -769,6 +784,10 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // ===========================================================================
 // Host side
 // ===========================================================================
+// Batches above this build the Top-K / top-p union from the flags in a
+// separate pass instead of per-token atomics.
+constexpr int kUnionAtomicMaxTokens = 64;
+
 // Tile shape of k_mfma_dma: TM x TN 32 x 32 MFMA tiles per wavefront, WM x WN
 // wavefronts.
 struct Cfg {
@@ -947,13 +966,15 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         }
         if (ev1) hipEventRecord(ev1, st);
     }
-    // ---- Top-K: per-token select, its flags and the union of the flags ----
-    if (a.mode == SFFN_TOPK) {
-        if ((e = launch_topk_select_flags(keys, T, F, a.k, act, G, ubits, st)) != hipSuccess) return e;
-    }
-    // ---- top-p: per-token select by cumulative mass, flags and union ----
-    if (a.mode == SFFN_TOPP) {
-        if ((e = launch_topp_select_flags(keys, T, F, a.tau, act, G, ubits, st)) != hipSuccess) return e;
+    // ---- Top-K / top-p: per-token select, its flags and the union of the
+    // flags (above 64 tokens the union comes from one pass over the flags:
+    // per-token atomics on the same few bitmap words would serialise) ----
+    if (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP) {
+        uint32_t *ub = T > kUnionAtomicMaxTokens ? nullptr : ubits;
+        e = a.mode == SFFN_TOPK ? launch_topk_select_flags(keys, T, F, a.k, act, G, ub, st)
+                                : launch_topp_select_flags(keys, T, F, a.tau, act, G, ub, st);
+        if (e != hipSuccess) return e;
+        if (!ub && (e = launch_union_flags(act, T, F, ubits, st)) != hipSuccess) return e;
     }
     // ---- 2:8: the top 2 of each group of 8 keys, its flags and the union ----
     if (a.mode == SFFN_TOPK_2_8) {

@@ -149,6 +149,8 @@ hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hi
 hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st);
 hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, uint8_t *act, uint16_t *G,
                                    uint32_t *ubits, hipStream_t st);
+// The union bitmap from the flags act [T][F] (replaces whatever it holds).
+hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits, hipStream_t st);
 // Batched 2:8: act[t][i], bf16 gate values G[t][i] and the union bitmap from
 // the keys, keeping the top 2 of every aligned group of 8 channels.
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,

@@ -36,8 +36,9 @@ __global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ key
 // Batched: token t's flags act[t][i], the gate values the up GEMM reads
 // (G[t][i] = bf16 key where selected, else 0) and its bits of the union
 // bitmap, ORed in with one atomic per 32-bit word and wavefront (the bitmap is
-// all zero on entry: the down GEMM clears it after use), from the boundary r
-// of a select; the keys are kf (KPT > 0) or re-read from s.
+// all zero on entry: the down GEMM clears it after use; ubits null: no union
+// bits, k_union_flags builds the bitmap afterwards), from the boundary r of a
+// select; the keys are kf (KPT > 0) or re-read from s.
 template <int KPT>
 __device__ __forceinline__ void write_flags(const float *__restrict__ s, int F, int2 r,
                                             const float (&kf)[KPT > 0 ? KPT : 1], uint8_t *__restrict__ a,
@@ -61,7 +62,7 @@ __device__ __forceinline__ void write_flags(const float *__restrict__ s, int F, 
         m <<= i0 & 31;
 #pragma unroll
         for (int o = 1; o < 32 / KPT; o <<= 1) m |= __shfl_xor(m, o, 64);
-        if ((lane & (32 / KPT - 1)) == 0 && m) atomicOr(&ubits[i0 >> 5], m);
+        if (ubits && (lane & (32 / KPT - 1)) == 0 && m) atomicOr(&ubits[i0 >> 5], m);
     } else {
         for (int i0 = tid - lane; i0 < F; i0 += 1024) {
             const int i = i0 + lane;
@@ -74,7 +75,7 @@ __device__ __forceinline__ void write_flags(const float *__restrict__ s, int F, 
             }
             const unsigned long long b = __ballot(on);
             const uint32_t bits = (uint32_t)(b >> (lane & 32));
-            if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
+            if (ubits && (lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
         }
     }
 }
@@ -124,43 +125,74 @@ __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restr
     write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
 }
 
-// Batched 2:8 structured selection: block (x, t) takes channels
-// [256 x, 256 x + 256) of token t (32 whole groups of 8). The keys go through
-// LDS; each channel is ranked within its group by (key descending, channel
-// ascending) and the first 2 are kept: act[t][i], G[t][i] = bf16 key where
-// kept, else 0, and the union bits (one atomic per 32-bit word).
-__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int F, uint8_t *__restrict__ act,
-                                                  uint16_t *__restrict__ G, uint32_t *__restrict__ ubits)
+// Batched 2:8 structured selection: block (x, y) takes channels
+// [256 x, 256 x + 256) (32 whole groups of 8) of tokens [kNmTokens y, + kNmTokens).
+// Per token the keys go through LDS; each channel is ranked within its group
+// by (key descending, channel ascending) and the first 2 are kept: act[t][i],
+// G[t][i] = bf16 key where kept, else 0. The union bits of the block's tokens
+// are ORed in registers and added with one atomic per 32-bit word.
+constexpr int kNmTokens = 16;
+__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F,
+                                                  uint8_t *__restrict__ act, uint16_t *__restrict__ G,
+                                                  uint32_t *__restrict__ ubits)
 {
     constexpr int GROUP = 8, KEEP = 2;
-    __shared__ float kl[256];
-    const int t = blockIdx.y, i0 = blockIdx.x * 256, tid = threadIdx.x, lane = tid & 63;
+    __shared__ float kl[2][256];
+    const int i0 = blockIdx.x * 256, tid = threadIdx.x, lane = tid & 63;
     const int i = i0 + tid;
-    const size_t o = (size_t)t * F + i;
-    const float k = i < F ? keys[o] : 0.f;
-    kl[tid] = k;
-    __syncthreads();
     const int b = tid & ~(GROUP - 1);
-    int rank = 0;
+    uint32_t acc_bits = 0;
+    const int t0 = blockIdx.y * kNmTokens, t1 = min(T, t0 + kNmTokens);
+    for (int t = t0; t < t1; ++t) {
+        float *k2 = kl[t & 1];  // two buffers: one barrier per token
+        const size_t o = (size_t)t * F + i;
+        const float k = i < F ? keys[o] : 0.f;
+        k2[tid] = k;
+        __syncthreads();
+        int rank = 0;
 #pragma unroll
-    for (int e = 0; e < GROUP; ++e) {
-        const float v = kl[b + e];
-        rank += i0 + b + e < F && (v > k || (v == k && b + e < tid));
+        for (int e = 0; e < GROUP; ++e) {
+            const float v = k2[b + e];
+            rank += i0 + b + e < F && (v > k || (v == k && b + e < tid));
+        }
+        const bool on = i < F && rank < KEEP;
+        if (i < F) {
+            act[o] = on;
+            G[o] = on ? f2bf(k) : (uint16_t)0;
+        }
+        const unsigned long long m = __ballot(on);
+        acc_bits |= (uint32_t)(m >> (lane & 32));
     }
-    const bool on = i < F && rank < KEEP;
-    if (i < F) {
-        act[o] = on;
-        G[o] = on ? f2bf(k) : (uint16_t)0;
-    }
-    const unsigned long long m = __ballot(on);
-    const uint32_t bits = (uint32_t)(m >> (lane & 32));
-    if ((lane & 31) == 0 && bits) atomicOr(&ubits[i >> 5], bits);
+    if ((lane & 31) == 0 && acc_bits) atomicOr(&ubits[i >> 5], acc_bits);
+}
+
+// The union bitmap from the flags of T tokens: channel i (one thread) is in
+// it when some act[t][i] is set; the scan stops at the first such token. Each
+// wavefront writes its 64 channels' two words (one writer per word).
+__global__ __launch_bounds__(256) void k_union_flags(const uint8_t *__restrict__ act, int T, int F,
+                                                     uint32_t *__restrict__ ubits)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
+    bool on = false;
+    if (i < F)
+        for (int t = 0; t < T && !on; ++t) on = act[(size_t)t * F + i] != 0;
+    const unsigned long long b = __ballot(on);
+    const int w = (i - lane) / 32, words = (F + 31) / 32;
+    if (lane == 0 && w < words) ubits[w] = (uint32_t)b;
+    if (lane == 32 && w + 1 < words) ubits[w + 1] = (uint32_t)(b >> 32);
+}
+
+hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_union_flags, dim3((F + 255) / 256), dim3(256), 0, st, act, T, F, ubits);
+    return hipGetLastError();
 }
 
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
                            hipStream_t st)
 {
-    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, T), dim3(256), 0, st, keys, F, act, G, ubits);
+    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + kNmTokens - 1) / kNmTokens), dim3(256), 0, st, keys,
+                       T, F, act, G, ubits);
     return hipGetLastError();
 }
 

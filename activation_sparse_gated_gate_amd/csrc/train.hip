@@ -61,17 +61,16 @@ hipError_t launch_save(const float *zd, const float *ud, const uint8_t *act, int
     return hipGetLastError();
 }
 
-// ZU = (NaN, 0) everywhere (every channel off), the union bitmap cleared, and
-// token columns [T, tp) of the first F rows of the transposed buffers zeroed
-// (the weight-gradient products read whole 8-token chunks).
-__global__ __launch_bounds__(256) void k_bwd_clear(float2 *__restrict__ ZU, size_t TF, uint32_t *__restrict__ ubits,
-                                                   int words, uint16_t *__restrict__ dut, uint16_t *__restrict__ dzt,
-                                                   uint16_t *__restrict__ ht, int F, int T, int tp)
+// ZU = (NaN, 0) everywhere (every channel off), and token columns [T, tp) of
+// the first F rows of the transposed buffers zeroed (the weight-gradient
+// products read whole 8-token chunks).
+__global__ __launch_bounds__(256) void k_bwd_clear(float2 *__restrict__ ZU, size_t TF, uint16_t *__restrict__ dut,
+                                                   uint16_t *__restrict__ dzt, uint16_t *__restrict__ ht, int F, int T,
+                                                   int tp)
 {
     const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (size_t)gridDim.x * blockDim.x;
     const float2 off = make_float2(__uint_as_float(0x7fc00000u), 0.f);
     for (size_t e = g; e < TF; e += stride) ZU[e] = off;
-    for (size_t w = g; w < (size_t)words; w += stride) ubits[w] = 0u;
     const int padw = tp - T;
     if (padw > 0)
         for (size_t e = g; e < (size_t)F * padw; e += stride) {
@@ -82,11 +81,11 @@ __global__ __launch_bounds__(256) void k_bwd_clear(float2 *__restrict__ ZU, size
         }
 }
 
-// Token t (one block): its stored (z, u) into ZU[t][i] and its channels into
-// the union bitmap. Channel indices outside [0, F) are skipped.
+// Token t (one block): its stored (z, u) into ZU[t][i]. Channel indices
+// outside [0, F) are skipped.
 __global__ __launch_bounds__(256) void k_bwd_scatter(const int32_t *__restrict__ cnt, const int32_t *__restrict__ idx,
                                                      const float *__restrict__ z, const float *__restrict__ u, int cap,
-                                                     int F, float2 *__restrict__ ZU, uint32_t *__restrict__ ubits)
+                                                     int F, float2 *__restrict__ ZU)
 {
     const int t = blockIdx.x;
     const int c = min(cnt[t], cap);
@@ -95,8 +94,29 @@ __global__ __launch_bounds__(256) void k_bwd_scatter(const int32_t *__restrict__
         const int i = idx[o];
         if (i < 0 || i >= F) continue;
         ZU[(size_t)t * F + i] = make_float2(z[o], u[o]);
-        atomicOr(&ubits[i >> 5], 1u << (i & 31));
     }
+}
+
+// The union bitmap: channel i (one thread) is in it when some token stored
+// it, i.e. some ZU[t][i].x is not NaN; the scan stops at the first such
+// token. Each wavefront writes its 64 channels' two words (no atomics: every
+// word has one writer).
+__global__ __launch_bounds__(256) void k_bwd_union(const float2 *__restrict__ ZU, int T, int F, int words,
+                                                   uint32_t *__restrict__ ubits)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
+    bool on = false;
+    if (i < F) {
+        const float *zc = reinterpret_cast<const float *>(ZU) + 2 * (size_t)i;
+        for (int t = 0; t < T && !on; ++t) {
+            const float v = zc[2 * (size_t)t * F];
+            on = v == v;
+        }
+    }
+    const unsigned long long b = __ballot(on);
+    const int w = (i - lane) / 32;
+    if (lane == 0 && w < words) ubits[w] = (uint32_t)b;
+    if (lane == 32 && w + 1 < words) ubits[w + 1] = (uint32_t)(b >> 32);
 }
 
 // The ascending union list from the bitmap: one block of 1024 threads, each
@@ -152,8 +172,9 @@ hipError_t launch_bwd_setup(const Saved &sv, int T, int F, int d, int tp, float2
     const int words = (F + 31) / 32;
     const size_t TF = (size_t)T * F;
     const int blocks = (int)std::min<size_t>(4096, (TF + 255) / 256 + 1);
-    hipLaunchKernelGGL(k_bwd_clear, dim3(blocks), dim3(256), 0, st, ZU, TF, ubits, words, dut, dzt, ht, F, T, tp);
-    hipLaunchKernelGGL(k_bwd_scatter, dim3(T), dim3(256), 0, st, sv.cnt, sv.idx, sv.z, sv.u, sv.cap, F, ZU, ubits);
+    hipLaunchKernelGGL(k_bwd_clear, dim3(blocks), dim3(256), 0, st, ZU, TF, dut, dzt, ht, F, T, tp);
+    hipLaunchKernelGGL(k_bwd_scatter, dim3(T), dim3(256), 0, st, sv.cnt, sv.idx, sv.z, sv.u, sv.cap, F, ZU);
+    hipLaunchKernelGGL(k_bwd_union, dim3((F + 255) / 256), dim3(256), 0, st, ZU, T, F, words, ubits);
     hipLaunchKernelGGL(k_bwd_list, dim3(1), dim3(1024), 0, st, ubits, words, uidx, ucount);
     hipLaunchKernelGGL(k_transpose_pad, dim3((tp + 63) / 64, (d + 63) / 64, 2), dim3(256), 0, st, x, dy, xt, dyt, T,
                        d, tp);

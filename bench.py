@@ -23,7 +23,8 @@ Prints one JSON line. Besides the contract fields it carries:
   sweep         every tau of the workload: sparsity, step time, tokens/s, HBM
                 fraction, and the speedup over this library's dense forward;
   points        the other workloads (tiny fp32 layer, LoPA ranks, Mixture-of-Channels
-                Top-K at 1/16/64 tokens, 70B-shaped prefill at 256/2048 tokens):
+                Top-K, 2:8 and top-p at 1/16/64 tokens, 70B-shaped prefill at 256/2048
+                tokens, and a 2048-token training step with masked activation storage):
                 tokens/s, HBM fraction on touched bytes or MFMA fraction on the
                 path's FLOPs, and the speedup over this library's dense forward;
   cpu_baseline  the CPU oracle (plain C, fp64, one thread) on a bounded sample.
@@ -63,7 +64,7 @@ def parse():
     p.add_argument("--no-points", action="store_true", help="skip the other workloads' points")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample length (0 = skip)")
     p.add_argument("--only", default="",
-                   help="comma list of point families to measure (tiny, lopa, moc, prefill); runs them even "
+                   help="comma list of point families to measure (tiny, lopa, moc, prefill, train); runs them even "
                         "with --no-sweep")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
@@ -152,6 +153,8 @@ def measure_points(args, dev, S, inputs, np, torch):
         out += points_moc(W, S, inputs, torch, dev, timed_union(torch), replicate)
     if want("prefill"):
         out += points_prefill(W, S, inputs, torch, dev, timed_union(torch), replicate)
+    if want("train"):
+        out += points_train(W, S, inputs, torch, dev, timed_union(torch))
     return out
 
 
@@ -292,6 +295,63 @@ def points_prefill(W, S, inputs, torch, dev, union, replicate):
                     "dense_us_per_step": round(de * 1e6, 2), "speedup_vs_dense": round(de / sp, 3),
                     "flop_ratio_vs_dense": round(3 * f / (f + 2 * na), 3)})
     del wlist, base
+    torch.cuda.empty_cache()
+    return out
+
+
+TRAIN_TOKENS = 2048
+
+
+def points_train(W, S, inputs, torch, dev, union):
+    """Training step on the MoC layer: the forward with masked activation
+    storage plus the backward, for a micro-batch of 2048 tokens, against the
+    same step in the dense SwiGLU mode (every channel stored)."""
+    out = []
+    wl = W["moc_topk_bf16_d2048_f5632"]
+    d, f, n = wl.d_model, wl.d_ff, TRAIN_TOKENS
+    lay = inputs.make_layer(0, d, f, "bf16")
+    w = S.SparseFFN.weights(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down))
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    xt = dev(inputs.make_x(0, n, d, "bf16"))
+    dyt = dev(inputs.make_x(1, n, d, "bf16"))
+    y = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    dx = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    dws = [torch.zeros(f, d, dtype=torch.float32, device="cuda") for _ in range(3)]
+
+    def step_time(mode, cap, k, steps=10, warmup=2):
+        cnt = torch.empty(n, dtype=torch.int32, device="cuda")
+        idx = torch.empty(n, cap, dtype=torch.int32, device="cuda")
+        z = torch.empty(n, cap, dtype=torch.float32, device="cuda")
+        u = torch.empty(n, cap, dtype=torch.float32, device="cuda")
+        sv = S.SparseFFN.saved(cap, cnt, idx, z, u)
+
+        def one():
+            ffn.forward_train(xt, w, mode, y, sv, k=k)
+            ffn.backward(xt, dyt, w, mode, sv, dx, *dws, k=k)
+
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            one()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    de = step_time("dense_silu", f, 0)
+    cases = [("topk", 704, 704), ("topk", 1408, 1408), ("topk_2_8", (f // 8) * 2 + min(f % 8, 2), 0)]
+    for mode, cap, k in cases:
+        na = union(ffn, xt, w, mode, y, k=k)
+        sp = step_time(mode, cap, k)
+        flops = 2 * n * d * (f + 8 * na)  # forward gate, up, down; backward dH, dx (2), dW (3)
+        out.append({"workload": wl.name, "tokens": n, "mode": "train_" + mode, "k": cap, "union": na,
+                    "union_frac": round(na / f, 4), "us_per_step": round(sp * 1e6, 2),
+                    "tokens_per_s": round(n / sp, 1), "flops": flops, "tflops": round(flops / sp / 1e12, 1),
+                    "mfma_frac": round(flops / sp / PEAK_BF16, 4), "dense_us_per_step": round(de * 1e6, 2),
+                    "speedup_vs_dense": round(de / sp, 3),
+                    "stored_bytes_per_token": 4 + 12 * cap, "dense_stored_bytes_per_token": 4 + 12 * f,
+                    "stored_ratio_vs_dense": round((4 + 12 * f) / (4 + 12 * cap), 2)})
+    del w, dws
     torch.cuda.empty_cache()
     return out
 

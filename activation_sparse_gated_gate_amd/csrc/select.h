@@ -267,8 +267,8 @@ namespace sffn {
 // significant bits, as exp is computed in fp32), so every sum is exact and
 // independent of order: Z = sum u (< 2^62 for d_ff <= 2^18) and the target
 // T = ceil(p * Z). The search is select_kth's with masses in place of counts:
-// 2048 value bins carrying a count and a mass each, and a wavefront finds the
-// bin where the mass from the top reaches T. Up to 64 candidates in that bin
+// 2048 value bins carrying a count and a mass each; a wavefront sums them to
+// Z and finds the bin where the mass from the top reaches T. Up to 64 candidates in that bin
 // are ranked by one wavefront, each summing the masses of the candidates
 // ahead of it; the boundary channel is the one whose prefix mass falls short
 // of T and reaches it with its own. A larger bin goes through four 8-bit
@@ -283,8 +283,7 @@ struct __align__(16) SelectMassLds {
     unsigned long long cand_w[CMAX];
     uint32_t cand_key[CMAX];
     int cand_idx[CMAX];
-    unsigned long long zred[16];
-    unsigned long long shm[2];  // mass above the crossing bin
+    unsigned long long shm[2];  // mass above the crossing bin; the target T
     float red[2][16];
     int sh[4];  // crossing bin, its count, gathered; then the result
     int scan_scratch[16];
@@ -359,16 +358,11 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
     auto mass_of = [&](float v) -> unsigned long long {
         return (unsigned long long)(expf(v - top) * 17592186044416.0f + 0.5f);  // 2^44
     };
-    unsigned long long zl = 0;
-    for_keys([&](int, float v) { zl += mass_of(v); });
-    zl = wave_sum_u64(zl);
-    if (lane == 0) L.zred[wave] = zl;
-    __syncthreads();
-    unsigned long long Z = 0;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) Z += L.zred[w];
-    unsigned long long T = (unsigned long long)ceil((double)p * (double)Z);
-    T = T < 1ull ? 1ull : T > Z ? Z : T;
+    // the target mass from the total Z (the sum of the bin masses below)
+    auto target = [&](unsigned long long Z) {
+        const unsigned long long T = (unsigned long long)ceil((double)p * (double)Z);
+        return T < 1ull ? 1ull : T > Z ? Z : T;
+    };
 
     // The channels equal to the key kth that the prefix needs, given the
     // mass `need` still missing, are the first ceil(need / u) of them in
@@ -417,7 +411,7 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
         return r;
     };
 
-    if (!(hi > lo)) return take_ties(f2key(hi), T);  // every key equal
+    if (!(hi > lo)) return take_ties(f2key(hi), target((unsigned long long)F << 44));  // every key equal: u = 2^44
     float scale = (float)NB / (hi - lo);
     if (!(scale < 1e30f)) scale = 0.f;  // range too narrow to scale: one bin, resolved below
     auto bin_of = [&](float v) {
@@ -437,7 +431,9 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
         const int b0 = NB - 32 - 32 * lane;
         unsigned long long tot = 0;
         for (int q = 0; q < 32; ++q) tot += L.mass[b0 + q];
+        const unsigned long long T = target(wave_sum_u64(tot));
         unsigned long long run = wave_incl_scan_u64(tot) - tot;
+        if (lane == 0) L.shm[1] = T;
         for (int q = 31; q >= 0; --q) {
             const unsigned long long m = L.mass[b0 + q];
             if (run < T && T <= run + m) {
@@ -451,7 +447,7 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
     }
     __syncthreads();
     const int bstar = L.sh[0], cnt = L.sh[1];
-    unsigned long long need = T - L.shm[0];  // in (0, mass of bin bstar]
+    unsigned long long need = L.shm[1] - L.shm[0];  // in (0, mass of bin bstar]
 
     // ---- stage 2a: few candidates, ranked by one wavefront ----
     if (cnt <= CMAX) {

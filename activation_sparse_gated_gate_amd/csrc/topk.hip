@@ -13,6 +13,8 @@
 // right after the select, to the keys the select holds, and writes the
 // batch's flags, gate values and union bitmap. Top-p (k_topp_*) finds the
 // same pair by cumulative softmax mass instead of a count (select_mass).
+#include <algorithm>
+
 #include "select.h"
 #include "sffn_internal.h"
 
@@ -126,13 +128,13 @@ __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restr
 }
 
 // Batched 2:8 structured selection: block (x, y) takes channels
-// [256 x, 256 x + 256) (32 whole groups of 8) of tokens [kNmTokens y, + kNmTokens).
+// [256 x, 256 x + 256) (32 whole groups of 8) of tokens [tpb y, tpb y + tpb).
 // Per token the keys go through LDS; each channel is ranked within its group
 // by (key descending, channel ascending) and the first 2 are kept: act[t][i],
 // G[t][i] = bf16 key where kept, else 0. The union bits of the block's tokens
-// are ORed in registers and added with one atomic per 32-bit word.
-constexpr int kNmTokens = 16;
-__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F,
+// are ORed in registers and added with one atomic per 32-bit word: tpb
+// tokens per block keep the atomics on each bitmap word at T / tpb.
+__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F, int tpb,
                                                   uint8_t *__restrict__ act, uint16_t *__restrict__ G,
                                                   uint32_t *__restrict__ ubits)
 {
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys
     const int i = i0 + tid;
     const int b = tid & ~(GROUP - 1);
     uint32_t acc_bits = 0;
-    const int t0 = blockIdx.y * kNmTokens, t1 = min(T, t0 + kNmTokens);
+    const int t0 = blockIdx.y * tpb, t1 = min(T, t0 + tpb);
     for (int t = t0; t < t1; ++t) {
         float *k2 = kl[t & 1];  // two buffers: one barrier per token
         const size_t o = (size_t)t * F + i;
@@ -191,8 +193,11 @@ hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits,
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
                            hipStream_t st)
 {
-    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + kNmTokens - 1) / kNmTokens), dim3(256), 0, st, keys,
-                       T, F, act, G, ubits);
+    // one token per block up to 255 tokens (enough blocks to fill the
+    // GPU), then up to 16, at most 128 atomics per word
+    const int tpb = T < 256 ? 1 : std::min(16, T / 128);
+    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + tpb - 1) / tpb), dim3(256), 0, st, keys, T, F, tpb,
+                       act, G, ubits);
     return hipGetLastError();
 }
 

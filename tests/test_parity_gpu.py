@@ -3,6 +3,8 @@
 Every case names itself before it touches the GPU. Workloads follow the
 seeded recipe in activation_sparse_gated_gate_amd/inputs.py.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -140,6 +142,26 @@ def test_topp_select_sizes_and_ties(f, n, tied):
                 for r in range(5):
                     kept = got.sets[t, r::5]
                     assert not np.any(~kept[:-1] & kept[1:]), f"token {t}: tie kept out of index order"
+
+
+@pytest.mark.parametrize("n", [1, 3, 12])
+@pytest.mark.parametrize("f", [700, 20000])
+def test_topp_all_keys_equal(n, f):
+    """A zero token makes every key SiLU(0) = 0: equal masses, so the kept
+    set is the first ceil(p d_ff) channels (ties in channel order). Token 1,
+    when present, is an ordinary one."""
+    d = 64
+    say(f"case top-p all keys equal F={f} n={n}")
+    lay = inputs.make_layer(35, d, f, "bf16")
+    x = inputs.make_x(35, n, d, "bf16")
+    x[0] = 0
+    for p in (0.25, 0.5):
+        ref = oracle_forward(lay, x, "topp", tau=p)
+        got = run_gpu(lay, x, "topp", tau=p, max_tokens=n)
+        compare(lay, x, "topp", ref, got)
+        want = np.zeros(f, dtype=bool)
+        want[:math.ceil(p * f)] = True
+        assert np.array_equal(got.sets[0], want)
 
 
 def test_topp_one_keeps_every_channel():

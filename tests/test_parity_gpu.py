@@ -245,6 +245,33 @@ def test_lopa_ragged(rank, n):
     compare(lay, x, "lopa", ref, got)
 
 
+@pytest.mark.parametrize("rank", [8, 264])
+@pytest.mark.parametrize("n", [1, 3])
+def test_lopa_ragged_f32(rank, n):
+    d, f = 136, 333
+    say(f"case lopa ragged f32 d={d} F={f} r={rank} n={n}")
+    lay = inputs.make_layer(14, d, f, "f32", rank=rank, with_gate=False)
+    x = inputs.make_x(14, n, d, "f32")
+    ref = oracle_forward(lay, x, "lopa", tau=0.5)
+    got = run_gpu(lay, x, "lopa", tau=0.5, max_tokens=8)
+    compare(lay, x, "lopa", ref, got)
+
+
+def test_lopa_consecutive_forwards_on_one_handle():
+    """Forwards with new tokens on the same handle (token counts that shrink
+    and grow) each match the oracle: nothing of t = x.A or of the selection
+    carries over between forwards."""
+    d, f, r = 520, 1001, 264
+    lay = inputs.make_layer(15, d, f, "bf16", rank=r, with_gate=False)
+    ffn = S.SparseFFN(d, f, 8, "bf16", r)
+    for seed, n in ((1, 4), (2, 4), (3, 1), (4, 7)):
+        say(f"case lopa consecutive seed={seed} n={n}")
+        x = inputs.make_x(seed, n, d, "bf16")
+        ref = oracle_forward(lay, x, "lopa", tau=0.5)
+        got = run_gpu(lay, x, "lopa", tau=0.5, ffn=ffn)
+        compare(lay, x, "lopa", ref, got)
+
+
 # ---------------------------------------------------------------------------
 # Degenerate cases of the method
 # ---------------------------------------------------------------------------

@@ -784,7 +784,7 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // ===========================================================================
 // Host side
 // ===========================================================================
-// Batches above this build the Top-K / top-p union from the flags in a
+// Above this many tokens the Top-K / top-p union comes from the flags in a
 // separate pass instead of per-token atomics.
 constexpr int kUnionAtomicMaxTokens = 64;
 

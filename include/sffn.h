@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
     SFFN_OK = 0,
     SFFN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad mode/k/n */
-    SFFN_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+    SFFN_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement */
     SFFN_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
     SFFN_ERR_WORKSPACE = -4    /* workspace null, misaligned or too small */
 } sffn_status;

@@ -244,3 +244,58 @@ def test_small_cap_truncates_and_counts():
         assert np.all(np.diff(row) > 0)
         stored[t, row] = 1
     check_backward(lay, x, dy, "threshold", tau, stored.astype(bool), dict(got, cap=cap))
+
+
+@pytest.mark.parametrize("mode,n", [("topk", 40), ("threshold", 12), ("topk_2_8", 130)])
+def test_training_step_graph_replay(mode, n):
+    """A captured training step (weight gradients cleared by fill kernels,
+    the forward with stored activations, the backward) replayed several times
+    equals the eager step bit for bit, with eager steps on other tokens in
+    between (so every buffer the step reads is rewritten by someone else)."""
+    d, f, k, tau = 264, 1000, 150, 0.9
+    say(f"case training graph replay {mode} n={n}")
+    lay = inputs.make_layer(16, d, f, "bf16")
+    cap = cap_for(mode, f, k)
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    w = S.SparseFFN.weights(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down))
+    xs = [dev(inputs.make_x(s, n, d, "bf16")) for s in (16, 17)]
+    dys = [dev(inputs.make_x(s, n, d, "bf16")) for s in (18, 19)]
+
+    def buffers():
+        return dict(y=torch.empty(n, d, dtype=torch.float32, device="cuda"),
+                    cnt=torch.empty(n, dtype=torch.int32, device="cuda"),
+                    idx=torch.empty(n, cap, dtype=torch.int32, device="cuda"),
+                    z=torch.empty(n, cap, dtype=torch.float32, device="cuda"),
+                    u=torch.empty(n, cap, dtype=torch.float32, device="cuda"),
+                    dx=torch.empty(n, d, dtype=torch.float32, device="cuda"),
+                    dwg=torch.empty(f, d, dtype=torch.float32, device="cuda"),
+                    dwu=torch.empty(f, d, dtype=torch.float32, device="cuda"),
+                    dwd=torch.empty(f, d, dtype=torch.float32, device="cuda"))
+
+    def step(b, x, dy):
+        sv = S.SparseFFN.saved(cap, b["cnt"], b["idx"], b["z"], b["u"])
+        for name in ("dwg", "dwu", "dwd"):
+            b[name].zero_()
+        ffn.forward_train(x, w, mode, b["y"], sv, tau=tau, k=k)
+        ffn.backward(x, dy, w, mode, sv, b["dx"], b["dwg"], b["dwu"], b["dwd"], tau=tau, k=k)
+
+    eager, other, graphed = buffers(), buffers(), buffers()
+    step(eager, xs[0], dys[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(graphed, xs[0], dys[0])
+    for _ in range(3):
+        for v in graphed.values():
+            v.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, v in eager.items():
+            if name in ("idx", "z", "u"):  # only each token's first cnt slots are defined
+                for t in range(n):
+                    c = int(eager["cnt"][t])
+                    assert torch.equal(graphed[name][t, :c], v[t, :c]), (name, t)
+            else:
+                assert torch.equal(graphed[name], v), name
+        step(other, xs[1], dys[1])
+        torch.cuda.synchronize()

@@ -175,18 +175,20 @@ def test_train_large_batch_sampled():
     toks = np.array([0, 1, 777, 1500, 2047])
     sets_s, flips, band, ry = check_forward(lay, x, "topk", 0.0, k, got, tokens=toks)
     sets = stored_sets(got, n, f)
+    errs = {"dx": 0.0}
     for j, t in enumerate(toks):
         gr = oracle.backward("topk", x[t:t + 1], dy[t:t + 1], lay.w_gate, lay.w_up, lay.w_down,
                              sets[t:t + 1].astype(np.uint8))
         e = rel_err(got["dx"][t:t + 1], gr["dx"])
         assert e <= TOL, f"dx token {t}: {e:.3e}"
+        errs["dx"] = max(errs["dx"], e)
     chans = np.array([0, 3, 1000, 2817, 5631])
     sub = sets[:, chans].astype(np.uint8)
     gr = oracle.backward("topk", x, dy, lay.w_gate[chans], lay.w_up[chans], lay.w_down[chans], sub)
     for name in ("dw_gate", "dw_up", "dw_down"):
-        e = rel_err(got[name][chans], gr[name])
-        assert e <= TOL, f"{name} sampled rows: {e:.3e}"
-    say(f"    sampled: flips={flips} y={ry:.2e}")
+        errs[name] = rel_err(got[name][chans], gr[name])
+        assert errs[name] <= TOL, f"{name} sampled rows: {errs[name]:.3e}"
+    say(f"    sampled: flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
 
 
 def test_weight_gradients_accumulate():

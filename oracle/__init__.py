@@ -273,11 +273,11 @@ def forward(mode: str, x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, *,
         mask, g, cum, kth, nxt = select_topp(z, tau)
         bnd = np.where(np.isfinite(nxt), 0.5 * (kth + nxt), -np.inf)
         band = np.abs(g - bnd[:, None]) <= BAND
-        for t in range(z.shape[0]):
-            if tau - cum[t, 0] <= BAND:
-                band[t] |= mask[t].astype(bool) & (g[t] == kth[t])
-            if cum[t, 1] - tau <= BAND and np.isfinite(nxt[t]):
-                band[t] |= ~mask[t].astype(bool) & (g[t] == nxt[t])
+        for tok in range(z.shape[0]):
+            if tau - cum[tok, 0] <= BAND:
+                band[tok] |= mask[tok].astype(bool) & (g[tok] == kth[tok])
+            if cum[tok, 1] - tau <= BAND and np.isfinite(nxt[tok]):
+                band[tok] |= ~mask[tok].astype(bool) & (g[tok] == nxt[tok])
     elif mode == "topk_2_8":
         mask, g, bound = select_nm(z, 2, 8)
         band = np.abs(g - bound) <= BAND

@@ -41,7 +41,8 @@ def _golden():
 
 
 def _eval(expr):
-    s = {"s0": 1.0 / (1.0 + math.exp(-1.0)), "s2": 3.0 / (1.0 + math.exp(-3.0))}
+    s = {"s0": 1.0 / (1.0 + math.exp(-1.0)), "s1": -1.5 / (1.0 + math.exp(1.5)),
+         "s2": 3.0 / (1.0 + math.exp(-3.0))}
     return float(eval(expr, {"__builtins__": {}}, s))
 
 
@@ -58,6 +59,8 @@ def test_golden_hand_worked(case):
         r = oracle.forward("topk", X, WU, WD, w_gate=WG, k=int(c["k"][0]))
     elif case == "dense_shift":
         r = oracle.forward("dense_relu", X, WU, WD, w_gate=WG, tau=float(c["tau"][0]), tau_f32=False)
+    elif case == "dense_silu":
+        r = oracle.forward("dense_silu", X, WU, WD, w_gate=WG)
     else:
         r = oracle.forward("threshold", X, WU, WD, w_gate=WG, tau=float(c["tau"][0]), tau_f32=False)
     assert list(np.nonzero(r.mask[0])[0]) == [int(v) for v in c["active"]]
@@ -148,6 +151,29 @@ def test_topk_all_channels_is_textbook_swiglu(dtype):
     zz = xv @ g.T
     ref = (zz / (1.0 + np.exp(-zz)) * (xv @ u.T)) @ dn
     np.testing.assert_allclose(r.y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", [inputs.F32, inputs.BF16])
+def test_dense_silu_is_textbook_swiglu(dtype):
+    """The dense SiLU mode is SwiGLU, (SiLU(xWg^T) * xWu^T) Wd, computed here
+    with library matmuls on fp64 copies of the same inputs. It is the
+    reference of the dense SiLU forward and of the speedup denominator, and
+    equals Top-K with K = d_ff and top-p with p = 1 (every channel kept)."""
+    d, f, n = 40, 96, 3
+    lay = _rand_layer(15, d, f, dtype)
+    x = inputs.make_x(15, n, d, dtype)
+    r = oracle.forward("dense_silu", x, lay.w_up, lay.w_down, w_gate=lay.w_gate)
+    assert r.mask.all() and not r.band.any()
+    xv, g, u, dn = _f64(x), _f64(lay.w_gate), _f64(lay.w_up), _f64(lay.w_down)
+    zz = xv @ g.T
+    np.testing.assert_allclose(r.g, zz / (1.0 + np.exp(-zz)), rtol=1e-14, atol=1e-15)
+    ref = (zz / (1.0 + np.exp(-zz)) * (xv @ u.T)) @ dn
+    np.testing.assert_allclose(r.y, ref, rtol=1e-12, atol=1e-12)
+    tk = oracle.forward("topk", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, k=f)
+    tp = oracle.forward("topp", x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=1.0)
+    assert tk.mask.all() and tp.mask.all()
+    np.testing.assert_allclose(tk.y, r.y, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(tp.y, r.y, rtol=1e-13, atol=1e-14)
 
 
 def test_threshold_below_min_is_dense():
@@ -306,6 +332,42 @@ def test_topp_is_topk_with_its_count():
     assert mask.all() and np.isneginf(nxt).all()
     mask, g, _, _, _ = oracle.select_topp(z, 1e-9)
     assert (mask.sum(axis=1) == 1).all() and all(mask[t, np.argmax(g[t])] for t in range(4))
+
+
+def test_topp_band_at_the_mass_boundary():
+    """Top-p's parity band holds a boundary channel whose inclusion changes a
+    prefix mass that lies within 1e-5 of p: the last kept channel when the
+    mass without it is within 1e-5 below p, the first dropped one when the
+    mass with the last kept one is within 1e-5 above p; nothing when both
+    masses are 5e-5 away and the keys are well apart. The prefix masses come
+    from numpy's softmax of the keys, not from the oracle."""
+    z = np.array([[0.3, 2.0, -0.5, 1.2, 0.8, 1.6]])
+    keys = z[0] / (1.0 + np.exp(-z[0]))
+    w = np.exp(keys - keys.max())
+    w /= w.sum()
+    order = np.argsort(-keys, kind="stable")  # distinct keys: channels 1, 5, 3, 4, 0, 2
+    assert list(order) == [1, 5, 3, 4, 0, 2]
+    c2 = w[order[:2]].sum()  # mass of the two largest keys
+    d, f = 1, 6
+    wg = z.T.copy()  # z_i = 1 * wg[i][0]
+    x = np.ones((1, d))
+    wu, wd = np.ones((f, d)), np.ones((f, d))
+
+    def band_of(p):
+        r = oracle.forward("topp", x, wu, wd, w_gate=wg, tau=p, tau_f32=False)
+        return list(np.nonzero(r.mask[0])[0]), list(np.nonzero(r.band[0])[0])
+
+    # p just above the 2-prefix mass: keep 3; the mass without the 3rd is 5e-6 short of p
+    assert band_of(c2 + 5e-6) == ([1, 3, 5], [3])
+    # p just below it: keep 2; the mass with the 2nd is 5e-6 above p, so the 3rd may join
+    assert band_of(c2 - 5e-6) == ([1, 5], [3])
+    # 5e-5 away on either side: no band
+    assert band_of(c2 + 5e-5) == ([1, 3, 5], [])
+    assert band_of(c2 - 5e-5) == ([1, 5], [])
+    # the 1-prefix mass: the 2nd largest key (channel 5) sits on the boundary
+    c1 = w[order[0]]
+    assert band_of(c1 + 5e-6) == ([1, 5], [5])
+    assert band_of(c1 - 5e-6) == ([1], [5])
 
 
 def test_topp_rejects_bad_p():

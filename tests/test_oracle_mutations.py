@@ -4,8 +4,11 @@ test_oracle.py catch every one (all on the CPU).
 Each mutation edits one spot of sffn_oracle.c (a dropped term, a flipped sign
 or compare, a transposed operand, a wrong token index, a reversed order),
 builds it to a temporary shared object, and runs the pin suite against it in a
-child process through SFFN_ORACLE_SO. The suite must fail for each one. All
-mutated index expressions stay inside their arrays.
+child process through SFFN_ORACLE_SO. The mutations of PY_MUTATIONS edit the
+oracle package's Python part (the parity-band rule) instead: the child process
+executes the edited module source in place of the package before the pins run.
+The suite must fail for each one. All mutated index expressions stay inside
+their arrays.
 """
 import concurrent.futures
 import os
@@ -17,6 +20,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "sffn_oracle.c")
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PIN_SUITE = os.path.join(ROOT, "tests", "test_oracle.py")
 
 MUTATIONS = {
     "non_strict_threshold": ("mask[e] = z[e] > tau;", "mask[e] = z[e] >= tau;"),
@@ -56,12 +61,56 @@ MUTATIONS = {
     "bwd_dwd_drops_gate": ("h = g * u;", "h = u;"),
     "bwd_dx_drops_gate_term": (" + dz * elem(wg, w_dt, (long)i * d + k);", ";"),
     "bwd_dwu_wrong_token": ("dwu[(long)i * d + k] += du * xv;", "dwu[(long)i * d + k] += du * elem(x, x_dt, k);"),
+    "dense_silu_half": ("g[e] = act == 0 ? (v > 0.0 ? v : 0.0) : silu(z[e]);",
+                        "g[e] = act == 0 ? (v > 0.0 ? v : 0.0) : 0.5 * silu(z[e]);"),
+    "dense_silu_is_relu": ("g[e] = act == 0 ? (v > 0.0 ? v : 0.0) : silu(z[e]);",
+                           "g[e] = act == 0 ? (v > 0.0 ? v : 0.0) : (z[e] > 0.0 ? z[e] : 0.0);"),
     "bwd_dh_transposed": ("dh += elem(dy, dy_dt, (long)t * d + k) * elem(wd, w_dt, (long)i * d + k);",
                           "dh += elem(dy, dy_dt, (long)t * d + k) * elem(wd, w_dt, (long)(k % F) * d + i % d);"),
 }
 
 
+# Mistakes in the top-p parity band (oracle/__init__.py): a widened band, and
+# each of its two mass clauses dropped or turned the wrong way.
+PY_MUTATIONS = {
+    "topp_band_widened": ("if tau - cum[tok, 0] <= BAND:", "if tau - cum[tok, 0] <= 10 * BAND:"),
+    "topp_band_last_kept_dropped": ("if tau - cum[tok, 0] <= BAND:", "if False:"),
+    "topp_band_first_dropped_dropped": ("if cum[tok, 1] - tau <= BAND and np.isfinite(nxt[tok]):",
+                                        "if False and np.isfinite(nxt[tok]):"),
+    "topp_band_mass_sides_swapped": ("if tau - cum[tok, 0] <= BAND:", "if tau - cum[tok, 1] <= BAND:"),
+}
+
+# Child process of a Python mutation: the edited source runs as the oracle
+# package (same file name, so it finds the unedited C build), then the pins.
+_PY_RUNNER = """
+import sys, types
+path, src_file, suite = sys.argv[1], sys.argv[2], sys.argv[3]
+m = types.ModuleType("oracle")
+m.__file__ = src_file
+m.__path__ = []
+sys.modules["oracle"] = m
+exec(compile(open(path).read(), src_file, "exec"), m.__dict__)
+import pytest
+sys.exit(pytest.main(["-x", "-q", "-p", "no:cacheprovider", suite]))
+"""
+
+
+def _run_py(name):
+    old, new = PY_MUTATIONS[name]
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: anchor found {src.count(old)} times"
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "oracle_init.py")
+        open(path, "w").write(src.replace(old, new))
+        env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+        p = subprocess.run([sys.executable, "-c", _PY_RUNNER, path, PY_SRC, PIN_SUITE], cwd=ROOT, env=env,
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=300)
+        return name, p.returncode
+
+
 def _run(name):
+    if name in PY_MUTATIONS:
+        return _run_py(name)
     old, new = MUTATIONS[name]
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation {name}: anchor found {src.count(old)} times"
@@ -79,9 +128,19 @@ def _run(name):
 
 def test_every_planted_mistake_is_caught():
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        results = dict(ex.map(_run, sorted(MUTATIONS)))
+        results = dict(ex.map(_run, sorted(MUTATIONS) + sorted(PY_MUTATIONS)))
     survived = [k for k, rc in results.items() if rc == 0]
     assert not survived, f"pins did not catch: {survived}"
+
+
+def test_unmutated_python_oracle_passes_the_pins_through_the_runner():
+    """The Python-mutation runner itself: the unedited source passes."""
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "oracle_init.py")
+        open(path, "w").write(open(PY_SRC).read())
+        p = subprocess.run([sys.executable, "-c", _PY_RUNNER, path, PY_SRC, PIN_SUITE], cwd=ROOT,
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=300)
+        assert p.returncode == 0, p.stdout.decode()[-2000:]
 
 
 def test_unmutated_oracle_passes_the_pins():

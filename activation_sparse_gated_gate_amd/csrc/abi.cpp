@@ -45,8 +45,8 @@ Layout make_layout(const sffn_shape &s)
     L.uidx = take(F * 4);
     L.hbuf = take(batched ? (F * ntp * 4 > T * FP * 2 ? F * ntp * 4 : T * FP * 2) : F * ntp * 4);
     L.any = take(F);
-    L.part_words = (size_t)kDownGroupsMax * ntp * d;
-    L.part = take(L.part_words * 4);
+    L.part_slots = (size_t)kDownGroupsMax * ntp * d;
+    L.part = take(L.part_slots * 8);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(rows * F * 4);  // also for a training forward of <= 8 tokens (union path)
     L.ubits = take((size_t)L.words * 4);
@@ -99,12 +99,87 @@ static int max_kept(int mode, int F, int k)
     return F;
 }
 
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+sffn_status forward_checks(const sffn_shape &s, const void *x, int n_tokens, const sffn_weights *w, int mode,
+                           float tau, int k, const float *y, const int32_t *active_idx, const int32_t *active_cnt,
+                           const int32_t *union_cnt, const float *debug_z)
+{
+    if (!w) return SFFN_ERR_INVALID_ARG;
+    if (n_tokens < 0 || n_tokens > s.max_tokens) return SFFN_ERR_INVALID_ARG;
+    if (mode < SFFN_THRESHOLD || mode > SFFN_TOPP) return SFFN_ERR_INVALID_ARG;
+    if (!x || !y || !aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID_ARG;
+    if (!w->w_up || !w->w_down || !aligned16(w->w_up) || !aligned16(w->w_down))
+        return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_LOPA) {
+        if (s.rank <= 0) return SFFN_ERR_INVALID_ARG;
+        if (!w->lopa_a || !w->lopa_b || !aligned16(w->lopa_a) || !aligned16(w->lopa_b))
+            return SFFN_ERR_INVALID_ARG;
+    } else {
+        if (!w->w_gate || !aligned16(w->w_gate)) return SFFN_ERR_INVALID_ARG;
+    }
+    if (mode == SFFN_TOPK && (k < 1 || k > s.d_ff)) return SFFN_ERR_INVALID_ARG;
+    if (mode != SFFN_TOPK && mode != SFFN_TOPK_2_8 && std::isnan(tau)) return SFFN_ERR_INVALID_ARG;
+    if (mode == SFFN_TOPP && !(tau > 0.f && tau <= 1.f)) return SFFN_ERR_INVALID_ARG;
+    if ((active_idx && !aligned4(active_idx)) || (active_cnt && !aligned4(active_cnt)) ||
+        (union_cnt && !aligned4(union_cnt)) || (debug_z && !aligned4(debug_z)))
+        return SFFN_ERR_INVALID_ARG;
+    if (n_tokens > kDecodeMaxTokens) {
+        // The union path runs bf16 MFMA with a full gate.
+        if (s.dtype != SFFN_BF16 || mode == SFFN_LOPA) return SFFN_ERR_UNSUPPORTED;
+    }
+    return SFFN_OK;
+}
+
+FwdArgs make_fwd(const void *x, int n_tokens, const sffn_weights *w, int mode, float tau, int k, float *y,
+                 int32_t *active_idx, int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream)
+{
+    FwdArgs a;
+    a.x = x;
+    a.n = n_tokens;
+    a.w = *w;
+    a.mode = mode;
+    a.tau = tau;
+    a.k = k;
+    a.y = y;
+    a.active_idx = active_idx;
+    a.active_cnt = active_cnt;
+    a.union_cnt = union_cnt;
+    a.debug_z = debug_z;
+    a.stream = static_cast<hipStream_t>(stream);
+    return a;
+}
+
+// The one-time clears of the control block and union bitmap, before the
+// first forward on a handle. A forward captured into a graph enqueues them
+// into the graph and leaves the handle uninitialised: they run only when the
+// graph is replayed, so the next eager forward clears again.
+static hipError_t ensure_init(sffn_ctx &c, hipStream_t st)
+{
+    if (c.inited) return hipSuccess;
+    hipError_t e = launch_init(c, st);
+    if (e != hipSuccess) return e;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(st, &cs)) != hipSuccess) return e;
+    c.inited = cs == hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
+
+sffn_status forward_enqueue(sffn_ctx &c, const FwdArgs &a)
+{
+    if (ensure_init(c, a.stream) != hipSuccess) return SFFN_ERR_HIP;
+    const hipError_t e = a.n > kDecodeMaxTokens ? launch_batched(c, a) : launch_decode(c, a);
+    if (e != hipSuccess) {
+        c.inited = false;  // counters may be stale: re-zero on the next forward
+        return e == hipErrorNotSupported ? SFFN_ERR_UNSUPPORTED : SFFN_ERR_HIP;
+    }
+    return SFFN_OK;
+}
+
 }  // namespace sffn
 
 using namespace sffn;
-
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-static bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 extern "C" {
 
@@ -131,7 +206,7 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
     c->L = L;
     c->inited = false;
     c->n_cu = 0;
-    c->lds_max = 0;
+    c->spin_max = kSpinMaxDefault;
     c->ev_start = c->ev_stop = nullptr;
     *out = c;
     return SFFN_OK;
@@ -153,6 +228,13 @@ sffn_status sffn_set_profile_events(sffn_handle handle, void *ev_start, void *ev
     return SFFN_OK;
 }
 
+sffn_status sffn_set_spin_limit(sffn_handle handle, int polls)
+{
+    if (!handle) return SFFN_ERR_INVALID_ARG;
+    handle->spin_max = polls < -1 ? -1 : polls;
+    return SFFN_OK;
+}
+
 const char *sffn_status_string(int status)
 {
     switch (status) {
@@ -170,63 +252,17 @@ sffn_status sffn_forward(sffn_handle handle, const void *x, int n_tokens, const 
                          int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream)
 {
     // ---- validation: host only, nothing enqueued on failure ----
-    if (!handle || !w) return SFFN_ERR_INVALID_ARG;
-    const sffn_shape &s = handle->shape;
-    if (n_tokens < 0 || n_tokens > s.max_tokens) return SFFN_ERR_INVALID_ARG;
-    if (mode < SFFN_THRESHOLD || mode > SFFN_TOPP) return SFFN_ERR_INVALID_ARG;
-    if (!x || !y || !aligned16(x) || !aligned16(y)) return SFFN_ERR_INVALID_ARG;
-    if (!w->w_up || !w->w_down || !aligned16(w->w_up) || !aligned16(w->w_down))
-        return SFFN_ERR_INVALID_ARG;
-    if (mode == SFFN_LOPA) {
-        if (s.rank <= 0) return SFFN_ERR_INVALID_ARG;
-        if (!w->lopa_a || !w->lopa_b || !aligned16(w->lopa_a) || !aligned16(w->lopa_b))
-            return SFFN_ERR_INVALID_ARG;
-    } else {
-        if (!w->w_gate || !aligned16(w->w_gate)) return SFFN_ERR_INVALID_ARG;
-    }
-    if (mode == SFFN_TOPK && (k < 1 || k > s.d_ff)) return SFFN_ERR_INVALID_ARG;
-    if (mode != SFFN_TOPK && mode != SFFN_TOPK_2_8 && std::isnan(tau)) return SFFN_ERR_INVALID_ARG;
-    if (mode == SFFN_TOPP && !(tau > 0.f && tau <= 1.f)) return SFFN_ERR_INVALID_ARG;
-    if ((active_idx && !aligned4(active_idx)) || (active_cnt && !aligned4(active_cnt)) ||
-        (union_cnt && !aligned4(union_cnt)) || (debug_z && !aligned4(debug_z)))
-        return SFFN_ERR_INVALID_ARG;
-    if (n_tokens == 0) return SFFN_OK;
-    const bool batched = n_tokens > kDecodeMaxTokens;
-    if (batched) {
-        // The union path runs bf16 MFMA with a full gate.
-        if (s.dtype != SFFN_BF16 || mode == SFFN_LOPA) return SFFN_ERR_UNSUPPORTED;
-    }
+    if (!handle) return SFFN_ERR_INVALID_ARG;
+    const sffn_status v =
+        forward_checks(handle->shape, x, n_tokens, w, mode, tau, k, y, active_idx, active_cnt, union_cnt, debug_z);
+    if (v != SFFN_OK || n_tokens == 0) return v;
 
     // ---- device set-up (first forward only) ----
     if (handle->n_cu == 0) {
         if (device_setup(*handle) != hipSuccess) return SFFN_ERR_HIP;
     }
-    if (!batched && !decode_fits(*handle, n_tokens, mode)) return SFFN_ERR_UNSUPPORTED;
-
-    FwdArgs a;
-    a.x = x;
-    a.n = n_tokens;
-    a.w = *w;
-    a.mode = mode;
-    a.tau = tau;
-    a.k = k;
-    a.y = y;
-    a.active_idx = active_idx;
-    a.active_cnt = active_cnt;
-    a.union_cnt = union_cnt;
-    a.debug_z = debug_z;
-    a.stream = static_cast<hipStream_t>(stream);
-
-    if (!handle->inited) {
-        if (launch_init(*handle, a.stream) != hipSuccess) return SFFN_ERR_HIP;
-        handle->inited = true;
-    }
-    hipError_t e = batched ? launch_batched(*handle, a) : launch_decode(*handle, a);
-    if (e != hipSuccess) {
-        handle->inited = false;  // counters may be stale: re-zero on the next forward
-        return e == hipErrorNotSupported ? SFFN_ERR_UNSUPPORTED : SFFN_ERR_HIP;
-    }
-    return SFFN_OK;
+    return forward_enqueue(*handle, make_fwd(x, n_tokens, w, mode, tau, k, y, active_idx, active_cnt, union_cnt,
+                                             debug_z, stream));
 }
 
 size_t sffn_train_workspace_bytes(const sffn_shape *shape)
@@ -276,23 +312,8 @@ sffn_status sffn_forward_train(sffn_handle handle, const void *x, int n_tokens, 
     if (handle->n_cu == 0) {
         if (device_setup(*handle) != hipSuccess) return SFFN_ERR_HIP;
     }
-    FwdArgs a;
-    a.x = x;
-    a.n = n_tokens;
-    a.w = *w;
-    a.mode = mode;
-    a.tau = tau;
-    a.k = k;
-    a.y = y;
-    a.active_idx = nullptr;
-    a.active_cnt = nullptr;
-    a.union_cnt = nullptr;
-    a.debug_z = nullptr;
-    a.stream = static_cast<hipStream_t>(stream);
-    if (!handle->inited) {
-        if (launch_init(*handle, a.stream) != hipSuccess) return SFFN_ERR_HIP;
-        handle->inited = true;
-    }
+    const FwdArgs a = make_fwd(x, n_tokens, w, mode, tau, k, y, nullptr, nullptr, nullptr, nullptr, stream);
+    if (ensure_init(*handle, a.stream) != hipSuccess) return SFFN_ERR_HIP;
     const hipError_t e = launch_forward_train(*handle, a, to_saved(saved), static_cast<char *>(train_ws));
     if (e != hipSuccess) {
         handle->inited = false;

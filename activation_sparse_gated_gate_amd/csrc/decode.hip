@@ -87,32 +87,45 @@ __global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int
 }
 
 // ---------------------------------------------------------------------------
-// Cross-workgroup slots inside one launch. A slot holds the marker, all ones
-// (a NaN bit pattern no sum of finite products has), until its producer
-// writes it with a relaxed device-scope atomic store (global_store ... sc1);
-// the consumer polls it with device-scope atomic loads (global_load ... sc1)
-// and writes the marker back after reading. Each slot carries its own
+// Cross-workgroup slots inside one launch. A slot is 64 bits: a value in the
+// low half and the epoch of the forward that wrote it in the high half. The
+// producer writes it with a relaxed device-scope atomic store
+// (global_store ... sc1); the consumer polls it with device-scope atomic
+// loads until the epoch is the current forward's. Each slot carries its own
 // readiness, which per-location coherence alone makes sound: no counter, no
-// fence (a device-scope release fence writes back the whole L2 of an XCD). A
-// consumer only waits on workgroups of lower index that never wait;
-// workgroups are dispatched in index order on each XCD, so every wait ends.
-// The polls are bounded anyway (kSpinMax), after which the marker itself (a
-// NaN) is used.
+// fence (a device-scope release fence writes back the whole L2 of an XCD),
+// and nothing to re-mark, so a value left by an earlier forward is never taken
+// for a new one. The epoch is a device counter that the gate kernel, the
+// first kernel of every decode forward, advances; the next kernels read it,
+// so graph replays get fresh epochs too. A consumer only waits on workgroups
+// of lower index that never wait; workgroups are dispatched in index order on
+// each XCD, so every wait ends. The polls are bounded anyway: a consumer that
+// gives up writes NaN to its outputs and sets bit 0 of the workspace's sticky
+// error word.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kSlotMarker = 0xffffffffu;
-constexpr int kSpinMax = 1 << 18;
-
-__device__ __forceinline__ uint32_t ld_slot(const uint32_t *p)
+__device__ __forceinline__ uint64_t ld_slot(const uint64_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_slot(uint32_t *p, uint32_t v)
+__device__ __forceinline__ void st_slot(uint64_t *p, uint32_t epoch, float v)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This forward's epoch, read by one thread into LDS (the caller's next
+// barrier publishes it). The gate kernel that wrote it has completed, so a
+// plain (cached) load sees it; one load per workgroup, issued after the
+// caller's own loads, keeps it off the critical path and off a single memory
+// channel (an atomic load from every thread queues there).
+__device__ __forceinline__ void read_epoch(const int *ctrl, int tid, uint32_t *epoch_s)
+{
+    if (tid == 0)
+        *epoch_s = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // ---------------------------------------------------------------------------
-// Down kernel: the split-channel two-stage reduction in one launch.
+// Down kernel: the split-channel two-stage reduction in one launch, over
+// G = gridDim.y channel groups.
 // Stage 1: workgroup (s, g) takes output columns [128 s, 128 s + 128) and
 // channels [F g / G, F (g+1) / G). It lists that range's channels some token
 // selected (any[i]; every channel in the dense modes) in LDS in ascending
@@ -120,63 +133,61 @@ __device__ __forceinline__ void st_slot(uint32_t *p, uint32_t v)
 // read the 256-byte segments of those W_down rows, UNR rows per stream in
 // flight:  P[g][t][c] = sum_i h[i][t] * W_down[i][c]   (fixed order).
 // Stage 2: workgroup (s, G-1) sums P[0][t][c], ..., P[G-1][t][c] in that
-// order and writes y. The other groups publish their P in marker-tagged slots
-// (above), which the summing workgroup polls, reads and re-marks.
-// Only the G-1 groups' summing workgroups wait, on workgroups that never wait.
+// order and writes y. The other groups publish their P in epoch-tagged slots
+// (above), which the summing workgroup polls, 16 at a time.
 // ---------------------------------------------------------------------------
 template <typename TW, int NT, int UNR>
 __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, int d, int n,
                                               const uint8_t *__restrict__ any, int dense,
-                                              const float *__restrict__ hbuf, uint32_t *__restrict__ part,
-                                              float *__restrict__ y)
+                                              const float *__restrict__ hbuf, uint64_t *__restrict__ part,
+                                              float *__restrict__ y, int *__restrict__ ctrl, int spin_max)
 {
-    extern __shared__ __align__(16) char smem[];
-    int *list = reinterpret_cast<int *>(smem);
+    __shared__ uint16_t list[kDownRangeMax];
     __shared__ float red[4][NT][kDownSliceCols];
     __shared__ int scan_scratch[4];
     __shared__ int total;
+    __shared__ uint32_t epoch_s;
     const int s = blockIdx.x, g = blockIdx.y, G = gridDim.y;
-    const int cb = (int)(((long long)F * g) / G), ce = (int)(((long long)F * (g + 1)) / G);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int cb = F * g / G, ce = F * (g + 1) / G;  // F * G < 2^31 (F <= 262144, G <= 64)
 
-    // ---- channels of this group selected by some token, ascending ----
+    // ---- this group's selected channels, ascending (offsets from cb) ----
     const int len = ce - cb;
-    const int seg = (len + blockDim.x - 1) / blockDim.x;  // <= 32, fixed on the host
+    const int seg = (len + 255) / 256;  // <= 32: a group has at most kDownRangeMax channels
     const int i0 = cb + min(len, tid * seg), i1 = cb + min(len, tid * seg + seg);
     uint32_t sel = 0;  // bit k: channel i0 + k
     for (int i = i0; i < i1; ++i) sel |= (uint32_t)(dense != 0 || any[i] != 0) << (i - i0);
+    read_epoch(ctrl, tid, &epoch_s);
     const int local = __popc(sel);
     const int incl = block_incl_scan(local, scan_scratch);
     int pos = incl - local;
     while (sel) {
         const int b = __ffs(sel) - 1;
         sel &= sel - 1;
-        list[pos++] = i0 + b;
+        list[pos++] = (uint16_t)(i0 + b - cb);
     }
-    if (tid == blockDim.x - 1) total = incl;
+    if (tid == 255) total = incl;
     __syncthreads();
-    const int cnt = total;
-
-    const int wave = tid >> 6, lane = tid & 63;
+    const int m = total;
+    const uint32_t epoch = epoch_s;
+    // ---- stage 1: this group's rows, 256-byte segments ----
     const int rs = wave * 4 + (lane >> 4), c8 = lane & 15;
     const int col = s * kDownSliceCols + c8 * 8;
     const bool colok = col < d;
-
     float acc[NT][8];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[t][e] = 0.f;
-
     if (colok) {
-        for (int k0 = rs; k0 < cnt; k0 += 16 * UNR) {
+        for (int k0 = rs; k0 < m; k0 += 16 * UNR) {
             typename Ld8<TW>::raw qv[UNR];
             float hv[UNR][NT];
 #pragma unroll
             for (int u = 0; u < UNR; ++u) {
                 const int k = k0 + 16 * u;
-                if (k < cnt) {
-                    const int i = list[k];
+                if (k < m) {
+                    const int i = cb + (int)list[k];
                     qv[u] = Ld8<TW>::load(wd + (size_t)i * d + col);
 #pragma unroll
                     for (int t = 0; t < NT; ++t) hv[u][t] = hbuf[(size_t)i * kDecodeMaxTokens + t];
@@ -225,46 +236,49 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
             const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
             if (t < n && c0 + c < d) {
                 const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
-                st_slot(part + (size_t)g * gs + (size_t)t * d + c0 + c, __float_as_uint(v));
+                st_slot(part + (size_t)g * gs + (size_t)t * d + c0 + c, epoch, v);
             }
         }
         return;
     }
     // ---- stage 2: ordered sum over the groups ----
+    constexpr int B = 16;  // slots polled together (32 at once made the wait twice as long)
+    bool gave_up = false;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int e = tid + 256 * q;
         const int t = e / kDownSliceCols, c = e - t * kDownSliceCols;
         if (t < n && c0 + c < d) {
             const float own = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
-            uint32_t *p = part + (size_t)t * d + c0 + c;
+            const uint64_t *p = part + (size_t)t * d + c0 + c;
             float v = 0.f;
-            for (int g0 = 0; g0 < G - 1; g0 += 16) {
-                uint32_t b[16];
+            bool ok = true;
+            for (int g0 = 0; g0 < G - 1; g0 += B) {
+                uint64_t b[B];
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    b[u] = g0 + u < G - 1 ? ld_slot(p + (size_t)(g0 + u) * gs) : 0u;
-                for (int spin = 0; spin < kSpinMax; ++spin) {
-                    bool ready = true;
+                for (int u = 0; u < B; ++u) b[u] = g0 + u < G - 1 ? ld_slot(p + (size_t)(g0 + u) * gs) : 0u;
+                bool ready = false;
+                for (int spin = 0; spin <= spin_max; ++spin) {
+                    ready = true;
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) ready = ready && b[u] != kSlotMarker;
-                    if (ready) break;
+                    for (int u = 0; u < B; ++u) ready = ready && (g0 + u >= G - 1 || (uint32_t)(b[u] >> 32) == epoch);
+                    if (ready || spin == spin_max) break;
                     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        if (b[u] == kSlotMarker)
+                    for (int u = 0; u < B; ++u)
+                        if (g0 + u < G - 1 && (uint32_t)(b[u] >> 32) != epoch)
                             b[u] = ld_slot(p + (size_t)(g0 + u) * gs);
                 }
+                ok = ok && ready;
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    if (g0 + u < G - 1) {
-                        v += __uint_as_float(b[u]);
-                        st_slot(p + (size_t)(g0 + u) * gs, kSlotMarker);
-                    }
+                for (int u = 0; u < B; ++u)
+                    if (g0 + u < G - 1) v += __uint_as_float((uint32_t)b[u]);
             }
-            y[(size_t)t * d + c0 + c] = v + own;
+            y[(size_t)t * d + c0 + c] = ok ? v + own : __builtin_nanf("");
+            gave_up = gave_up || !ok;
         }
     }
+    if (gave_up) atomicOr(ctrl + kCtrlError, kErrDownWait);
 }
 
 // ---------------------------------------------------------------------------
@@ -340,19 +354,13 @@ static int lpr_for(int len)
 
 static int nt_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
-// 16 channel groups, more for very wide layers so that a thread of the list
-// prologue scans at most 32 channels of its group.
+// Channel groups of the down projection: 16, so that the summing workgroup
+// polls the 15 others' slots in one batch, and more for very wide layers so
+// that a group has at most kDownRangeMax channels.
 static int down_groups(const sffn_ctx &c)
 {
     const int F = c.shape.d_ff;
-    const int G = max(16, (F + 256 * 32 - 1) / (256 * 32));
-    return max(1, min(min(G, kDownGroupsMax), F));
-}
-
-static size_t down_lds(const sffn_ctx &c)
-{
-    const int F = c.shape.d_ff, G = down_groups(c);
-    return (size_t)4 * ((F + G - 1) / G + 1);
+    return max(1, min(F, max(16, (F + kDownRangeMax - 1) / kDownRangeMax)));
 }
 
 hipError_t device_setup(sffn_ctx &c)
@@ -360,30 +368,25 @@ hipError_t device_setup(sffn_ctx &c)
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int cu = 0, lds = 0;
+    int cu = 0;
     e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-    if (e != hipSuccess) return e;
     c.n_cu = cu > 0 ? cu : 1;
-    // Dynamic LDS stays within 64 KB per workgroup (static LDS comes on top).
-    c.lds_max = (size_t)min(lds, 65536) - 4096;
     return hipSuccess;
 }
 
-bool decode_fits(const sffn_ctx &c, int, int) { return down_lds(c) <= c.lds_max; }
-
-__global__ void k_fill_u32(uint32_t *__restrict__ p, size_t count, uint32_t v)
+__global__ void k_zero_u64(uint64_t *__restrict__ p, size_t count)
 {
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
-        p[i] = v;
+        p[i] = 0;
 }
 
 hipError_t launch_init(sffn_ctx &c, hipStream_t s)
 {
-    // the down projection's group slots start out holding their marker
-    hipLaunchKernelGGL(k_fill_u32, dim3(256), dim3(256), 0, s, reinterpret_cast<uint32_t *>(c.ws + c.L.part),
-                       c.L.part_words, kSlotMarker);
+    // slots start with epoch 0, which no forward uses (the gate kernel's
+    // epochs start at 1 and skip 0 when they wrap)
+    hipLaunchKernelGGL(k_zero_u64, dim3(256), dim3(256), 0, s, reinterpret_cast<uint64_t *>(c.ws + c.L.part),
+                       c.L.part_slots);
     hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
     hipLaunchKernelGGL(k_zero_ints, dim3(16), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ubits), c.L.words);
     return hipGetLastError();
@@ -429,6 +432,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     g.stream = st;
     g.ev_start = c.ev_start;
     g.ev_stop = c.ev_stop;
+    g.ctrl = reinterpret_cast<int *>(ws + c.L.ctrl);
     g.lpr = lpr_for(d);
     const bool ranked = a.mode == SFFN_TOPK || a.mode == SFFN_TOPP;  // keys, then a per-token select
     g.kind = dense ? DENSE : ranked ? KEYS : a.mode == SFFN_TOPK_2_8 ? SELECT_NM : SELECT_UP;
@@ -470,11 +474,11 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     }
 
     // ---- down projection: group partials and their ordered sum ----
-    uint32_t *part = reinterpret_cast<uint32_t *>(ws + c.L.part);
+    uint64_t *part = reinterpret_cast<uint64_t *>(ws + c.L.part);
     const int slices = (d + kDownSliceCols - 1) / kDownSliceCols;
-    const int G = down_groups(c);
-    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, G), dim3(256), down_lds(c), st, wdn, F, d, n, any,
-                       dense ? 1 : 0, hbuf, part, a.y);
+    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, down_groups(c)), dim3(256), 0, st, wdn, F, d, n, any,
+                       dense ? 1 : 0, hbuf, part, a.y, reinterpret_cast<int *>(ws + c.L.ctrl),
+                       c.spin_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
     // ---- optional outputs ----

@@ -37,8 +37,13 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
                                               int F, int mode, float tau,
                                               float *__restrict__ gsel, uint8_t *__restrict__ act,
                                               uint8_t *__restrict__ any, float *__restrict__ hbuf,
-                                              float *__restrict__ debug_z)
+                                              float *__restrict__ debug_z, int *__restrict__ ctrl)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        // this forward's epoch for the down projection's slots (never 0)
+        uint32_t e = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        __hip_atomic_store(ctrl + kCtrlEpoch, (int)(e == 0 ? 1u : e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     constexpr int SUB = 64 / LPR;
     constexpr int R = RowsPer<NT>::v;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -157,17 +162,17 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 template <typename TW, typename TX, int NT, int KIND>
 static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
                         const TW *xu, int d, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel,
-                        uint8_t *act, uint8_t *any, float *hbuf, float *dz)
+                        uint8_t *act, uint8_t *any, float *hbuf, float *dz, int *ctrl)
 {
     const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
 #define SFFN_G(LP)                                                                                               \
     do {                                                                                                         \
         if (ev0)                                                                                                 \
             hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
-                                  xu, d, wg, wu, F, mode, tau, gsel, act, any, hbuf, dz);                       \
+                                  xu, d, wg, wu, F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                 \
         else                                                                                                     \
             hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
-                               F, mode, tau, gsel, act, any, hbuf, dz);                                          \
+                               F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                                    \
     } while (0)
     // 2:8 needs whole groups of 8 rows per workgroup: 64 lanes per row only
     // with at least two rows per lane group (the host picks 32 otherwise)
@@ -197,20 +202,20 @@ hipError_t launch_gate(const GateArgs &g)
         switch (g.kind) {
         case KEYS:
             launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                            g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
+                                            g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         case DENSE:
             launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                             g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
+                                             g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         case SELECT_NM:
             if constexpr (std::is_same<TX, TW>::value)  // 2:8 takes the full gate
                 launch_gate_k<TW, TX, NT, SELECT_NM>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                                     g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
+                                                     g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         default:
             launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                                 g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z);
+                                                 g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         }
     };

@@ -10,6 +10,9 @@
 
 namespace sffn {
 
+constexpr int kMaxDffConst = 262144;
+constexpr int kMaxDff = kMaxDffConst;
+
 // Token counts up to this use the GEMV kernels (each weight row read once for
 // all tokens); larger batches use the MFMA union path.
 constexpr int kDecodeMaxTokens = 8;
@@ -18,6 +21,12 @@ constexpr int kDecodeMaxTokens = 8;
 // first forward on a handle; reserved for counters of the batched path.
 constexpr int kCtrlInts = 1024;
 constexpr int kCtrlUnionSize = 0;    // batched path: size of the union list
+constexpr int kCtrlError = 1;        // sticky error word (bits kErr*), workspace byte offset 4
+constexpr int kCtrlEpoch = 2;        // decode forward counter (epoch of the slots), advanced by the gate kernel
+constexpr int kErrDownWait = 1;      // a down-projection sum gave up waiting for a group's slot
+
+// Polls after which a waiting workgroup gives up (sffn_set_spin_limit).
+constexpr int kSpinMaxDefault = 1 << 18;
 
 // K splits of a batched GEMM (partial slices): up to 16 below 65 tokens, 8 up
 // to 511 tokens, none from 512.
@@ -26,8 +35,9 @@ inline int splits_max(int T) { return T <= 64 ? 16 : T < 512 ? 8 : 1; }
 
 constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
+constexpr int kDownRangeMax = 8192;  // channels of one down-projection group (32 per thread)
+static_assert(kMaxDffConst <= kDownGroupsMax * kDownRangeMax, "the widest layer fits the groups");
 
-constexpr int kMaxDff = 262144;
 
 struct Layout {
     int words;        // ceil(d_ff / 32)
@@ -38,8 +48,8 @@ struct Layout {
     size_t uidx;      // int32 [d_ff] ascending union list
     size_t hbuf;      // decode: fp32 [d_ff][ntp] gated up values; batched: bf16 [T][d_ff]
     size_t any;       // decode: uint8 [d_ff] union of the tokens' active flags
-    size_t part;      // decode: fp32 bits [kDownGroupsMax][ntp][d_model] down-projection group slots
-    size_t part_words;
+    size_t part;      // decode: 64-bit slots [kDownGroupsMax][ntp][d_model] down-projection group sums
+    size_t part_slots;
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
@@ -114,12 +124,21 @@ struct sffn_ctx {
     sffn::Layout L;
     bool inited;        // control block zeroed on the device
     int n_cu;           // compute units, read on the first forward
-    size_t lds_max;     // bytes of LDS one workgroup may allocate
+    int spin_max;       // polls before a waiting workgroup gives up
     void *ev_start;     // optional hipEvent_t pair around the dominant kernel
     void *ev_stop;
 };
 
 namespace sffn {
+// Host checks of a forward's arguments against a shape (nothing is enqueued):
+// SFFN_OK or the status to return.
+sffn_status forward_checks(const sffn_shape &s, const void *x, int n_tokens, const sffn_weights *w, int mode,
+                           float tau, int k, const float *y, const int32_t *active_idx, const int32_t *active_cnt,
+                           const int32_t *union_cnt, const float *debug_z);
+FwdArgs make_fwd(const void *x, int n_tokens, const sffn_weights *w, int mode, float tau, int k, float *y,
+                 int32_t *active_idx, int32_t *active_cnt, int32_t *union_cnt, float *debug_z, void *stream);
+// Enqueue a checked forward of n_tokens >= 1 on a set-up handle.
+sffn_status forward_enqueue(sffn_ctx &c, const FwdArgs &a);
 hipError_t device_setup(sffn_ctx &c);
 hipError_t launch_init(sffn_ctx &c, hipStream_t s);
 hipError_t launch_decode(sffn_ctx &c, const FwdArgs &a);
@@ -181,8 +200,7 @@ struct GateArgs {
     float *debug_z;
     hipStream_t stream;
     void *ev_start, *ev_stop;  // optional: this kernel's own begin / end timestamps
+    int *ctrl;            // control block: the gate kernel advances the decode epoch
 };
 hipError_t launch_gate(const GateArgs &g);
-// Host-side check that the decode kernels' LDS needs fit; false -> unsupported.
-bool decode_fits(const sffn_ctx &c, int n, int mode);
 }  // namespace sffn

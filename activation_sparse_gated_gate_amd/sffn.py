@@ -41,8 +41,12 @@ DTYPES = {"f32": SFFN_F32, "bf16": SFFN_BF16}
 
 # Names exported by the library, as declared in include/sffn.h.
 EXPORTS = ("sffn_workspace_bytes", "sffn_create", "sffn_forward", "sffn_set_profile_events",
-           "sffn_destroy", "sffn_status_string", "sffn_train_workspace_bytes", "sffn_forward_train",
-           "sffn_backward")
+           "sffn_set_spin_limit", "sffn_destroy", "sffn_status_string", "sffn_train_workspace_bytes",
+           "sffn_forward_train", "sffn_backward")
+
+# Sticky error word of the workspace (include/sffn.h).
+SFFN_WS_ERROR_OFFSET = 4
+SFFN_ERR_BIT_DOWN_WAIT = 1
 
 
 class sffn_shape(ctypes.Structure):
@@ -88,6 +92,8 @@ def lib() -> ctypes.CDLL:
             L.sffn_forward.restype = I
             L.sffn_set_profile_events.argtypes = [P, P, P]
             L.sffn_set_profile_events.restype = I
+            L.sffn_set_spin_limit.argtypes = [P, I]
+            L.sffn_set_spin_limit.restype = I
             L.sffn_destroy.argtypes = [P]
             L.sffn_destroy.restype = I
             L.sffn_train_workspace_bytes.argtypes = [ctypes.POINTER(sffn_shape)]
@@ -163,6 +169,10 @@ def sffn_backward(handle: int, x: int, dy: int, n_tokens: int, weights: sffn_wei
 def sffn_set_profile_events(handle: int, ev_start: int, ev_stop: int) -> None:
     _check(lib().sffn_set_profile_events(ctypes.c_void_p(handle), ctypes.c_void_p(ev_start or None),
                                          ctypes.c_void_p(ev_stop or None)), "sffn_set_profile_events")
+
+
+def sffn_set_spin_limit(handle: int, polls: int) -> None:
+    _check(lib().sffn_set_spin_limit(ctypes.c_void_p(handle), int(polls)), "sffn_set_spin_limit")
 
 
 def sffn_destroy(handle: int) -> None:
@@ -250,6 +260,9 @@ class SparseFFN:
         ws, nb = self._train_ws()
         sffn_backward(self.handle, x.data_ptr(), dy.data_ptr(), x.shape[0], weights, m, tau, k, saved,
                       dx.data_ptr(), dw_gate.data_ptr(), dw_up.data_ptr(), dw_down.data_ptr(), ws, nb, stream)
+
+    def set_spin_limit(self, polls: int) -> None:
+        sffn_set_spin_limit(self.handle, polls)
 
     def set_profile_events(self, start_event, stop_event) -> None:
         sffn_set_profile_events(self.handle, start_event.cuda_event if start_event is not None else 0,

@@ -212,6 +212,20 @@ sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int
                           int mode, float tau, int k, const sffn_saved *saved, float *dx, float *dw_gate,
                           float *dw_up, float *dw_down, void *train_ws, size_t train_ws_bytes, void *stream);
 
+/* Bounded waits. The decode regime's down projection (1..8 tokens) sums its
+ * channel groups inside one launch: the workgroup that sums a column slice
+ * polls the other groups' partial sums, each tagged with the forward it
+ * belongs to. It gives up after `polls` polls (default 262144; -1 gives up
+ * at once, without polling, to exercise this path in tests), writes NaN to
+ * the y entries it could not sum, and sets SFFN_ERR_BIT_DOWN_WAIT in the
+ * sticky error word: the int32 at byte offset SFFN_WS_ERROR_OFFSET of the
+ * workspace. The first forward on a handle zeroes that word; the library
+ * never clears it afterwards (the caller may). A later forward is not
+ * affected by a give-up. Host-side only; no HIP call here. */
+#define SFFN_WS_ERROR_OFFSET 4
+#define SFFN_ERR_BIT_DOWN_WAIT 1
+sffn_status sffn_set_spin_limit(sffn_handle handle, int polls);
+
 /* Record two caller-created hipEvent_t (passed as void*) around the dominant
  * kernel of every later forward on this handle (the gate kernel, or the gate
  * GEMM on the batched path): ev_start before it, ev_stop after it, on the

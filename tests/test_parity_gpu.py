@@ -220,9 +220,9 @@ def test_ragged_shapes(dtype, d, f, n, mode):
 @pytest.mark.parametrize("n", [1, 5, 8])
 @pytest.mark.parametrize("mode", ["threshold", "dense_relu"])
 def test_down_channel_passes(f, n, mode):
-    """The down projection lists the selected channels in passes of 8192
-    (8 tokens) or 16384 channels: one, two and several passes, with ragged
-    output pieces (d = 136) and every token count class."""
+    """The down projection lists the selected channels in passes of 12288
+    channels: one, two and several passes, with ragged output pieces
+    (d = 136) and every token count class."""
     d = 136
     say(f"case down passes bf16 d={d} F={f} n={n} {mode}")
     lay = inputs.make_layer(12, d, f, "bf16")
@@ -230,6 +230,23 @@ def test_down_channel_passes(f, n, mode):
     ref = oracle_forward(lay, x, mode, tau=1.0)
     got = run_gpu(lay, x, mode, tau=1.0, max_tokens=8)
     rep = compare(lay, x, mode, ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
+@pytest.mark.parametrize("f", [12289, 30000])
+@pytest.mark.parametrize("n", [1, 8])
+def test_down_list_overflow(f, n):
+    """Every channel selected (tau below every pre-activation) on layers wider
+    than one list pass: the down projection processes a full list before it
+    lists the next pass."""
+    d = 264
+    say(f"case down list overflow bf16 d={d} F={f} n={n}")
+    lay = inputs.make_layer(13, d, f, "bf16")
+    x = inputs.make_x(13, n, d, "bf16")
+    ref = oracle_forward(lay, x, "threshold", tau=-8.0)
+    assert ref.mask.all()
+    got = run_gpu(lay, x, "threshold", tau=-8.0, max_tokens=8)
+    rep = compare(lay, x, "threshold", ref, got)
     assert rep.rel_err <= DECODE_GUARD
 
 
@@ -443,6 +460,42 @@ def test_repeated_forwards_are_bitwise_deterministic():
         again = run_gpu(lay, x, "threshold", tau=1.2816, ffn=ffn, repeat=5)
         assert np.array_equal(first.y.view(np.uint32), again.y.view(np.uint32))
         assert np.array_equal(first.sets, again.sets)
+
+
+def test_down_wait_give_up_is_reported_and_heals():
+    """With the poll limit at -1 the down projection's summing workgroups give
+    up at once (every kernel still exits normally): y holds NaN where they did,
+    and the sticky error word in the workspace has the down-wait bit. The next
+    forward with the default limit reproduces a forward from before the
+    give-up bit for bit, and the word stays set until the caller clears it."""
+    d, f, n = 1024, 4096, 2
+    say(f"case down give-up bf16 d={d} F={f} n={n}")
+    lay = inputs.make_layer(31, d, f, "bf16")
+    x = torch.from_numpy(inputs.make_x(31, n, d, "bf16").view(np.int16)).cuda()
+    tens = [torch.from_numpy(a.view(np.int16)).cuda() for a in (lay.w_gate, lay.w_up, lay.w_down)]
+    w = S.SparseFFN.weights(w_gate=tens[0], w_up=tens[1], w_down=tens[2])
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    off = ((ffn.workspace.data_ptr() + 255) & ~255) - ffn.workspace.data_ptr() + S.SFFN_WS_ERROR_OFFSET
+    err_word = lambda: int(ffn.workspace[off:off + 4].view(torch.int32).item())  # noqa: E731
+    ucnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y0 = torch.empty(n, d, dtype=torch.float32, device="cuda")
+    ffn.forward(x, w, "threshold", y0, tau=0.0, union_cnt=ucnt)
+    torch.cuda.synchronize()
+    assert int(ucnt.item()) > 1000  # several channel groups, so there are waits
+    assert err_word() == 0 and torch.isfinite(y0).all()
+    ffn.set_spin_limit(-1)
+    y1 = torch.empty_like(y0)
+    ffn.forward(x, w, "threshold", y1, tau=0.0)
+    torch.cuda.synchronize()
+    assert err_word() & S.SFFN_ERR_BIT_DOWN_WAIT
+    assert torch.isnan(y1).any()
+    ffn.set_spin_limit(1 << 18)
+    y2 = torch.empty_like(y0)
+    for _ in range(3):
+        ffn.forward(x, w, "threshold", y2, tau=0.0)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y0)
+    assert err_word() & S.SFFN_ERR_BIT_DOWN_WAIT  # sticky
 
 
 def test_channel_permutation_permutes_the_set():

@@ -45,7 +45,7 @@ Layout make_layout(const sffn_shape &s)
     L.uidx = take(F * 4);
     L.hbuf = take(batched ? (F * ntp * 4 > T * FP * 2 ? F * ntp * 4 : T * FP * 2) : F * ntp * 4);
     L.any = take(F);
-    L.part_slots = (size_t)kDownGroupsMax * ntp * d;
+    L.part_slots = (size_t)(down_groups(s.d_ff) - 1) * ntp * d;
     L.part = take(L.part_slots * 8);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(rows * F * 4);  // also for a training forward of <= 8 tokens (union path)

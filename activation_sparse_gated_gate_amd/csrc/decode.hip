@@ -354,15 +354,6 @@ static int lpr_for(int len)
 
 static int nt_for(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
-// Channel groups of the down projection: 16, so that the summing workgroup
-// polls the 15 others' slots in one batch, and more for very wide layers so
-// that a group has at most kDownRangeMax channels.
-static int down_groups(const sffn_ctx &c)
-{
-    const int F = c.shape.d_ff;
-    return max(1, min(F, max(16, (F + kDownRangeMax - 1) / kDownRangeMax)));
-}
-
 hipError_t device_setup(sffn_ctx &c)
 {
     int dev = 0;
@@ -476,7 +467,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     // ---- down projection: group partials and their ordered sum ----
     uint64_t *part = reinterpret_cast<uint64_t *>(ws + c.L.part);
     const int slices = (d + kDownSliceCols - 1) / kDownSliceCols;
-    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, down_groups(c)), dim3(256), 0, st, wdn, F, d, n, any,
+    hipLaunchKernelGGL((k_down<TW, NT, 8>), dim3(slices, down_groups(c.shape.d_ff)), dim3(256), 0, st, wdn, F, d, n, any,
                        dense ? 1 : 0, hbuf, part, a.y, reinterpret_cast<int *>(ws + c.L.ctrl),
                        c.spin_max);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -37,6 +37,15 @@ constexpr int kDownGroupsMax = 64;   // channel groups of the split down project
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
 constexpr int kDownRangeMax = 8192;  // channels of one down-projection group (32 per thread)
 static_assert(kMaxDffConst <= kDownGroupsMax * kDownRangeMax, "the widest layer fits the groups");
+// Channel groups of the decode down projection for d_ff = F: 16, so that the
+// summing workgroup polls the 15 others' slots in one batch (32 at once made
+// the wait twice as long), more for very wide layers so that a group has at
+// most kDownRangeMax channels, at most F.
+inline int down_groups(int F)
+{
+    const int G = (F + kDownRangeMax - 1) / kDownRangeMax;
+    return F < 16 ? F : G > 16 ? G : 16;
+}
 
 
 struct Layout {
@@ -48,7 +57,7 @@ struct Layout {
     size_t uidx;      // int32 [d_ff] ascending union list
     size_t hbuf;      // decode: fp32 [d_ff][ntp] gated up values; batched: bf16 [T][d_ff]
     size_t any;       // decode: uint8 [d_ff] union of the tokens' active flags
-    size_t part;      // decode: 64-bit slots [kDownGroupsMax][ntp][d_model] down-projection group sums
+    size_t part;      // decode: 64-bit slots [down_groups - 1][ntp][d_model] down-projection group sums
     size_t part_slots;
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys

@@ -168,6 +168,9 @@ static hipError_t ensure_init(sffn_ctx &c, hipStream_t st)
 
 sffn_status forward_enqueue(sffn_ctx &c, const FwdArgs &a)
 {
+    // launches report errors through the thread's last-error slot: clear what
+    // an earlier call of the caller's may have left there
+    (void)hipGetLastError();
     if (ensure_init(c, a.stream) != hipSuccess) return SFFN_ERR_HIP;
     const hipError_t e = a.n > kDecodeMaxTokens ? launch_batched(c, a) : launch_decode(c, a);
     if (e != hipSuccess) {
@@ -313,6 +316,7 @@ sffn_status sffn_forward_train(sffn_handle handle, const void *x, int n_tokens, 
         if (device_setup(*handle) != hipSuccess) return SFFN_ERR_HIP;
     }
     const FwdArgs a = make_fwd(x, n_tokens, w, mode, tau, k, y, nullptr, nullptr, nullptr, nullptr, stream);
+    (void)hipGetLastError();  // as in forward_enqueue
     if (ensure_init(*handle, a.stream) != hipSuccess) return SFFN_ERR_HIP;
     const hipError_t e = launch_forward_train(*handle, a, to_saved(saved), static_cast<char *>(train_ws));
     if (e != hipSuccess) {
@@ -349,6 +353,7 @@ sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int
     a.dwd = dw_down;
     a.tws = static_cast<char *>(train_ws);
     a.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // as in forward_enqueue
     return launch_backward(*handle, a) == hipSuccess ? SFFN_OK : SFFN_ERR_HIP;
 }
 

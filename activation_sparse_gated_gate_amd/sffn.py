@@ -79,6 +79,13 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
+            # torch ships its own HIP runtime under the same soname: when it
+            # is importable it goes first, so the library binds to that
+            # runtime (a second runtime loaded beside it finds no device)
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             if not os.path.exists(LIB_PATH):
                 from . import _build
                 _build.build()

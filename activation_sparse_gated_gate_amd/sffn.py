@@ -42,7 +42,10 @@ DTYPES = {"f32": SFFN_F32, "bf16": SFFN_BF16}
 # Names exported by the library, as declared in include/sffn.h.
 EXPORTS = ("sffn_workspace_bytes", "sffn_create", "sffn_forward", "sffn_set_profile_events",
            "sffn_set_spin_limit", "sffn_destroy", "sffn_status_string", "sffn_train_workspace_bytes",
-           "sffn_forward_train", "sffn_backward")
+           "sffn_forward_train", "sffn_backward", "sffn_forward_noalloc")
+
+# Bytes of the library's static device workspace (sffn_forward_noalloc).
+SFFN_STATIC_SCRATCH_BYTES = 16 << 20
 
 # Sticky error word of the workspace (include/sffn.h).
 SFFN_WS_ERROR_OFFSET = 4
@@ -97,6 +100,9 @@ def lib() -> ctypes.CDLL:
             L.sffn_create.restype = I
             L.sffn_forward.argtypes = [P, P, I, ctypes.POINTER(sffn_weights), I, F, I, P, P, P, P, P, P]
             L.sffn_forward.restype = I
+            L.sffn_forward_noalloc.argtypes = [ctypes.POINTER(sffn_shape), P, I, ctypes.POINTER(sffn_weights), I, F,
+                                               I, P, P, P, P, P, P]
+            L.sffn_forward_noalloc.restype = I
             L.sffn_set_profile_events.argtypes = [P, P, P]
             L.sffn_set_profile_events.restype = I
             L.sffn_set_spin_limit.argtypes = [P, I]
@@ -149,6 +155,16 @@ def sffn_forward(handle: int, x: int, n_tokens: int, weights: sffn_weights, mode
                               float(tau), int(k), P(y), P(active_idx or None), P(active_cnt or None),
                               P(union_cnt or None), P(debug_z or None), P(stream or None)),
            "sffn_forward")
+
+
+def sffn_forward_noalloc(shape: sffn_shape, x: int, n_tokens: int, weights: sffn_weights, mode: int, tau: float,
+                         k: int, y: int, active_idx: int = 0, active_cnt: int = 0, union_cnt: int = 0,
+                         debug_z: int = 0, stream: int = 0) -> None:
+    P = ctypes.c_void_p
+    _check(lib().sffn_forward_noalloc(ctypes.byref(shape), P(x), int(n_tokens), ctypes.byref(weights), int(mode),
+                                      float(tau), int(k), P(y), P(active_idx or None), P(active_cnt or None),
+                                      P(union_cnt or None), P(debug_z or None), P(stream or None)),
+           "sffn_forward_noalloc")
 
 
 def sffn_train_workspace_bytes(shape: sffn_shape) -> int:

@@ -226,6 +226,29 @@ sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int
 #define SFFN_ERR_BIT_DOWN_WAIT 1
 sffn_status sffn_set_spin_limit(sffn_handle handle, int polls);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid it): sffn_forward for
+ * one to 8 tokens (the decode regime) with no handle and no caller workspace.
+ * Its workspace is a device array inside the library, SFFN_STATIC_SCRATCH_BYTES
+ * bytes per GPU, held from the library's load until the process ends; the
+ * first call on a GPU looks up that GPU's copy (hipGetSymbolAddress), and no
+ * call allocates or frees anything.
+ *   shape  as for sffn_create, with max_tokens <= 8; its workspace
+ *          (sffn_workspace_bytes) must fit the array: SFFN_ERR_WORKSPACE
+ *          otherwise, SFFN_ERR_UNSUPPORTED for max_tokens > 8
+ *   other arguments, checks and results as sffn_forward, on the current device.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two streams, or two host threads
+ * with work in flight on different streams) race and give wrong results;
+ * calls on one stream are ordered and safe. A call with a shape other than the
+ * previous call's on that GPU first clears the array's control block and
+ * slots. The sticky error word (sffn_set_spin_limit) sits at
+ * SFFN_WS_ERROR_OFFSET of the array; the poll limit is the default. */
+#define SFFN_STATIC_SCRATCH_BYTES (16u << 20)
+sffn_status sffn_forward_noalloc(const sffn_shape *shape, const void *x, int n_tokens, const sffn_weights *w,
+                                 int mode, float tau, int k, float *y, int32_t *active_idx, int32_t *active_cnt,
+                                 int32_t *union_cnt, float *debug_z, void *stream);
+
 /* Record two caller-created hipEvent_t (passed as void*) around the dominant
  * kernel of every later forward on this handle (the gate kernel, or the gate
  * GEMM on the batched path): ev_start before it, ev_stop after it, on the

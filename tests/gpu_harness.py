@@ -23,6 +23,12 @@ from activation_sparse_gated_gate_amd import inputs
 from activation_sparse_gated_gate_amd import sffn as S
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+# The batched (MFMA) path rounds the gate values G and the gated up values H to
+# bf16 before the products: measured errors stay below 3e-3 of max |y|. This
+# guard, about 3x that, sits inside the 2e-2 contract so that one union row
+# dropped or doubled (a shift of about 1/sqrt(active channels) of a token's y)
+# fails.
+BATCHED_GUARD = 8e-3
 
 
 def say(msg: str) -> None:
@@ -114,9 +120,10 @@ def compare(lay: inputs.Layer, x: np.ndarray, mode: str, ref: oracle.Result, got
     scale = float(np.max(np.abs(y_ref))) if y_ref.size else 0.0
     err = float(np.max(np.abs(got.y - y_ref))) if y_ref.size else 0.0
     rel = err / scale if scale > 0 else err
-    tol = TOL[lay.dtype] if tol is None else tol
+    if tol is None:
+        tol = BATCHED_GUARD if (lay.dtype == "bf16" and n > 8) else TOL[lay.dtype]
     assert np.all(np.isfinite(got.y))
-    assert rel <= tol, f"y rel err {rel:.3e} > {tol:.1e}"
+    assert rel <= min(tol, TOL[lay.dtype]), f"y rel err {rel:.3e} > {tol:.1e}"
     z_err = float(np.max(np.abs(got.z - ref.z))) if ref.z.size else 0.0
     rep = Report(band=int(ref.band.sum()), band_flips=int(diff.sum()),
                  active_mean=float(got.sets.sum(axis=1).mean()), union=got.union, rel_err=rel, z_err=z_err)

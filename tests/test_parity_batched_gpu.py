@@ -13,7 +13,7 @@ import torch
 import oracle
 from activation_sparse_gated_gate_amd import inputs
 from activation_sparse_gated_gate_amd import sffn as S
-from gpu_harness import TOL, compare, dev, oracle_forward, run_gpu, say
+from gpu_harness import BATCHED_GUARD, compare, dev, oracle_forward, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 W = inputs.WORKLOADS
@@ -69,6 +69,58 @@ def test_moc_topp_batched(moc_layer, n):
     got = run_gpu(moc_layer, x, "topp", tau=0.5)
     rep = compare(moc_layer, x, "topp", ref, got)
     say(f"    union fraction {rep.union / wl.d_ff:.3f}")
+
+
+def _one_token_channel(ref, n):
+    """A channel that exactly one token selects, outside every token's band."""
+    m = ref.mask.astype(bool)
+    counts = m.sum(axis=0)
+    clean = ~ref.band.any(axis=0)
+    cands = np.nonzero((counts == 1) & clean)[0]
+    assert cands.size, "no channel selected by exactly one token"
+    return int(cands[len(cands) // 2])
+
+
+def _scale_down_row(lay, ch, factor=64.0):
+    """A copy of the layer with W_down[ch] scaled by a power of two (exact in
+    bf16; the selection does not depend on W_down)."""
+    w = inputs.bf16_bits_to_f32(lay.w_down).copy()
+    w[ch] *= factor
+    return inputs.Layer(**{**lay.__dict__, "w_down": inputs.bf16_bits(w)})
+
+
+@pytest.mark.parametrize("case", ["moc16_topk", "ragged33_threshold", "ragged100_topk", "ragged12_topk_2_8"])
+def test_batched_single_token_channel_is_neither_dropped_nor_doubled(moc_layer, case):
+    """The channel of the union that only one token selected has its W_down row
+    scaled by 64, so it dominates that token's y: leaving its row out of the
+    union gather, or counting it twice, misses the guard by a wide margin."""
+    if case == "moc16_topk":
+        wl = W["moc_topk_bf16_d2048_f5632"]
+        lay, n, mode, kw = moc_layer, 16, "topk", dict(k=704)
+        x = inputs.make_x(3, n, wl.d_model, wl.dtype)
+    elif case == "ragged33_threshold":
+        lay, n, mode, kw = inputs.make_layer(28, 264, 1000, "bf16"), 33, "threshold", dict(tau=1.5)
+        x = inputs.make_x(28, n, 264, "bf16", correlated=True)
+    elif case == "ragged100_topk":
+        lay, n, mode, kw = inputs.make_layer(29, 264, 1000, "bf16"), 100, "topk", dict(k=20)
+        x = inputs.make_x(29, n, 264, "bf16")
+    else:
+        lay, n, mode, kw = inputs.make_layer(30, 264, 1000, "bf16"), 12, "topk_2_8", {}
+        x = inputs.make_x(30, n, 264, "bf16")
+    say(f"case batched one-token channel x64: {case}")
+    ref = oracle_forward(lay, x, mode, **kw)
+    ch = _one_token_channel(ref, n)
+    tok = int(np.nonzero(ref.mask[:, ch])[0][0])
+    lay64 = _scale_down_row(lay, ch)
+    ref64 = oracle_forward(lay64, x, mode, **kw)
+    assert np.array_equal(ref64.mask, ref.mask)
+    # the scaled channel carries most of that token's output
+    share = float(np.abs(ref64.h[tok, ch] * inputs.bf16_bits_to_f32(lay64.w_down)[ch]).max()
+                  / np.abs(ref64.y[tok]).max())
+    say(f"    channel {ch} (token {tok}) share of max|y| {share:.2f}")
+    assert share > 10 * BATCHED_GUARD
+    got = run_gpu(lay64, x, mode, max_tokens=n, **kw)
+    compare(lay64, x, mode, ref64, got)
 
 
 # ---------------------------------------------------------------------------
@@ -209,4 +261,4 @@ def test_prefill70b_sampled(prefill_layer, n):
             y_ref = ref.y[0]
         rel = float(np.abs(y_h[t] - y_ref).max() / np.abs(y_ref).max())
         say(f"    token {t}: active {cnt_h[t]} band {int(ref.band.sum())} y_rel_err {rel:.2e}")
-        assert rel <= TOL["bf16"]
+        assert rel <= BATCHED_GUARD

@@ -27,6 +27,9 @@ from gpu_harness import dev, oracle_forward, say
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+# Measured errors stay below 3.5e-3; the checks use this guard, about 3x
+# that and inside the contract, so a dropped or doubled stored channel fails.
+GUARD = 1e-2
 NAMES = ("dx", "dw_gate", "dw_up", "dw_down")
 
 
@@ -106,7 +109,7 @@ def check_forward(lay, x, mode, tau, k, got, tokens=None):
     y_ref = oracle.forward_with_mask(xs, lay.w_up, lay.w_down, ref.g, sets.astype(np.uint8))
     assert np.all(np.isfinite(got["y"][tokens]))
     ry = rel_err(got["y"][tokens], y_ref)
-    assert ry <= TOL, f"y rel err {ry:.3e}"
+    assert ry <= GUARD, f"y rel err {ry:.3e}"
     return sets, int((sets ^ kept).sum()), int(band.sum()), ry
 
 
@@ -119,7 +122,7 @@ def check_backward(lay, x, dy, mode, tau, sets, got, dw_init=0.0, calls=1):
         if name != "dx":
             g = (g - dw_init) / calls
         errs[name] = rel_err(g, gr[name])
-        assert errs[name] <= TOL, f"{name} rel err {errs[name]:.3e}"
+        assert errs[name] <= GUARD, f"{name} rel err {errs[name]:.3e}"
     return errs
 
 
@@ -180,14 +183,14 @@ def test_train_large_batch_sampled():
         gr = oracle.backward("topk", x[t:t + 1], dy[t:t + 1], lay.w_gate, lay.w_up, lay.w_down,
                              sets[t:t + 1].astype(np.uint8))
         e = rel_err(got["dx"][t:t + 1], gr["dx"])
-        assert e <= TOL, f"dx token {t}: {e:.3e}"
+        assert e <= GUARD, f"dx token {t}: {e:.3e}"
         errs["dx"] = max(errs["dx"], e)
     chans = np.array([0, 3, 1000, 2817, 5631])
     sub = sets[:, chans].astype(np.uint8)
     gr = oracle.backward("topk", x, dy, lay.w_gate[chans], lay.w_up[chans], lay.w_down[chans], sub)
     for name in ("dw_gate", "dw_up", "dw_down"):
         errs[name] = rel_err(got[name][chans], gr[name])
-        assert errs[name] <= TOL, f"{name} sampled rows: {errs[name]:.3e}"
+        assert errs[name] <= GUARD, f"{name} sampled rows: {errs[name]:.3e}"
     say(f"    sampled: flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
 
 

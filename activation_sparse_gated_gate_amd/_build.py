@@ -12,7 +12,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gate.hip", "decode.hip", "batched.hip", "topk.hip", "train.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "gate.hip", "decode.hip", "batched.hip", "topk.hip", "train.hip", "groups.hip", "noalloc.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

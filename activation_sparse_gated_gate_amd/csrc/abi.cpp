@@ -56,6 +56,18 @@ Layout make_layout(const sffn_shape &s)
     L.bpart_rows = batched ? (int)(prow > pmin ? prow : pmin) : 0;
     L.bpart = take((size_t)L.bpart_rows * (F > d ? F : d) * 4);
     L.thr = take(rows * 8);
+    if (batched) {
+        const size_t W = (size_t)L.words, NG = kMaxTokenGroups;
+        L.gbits = take(T * W * 4);
+        L.gcnt = take(NG * F * 4);
+        L.gstat = take(NG * 4 + NG * 8);
+        L.grp = take(T * 4);
+        L.tmap = take(T * 4);
+        L.xp = take(T * d * 2);
+        L.gub = take(NG * W * 4);
+        L.guidx = take(NG * F * 4);
+        L.gcount = take(NG * 4);
+    }
     L.total = off;
     return L;
 }
@@ -210,6 +222,7 @@ sffn_status sffn_create(const sffn_shape *shape, void *workspace, size_t workspa
     c->inited = false;
     c->n_cu = 0;
     c->spin_max = kSpinMaxDefault;
+    c->token_groups = 1;
     c->ev_start = c->ev_stop = nullptr;
     *out = c;
     return SFFN_OK;
@@ -228,6 +241,13 @@ sffn_status sffn_set_profile_events(sffn_handle handle, void *ev_start, void *ev
     if ((ev_start == nullptr) != (ev_stop == nullptr)) return SFFN_ERR_INVALID_ARG;
     handle->ev_start = ev_start;
     handle->ev_stop = ev_stop;
+    return SFFN_OK;
+}
+
+sffn_status sffn_set_token_groups(sffn_handle handle, int groups)
+{
+    if (!handle || groups < 1 || groups > kMaxTokenGroups) return SFFN_ERR_INVALID_ARG;
+    handle->token_groups = groups;
     return SFFN_OK;
 }
 

@@ -66,6 +66,8 @@ struct EpiArgs {
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
     float *Y;           // [T][d] fp32 (down writes; WGRAD: the gradient [F][d], added into)
     float *usave;       // optional [T][F] fp32: the up values x . W_up[i] (up writes, training forward)
+    const int *tmap;    // optional: token of GEMM row m, for the rows of G the up epilogue reads and
+                        // of Y the down epilogue writes (token groups: the products run in group order)
     // backward (EPI_BWD): mode is the derivative kind (0: g = z - tau,
     // g' = 1; 1: SiLU), ZU[t][i] the stored (z, u) of channel i (z NaN where
     // channel i is off for token t); writes dU into H and dZ into H2 (token
@@ -118,8 +120,9 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
     }
     if (e.kind == EPI_UP) {
         const int i = e.uidx[n];
-        e.H[(size_t)m * e.hld + n] = f2bf(bf2f(e.G[(size_t)m * e.F + i]) * v);
-        if (e.usave) e.usave[(size_t)m * e.F + i] = v;
+        const int tr = e.tmap ? e.tmap[m] : m;
+        e.H[(size_t)m * e.hld + n] = f2bf(bf2f(e.G[(size_t)tr * e.F + i]) * v);
+        if (e.usave) e.usave[(size_t)tr * e.F + i] = v;
         return false;
     }
     if (e.kind == EPI_BWD) {
@@ -141,7 +144,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
         e.Y[(size_t)e.uidx[n] * e.d + m] += v;
         return false;
     }
-    e.Y[(size_t)m * e.d + n] = v;
+    e.Y[(size_t)(e.tmap ? e.tmap[m] : m) * e.d + n] = v;
     return false;
 }
 
@@ -188,7 +191,7 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                 for (int r = 0; r < ACC; ++r) {
                     const int m = rowof(i, r);
                     if (m >= M) continue;
-                    float *o = epi.Y + (size_t)m * epi.d + n;
+                    float *o = epi.Y + (size_t)(epi.tmap ? epi.tmap[m] : m) * epi.d + n;
                     if constexpr (EK == EPI_DOWN_ACC) *o += acc[i][j][r];
                     else *o = acc[i][j][r];
                 }
@@ -270,8 +273,9 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                     if (m >= M) continue;
                     uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
                     if (live) {
-                        h = f2bf(bf2f(epi.G[(size_t)m * epi.F + src]) * acc[i][j][r]);
-                        if (epi.usave) epi.usave[(size_t)m * epi.F + src] = acc[i][j][r];
+                        const int tr = epi.tmap ? epi.tmap[m] : m;
+                        h = f2bf(bf2f(epi.G[(size_t)tr * epi.F + src]) * acc[i][j][r]);
+                        if (epi.usave) epi.usave[(size_t)tr * epi.F + src] = acc[i][j][r];
                     }
                     epi.H[(size_t)m * epi.hld + n] = h;
                 }
@@ -979,6 +983,67 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 2:8: the top 2 of each group of 8 keys, its flags and the union ----
     if (a.mode == SFFN_TOPK_2_8) {
         if ((e = launch_nm_flags(keys, T, F, act, G, ubits, st)) != hipSuccess) return e;
+    }
+    // ---- token groups: each group's up and down products over its own union ----
+    const int ng = c.token_groups;
+    if (ng > 1 && !dense && T >= ng * kTokenGroupMinTokens) {
+        GroupArgs ga{};
+        ga.T = T;
+        ga.F = F;
+        ga.d = d;
+        ga.ng = ng;
+        ga.G = G;
+        ga.x = x;
+        ga.ubits = ubits;
+        ga.ncount = ncount;
+        ga.Mb = reinterpret_cast<uint32_t *>(ws + c.L.gbits);
+        ga.cnt = reinterpret_cast<int *>(ws + c.L.gcnt);
+        ga.nsz = reinterpret_cast<int *>(ws + c.L.gstat);
+        ga.Q = reinterpret_cast<long long *>(ws + c.L.gstat + 4 * kMaxTokenGroups);
+        ga.grp = reinterpret_cast<int *>(ws + c.L.grp);
+        ga.tmap = reinterpret_cast<int *>(ws + c.L.tmap);
+        ga.xp = reinterpret_cast<uint16_t *>(ws + c.L.xp);
+        ga.gub = reinterpret_cast<uint32_t *>(ws + c.L.gub);
+        ga.stream = st;
+        int nh[kMaxTokenGroups] = {};
+        if ((e = launch_token_groups(ga, nh)) != hipSuccess) return e;
+        const int W = (F + 31) / 32;
+        int s0 = 0;
+        for (int g = 0; g < ng; s0 += nh[g], ++g) {
+            const int Tg = nh[g];
+            if (Tg <= 0) continue;
+            EpiArgs eg = ep;
+            eg.T = Tg;
+            eg.ubits = ga.gub + (size_t)g * W;
+            eg.uidx = reinterpret_cast<int32_t *>(ws + c.L.guidx) + (size_t)g * F;
+            eg.ucount = reinterpret_cast<int *>(ws + c.L.gcount) + g;
+            eg.H = H + (size_t)s0 * ep.hld;
+            eg.tmap = ga.tmap + s0;
+            const Cfg cg = cfg_for(Tg);
+            Cfg cgd = cg;
+            if (cgd.wn == 4 && ((Tg + 255) / 256) * ((d + 255) / 256) < c.n_cu) cgd = Cfg{4, 2, 2, 2};
+            const int mtg = (Tg + cg.bm() - 1) / cg.bm(), mtgd = (Tg + cgd.bm() - 1) / cgd.bm();
+            eg.kind = EPI_UP;
+            int nt = (F + cg.bn() - 1) / cg.bn();
+            int sk = split_for(c, (long long)mtg * nt / 2, d, Tg);
+            dispatch_mfma<false, EPI_UP>(cg, tile_grid(nt, mtg, sk), st, Tg, F, d, ga.xp + (size_t)s0 * d, d, wu, d,
+                                         nullptr, nullptr, part, F, eg);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (sk > 1 && (e = launch_splitk_sum(st, part, sk, Tg, F, F, eg.ucount, eg)) != hipSuccess) return e;
+            eg.kind = EPI_DOWN;
+            nt = (d + cgd.bn() - 1) / cgd.bn();
+            sk = split_for(c, (long long)mtgd * nt, F / 2, Tg);
+            dispatch_mfma<true, EPI_DOWN>(cgd, tile_grid(nt, mtgd, sk), st, Tg, d, F, eg.H, ep.hld, wdn, d, eg.uidx,
+                                          eg.ucount, part, d, eg);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (sk > 1 && (e = launch_splitk_sum(st, part, sk, Tg, d, d, nullptr, eg)) != hipSuccess) return e;
+        }
+        if (a.active_idx || a.active_cnt || a.union_cnt) {
+            hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount,
+                               a.active_idx, a.active_cnt, a.union_cnt);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
     // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {

@@ -4,7 +4,8 @@
 // Pipeline per forward (modes as in include/sffn.h):
 //   threshold  k_gate<SELECT_UP>: gate GEMV, shifted-ReLU select, and the W_up
 //              rows of the channels just found active -> k_down
-//   LoPA       k_lopa_xa (t = x.A) -> k_gate<SELECT_UP> on B with t -> k_down
+//   LoPA       k_lopa_xa (t = x.A, a workgroup per row of A) -> k_gate<SELECT_UP>
+//              on B with t -> k_down
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
 //              K-th key) -> k_up (flags + up rows) -> k_down
 //   top-p      as Top-K, with k_topp_thr (the boundary of the cumulative
@@ -283,21 +284,31 @@ __global__ __launch_bounds__(256) void k_down(const TW *__restrict__ wd, int F, 
 
 // ---------------------------------------------------------------------------
 // LoPA first product t[t][k] = x_t . A[k] (fp32) for the r rows of A, stored
-// [r][d]: one row per wavefront, read once for all tokens; the gate kernel
-// then dots the rows of B with t.
+// [r][d]: one workgroup per row, its 4 wavefronts each dotting a quarter of
+// the row with all tokens (read once), summed in wavefront order; the gate
+// kernel then dots the rows of B with t. A row per workgroup keeps r
+// workgroups in flight (one row per wavefront left most CUs idle at r = 256).
 // ---------------------------------------------------------------------------
 template <typename TW, int NT>
 __global__ __launch_bounds__(256) void k_lopa_xa(const TW *__restrict__ x, int n, int d, const TW *__restrict__ a,
                                                  int r, float *__restrict__ tvec)
 {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const TW *rows[1] = {a + (size_t)min(row, r - 1) * d};
+    __shared__ float part[4][NT];
+    const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int q = (d + 31) / 32 * 8;  // a multiple of 8 elements, 4 q >= d
+    const int j0 = min(d, wave * q), len = min(d, j0 + q) - j0;
+    const TW *rows[1] = {a + (size_t)row * d + j0};
     RowDot<TW, TW, NT, 1, 64, Batch<TW, TW, NT, 1>::v> dot;
-    dot.run(rows, row < r ? 1u : 0u, d, lane, x, d, n);
+    dot.run(rows, len > 0 ? 1u : 0u, len, lane, x + j0, d, n);
+    if (lane == 0) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-        if (row < r && t < n && lane == t) tvec[(size_t)t * r + row] = dot.acc[0][t];
+        for (int t = 0; t < NT; ++t) part[wave][t] = dot.acc[0][t];
+    }
+    __syncthreads();
+    if (threadIdx.x < NT && (int)threadIdx.x < n) {
+        const int t = threadIdx.x;
+        tvec[(size_t)t * r + row] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -431,7 +442,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     if (a.mode == SFFN_LOPA) {
         const int r = S.rank;
         float *tvec = reinterpret_cast<float *>(ws + c.L.tvec);
-        hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3((r + 3) / 4), dim3(256), 0, st, x, n, d,
+        hipLaunchKernelGGL((k_lopa_xa<TW, NT>), dim3(r), dim3(256), 0, st, x, n, d,
                            static_cast<const TW *>(a.w.lopa_a), r, tvec);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // gate rows are B (length r) dotted with t = x.A; the gate rows and

@@ -80,6 +80,7 @@ extern "C" sffn_status sffn_forward_noalloc(const sffn_shape *shape, const void 
     c.inited = ds.inited;
     c.n_cu = ds.n_cu;
     c.spin_max = kSpinMaxDefault;
+    c.token_groups = 1;
     c.ev_start = c.ev_stop = nullptr;
     const sffn_status st = forward_enqueue(
         c, make_fwd(x, n_tokens, w, mode, tau, k, y, active_idx, active_cnt, union_cnt, debug_z, stream));

@@ -13,6 +13,12 @@ namespace sffn {
 constexpr int kMaxDffConst = 262144;
 constexpr int kMaxDff = kMaxDffConst;
 
+// Token grouping of large batches (groups.hip): at most this many groups,
+// this many assignment rounds, and at least this many tokens per group.
+constexpr int kMaxTokenGroups = 8;
+constexpr int kTokenGroupIters = 4;
+constexpr int kTokenGroupMinTokens = 64;
+
 // Token counts up to this use the GEMV kernels (each weight row read once for
 // all tokens); larger batches use the MFMA union path.
 constexpr int kDecodeMaxTokens = 8;
@@ -65,6 +71,16 @@ struct Layout {
     size_t bpart;     // batched split-K partials: fp32 [bpart_rows][max(d_ff, d_model)]
     int bpart_rows;   // splits x tokens that fit in bpart
     size_t thr;       // Top-K: int2 [max(ntp, max_tokens)] per-token K-th key and tie cutoff
+    // batched token grouping (groups.hip)
+    size_t gbits;     // uint32 [T][words] per-token channel masks
+    size_t gcnt;      // int32 [kMaxTokenGroups][d_ff] per-group channel counts
+    size_t gstat;     // int32 [kMaxTokenGroups] sizes, then int64 [kMaxTokenGroups] sums of squares
+    size_t grp;       // int32 [T] group of each token
+    size_t tmap;      // int32 [T] tokens in group order
+    size_t xp;        // bf16 [T][d_model] x in group order
+    size_t gub;       // uint32 [kMaxTokenGroups][words] union bitmap of each group
+    size_t guidx;     // int32 [kMaxTokenGroups][d_ff] union list of each group
+    size_t gcount;    // int32 [kMaxTokenGroups] union size of each group
     size_t total;
 };
 
@@ -86,6 +102,27 @@ struct FwdArgs {
     hipStream_t stream;
     float *usave = nullptr;  // training forward: fp32 [n][d_ff] up values of the union's channels
 };
+
+// Token grouping of a batch (groups.hip): groups by k-means on the tokens'
+// channel masks (from G != 0), then each group's union bitmap (gub), the
+// tokens in group order (tmap) and x in that order (xp); the batch's union
+// size into *ncount and its bitmap cleared. Synchronises the stream once to
+// return the group sizes in n_host[ng].
+struct GroupArgs {
+    int T, F, d, ng;
+    const uint16_t *G;    // [T][F] bf16 gate values, 0 where off
+    const uint16_t *x;    // [T][d]
+    uint32_t *ubits;      // the batch's union bitmap
+    int *ncount;
+    uint32_t *Mb;
+    int *cnt, *nsz;
+    long long *Q;
+    int *grp, *tmap;
+    uint16_t *xp;
+    uint32_t *gub;
+    hipStream_t stream;
+};
+hipError_t launch_token_groups(const GroupArgs &a, int *n_host);
 
 // Training workspace (sffn_train_workspace_bytes): buffers of the training
 // forward's save step and of the backward, for up to T = max_tokens tokens.
@@ -134,6 +171,7 @@ struct sffn_ctx {
     bool inited;        // control block zeroed on the device
     int n_cu;           // compute units, read on the first forward
     int spin_max;       // polls before a waiting workgroup gives up
+    int token_groups;   // batched forwards of enough tokens: this many token groups (<= 1: one union)
     void *ev_start;     // optional hipEvent_t pair around the dominant kernel
     void *ev_stop;
 };

@@ -42,7 +42,7 @@ DTYPES = {"f32": SFFN_F32, "bf16": SFFN_BF16}
 # Names exported by the library, as declared in include/sffn.h.
 EXPORTS = ("sffn_workspace_bytes", "sffn_create", "sffn_forward", "sffn_set_profile_events",
            "sffn_set_spin_limit", "sffn_destroy", "sffn_status_string", "sffn_train_workspace_bytes",
-           "sffn_forward_train", "sffn_backward", "sffn_forward_noalloc")
+           "sffn_forward_train", "sffn_backward", "sffn_forward_noalloc", "sffn_set_token_groups")
 
 # Bytes of the library's static device workspace (sffn_forward_noalloc).
 SFFN_STATIC_SCRATCH_BYTES = 16 << 20
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
             L.sffn_forward_noalloc.restype = I
             L.sffn_set_profile_events.argtypes = [P, P, P]
             L.sffn_set_profile_events.restype = I
+            L.sffn_set_token_groups.argtypes = [P, I]
+            L.sffn_set_token_groups.restype = I
             L.sffn_set_spin_limit.argtypes = [P, I]
             L.sffn_set_spin_limit.restype = I
             L.sffn_destroy.argtypes = [P]
@@ -192,6 +194,10 @@ def sffn_backward(handle: int, x: int, dy: int, n_tokens: int, weights: sffn_wei
 def sffn_set_profile_events(handle: int, ev_start: int, ev_stop: int) -> None:
     _check(lib().sffn_set_profile_events(ctypes.c_void_p(handle), ctypes.c_void_p(ev_start or None),
                                          ctypes.c_void_p(ev_stop or None)), "sffn_set_profile_events")
+
+
+def sffn_set_token_groups(handle: int, groups: int) -> None:
+    _check(lib().sffn_set_token_groups(ctypes.c_void_p(handle), int(groups)), "sffn_set_token_groups")
 
 
 def sffn_set_spin_limit(handle: int, polls: int) -> None:
@@ -283,6 +289,9 @@ class SparseFFN:
         ws, nb = self._train_ws()
         sffn_backward(self.handle, x.data_ptr(), dy.data_ptr(), x.shape[0], weights, m, tau, k, saved,
                       dx.data_ptr(), dw_gate.data_ptr(), dw_up.data_ptr(), dw_down.data_ptr(), ws, nb, stream)
+
+    def set_token_groups(self, groups: int) -> None:
+        sffn_set_token_groups(self.handle, groups)
 
     def set_spin_limit(self, polls: int) -> None:
         sffn_set_spin_limit(self.handle, polls)

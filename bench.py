@@ -294,6 +294,16 @@ def points_prefill(W, S, inputs, torch, dev, union, replicate):
                     "tflops": round(flops / sp / 1e12, 1), "mfma_frac": round(flops / sp / PEAK_BF16, 4),
                     "dense_us_per_step": round(de * 1e6, 2), "speedup_vs_dense": round(de / sp, 3),
                     "flop_ratio_vs_dense": round(3 * f / (f + 2 * na), 3)})
+        # token groups (opt-in): each group's up and down products over its own union
+        for groups in (2, 4, 8):
+            if n < 64 * groups:
+                continue
+            ffn.set_token_groups(groups)
+            sg = timed(ffn, xt, wlist, "threshold", y, steps, 3, tau=tau)
+            ffn.set_token_groups(1)
+            out.append({"workload": wl.name, "tokens": n, "mode": "threshold", "tau": tau, "token_groups": groups,
+                        "us_per_step": round(sg * 1e6, 2), "tokens_per_s": round(n / sg, 1),
+                        "speedup_vs_one_union": round(sp / sg, 3), "speedup_vs_dense": round(de / sg, 3)})
     del wlist, base
     torch.cuda.empty_cache()
     return out

@@ -212,6 +212,21 @@ sffn_status sffn_backward(sffn_handle handle, const void *x, const void *dy, int
                           int mode, float tau, int k, const sffn_saved *saved, float *dx, float *dw_gate,
                           float *dw_up, float *dw_down, void *train_ws, size_t train_ws_bytes, void *stream);
 
+/* Token grouping for batches (opt-in; 1 = off, the default). With 2..8
+ * groups, a forward of more than 8 tokens, at least 64 per group, and a
+ * mode other than the dense ones groups its tokens by the channels they keep
+ * and runs the up and down products of each group over the union of that
+ * group's channels, instead of every token over the batch's union. SPT
+ * abstract on the Hugging Face "Daily Papers" listing (query "FFN
+ * modules"): a routed FFN batches tokens by the parameters they activate.
+ * The grouping is k-means on the tokens' 0/1 channel masks (4 rounds,
+ * seeded with evenly spaced tokens, deterministic). Outputs are the
+ * forward's (a token's y uses only its own channels; sums may run in another
+ * order). Such a forward SYNCHRONISES its stream once (the group sizes set
+ * the launches), so it cannot be captured into a graph. Host-side only; no
+ * HIP call here. SFFN_ERR_INVALID_ARG for groups outside 1..8. */
+sffn_status sffn_set_token_groups(sffn_handle handle, int groups);
+
 /* Bounded waits. The decode regime's down projection (1..8 tokens) sums its
  * channel groups inside one launch: the workgroup that sums a column slice
  * polls the other groups' partial sums, each tagged with the forward it

@@ -242,3 +242,16 @@ def test_train_entry_points_need_bf16():
         assert _train_calls(f) == (S.SFFN_ERR_UNSUPPORTED, S.SFFN_ERR_UNSUPPORTED)
     finally:
         S.sffn_destroy(f.h)
+
+
+def test_token_groups_setter_checks_its_range():
+    shape = S.make_shape(64, 100, 0, 300, "bf16")
+    h = S.sffn_create(shape, FAKE_WS, S.sffn_workspace_bytes(shape))
+    try:
+        for bad in (0, -1, 9):
+            assert S.lib().sffn_set_token_groups(ctypes.c_void_p(h), bad) == S.SFFN_ERR_INVALID_ARG
+        for ok in (1, 2, 8):
+            assert S.lib().sffn_set_token_groups(ctypes.c_void_p(h), ok) == S.SFFN_OK
+        assert S.lib().sffn_set_token_groups(None, 2) == S.SFFN_ERR_INVALID_ARG
+    finally:
+        S.sffn_destroy(h)

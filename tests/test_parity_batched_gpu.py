@@ -206,6 +206,42 @@ def test_batched_handle_larger_than_batch_splits_within_its_buffer():
 
 
 # ---------------------------------------------------------------------------
+# Token groups: each group's up and down products over its own union
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("groups", [2, 4, 8])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "topp"])
+def test_token_groups_match_the_oracle(mode, groups):
+    """Grouped forwards give the oracle's sets and y (a token's output uses
+    only its own channels), and the batch's union count of the single-union
+    forward; a repeated grouped forward is bit-identical."""
+    d, f, n = 264, 1000, 64 * groups + 37
+    say(f"case token groups bf16 d={d} F={f} n={n} {mode} groups={groups}")
+    lay = inputs.make_layer(40, d, f, "bf16")
+    x = inputs.make_x(40, n, d, "bf16", correlated=True)
+    ref = oracle_forward(lay, x, mode, tau=1.0, k=150)
+    one = run_gpu(lay, x, mode, tau=1.0, k=150, max_tokens=n)
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    ffn.set_token_groups(groups)
+    got = run_gpu(lay, x, mode, tau=1.0, k=150, ffn=ffn)
+    compare(lay, x, mode, ref, got)
+    assert got.union == one.union
+    again = run_gpu(lay, x, mode, tau=1.0, k=150, ffn=ffn)
+    assert np.array_equal(got.y.view(np.uint32), again.y.view(np.uint32))
+
+
+def test_token_groups_too_few_tokens_use_one_union():
+    """Below 64 tokens per group the forward keeps the single union (and
+    matches the oracle either way)."""
+    d, f, n = 264, 1000, 100
+    lay = inputs.make_layer(41, d, f, "bf16")
+    x = inputs.make_x(41, n, d, "bf16", correlated=True)
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    ffn.set_token_groups(4)
+    got = run_gpu(lay, x, "threshold", tau=1.0, ffn=ffn)
+    compare(lay, x, "threshold", oracle_forward(lay, x, "threshold", tau=1.0), got)
+
+
+# ---------------------------------------------------------------------------
 # 70B-shaped prefill layer at full size, sampled tokens
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
@@ -215,15 +251,16 @@ def prefill_layer():
     return inputs.make_layer(0, wl.d_model, wl.d_ff, wl.dtype)
 
 
-@pytest.mark.parametrize("n", W["prefill70b_ffn_bf16_d8192_f28672"].tokens)
-def test_prefill70b_sampled(prefill_layer, n):
+@pytest.mark.parametrize("n,groups", [(t, 1) for t in W["prefill70b_ffn_bf16_d8192_f28672"].tokens] + [(2048, 4)])
+def test_prefill70b_sampled(prefill_layer, n, groups):
     wl = W["prefill70b_ffn_bf16_d8192_f28672"]
     tau = wl.taus[0]
     d, f = wl.d_model, wl.d_ff
-    say(f"case prefill70b bf16 d={d} F={f} T={n} tau={tau} (sampled tokens)")
+    say(f"case prefill70b bf16 d={d} F={f} T={n} tau={tau} groups={groups} (sampled tokens)")
     x = inputs.make_x(0, n, d, wl.dtype, correlated=True)
     lay = prefill_layer
     ffn = S.SparseFFN(d, f, n, "bf16")
+    ffn.set_token_groups(groups)
     w = S.SparseFFN.weights(w_gate=dev(lay.w_gate), w_up=dev(lay.w_up), w_down=dev(lay.w_down))
     xt = dev(x)
     y = torch.full((n, d), float("nan"), dtype=torch.float32, device="cuda")

@@ -15,7 +15,9 @@ import threading
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsffn.so")
+# SFFN_LIBRARY points the loader at another build of the library (the host
+# sanitizer test uses it); by default the in-tree build.
+LIB_PATH = os.environ.get("SFFN_LIBRARY") or os.path.join(_PKG, "libsffn.so")
 
 SFFN_OK = 0
 SFFN_ERR_INVALID_ARG = -1

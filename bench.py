@@ -27,7 +27,10 @@ Prints one JSON line. Besides the contract fields it carries:
                 tokens, and a 2048-token training step with masked activation storage):
                 tokens/s, HBM fraction on touched bytes or MFMA fraction on the
                 path's FLOPs, and the speedup over this library's dense forward;
-  cpu_baseline  the CPU oracle (plain C, fp64, one thread) on a bounded sample.
+  cpu_baseline  the CPU oracle (plain C, fp64) on a bounded sample: sparse skip and
+                masked dense, one thread and every core (OpenMP build), host CPU;
+                each sweep point also carries its parity against the oracle
+                (band, flips, out-of-band mismatches, y error) and the oracle's time.
 """
 from __future__ import annotations
 
@@ -366,6 +369,60 @@ def points_train(W, S, inputs, torch, dev, union):
     return out
 
 
+class OracleLeg:
+    """The CPU oracle (plain C, fp64; its OpenMP build, where the pragmas only
+    share out independent outputs) for the CPU baseline and the per-point
+    parity: timing at one thread and at every core the process may use."""
+
+    def __init__(self):
+        import ctypes
+
+        import oracle
+
+        oracle.use_openmp()
+        oracle.lib()
+        self.oracle = oracle
+        self.gomp = ctypes.CDLL("libgomp.so.1")
+        self.cores = int(self.gomp.omp_get_max_threads())
+
+    def threads(self, k):
+        self.gomp.omp_set_num_threads(int(k))
+
+    def forward(self, x_h, lay, tau, skip):
+        t0 = time.perf_counter()
+        r = self.oracle.forward("threshold", x_h, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=tau, skip=skip)
+        return r, time.perf_counter() - t0
+
+    def parity(self, ref, idx, cnt, y, x_h, lay):
+        """Band channels, out-of-band set mismatches and y error (max-abs over
+        max-abs, against the oracle on the GPU's own set) of one token."""
+        import numpy as np
+
+        f = ref.mask.shape[1]
+        got = np.zeros(f, dtype=bool)
+        got[idx[:cnt]] = True
+        oset = ref.mask[0].astype(bool)
+        diff = got ^ oset
+        y_ref = ref.y[0]
+        if diff.any():
+            y_ref = self.oracle.forward_with_mask(x_h, lay.w_up, lay.w_down, ref.g, got[None].astype(np.uint8))[0]
+        return {"band": int(ref.band.sum()), "band_flips": int(diff.sum()),
+                "out_of_band_mismatches": int((diff & ~ref.band[0]).sum()),
+                "y_rel_err": float(np.abs(y - y_ref).max() / np.abs(y_ref).max())}
+
+
+def host_cpu():
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable": len(os.sched_getaffinity(0)), "model": model}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -487,11 +544,18 @@ def main():
 
     # ---- sweep over tau, with the dense forward as denominator ----
     sweep = []
+    gpu_out = {}
     dense_sec = run("dense_relu", 0.0, max(50, args.steps // 4), 10)
     if not args.no_sweep:
+        idx_t = torch.empty(n, f, dtype=torch.int32, device="cuda")
+        cnt_t = torch.empty(n, dtype=torch.int32, device="cuda")
         for tau in wl.taus:
             na = active_count("threshold", tau)
             s = run("threshold", tau, max(50, args.steps // 2), 10)
+            # this point's GPU outputs, checked against the oracle in the CPU leg below
+            ffn.forward(x, weights[0], "threshold", y, tau=tau, active_idx=idx_t, active_cnt=cnt_t)
+            torch.cuda.synchronize()
+            gpu_out[tau] = (idx_t[0].cpu().numpy(), int(cnt_t[0].item()), y[0].cpu().numpy())
             sweep.append({
                 "tau": tau, "sparsity": round(1 - na / f, 4), "active": na,
                 "us_per_step": round(s * 1e6, 2), "tokens_per_s": round(n / s, 1),
@@ -516,23 +580,38 @@ def main():
         torch.cuda.empty_cache()
         pts = measure_points(args, dev, S, inputs, np, torch)
 
-    # ---- CPU oracle baseline (bounded sample) ----
+    # ---- CPU oracle baseline (bounded sample): sparse skip and masked dense,
+    # at one thread and at every core ----
     cpu = None
     if args.cpu_seconds > 0:
-        import oracle
-
-        oracle.lib()
-        t0 = time.perf_counter()
-        reps = 0
-        while True:
-            oracle.forward("threshold", x_h, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=HEADLINE_TAU)
-            reps += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-        el = time.perf_counter() - t0
-        cpu = {"value": round(reps * n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} single-token forwards (tau={HEADLINE_TAU}, sparse skip, fp64) of the "
-                         f"same layer, {el:.1f} s, one thread"}
+        leg = OracleLeg()
+        # each sweep point: the oracle's time (both forms, every core) and the
+        # GPU result's parity against it
+        for pt in sweep:
+            tau = pt["tau"]
+            ref, t_skip = leg.forward(x_h, lay, tau, True)
+            _, t_mask = leg.forward(x_h, lay, tau, False)
+            pt["oracle"] = {"sparse_skip_ms": round(t_skip * 1e3, 2), "masked_dense_ms": round(t_mask * 1e3, 2),
+                            "threads": leg.cores}
+            pt["parity"] = leg.parity(ref, *gpu_out[tau], x_h, lay)
+        legs = []
+        per = args.cpu_seconds / 4
+        for variant, skip in (("sparse_skip", True), ("masked_dense", False)):
+            for k in (1, leg.cores):
+                leg.threads(k)
+                reps, el = 0, 0.0
+                while el < per or reps == 0:
+                    el += leg.forward(x_h, lay, HEADLINE_TAU, skip)[1]
+                    reps += 1
+                legs.append({"variant": variant, "threads": k, "forwards": reps, "seconds": round(el, 2),
+                             "tokens_per_s": round(reps * n / el, 3)})
+        leg.threads(leg.cores)
+        best = [g for g in legs if g["variant"] == "sparse_skip" and g["threads"] == leg.cores][0]
+        cpu = {"value": best["tokens_per_s"], "unit": "tokens/s", "cores": leg.cores, "kind": "oracle",
+               "sample": f"{best['forwards']} single-token forwards of the same layer (tau={HEADLINE_TAU}, sparse "
+                         f"skip, fp64, OpenMP over channels and columns), {best['seconds']} s on {leg.cores} "
+                         f"threads; 'legs' has the masked-dense form and one thread",
+               "legs": legs, "host": host_cpu()}
 
     out = {
         "metric": METRIC,

@@ -27,6 +27,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sffn_oracle.c")
 _SO = os.path.join(_HERE, "libsffn_oracle.so")
+_SO_OMP = os.path.join(_HERE, "libsffn_oracle_omp.so")  # the same source with OpenMP (multi-core timing)
 
 DT = {"f32": 0, "bf16": 1, "f64": 2}
 
@@ -37,17 +38,27 @@ DT = {"f32": 0, "bf16": 1, "f64": 2}
 BAND = 1e-5
 
 
-def build(force: bool = False) -> str:
-    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
-        tmp = _SO + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+def build(force: bool = False, omp: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2, no fast-math, no FMA contraction);
+    omp: the OpenMP build of the same source (for the multi-core timing)."""
+    so = _SO_OMP if omp else _SO
+    if force or not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(_SRC):
+        tmp = so + ".tmp"
+        flags = ["-fopenmp"] if omp else ["-Wno-unknown-pragmas"]
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", *flags,
                                _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _SO)
-    return _SO
+        os.replace(tmp, so)
+    return so
 
 
 _lib = None
+
+
+def use_openmp() -> None:
+    """Load the OpenMP build (before the first call; for the multi-core timing)."""
+    global _lib
+    assert _lib is None, "the oracle library is already loaded"
+    os.environ["SFFN_ORACLE_SO"] = build(omp=True)
 
 
 def lib() -> ctypes.CDLL:

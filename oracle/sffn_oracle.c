@@ -46,6 +46,10 @@
  *
  * Parity of every function here is pinned by the CPU tests (hand-worked
  * examples, textbook special cases, brute force and exact invariants).
+ *
+ * The OpenMP pragmas only share out independent outputs (channels, columns)
+ * for the multi-core timing build; each output is the same sequential sum
+ * with or without them, and the plain build ignores them.
  */
 #include <math.h>
 #include <stdint.h>
@@ -79,6 +83,7 @@ void oracle_gate_full(int n, int d, int F, const void *x, int x_dt, const void *
                       double *z)
 {
     for (int t = 0; t < n; ++t)
+#pragma omp parallel for schedule(static)
         for (int i = 0; i < F; ++i) {
             double acc = 0.0;
             for (int j = 0; j < d; ++j)
@@ -94,12 +99,14 @@ void oracle_gate_lopa(int n, int d, int r, int F, const void *x, int x_dt, const
 {
     for (int t = 0; t < n; ++t) {
         double *tv = tbuf + (long)t * r;
+#pragma omp parallel for schedule(static)
         for (int k = 0; k < r; ++k) {
             double acc = 0.0;
             for (int j = 0; j < d; ++j)
                 acc += elem(x, x_dt, (long)t * d + j) * elem(at, w_dt, (long)k * d + j);
             tv[k] = acc;
         }
+#pragma omp parallel for schedule(static)
         for (int i = 0; i < F; ++i) {
             double acc = 0.0;
             for (int k = 0; k < r; ++k)
@@ -273,6 +280,7 @@ void oracle_up(int n, int d, int F, const void *x, int x_dt, const void *wu, int
                const unsigned char *mask, const double *g, int skip, double *h)
 {
     for (int t = 0; t < n; ++t)
+#pragma omp parallel for schedule(static)
         for (int i = 0; i < F; ++i) {
             long e = (long)t * F + i;
             if (skip && !mask[e]) {
@@ -288,21 +296,27 @@ void oracle_up(int n, int d, int F, const void *x, int x_dt, const void *wu, int
 
 /* Down projection: y[t][c] = sum_i h[t][i] Wd[i][c], i ascending.
  * skip = 0: every channel's row is visited (inactive ones add h = 0);
- * skip = 1: only active channels' rows are visited. */
+ * skip = 1: only active channels' rows are visited.
+ * Columns are taken in blocks of 64 (one block per thread in an OpenMP
+ * build); every y[t][c] is still one sum in ascending i. */
 void oracle_down(int n, int d, int F, const double *h, const void *wd, int w_dt,
                  const unsigned char *mask, int skip, double *y)
 {
     for (int t = 0; t < n; ++t) {
         double *yt = y + (long)t * d;
-        for (int c = 0; c < d; ++c)
-            yt[c] = 0.0;
-        for (int i = 0; i < F; ++i) {
-            long e = (long)t * F + i;
-            if (skip && !mask[e])
-                continue;
-            double hv = h[e];
-            for (int c = 0; c < d; ++c)
-                yt[c] += hv * elem(wd, w_dt, (long)i * d + c);
+#pragma omp parallel for schedule(static)
+        for (int c0 = 0; c0 < d; c0 += 64) {
+            const int c1 = c0 + 64 < d ? c0 + 64 : d;
+            for (int c = c0; c < c1; ++c)
+                yt[c] = 0.0;
+            for (int i = 0; i < F; ++i) {
+                long e = (long)t * F + i;
+                if (skip && !mask[e])
+                    continue;
+                double hv = h[e];
+                for (int c = c0; c < c1; ++c)
+                    yt[c] += hv * elem(wd, w_dt, (long)i * d + c);
+            }
         }
     }
 }

@@ -643,3 +643,35 @@ def test_backward_empty_set_and_bf16_widening():
     g64 = oracle.backward("threshold", *[oracle.widen(a) for a in b], mask, 0.25)
     for k in g16:
         assert np.array_equal(g16[k], g64[k]), k
+
+
+# ---------------------------------------------------------------------------
+# The OpenMP build (multi-core timing of the CPU baseline) is the same oracle
+# ---------------------------------------------------------------------------
+def test_openmp_build_gives_the_same_bits():
+    """The OpenMP pragmas only share out independent outputs: the OpenMP build
+    returns bit-identical results in every mode (run in a child process,
+    which loads that build)."""
+    import subprocess
+    import sys
+    so = oracle.build(omp=True)
+    code = (
+        "import sys, numpy as np; sys.path.insert(0, %r); import oracle\n"
+        "from activation_sparse_gated_gate_amd import inputs\n"
+        "lay = inputs.make_layer(3, 136, 700, 'bf16', rank=16); x = inputs.make_x(3, 3, 136, 'bf16')\n"
+        "out = []\n"
+        "for m in ('threshold', 'topk', 'topk_2_8', 'topp', 'dense_silu'):\n"
+        "    r = oracle.forward(m, x, lay.w_up, lay.w_down, w_gate=lay.w_gate, tau=0.4, k=90, skip=False)\n"
+        "    out.append(r.y)\n"
+        "r = oracle.forward('lopa', x, lay.w_up, lay.w_down, lopa_a=lay.lopa_a, lopa_b=lay.lopa_b, tau=0.3)\n"
+        "out.append(r.y)\n"
+        "np.save(sys.argv[1], np.stack(out))\n") % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    import tempfile
+    with tempfile.TemporaryDirectory() as td:
+        res = {}
+        for name, lib_path in (("plain", oracle.build()), ("omp", so)):
+            f = os.path.join(td, name + ".npy")
+            env = dict(os.environ, SFFN_ORACLE_SO=lib_path, OMP_NUM_THREADS="4")
+            subprocess.check_call([sys.executable, "-c", code, f], env=env)
+            res[name] = np.load(f)
+    assert np.array_equal(res["plain"].view(np.uint64), res["omp"].view(np.uint64))

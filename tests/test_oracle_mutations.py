@@ -36,8 +36,10 @@ MUTATIONS = {
     "down_transposed": ("elem(wd, w_dt, (long)i * d + c)", "elem(wd, w_dt, (long)c * F + i)"),
     "up_wrong_token": ("u += elem(x, x_dt, (long)t * d + j)", "u += elem(x, x_dt, (long)0 * d + j)"),
     "up_drops_gate": ("h[e] = (mask[e] ? 1.0 : 0.0) * g[e] * u;", "h[e] = (mask[e] ? 1.0 : 0.0) * u;"),
-    "down_drops_last_channel": ("for (int i = 0; i < F; ++i) {\n            long e = (long)t * F + i;\n            if (skip && !mask[e])\n                continue;\n            double hv",
-                                "for (int i = 0; i < F - 1; ++i) {\n            long e = (long)t * F + i;\n            if (skip && !mask[e])\n                continue;\n            double hv"),
+    "down_drops_last_channel": ("for (int i = 0; i < F; ++i) {\n                long e = (long)t * F + i;\n                if (skip && !mask[e])\n                    continue;\n                double hv",
+                                "for (int i = 0; i < F - 1; ++i) {\n                long e = (long)t * F + i;\n                if (skip && !mask[e])\n                    continue;\n                double hv"),
+    "down_block_skips_a_column": ("for (int c = c0; c < c1; ++c)\n                    yt[c] += hv",
+                                  "for (int c = c0; c < c1 - 1; ++c)\n                    yt[c] += hv"),
     "topk_ascending": ("if (a->s > b->s) return -1;\n    if (a->s < b->s) return 1;",
                        "if (a->s > b->s) return 1;\n    if (a->s < b->s) return -1;"),
     "topk_ties_to_higher_index": ("return (a->i > b->i) - (a->i < b->i);",
@@ -118,7 +120,8 @@ def _run(name):
         c = os.path.join(td, "m.c")
         so = os.path.join(td, "m.so")
         open(c, "w").write(src.replace(old, new))
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", c, "-o", so, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wno-unknown-pragmas",
+                               c, "-o", so, "-lm"])
         env = dict(os.environ, SFFN_ORACLE_SO=so, PYTHONDONTWRITEBYTECODE="1")
         p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                             os.path.join(ROOT, "tests", "test_oracle.py")],

@@ -47,6 +47,7 @@ Layout make_layout(const sffn_shape &s)
     L.any = take(F);
     L.part_slots = (size_t)(down_groups(s.d_ff) - 1) * ntp * d;
     L.part = take(L.part_slots * 8);
+    L.tslot = take((size_t)kTopkSlots * 8);
     L.tvec = take(r ? ntp * r * 4 : 0);
     L.keys = take(rows * F * 4);  // also for a training forward of <= 8 tokens (union path)
     L.ubits = take((size_t)L.words * 4);

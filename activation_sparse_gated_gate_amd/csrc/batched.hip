@@ -372,18 +372,6 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
 // Source of the chunks outside the operands; never written.
 static __device__ __align__(16) uint4 g_zero16[1] = {};
 
-typedef __attribute__((address_space(1))) const void gmem_t;
-typedef __attribute__((address_space(3))) void lmem_t;
-
-// s_waitcnt: at most N vector-memory operations of this wavefront in flight,
-// and every LDS operation done.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
 template <int TM, int TN, int WM, int WN, int BKT, int NS, int OCC, bool BNN, int EK, int GM>
 __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int K, const bf16_t *__restrict__ A,
                                                               int lda,

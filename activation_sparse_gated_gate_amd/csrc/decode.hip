@@ -6,10 +6,11 @@
 //              rows of the channels just found active -> k_down
 //   LoPA       k_lopa_xa (t = x.A, a workgroup per row of A) -> k_gate<SELECT_UP>
 //              on B with t -> k_down
-//   Top-K      k_gate<KEYS> (SiLU keys) -> k_topk_thr (select of each token's
-//              K-th key) -> k_up (flags + up rows) -> k_down
-//   top-p      as Top-K, with k_topp_thr (the boundary of the cumulative
-//              softmax mass p) in place of k_topk_thr
+//   Top-K      k_gate<KEYS> (SiLU keys) -> k_up_topk (select workgroups find
+//              each token's boundary, the rest wait for it; flags + up
+//              rows) -> k_down
+//   top-p      k_gate<KEYS> -> k_topp_thr (the boundary of the cumulative
+//              softmax mass p) -> k_up (flags + up rows) -> k_down
 //   2:8        k_gate<SELECT_NM>: gate GEMV, SiLU keys ranked within each
 //              aligned group of 8 channels, and the W_up rows of the 2 kept
 //              per group -> k_down
@@ -25,11 +26,15 @@
 // 1/256 of the HBM bandwidth, so a kernel lasts as long as its most loaded CU.
 // Active channels are byte flags act[t][i], and any[i] for the union over the
 // tokens, with one writer each, so any row partition works without atomics.
-// Only the down kernel's summing workgroups wait on other workgroups (for
-// their partial sums, see k_down); everything else passes through global
-// memory to the next kernel.
+// Two kernels have workgroups wait on others of the same launch: the down
+// kernel's summing workgroups (for the partial sums, see k_down) and the
+// Top-K up kernel's (for the per-token boundary, see k_up_topk); everything
+// else passes through global memory to the next kernel.
 #include "compact.h"
 #include "rowdot.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace sffn {
 
@@ -122,6 +127,358 @@ __device__ __forceinline__ void read_epoch(const int *ctrl, int tid, uint32_t *e
 {
     if (tid == 0)
         *epoch_s = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// ---------------------------------------------------------------------------
+// Top-K boundary of one token's keys s[0 .. F) by a workgroup of 256 threads:
+// {f2key of the K-th largest key, the last channel kept among the keys equal
+// to it}, the pair topk_on applies (1 <= K <= F).
+//
+// Pass 1 counts the keys into kKeyBins equal value bins over
+// [kKeyLo, kKeyLo + 8) (SiLU keys are >= -0.2785; keys past either end go to
+// the end bins, a NaN to bin 0). The bin is non-decreasing in the key, so
+// every key of a higher bin ranks at least as high as every key of a lower
+// one (equal keys share a bin) and the K-th largest lies in the bin b* where
+// the count from the top reaches K; need of b*'s keys are kept. Pass 2
+// gathers b*'s keys (up to kCandMax) in LDS and ranks each by (f2key
+// descending, channel ascending): the one of rank need - 1 is the boundary.
+// A fuller bin (ties, or keys far outside the range) goes through an MSD
+// radix select on f2key restricted to b*, 8 bits per pass, then a block scan
+// of the keys equal to the K-th gives the cutoff.
+//
+// The passes are written without branches per key: the four wavefronts of
+// the workgroup share one scalar unit, and an exec-mask branch per key (a
+// bounds test, a NaN test) also serializes the LDS reads behind it. So the
+// positions past F hold -inf keys: they count in bin 0 below every channel,
+// rank after every channel there (same or larger key, lower index), and the
+// boundary, at rank need - 1 < the channels in b*, is never one of them.
+// ---------------------------------------------------------------------------
+constexpr int kKeyBins = 2048, kCandMax = 512;
+constexpr float kKeyLo = -0.3f, kKeyScale = kKeyBins / 8.0f;
+
+__device__ __forceinline__ int key_bin(float v)
+{
+    // fmaxf takes the number when the other operand is NaN; the clamp and the
+    // truncation keep the order of (v - kKeyLo) * kKeyScale
+    return (int)fminf(fmaxf((v - kKeyLo) * kKeyScale, 0.f), (float)(kKeyBins - 1));
+}
+
+struct __align__(16) TopkLds {
+    int hist[kKeyBins];  // value bins, then 256 radix digits
+    uint32_t cand_key[kCandMax];
+    int cand_idx[kCandMax];
+    int sh[6];  // b*, keys of it kept, keys in it, gathered; then the result
+    int scan_scratch[4];
+};
+
+// Keys of one token kept in LDS by a select workgroup, for d_ff up to
+// kTopkLdsKeys; larger layers stream them from global memory in each pass.
+constexpr int kTopkLdsKeys = 24 * 256;
+
+// The key of the positions past F.
+static __device__ const float g_key_pad = -INFINITY;
+
+// Keys j = tid + 256 u, u < U, of s[0 .. F) into kl[j], loaded straight
+// into LDS (no registers; -inf past F). The caller waits (wait_vm_lgkm<0>)
+// and syncs before reading kl.
+template <int U>
+__device__ __forceinline__ void topk_stage_keys(const float *__restrict__ s, int F, float *__restrict__ kl)
+{
+    const int tid = threadIdx.x, wave = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_global_load_lds((gmem_t *)(u * 256 + tid < F ? s + u * 256 + tid : &g_key_pad),
+                                         (lmem_t *)(kl + u * 256 + wave * 64), 4, 0, 0);
+}
+
+// kl: the keys staged by topk_stage_keys<U> and a barrier since (U > 0), or
+// null (U == 0: streamed from s).
+template <int U>
+__device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, int F, int K, TopkLds &L,
+                                                 const float *__restrict__ kl)
+{
+    constexpr int V = U > 0 ? U : 16;  // keys per thread and round
+    const int tid = threadIdx.x;
+    int *hist = L.hist, *sh = L.sh;
+    // fn(u, j, v) over this thread's positions j = tid + 256 u, the keys
+    // past F being -inf; T positions in all
+    const int T = U > 0 ? U * 256 : (F + 256 * V - 1) / (256 * V) * (256 * V);
+    auto for_keys = [&](auto &&fn) {
+        if constexpr (U > 0) {
+            static_assert(U % 8 == 0, "keys in rounds of 8 per thread");
+#pragma unroll 1
+            for (int u0 = 0; u0 < U; u0 += 8) {  // rounds of 8 LDS reads keep the registers few
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = kl[(u0 + e) * 256 + tid];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fn(u0 + e, (u0 + e) * 256 + tid, o[e]);
+            }
+        } else {
+            for (int j0 = 0; j0 < F; j0 += 256 * V) {
+                float o[V];
+#pragma unroll
+                for (int u = 0; u < V; ++u) o[u] = s[min(j0 + u * 256 + tid, F - 1)];
+#pragma unroll
+                for (int u = 0; u < V; ++u) fn(u, j0 + u * 256 + tid, j0 + u * 256 + tid < F ? o[u] : -INFINITY);
+            }
+        }
+    };
+    reinterpret_cast<int4 *>(hist)[2 * tid] = make_int4(0, 0, 0, 0);
+    reinterpret_cast<int4 *>(hist)[2 * tid + 1] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    for_keys([&](int, int, float v) { atomicAdd(&hist[key_bin(v)], 1); });
+    __syncthreads();
+    {
+        // thread tid owns bins 8 tid .. 8 tid + 7
+        const int4 h0 = reinterpret_cast<const int4 *>(hist)[2 * tid];
+        const int4 h1 = reinterpret_cast<const int4 *>(hist)[2 * tid + 1];
+        const int c[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        int local = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) local += c[e];
+        int run = T - block_incl_scan(local, L.scan_scratch);  // keys in the bins above this thread's
+        if (run < K && K <= run + local) {
+#pragma unroll
+            for (int e = 7; e >= 0; --e) {
+                if (run < K && K <= run + c[e]) {
+                    sh[0] = 8 * tid + e;
+                    sh[1] = K - run;
+                    sh[2] = c[e];
+                    sh[3] = 0;
+                }
+                run += c[e];
+            }
+        }
+    }
+    __syncthreads();
+    const int bs = sh[0], cnt = sh[2];
+    int need = sh[1];
+    if (cnt <= kCandMax) {
+        // gather b*'s keys: match bits in a register, one slot claim per
+        // thread that has any, then the writes
+        if constexpr (U > 0) {
+            static_assert(U <= 32, "one match bit per key");
+            uint32_t mb = 0;
+            for_keys([&](int u, int, float v) { mb |= (uint32_t)(key_bin(v) == bs) << u; });
+            if (mb) {
+                int slot = atomicAdd(&sh[3], __popc(mb));  // < cnt: the same keys as the count
+                for (uint32_t m = mb; m; m &= m - 1) {
+                    const int j = (__ffs(m) - 1) * 256 + tid;
+                    if (slot < kCandMax) {
+                        L.cand_key[slot] = f2key(kl[j]);
+                        L.cand_idx[slot] = j;
+                    }
+                    ++slot;
+                }
+            }
+        } else {
+            for_keys([&](int, int j, float v) {  // the same positions as the count, -inf ones included
+                if (key_bin(v) == bs) {
+                    const int slot = atomicAdd(&sh[3], 1);
+                    if (slot < kCandMax) {
+                        L.cand_key[slot] = f2key(v);
+                        L.cand_idx[slot] = j;
+                    }
+                }
+            });
+        }
+        __syncthreads();
+        for (int c = tid; c < cnt; c += 256) {
+            const uint32_t mk = L.cand_key[c];
+            const int mi = L.cand_idx[c];
+            int rank = 0;
+            for (int m = 0; m < cnt; ++m) {
+                const uint32_t ok = L.cand_key[m];
+                rank += ok > mk || (ok == mk && L.cand_idx[m] < mi);
+            }
+            if (rank == need - 1) {
+                sh[4] = (int)mk;
+                sh[5] = mi;
+            }
+        }
+        __syncthreads();
+        const int2 r = make_int2(sh[4], sh[5]);
+        __syncthreads();  // sh and the candidates are reused by the next select
+        return r;
+    }
+    // ---- a full bin: radix select on f2key within b* ----
+    uint32_t prefix = 0, pmask = 0;
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+        const int shift = 24 - 8 * p;
+        hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < F; j += 256) {
+            const float v = s[j];
+            const uint32_t key = f2key(v);
+            if (key_bin(v) == bs && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        const int c = hist[255 - tid];  // thread tid owns digit 255 - tid: the scan runs from the top
+        const int incl = block_incl_scan(c, L.scan_scratch);
+        if (incl - c < need && need <= incl) {
+            sh[0] = 255 - tid;
+            sh[1] = need - (incl - c);
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh[0] << shift;
+        pmask |= 0xffu << shift;
+        need = sh[1];
+        __syncthreads();  // hist and sh are rewritten by the next pass
+    }
+    // the first `need` keys equal to the K-th, in channel order: contiguous
+    // segments per thread make "equal keys before mine" an exclusive scan
+    const int seg = (F + 255) / 256;
+    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+    int eq = 0;
+    for (int i = i0; i < i1; ++i) eq += f2key(s[i]) == prefix;
+    const int before = block_incl_scan(eq, L.scan_scratch) - eq;
+    if (before < need && need <= before + eq) {
+        int left = need - before, cut = i0;
+        for (int i = i0; i < i1 && left > 0; ++i)
+            if (f2key(s[i]) == prefix) {
+                cut = i;
+                --left;
+            }
+        sh[4] = (int)prefix;
+        sh[5] = cut;
+    }
+    __syncthreads();
+    const int2 r = make_int2(sh[4], sh[5]);
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Up kernel of the decode Top-K, with the per-token select folded in (no
+// separate select launch between the gate and the up rows). The first
+// sets * n workgroups (sets = min(8, grid / n)) are select workgroups:
+// workgroup b finds the boundary of token b / sets in the keys the gate
+// kernel wrote (wg_topk_boundary) and publishes it in its set's slot pair,
+// tagged with this forward's epoch. Every workgroup waits for its tokens' pairs in
+// set b % sets (one thread per token polls; blocks are dispatched in index
+// order, so the select workgroups, which have the lowest indices, are
+// already running), then, as k_up: the flags act[t][i] (topk_on), the union
+// flags any[i] and the W_up rows of the channels some token kept:
+// h[i][t] = g * (x_t . W_up[i]). On a block-dispatch order of 8 XCDs in turn,
+// set s lies on XCD s, so the pollers of a slot share its XCD. A wait that
+// reaches the spin limit is no error: that workgroup runs the select itself.
+// ---------------------------------------------------------------------------
+// At least two rows per wavefront (4 waves x SUB x R rows per workgroup), so
+// that the workgroups of a layer fit on the GPU at once while they wait.
+template <int NT>
+struct TopkRows {
+    static constexpr int v = RowsPer<NT>::v < 2 ? 2 : RowsPer<NT>::v;
+};
+
+template <typename TW, int NT, int LPR, int U>
+__global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n, int d,
+                                                 const TW *__restrict__ wu, int F, int K, uint8_t *__restrict__ act,
+                                                 uint8_t *__restrict__ any, const float *__restrict__ gsel,
+                                                 float *__restrict__ hbuf, uint64_t *__restrict__ tslot,
+                                                 const int *__restrict__ ctrl, int spin_max)
+{
+    constexpr int SUB = 64 / LPR;
+    constexpr int R = TopkRows<NT>::v;
+    __shared__ TopkLds L;
+    __shared__ float kl[U > 0 ? U * 256 : 1];  // a select's keys (U > 0)
+    __shared__ int2 thr_s[NT];
+    __shared__ int miss_s[NT];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = lane / LPR, li = lane % LPR;
+    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
+    const int nv = max(0, min(R, F - row0));
+    const int sets = min(8, (int)gridDim.x / n), b = blockIdx.x, set = b % sets;
+    const int own = b < sets * n ? b / sets : -1;  // the token this workgroup selects for its set
+
+    // this forward's epoch, read by the threads that publish or poll (the
+    // gate kernel that wrote it has completed, so a cached load sees it)
+    uint32_t epoch = 0;
+    if (tid < n) epoch = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    float kv[R][NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) kv[r][t] = (r < nv && t < n) ? gsel[(size_t)t * F + row0 + r] : 0.f;
+
+    // round 0: the select workgroup's own token, published; then every
+    // other token's boundary from the slots. Round 1: the tokens whose wait
+    // reached the spin limit, selected here.
+    uint32_t todo = own >= 0 ? 1u << own : 0u;
+    for (int round = 0; round < 2; ++round) {
+        for (; todo; todo &= todo - 1) {  // uniform over the workgroup
+            const int t = __ffs(todo) - 1;
+            if constexpr (U > 0) {
+                topk_stage_keys<U>(gsel + (size_t)t * F, F, kl);
+                wait_vm_lgkm<0>();
+                __syncthreads();
+            }
+            const int2 r = wg_topk_boundary<U>(gsel + (size_t)t * F, F, K, L, kl);
+            if (tid == 0) {
+                if (round == 0) {
+                    uint64_t *p = tslot + ((size_t)set * kDecodeMaxTokens + t) * 2;
+                    __hip_atomic_store(p, ((uint64_t)epoch << 32) | (uint32_t)r.x, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(p + 1, ((uint64_t)epoch << 32) | (uint32_t)r.y, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                thr_s[t] = r;
+            }
+        }
+        if (round == 1) break;
+        if (tid < n) {
+            bool ready = tid == own;
+            if (!ready) {
+                const uint64_t *p = tslot + ((size_t)set * kDecodeMaxTokens + tid) * 2;
+                uint64_t v0 = ld_slot(p), v1 = ld_slot(p + 1);
+                for (int spin = 0; spin <= spin_max; ++spin) {
+                    ready = (uint32_t)(v0 >> 32) == epoch && (uint32_t)(v1 >> 32) == epoch;
+                    if (ready || spin == spin_max) break;
+                    __builtin_amdgcn_s_sleep(1);
+                    if ((uint32_t)(v0 >> 32) != epoch) v0 = ld_slot(p);
+                    if ((uint32_t)(v1 >> 32) != epoch) v1 = ld_slot(p + 1);
+                }
+                if (ready) thr_s[tid] = make_int2((int)(uint32_t)v0, (int)(uint32_t)v1);
+            }
+            miss_s[tid] = !ready;
+        }
+        __syncthreads();
+        for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[t] << t;
+    }
+    __syncthreads();
+
+    float gv[R][NT];
+    uint32_t amask = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            gv[r][t] = 0.f;
+            if (r < nv && t < n) {
+                const bool on = topk_on(kv[r][t], row0 + r, thr_s[t]);
+                if (li == ((r * NT + t) & (LPR - 1))) act[(size_t)t * F + row0 + r] = on;
+                if (on) {
+                    gv[r][t] = kv[r][t];
+                    amask |= 1u << r;
+                }
+            }
+        }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
+    if (__ballot(amask != 0) == 0) return;
+    const TW *rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
+    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+    up.run(rows, amask, d, li, x, d, n);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
+                hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
 }
 
 // ---------------------------------------------------------------------------
@@ -389,6 +746,8 @@ hipError_t launch_init(sffn_ctx &c, hipStream_t s)
     // epochs start at 1 and skip 0 when they wrap)
     hipLaunchKernelGGL(k_zero_u64, dim3(256), dim3(256), 0, s, reinterpret_cast<uint64_t *>(c.ws + c.L.part),
                        c.L.part_slots);
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, s, reinterpret_cast<uint64_t *>(c.ws + c.L.tslot),
+                       (size_t)kTopkSlots);
     hipLaunchKernelGGL(k_zero_ints, dim3(4), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ctrl), kCtrlInts);
     hipLaunchKernelGGL(k_zero_ints, dim3(16), dim3(256), 0, s, reinterpret_cast<int *>(c.ws + c.L.ubits), c.L.words);
     return hipGetLastError();
@@ -455,12 +814,30 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     }
     if ((e = launch_gate(g)) != hipSuccess) return e;
 
-    // ---- Top-K / top-p: select, then the up rows ----
-    if (ranked) {
+    // ---- Top-K: the select folded into the up rows ----
+    if (a.mode == SFFN_TOPK) {
+        const int lpr = lpr_for(d);
+        const dim3 ugrid(std::max(row_blocks(F, lpr, TopkRows<NT>::v), n));  // one select workgroup per token at least
+        uint64_t *tslot = reinterpret_cast<uint64_t *>(ws + c.L.tslot);
+        const int *ctrl = reinterpret_cast<const int *>(ws + c.L.ctrl);
+        auto go = [&](auto lpr_c, auto u_c) {
+            hipLaunchKernelGGL((k_up_topk<TW, NT, decltype(lpr_c)::value, decltype(u_c)::value>), ugrid, dim3(256), 0,
+                               st, x, n, d, wu, F, a.k, act, any, gsel, hbuf, tslot, ctrl, c.spin_max);
+        };
+        auto go_lpr = [&](auto u_c) {
+            if (lpr == 64) go(std::integral_constant<int, 64>{}, u_c);
+            else if (lpr == 32) go(std::integral_constant<int, 32>{}, u_c);
+            else go(std::integral_constant<int, 16>{}, u_c);
+        };
+        // the select workgroups keep a token's keys in LDS, or stream them for wider layers
+        if (F <= kTopkLdsKeys) go_lpr(std::integral_constant<int, kTopkLdsKeys / 256>{});
+        else go_lpr(std::integral_constant<int, 0>{});
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // ---- top-p: select, then the up rows ----
+    if (a.mode == SFFN_TOPP) {
         int2 *thr = reinterpret_cast<int2 *>(ws + c.L.thr);
-        e = a.mode == SFFN_TOPK ? launch_topk_thr(gsel, n, F, a.k, thr, st)
-                                : launch_topp_thr(gsel, n, F, a.tau, thr, st);
-        if (e != hipSuccess) return e;
+        if ((e = launch_topp_thr(gsel, n, F, a.tau, thr, st)) != hipSuccess) return e;
         const int lpr = lpr_for(d);
         const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
         if (lpr == 64)

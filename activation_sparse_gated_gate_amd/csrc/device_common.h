@@ -174,6 +174,20 @@ __device__ __forceinline__ uint32_t f2key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Operand types of __builtin_amdgcn_global_load_lds (global source, LDS
+// destination: each lane's bytes land at the destination + lane * size).
+typedef __attribute__((address_space(1))) const void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
+
+// s_waitcnt: at most N vector-memory operations of this wavefront in flight,
+// and every LDS operation done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // Top-K membership of channel i from its token's threshold: thr.x is the
 // K-th largest key (f2key encoding), thr.y the last channel index kept among
 // the keys equal to it.

@@ -41,6 +41,8 @@ inline int splits_max(int T) { return T <= 64 ? 16 : T < 512 ? 8 : 1; }
 
 constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
+// Decode Top-K boundary slots: 8 sets x kDecodeMaxTokens tokens x {key, cutoff}.
+constexpr int kTopkSlots = 8 * 8 * 2;
 constexpr int kDownRangeMax = 8192;  // channels of one down-projection group (32 per thread)
 static_assert(kMaxDffConst <= kDownGroupsMax * kDownRangeMax, "the widest layer fits the groups");
 // Channel groups of the decode down projection for d_ff = F: 16, so that the
@@ -65,12 +67,13 @@ struct Layout {
     size_t any;       // decode: uint8 [d_ff] union of the tokens' active flags
     size_t part;      // decode: 64-bit slots [down_groups - 1][ntp][d_model] down-projection group sums
     size_t part_slots;
+    size_t tslot;     // decode Top-K: 64-bit slots [8 sets][8 tokens][2] of the per-token boundaries
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap
     size_t bpart;     // batched split-K partials: fp32 [bpart_rows][max(d_ff, d_model)]
     int bpart_rows;   // splits x tokens that fit in bpart
-    size_t thr;       // Top-K: int2 [max(ntp, max_tokens)] per-token K-th key and tie cutoff
+    size_t thr;       // top-p: int2 [max(ntp, max_tokens)] per-token boundary key and tie cutoff
     // batched token grouping (groups.hip)
     size_t gbits;     // uint32 [T][words] per-token channel masks
     size_t gcnt;      // int32 [kMaxTokenGroups][d_ff] per-group channel counts
@@ -207,9 +210,6 @@ hipError_t launch_save(const float *zd, const float *ud, const uint8_t *act, int
 hipError_t launch_bwd_setup(const Saved &sv, int T, int F, int d, int tp, float2 *ZU, uint32_t *ubits,
                             int32_t *uidx, int *ucount, uint16_t *dut, uint16_t *dzt, uint16_t *ht,
                             const uint16_t *x, const uint16_t *dy, uint16_t *xt, uint16_t *dyt, hipStream_t st);
-// Per-token Top-K (topk.hip), shared by both regimes: thr[t] = {K-th largest
-// key in the f2key encoding, last channel index kept among keys equal to it}.
-hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st);
 // Top-p: the same per-token pair, found by cumulative softmax mass p
 // (decode), and the batched select + flags.
 hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st);

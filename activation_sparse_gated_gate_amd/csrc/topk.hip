@@ -4,36 +4,22 @@
 // structured selection (the same summary's 2:8 option: the top 2 of every
 // aligned group of 8 channels).
 //
-// k_topk_thr finds, per token, the K-th largest key and a tie cutoff; it
-// writes no per-channel output. Channel i of token t is then selected iff
+// The select (select.h) finds, per token, the K-th largest key and a tie
+// cutoff. Channel i of token t is then selected iff
 //   key > kth  or  (key == kth and i <= cut)
 // (topk_on), so ties at the K-th value go to the lower channel indices and
-// exactly K channels are selected. The decode up kernel applies that rule
-// where it reads the keys anyway; for a batch, k_topk_select_flags applies it
+// exactly K channels are selected. For a batch, k_topk_select_flags applies it
 // right after the select, to the keys the select holds, and writes the
 // batch's flags, gate values and union bitmap. Top-p (k_topp_*) finds the
-// same pair by cumulative softmax mass instead of a count (select_mass).
+// same pair by cumulative softmax mass instead of a count (select_mass); the
+// decode up kernel applies it where it reads the keys anyway. (The decode
+// Top-K folds its select into the up kernel, decode.hip.)
 #include <algorithm>
 
 #include "select.h"
 #include "sffn_internal.h"
 
 namespace sffn {
-
-// One workgroup (1024 threads) per token; the select itself is select_kth
-// (select.h).
-template <int KPT>
-__global__ __launch_bounds__(1024) void k_topk_thr(const float *__restrict__ keys, int F, int K,
-                                                   int2 *__restrict__ thr)
-{
-    __shared__ SelectLds L;
-    const int t = blockIdx.x;
-    const float *s = keys + (size_t)t * F;
-    float kf[KPT > 0 ? KPT : 1];
-    load_keys<KPT>(s, F, kf);
-    const int2 r = select_kth<KPT>(s, F, K, L, kf);
-    if (threadIdx.x == 0) thr[t] = r;
-}
 
 // Batched: token t's flags act[t][i], the gate values the up GEMM reads
 // (G[t][i] = bf16 key where selected, else 0) and its bits of the union
@@ -98,7 +84,7 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
     write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
 }
 
-// Top-p (decode): each token's boundary key and tie cutoff, as k_topk_thr.
+// Top-p (decode): each token's boundary key and tie cutoff.
 template <int KPT>
 __global__ __launch_bounds__(1024) void k_topp_thr(const float *__restrict__ keys, int F, float p,
                                                    int2 *__restrict__ thr)
@@ -198,16 +184,6 @@ hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16
     const int tpb = T < 256 ? 1 : std::min(16, T / 128);
     hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + tpb - 1) / tpb), dim3(256), 0, st, keys, T, F, tpb,
                        act, G, ubits);
-    return hipGetLastError();
-}
-
-hipError_t launch_topk_thr(const float *keys, int T, int F, int K, int2 *thr, hipStream_t st)
-{
-    const dim3 grid(T), block(1024);
-    if (F <= 1024 * 4) hipLaunchKernelGGL(k_topk_thr<4>, grid, block, 0, st, keys, F, K, thr);
-    else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topk_thr<8>, grid, block, 0, st, keys, F, K, thr);
-    else if (F <= 1024 * 16) hipLaunchKernelGGL(k_topk_thr<16>, grid, block, 0, st, keys, F, K, thr);
-    else hipLaunchKernelGGL(k_topk_thr<0>, grid, block, 0, st, keys, F, K, thr);
     return hipGetLastError();
 }
 

@@ -404,6 +404,75 @@ def test_topk_select_crowded_bin(n):
     compare(lay, x, "topk", ref, got)
     assert (got.cnt[:n] == 400).all()
 
+    # more than 512 equal keys at the cut, and a gate scaled so that about
+    # half of the keys lie above the value-bin range (both: the radix path)
+    lay = inputs.make_layer(36, d, f, "bf16")
+    tied = list(range(3, f, 5))[:560]
+    for i in tied[1:]:
+        lay.w_gate[i] = lay.w_gate[tied[0]]
+    x = inputs.make_x(36, n, d, "bf16")
+    z0 = oracle_forward(lay, x[:1], "dense_silu").z[0]
+    key0 = z0 / (1.0 + np.exp(-z0))
+    k = int((key0 > key0[tied[0]]).sum()) + 301
+    say(f"case topk crowded bin: 560 ties, n={n} K={k}")
+    ref = oracle_forward(lay, x, "topk", k=k)
+    got = run_gpu(lay, x, "topk", k=k, max_tokens=n)
+    compare(lay, x, "topk", ref, got)
+    assert (got.cnt[:n] == k).all()
+    for t in range(n):
+        sel = got.sets[t, tied]
+        assert not np.any(~sel[:-1] & sel[1:]), f"token {t}: tied channels kept out of index order"
+
+    lay = inputs.make_layer(37, d, f, "bf16")
+    lay.w_gate[:] = inputs.bf16_bits(inputs.bf16_bits_to_f32(lay.w_gate) * 64.0)
+    x = inputs.make_x(37, n, d, "bf16")
+    z0 = oracle_forward(lay, x[:1], "dense_silu").z[0]
+    assert (z0 / (1.0 + np.exp(-z0)) > 8.0).sum() > 1000
+    say(f"case topk crowded bin: gate x64, n={n}")
+    for k in (400, 1200):
+        ref = oracle_forward(lay, x, "topk", k=k)
+        got = run_gpu(lay, x, "topk", k=k, max_tokens=n)
+        compare(lay, x, "topk", ref, got)
+        assert (got.cnt[:n] == k).all()
+
+
+@pytest.mark.parametrize("n", [1, 3])
+def test_topk_consecutive_forwards_take_their_own_boundary(n):
+    """Forwards in a row on one handle with a different K and input each time:
+    every forward's select must use its own per-token boundary, never one left
+    in the workspace by the forward before."""
+    d, f = 256, 3000
+    lay = inputs.make_layer(38, d, f, "bf16")
+    ffn = S.SparseFFN(d, f, 8, "bf16")
+    for q, k in enumerate((37, 1500, 37, 2999, 1)):
+        say(f"case topk consecutive forwards n={n} K={k}")
+        x = inputs.make_x(38 + q, n, d, "bf16")
+        ref = oracle_forward(lay, x, "topk", k=k)
+        got = run_gpu(lay, x, "topk", k=k, ffn=ffn)
+        compare(lay, x, "topk", ref, got)
+        assert (got.cnt[:n] == k).all()
+
+
+def test_topk_select_wait_give_up_selects_locally():
+    """With the poll limit at -1 no workgroup of the Top-K up kernel waits for
+    the select workgroups: each runs the select itself, and the sets are those
+    of a forward that waited (the down projection gives up too, so y is not
+    compared). With the default limit back, the forward matches the oracle."""
+    d, f, n, k = 512, 4096, 3, 500
+    say(f"case topk select give-up d={d} F={f} n={n}")
+    lay = inputs.make_layer(39, d, f, "bf16")
+    x = inputs.make_x(39, n, d, "bf16")
+    ffn = S.SparseFFN(d, f, n, "bf16")
+    ref = oracle_forward(lay, x, "topk", k=k)
+    waited = run_gpu(lay, x, "topk", k=k, ffn=ffn)
+    compare(lay, x, "topk", ref, waited)
+    ffn.set_spin_limit(-1)
+    local = run_gpu(lay, x, "topk", k=k, ffn=ffn)
+    assert np.array_equal(local.sets, waited.sets)
+    ffn.set_spin_limit(1 << 18)
+    got = run_gpu(lay, x, "topk", k=k, ffn=ffn)
+    compare(lay, x, "topk", ref, got)
+
 
 @pytest.mark.parametrize("n", [1, 2, 12])
 def test_topk_all_keys_equal_takes_first_k(n):

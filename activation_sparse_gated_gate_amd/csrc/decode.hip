@@ -165,6 +165,7 @@ __device__ __forceinline__ int key_bin(float v)
 
 struct __align__(16) TopkLds {
     int hist[kKeyBins];  // value bins, then 256 radix digits
+    int hist64[64];      // the sample's coarse bins (32 value bins each)
     uint32_t cand_key[kCandMax];
     int cand_idx[kCandMax];
     int sh[6];  // b*, keys of it kept, keys in it, gathered; then the result
@@ -192,10 +193,14 @@ __device__ __forceinline__ void topk_stage_keys(const float *__restrict__ s, int
 }
 
 // kl: the keys staged by topk_stage_keys<U> and a barrier since (U > 0), or
-// null (U == 0: streamed from s).
+// null (U == 0: streamed from s). eslot, cslot: if not null, thread 0
+// publishes there, tagged with epoch, a prefetch estimate (a coarse bin from
+// a sample; 64: none) before the count, and the boundary bin b* as soon as
+// it is known.
 template <int U>
 __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, int F, int K, TopkLds &L,
-                                                 const float *__restrict__ kl)
+                                                 const float *__restrict__ kl, uint64_t *eslot, uint64_t *cslot,
+                                                 uint32_t epoch)
 {
     constexpr int V = U > 0 ? U : 16;  // keys per thread and round
     const int tid = threadIdx.x;
@@ -224,6 +229,27 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
             }
         }
     };
+    if (eslot) {
+        // a prefetch estimate first: the coarse bin (32 value bins) where the
+        // count from the top of every 8th position, times 8, passes 1.25 K
+        int cb = 64;  // none: nothing to prefetch (keys not in LDS)
+        if constexpr (U > 0) {
+            static_assert(U % 8 == 0, "whole sample rounds");
+            if (tid < 64) L.hist64[tid] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < U / 8; ++v) atomicAdd(&L.hist64[key_bin(kl[8 * (v * 256 + tid)]) >> 5], 1);
+            __syncthreads();
+            if (tid < 64) {
+                const int c = L.hist64[63 - tid];  // lane l: coarse bin 63 - l, from the top
+                const int ks = min(U * 32, (K + 7) / 8 + (K + 7) / 32 + 2);
+                const uint64_t hit = __ballot(wave_incl_scan(c) >= ks);
+                cb = hit ? 63 - (__ffsll((long long)hit) - 1) : 0;
+            }
+        }
+        if (tid == 0)
+            __hip_atomic_store(eslot, ((uint64_t)epoch << 32) | (uint32_t)cb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     reinterpret_cast<int4 *>(hist)[2 * tid] = make_int4(0, 0, 0, 0);
     reinterpret_cast<int4 *>(hist)[2 * tid + 1] = make_int4(0, 0, 0, 0);
     __syncthreads();
@@ -254,6 +280,8 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
     __syncthreads();
     const int bs = sh[0], cnt = sh[2];
     int need = sh[1];
+    if (cslot && tid == 0)
+        __hip_atomic_store(cslot, ((uint64_t)epoch << 32) | (uint32_t)bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (cnt <= kCandMax) {
         // gather b*'s keys: match bits in a register, one slot claim per
         // thread that has any, then the writes
@@ -352,17 +380,22 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
 
 // ---------------------------------------------------------------------------
 // Up kernel of the decode Top-K, with the per-token select folded in (no
-// separate select launch between the gate and the up rows). The first
-// sets * n workgroups (sets = min(8, grid / n)) are select workgroups:
-// workgroup b finds the boundary of token b / sets in the keys the gate
-// kernel wrote (wg_topk_boundary) and publishes it in its set's slot pair,
-// tagged with this forward's epoch. Every workgroup waits for its tokens' pairs in
-// set b % sets (one thread per token polls; blocks are dispatched in index
-// order, so the select workgroups, which have the lowest indices, are
-// already running), then, as k_up: the flags act[t][i] (topk_on), the union
-// flags any[i] and the W_up rows of the channels some token kept:
-// h[i][t] = g * (x_t . W_up[i]). On a block-dispatch order of 8 XCDs in turn,
-// set s lies on XCD s, so the pollers of a slot share its XCD. A wait that
+// separate select launch between the gate and the up rows). The first 8 n
+// workgroups select: workgroup b finds the boundary of token b / 8 in the
+// keys the gate kernel wrote (wg_topk_boundary) and publishes it in set
+// b % 8, tagged with this forward's epoch, in three steps: a prefetch
+// estimate from a sample of the keys, the boundary bin b*, the exact pair.
+// The other workgroups take the rows; each reads its tokens' slots in set
+// b % 8 (one thread per token polls; blocks are dispatched in index order,
+// so the select workgroups, which have the lowest indices, are running).
+// With the estimate they prefetch the W_up rows likely to be kept into the
+// cache (loads into a scratch LDS area that nothing reads). With b* alone a
+// row is kept if its key's bin is above b* and dropped if below; the rows in
+// b* itself (a few per token) are computed as if kept and settled by the
+// exact pair (topk_on), read after their dot products. Then, as k_up: the
+// flags act[t][i], the union flags any[i] and the W_up rows of the channels
+// some token kept: h[i][t] = g * (x_t . W_up[i]). On a block-dispatch order
+// of 8 XCDs in turn, set s lies on XCD s with its pollers. A wait that
 // reaches the spin limit is no error: that workgroup runs the select itself.
 // ---------------------------------------------------------------------------
 // At least two rows per wavefront (4 waves x SUB x R rows per workgroup), so
@@ -371,6 +404,57 @@ template <int NT>
 struct TopkRows {
     static constexpr int v = RowsPer<NT>::v < 2 ? 2 : RowsPer<NT>::v;
 };
+
+// Slots of token t in set s: {b*, K-th key, cutoff, prefetch estimate}.
+__device__ __forceinline__ uint64_t *topk_slot(uint64_t *tslot, int set, int t)
+{
+    return tslot + ((size_t)set * kDecodeMaxTokens + t) * 4;
+}
+
+// Polls a slot until it carries `epoch` or spin_max polls have passed;
+// true and the slot's low 32 bits in v when it did.
+__device__ __forceinline__ bool topk_poll(const uint64_t *p, uint32_t epoch, int spin_max, uint32_t &v)
+{
+    uint64_t w = ld_slot(p);
+    for (int spin = 0; spin <= spin_max; ++spin) {
+        if ((uint32_t)(w >> 32) == epoch) {
+            v = (uint32_t)w;
+            return true;
+        }
+        if (spin == spin_max) break;
+        __builtin_amdgcn_s_sleep(1);
+        w = ld_slot(p);
+    }
+    return false;
+}
+
+// One token's select by the whole workgroup: its keys staged (U > 0), its
+// boundary into thr_s[t] (bs_s[t] = -1: exact), and, with slot, the
+// prefetch estimate, b* and then the exact pair published there.
+template <int U>
+__device__ __noinline__ void topk_select_token(const float *__restrict__ gsel, int F, int K, TopkLds &L, float *kl,
+                                               int t, uint64_t *slot, uint32_t epoch, int2 *thr_s, int *bs_s)
+{
+    const float *s = gsel + (size_t)t * F;
+    if constexpr (U > 0) {
+        topk_stage_keys<U>(s, F, kl);
+        wait_vm_lgkm<0>();
+        __syncthreads();
+    }
+    const int2 r = wg_topk_boundary<U>(s, F, K, L, kl, slot ? slot + 3 : nullptr, slot, epoch);
+    if (threadIdx.x == 0) {
+        if (slot) {
+            __hip_atomic_store(slot + 1, ((uint64_t)epoch << 32) | (uint32_t)r.x, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slot + 2, ((uint64_t)epoch << 32) | (uint32_t)r.y, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (thr_s) {
+            thr_s[t] = r;
+            bs_s[t] = -1;
+        }
+    }
+}
 
 template <typename TW, int NT, int LPR, int U>
 __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n, int d,
@@ -383,102 +467,156 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     constexpr int R = TopkRows<NT>::v;
     __shared__ TopkLds L;
     __shared__ float kl[U > 0 ? U * 256 : 1];  // a select's keys (U > 0)
-    __shared__ int2 thr_s[NT];
-    __shared__ int miss_s[NT];
+    __shared__ __align__(16) uint32_t pf_lds[4][256];  // where the prefetch loads land (never read)
+    __shared__ int2 thr_s[NT];                 // exact boundaries
+    __shared__ int bs_s[NT];                   // boundary bins; -1: thr_s holds the exact pair
+    __shared__ int est_s[NT];                  // prefetch estimates (coarse bins)
+    __shared__ int miss_s[2][NT];              // waits that reached the spin limit
+    __shared__ int need_s[NT];                 // this workgroup has rows in the token's b*
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int q = lane / LPR, li = lane % LPR;
-    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
-    const int nv = max(0, min(R, F - row0));
-    const int sets = min(8, (int)gridDim.x / n), b = blockIdx.x, set = b % sets;
-    const int own = b < sets * n ? b / sets : -1;  // the token this workgroup selects for its set
+    const int b = blockIdx.x, set = b & 7;
 
     // this forward's epoch, read by the threads that publish or poll (the
     // gate kernel that wrote it has completed, so a cached load sees it)
     uint32_t epoch = 0;
     if (tid < n) epoch = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (b < 8 * n) {  // a select workgroup
+        topk_select_token<U>(gsel, F, K, L, kl, b >> 3, topk_slot(tslot, set, b >> 3), epoch, nullptr,
+                             nullptr);  // (thread 0, which publishes, has the epoch)
+        return;
+    }
+
+    const int q = lane / LPR, li = lane % LPR;
+    const int wrow0 = ((b - 8 * n) * 4 + wave) * SUB * R;  // this wavefront's first row
+    const int row0 = wrow0 + q * R;
+    const int nv = max(0, min(R, F - row0));
     float kv[R][NT];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < NT; ++t) kv[r][t] = (r < nv && t < n) ? gsel[(size_t)t * F + row0 + r] : 0.f;
-
-    // round 0: the select workgroup's own token, published; then every
-    // other token's boundary from the slots. Round 1: the tokens whose wait
-    // reached the spin limit, selected here.
-    uint32_t todo = own >= 0 ? 1u << own : 0u;
-    for (int round = 0; round < 2; ++round) {
-        for (; todo; todo &= todo - 1) {  // uniform over the workgroup
-            const int t = __ffs(todo) - 1;
-            if constexpr (U > 0) {
-                topk_stage_keys<U>(gsel + (size_t)t * F, F, kl);
-                wait_vm_lgkm<0>();
-                __syncthreads();
-            }
-            const int2 r = wg_topk_boundary<U>(gsel + (size_t)t * F, F, K, L, kl);
-            if (tid == 0) {
-                if (round == 0) {
-                    uint64_t *p = tslot + ((size_t)set * kDecodeMaxTokens + t) * 2;
-                    __hip_atomic_store(p, ((uint64_t)epoch << 32) | (uint32_t)r.x, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(p + 1, ((uint64_t)epoch << 32) | (uint32_t)r.y, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-                thr_s[t] = r;
-            }
-        }
-        if (round == 1) break;
-        if (tid < n) {
-            bool ready = tid == own;
-            if (!ready) {
-                const uint64_t *p = tslot + ((size_t)set * kDecodeMaxTokens + tid) * 2;
-                uint64_t v0 = ld_slot(p), v1 = ld_slot(p + 1);
-                for (int spin = 0; spin <= spin_max; ++spin) {
-                    ready = (uint32_t)(v0 >> 32) == epoch && (uint32_t)(v1 >> 32) == epoch;
-                    if (ready || spin == spin_max) break;
-                    __builtin_amdgcn_s_sleep(1);
-                    if ((uint32_t)(v0 >> 32) != epoch) v0 = ld_slot(p);
-                    if ((uint32_t)(v1 >> 32) != epoch) v1 = ld_slot(p + 1);
-                }
-                if (ready) thr_s[tid] = make_int2((int)(uint32_t)v0, (int)(uint32_t)v1);
-            }
-            miss_s[tid] = !ready;
-        }
-        __syncthreads();
-        for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[t] << t;
+    if (tid < NT) {
+        miss_s[0][tid] = miss_s[1][tid] = 0;
+        need_s[tid] = 0;
+    }
+    // the prefetch estimates, then the rows likely kept into the cache: one
+    // 16-byte load per 128-byte line of each such row of the wavefront
+    if (tid < n) {
+        uint32_t v = 64;
+        est_s[tid] = topk_poll(topk_slot(tslot, set, tid) + 3, epoch, spin_max, v) ? (int)v : 64;
     }
     __syncthreads();
+    {
+        uint32_t pf = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (r < nv && t < n && (key_bin(kv[r][t]) >> 5) >= est_s[t]) pf |= 1u << r;
+        uint32_t M = 0;  // bit q R + r: row wrow0 + q R + r, for the whole wavefront
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t bal = __ballot((pf >> r) & 1u);
+#pragma unroll
+            for (int g = 0; g < SUB; ++g) M |= (uint32_t)((bal >> (g * LPR)) & 1u) << (g * R + r);
+        }
+        if (M) {
+            const int lines = (d * (int)sizeof(TW) + 127) / 128;
+            for (int p0 = 0; p0 < SUB * R * lines; p0 += 64) {
+                const int p = p0 + lane, slotr = p / lines, line = p - slotr * lines;
+                if (slotr < SUB * R && ((M >> slotr) & 1u))
+                    __builtin_amdgcn_global_load_lds(
+                        (gmem_t *)(reinterpret_cast<const char *>(wu + (size_t)(wrow0 + slotr) * d) + line * 128),
+                        (lmem_t *)pf_lds[wave], 16, 0, 0);
+            }
+        }
+    }
 
+    // the boundary bins; a wait that reaches the limit selects here
+    if (tid < n) {
+        uint32_t v = 0;
+        if (topk_poll(topk_slot(tslot, set, tid), epoch, spin_max, v))
+            bs_s[tid] = (int)v;
+        else
+            miss_s[0][tid] = 1;
+    }
+    __syncthreads();
+    uint32_t todo = 0;
+    for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[0][t] << t;
+    for (; todo; todo &= todo - 1)  // uniform over the workgroup
+        topk_select_token<U>(gsel, F, K, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
+    __syncthreads();
+
+    // the rows kept by bin, and the rows in b* (computed as if kept)
+    const TW *rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
+    uint32_t amask = 0;  // rows computed
+    uint32_t amb = 0;    // bit r * NT + t: row r is in token t's b*
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (r < nv && t < n) {
+                const int bs = bs_s[t];
+                const int kb = key_bin(kv[r][t]);
+                if (bs >= 0 && kb == bs) {
+                    amb |= 1u << (r * NT + t);
+                    amask |= 1u << r;
+                    need_s[t] = 1;
+                } else if (bs < 0 ? topk_on(kv[r][t], row0 + r, thr_s[t]) : kb > bs) {
+                    amask |= 1u << r;
+                }
+            }
+    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+    if (__ballot(amask != 0)) up.run(rows, amask, d, li, x, d, n);
+    __syncthreads();  // need_s
+    // the exact pairs the rows in b* need; a wait that reaches the limit
+    // selects here
+    if (tid < n && need_s[tid] && bs_s[tid] >= 0) {
+        uint32_t key = 0, cut = 0;
+        const uint64_t *p = topk_slot(tslot, set, tid);
+        if (topk_poll(p + 1, epoch, spin_max, key) && topk_poll(p + 2, epoch, spin_max, cut))
+            thr_s[tid] = make_int2((int)key, (int)cut);
+        else
+            miss_s[1][tid] = 1;
+    }
+    __syncthreads();
+    todo = 0;
+    for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[1][t] << t;
+    for (; todo; todo &= todo - 1)
+        topk_select_token<U>(gsel, F, K, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
+    __syncthreads();
+
+    // the flags: kept by bin, or settled by the exact pair in b*
     float gv[R][NT];
-    uint32_t amask = 0;
+    uint32_t kmask = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             gv[r][t] = 0.f;
             if (r < nv && t < n) {
-                const bool on = topk_on(kv[r][t], row0 + r, thr_s[t]);
+                const int bs = bs_s[t];
+                const bool on = (bs < 0 || ((amb >> (r * NT + t)) & 1u)) ? topk_on(kv[r][t], row0 + r, thr_s[t])
+                                                                          : key_bin(kv[r][t]) > bs;
                 if (li == ((r * NT + t) & (LPR - 1))) act[(size_t)t * F + row0 + r] = on;
                 if (on) {
                     gv[r][t] = kv[r][t];
-                    amask |= 1u << r;
+                    kmask |= 1u << r;
                 }
             }
         }
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
-    if (__ballot(amask != 0) == 0) return;
-    const TW *rows[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
-    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
-    up.run(rows, amask, d, li, x, d, n);
+        if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (kmask >> r) & 1u;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
+            if (((kmask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
                 hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
+    wait_vm_lgkm<0>();  // no prefetch is still writing this workgroup's LDS when it ends
 }
 
 // ---------------------------------------------------------------------------
@@ -817,7 +955,7 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     // ---- Top-K: the select folded into the up rows ----
     if (a.mode == SFFN_TOPK) {
         const int lpr = lpr_for(d);
-        const dim3 ugrid(std::max(row_blocks(F, lpr, TopkRows<NT>::v), n));  // one select workgroup per token at least
+        const dim3 ugrid(8 * n + row_blocks(F, lpr, TopkRows<NT>::v));  // 8 select workgroups per token, then the rows
         uint64_t *tslot = reinterpret_cast<uint64_t *>(ws + c.L.tslot);
         const int *ctrl = reinterpret_cast<const int *>(ws + c.L.ctrl);
         auto go = [&](auto lpr_c, auto u_c) {

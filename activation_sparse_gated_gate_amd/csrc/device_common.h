@@ -137,15 +137,18 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
-// Inclusive prefix sum across one 64-lane wavefront.
+// Inclusive prefix sum across one 64-lane wavefront, in registers with DPP
+// moves: shifts by 1, 2, 4 and 8 within each row of 16 lanes (a lane with no
+// source adds 0), then lane 15 of rows 0 and 2 into rows 1 and 3, then lane
+// 31 into rows 2 and 3. Every lane must be active.
 __device__ __forceinline__ int wave_incl_scan(int v)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
     return v;
 }
 

@@ -41,8 +41,8 @@ inline int splits_max(int T) { return T <= 64 ? 16 : T < 512 ? 8 : 1; }
 
 constexpr int kDownGroupsMax = 64;   // channel groups of the split down projection
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
-// Decode Top-K boundary slots: 8 sets x kDecodeMaxTokens tokens x {key, cutoff}.
-constexpr int kTopkSlots = 8 * 8 * 2;
+// Decode Top-K boundary slots: 8 sets x kDecodeMaxTokens tokens x {boundary bin, key, cutoff, prefetch estimate}.
+constexpr int kTopkSlots = 8 * 8 * 4;
 constexpr int kDownRangeMax = 8192;  // channels of one down-projection group (32 per thread)
 static_assert(kMaxDffConst <= kDownGroupsMax * kDownRangeMax, "the widest layer fits the groups");
 // Channel groups of the decode down projection for d_ff = F: 16, so that the
@@ -67,7 +67,7 @@ struct Layout {
     size_t any;       // decode: uint8 [d_ff] union of the tokens' active flags
     size_t part;      // decode: 64-bit slots [down_groups - 1][ntp][d_model] down-projection group sums
     size_t part_slots;
-    size_t tslot;     // decode Top-K: 64-bit slots [8 sets][8 tokens][2] of the per-token boundaries
+    size_t tslot;     // decode Top-K: 64-bit slots [8 sets][8 tokens][4] of the per-token boundaries
     size_t tvec;      // fp32 [ntp][rank] LoPA x.A
     size_t keys;      // batched Top-K: fp32 [T][d_ff] SiLU keys
     size_t ubits;     // batched: uint32 [words] union bitmap

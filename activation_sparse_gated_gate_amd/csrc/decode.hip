@@ -166,8 +166,8 @@ __device__ __forceinline__ int key_bin(float v)
 struct __align__(16) TopkLds {
     int hist[kKeyBins];  // value bins, then 256 radix digits
     int hist64[64];      // the sample's coarse bins (32 value bins each)
-    uint32_t cand_key[kCandMax];
-    int cand_idx[kCandMax];
+    uint64_t cand[kCandMax];  // b*'s keys: f2key << 32 | ~channel (larger: earlier in the Top-K order)
+    int cand_rank[64];
     int sh[6];  // b*, keys of it kept, keys in it, gathered; then the result
     int scan_scratch[4];
 };
@@ -293,10 +293,7 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
                 int slot = atomicAdd(&sh[3], __popc(mb));  // < cnt: the same keys as the count
                 for (uint32_t m = mb; m; m &= m - 1) {
                     const int j = (__ffs(m) - 1) * 256 + tid;
-                    if (slot < kCandMax) {
-                        L.cand_key[slot] = f2key(kl[j]);
-                        L.cand_idx[slot] = j;
-                    }
+                    if (slot < kCandMax) L.cand[slot] = (uint64_t)f2key(kl[j]) << 32 | (uint32_t)~j;
                     ++slot;
                 }
             }
@@ -304,25 +301,38 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
             for_keys([&](int, int j, float v) {  // the same positions as the count, -inf ones included
                 if (key_bin(v) == bs) {
                     const int slot = atomicAdd(&sh[3], 1);
-                    if (slot < kCandMax) {
-                        L.cand_key[slot] = f2key(v);
-                        L.cand_idx[slot] = j;
-                    }
+                    if (slot < kCandMax) L.cand[slot] = (uint64_t)f2key(v) << 32 | (uint32_t)~j;
                 }
             });
         }
+        if (tid < 64) L.cand_rank[tid] = 0;
         __syncthreads();
-        for (int c = tid; c < cnt; c += 256) {
-            const uint32_t mk = L.cand_key[c];
-            const int mi = L.cand_idx[c];
-            int rank = 0;
-            for (int m = 0; m < cnt; ++m) {
-                const uint32_t ok = L.cand_key[m];
-                rank += ok > mk || (ok == mk && L.cand_idx[m] < mi);
+        // rank of each candidate = candidates with a larger composite (the
+        // channels are distinct, so the composites are); up to 64 candidates:
+        // wavefront w counts over its quarter of them
+        if (cnt <= 64) {
+            const int c = tid & 63, w = tid >> 6;
+            if (c < cnt) {
+                const uint64_t me = L.cand[c];
+                int rank = 0;
+                for (int m = w * 16; m < min(cnt, w * 16 + 16); ++m) rank += L.cand[m] > me;
+                if (rank) atomicAdd(&L.cand_rank[c], rank);
             }
-            if (rank == need - 1) {
-                sh[4] = (int)mk;
-                sh[5] = mi;
+            __syncthreads();
+            if (tid < cnt && L.cand_rank[tid] == need - 1) {
+                const uint64_t me = L.cand[tid];
+                sh[4] = (int)(uint32_t)(me >> 32);
+                sh[5] = (int)~(uint32_t)me;
+            }
+        } else {
+            for (int c = tid; c < cnt; c += 256) {
+                const uint64_t me = L.cand[c];
+                int rank = 0;
+                for (int m = 0; m < cnt; ++m) rank += L.cand[m] > me;
+                if (rank == need - 1) {
+                    sh[4] = (int)(uint32_t)(me >> 32);
+                    sh[5] = (int)~(uint32_t)me;
+                }
             }
         }
         __syncthreads();

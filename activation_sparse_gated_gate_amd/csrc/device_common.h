@@ -131,9 +131,18 @@ __device__ __forceinline__ float dot8(const typename Ld8<TW>::raw &w, const type
 template <int G>
 __device__ __forceinline__ float group_sum(float v)
 {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "power of two <= 64");
+    // within 16 lanes by DPP moves (every lane ends with its group's sum):
+    // pairs, quads, the two quads of 8 lanes (half-row mirror), the two
+    // halves of 16 (row mirror); then shuffles across rows
+#define SFFN_DPP_F(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false))
+    if constexpr (G >= 2) v += SFFN_DPP_F(v, 0xb1);   // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) v += SFFN_DPP_F(v, 0x4e);   // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) v += SFFN_DPP_F(v, 0x141);  // row_half_mirror
+    if constexpr (G >= 16) v += SFFN_DPP_F(v, 0x140); // row_mirror
+#undef SFFN_DPP_F
+    if constexpr (G >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32, 64);
     return v;
 }
 

@@ -180,22 +180,36 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
                 }
         return;
     }
-    if constexpr (EK == EPI_DOWN || EK == EPI_DOWN_ACC) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = colof(j);
-            if (n >= nlim) continue;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m >= M) continue;
-                    float *o = epi.Y + (size_t)(epi.tmap ? epi.tmap[m] : m) * epi.d + n;
-                    if constexpr (EK == EPI_DOWN_ACC) *o += acc[i][j][r];
-                    else *o = acc[i][j][r];
-                }
+    // tok(m): the token of GEMM row m. The row map (token groups) is tested
+    // once here, so each element loop below is compiled for one case; a load
+    // of the map inside the loop would also have to be repeated after every
+    // store, which the compiler cannot prove it does not alias.
+    auto with_rows = [&](auto &&body) {
+        if (epi.tmap) {
+            const int *__restrict__ tm = epi.tmap;
+            body([tm](int m) { return tm[m]; });
+        } else {
+            body([](int m) { return m; });
         }
+    };
+    if constexpr (EK == EPI_DOWN || EK == EPI_DOWN_ACC) {
+        with_rows([&](auto tok) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = colof(j);
+                if (n >= nlim) continue;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < ACC; ++r) {
+                        const int m = rowof(i, r);
+                        if (m >= M) continue;
+                        float *o = epi.Y + (size_t)tok(m) * epi.d + n;
+                        if constexpr (EK == EPI_DOWN_ACC) *o += acc[i][j][r];
+                        else *o = acc[i][j][r];
+                    }
+            }
+        });
     } else if constexpr (EK == EPI_WGRAD) {
         // column n is union entry n: row U[n] of the gradient; rows m are
         // model dimensions, four consecutive ones per lane and register group
@@ -259,30 +273,32 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
         }
     } else if constexpr (EK == EPI_UP) {
         const int padlim = (nlim + 7) & ~7;
+        with_rows([&](auto tok) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = colof(j);
-            if (n >= padlim) continue;
-            const bool live = n < nlim;
-            const int src = live ? uloc[n - n0] : 0;  // this tile's part of the union list (LDS)
+            for (int j = 0; j < TN; ++j) {
+                const int n = colof(j);
+                if (n >= padlim) continue;
+                const bool live = n < nlim;
+                const int src = live ? uloc[n - n0] : 0;  // this tile's part of the union list (LDS)
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int r = 0; r < ACC; ++r) {
-                    const int m = rowof(i, r);
-                    if (m >= M) continue;
-                    uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
-                    if (live) {
-                        const int tr = epi.tmap ? epi.tmap[m] : m;
-                        h = f2bf(bf2f(epi.G[(size_t)tr * epi.F + src]) * acc[i][j][r]);
-                        if (epi.usave) epi.usave[(size_t)tr * epi.F + src] = acc[i][j][r];
+                    for (int r = 0; r < ACC; ++r) {
+                        const int m = rowof(i, r);
+                        if (m >= M) continue;
+                        uint16_t h = 0;  // pad columns: the down GEMM reads H in 8-wide chunks
+                        if (live) {
+                            const int tr = tok(m);
+                            h = f2bf(bf2f(epi.G[(size_t)tr * epi.F + src]) * acc[i][j][r]);
+                            if (epi.usave) epi.usave[(size_t)tr * epi.F + src] = acc[i][j][r];
+                        }
+                        epi.H[(size_t)m * epi.hld + n] = h;
                     }
-                    epi.H[(size_t)m * epi.hld + n] = h;
-                }
-            // keep each sub-tile's gathered G loads from being hoisted over the
-            // whole tile (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                // keep each sub-tile's gathered G loads from being hoisted over
+                // the whole tile (register pressure)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
     } else {
         // gate; GM is the mode, a template parameter so each instantiation
         // carries one straight-line epilogue

@@ -56,7 +56,6 @@ Layout make_layout(const sffn_shape &s)
     const size_t prow = T < 512 ? (size_t)splits_max((int)T) * T : 0, pmin = 16 * (T < 64 ? T : 64);
     L.bpart_rows = batched ? (int)(prow > pmin ? prow : pmin) : 0;
     L.bpart = take((size_t)L.bpart_rows * (F > d ? F : d) * 4);
-    L.thr = take(rows * 8);
     if (batched) {
         const size_t W = (size_t)L.words, NG = kMaxTokenGroups;
         L.gbits = take(T * W * 4);

@@ -9,8 +9,8 @@
 //   Top-K      k_gate<KEYS> (SiLU keys) -> k_up_topk (select workgroups find
 //              each token's boundary, the rest wait for it; flags + up
 //              rows) -> k_down
-//   top-p      k_gate<KEYS> -> k_topp_thr (the boundary of the cumulative
-//              softmax mass p) -> k_up (flags + up rows) -> k_down
+//   top-p      the same, the select workgroups finding the boundary of the
+//              cumulative softmax mass p (wg_topp_boundary)
 //   2:8        k_gate<SELECT_NM>: gate GEMV, SiLU keys ranked within each
 //              aligned group of 8 channels, and the W_up rows of the 2 kept
 //              per group -> k_down
@@ -38,60 +38,6 @@
 #include <type_traits>
 
 namespace sffn {
-
-// ---------------------------------------------------------------------------
-// Up kernel (Top-K): the gate kernel's row partition. Each lane group applies
-// the tokens' Top-K thresholds to its channels' keys (topk_on), writes the
-// flags act[t][i], and reads the W_up rows of its channels that some token
-// selected. h[i][t] = g[t][i] * (x_t . W_up[i]) if token t selected i, else 0.
-// ---------------------------------------------------------------------------
-template <typename TW, int NT, int LPR>
-__global__ __launch_bounds__(256) void k_up(const TW *__restrict__ x, int n, int d,
-                                            const TW *__restrict__ wu, int F,
-                                            const int2 *__restrict__ thr, uint8_t *__restrict__ act,
-                                            uint8_t *__restrict__ any, const float *__restrict__ gsel,
-                                            float *__restrict__ hbuf)
-{
-    constexpr int SUB = 64 / LPR;
-    constexpr int R = RowsPer<NT>::v;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int q = lane / LPR, li = lane % LPR;
-    const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
-    const int nv = max(0, min(R, F - row0));
-    float gv[R][NT];
-    uint32_t amask = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            gv[r][t] = 0.f;
-            if (r < nv && t < n) {
-                const size_t o = (size_t)t * F + row0 + r;
-                const float g = gsel[o];
-                const bool on = topk_on(g, row0 + r, thr[t]);
-                if (li == ((r * NT + t) & (LPR - 1))) act[o] = on;
-                if (on) {
-                    gv[r][t] = g;
-                    amask |= 1u << r;
-                }
-            }
-        }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
-    if (__ballot(amask != 0) == 0) return;
-    const TW *rows[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
-    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
-    up.run(rows, amask, d, li, x, d, n);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (((amask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
-                hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
-}
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup slots inside one launch. A slot is 64 bits: a value in the
@@ -180,12 +126,18 @@ __device__ __forceinline__ bool topk_poll(const uint64_t *p, uint32_t epoch, int
     return false;
 }
 
+// The select workgroups' LDS: counts per value bin (Top-K) or masses (top-p).
+template <bool MASS>
+using SelLds = typename std::conditional<MASS, ToppLds, TopkLds>::type;
+
 // One token's select by the whole workgroup: its keys staged (U > 0), its
 // boundary into thr_s[t] (bs_s[t] = -1: exact), and, with slot, the
-// prefetch estimate, b* and then the exact pair published there.
-template <int U>
-__device__ __noinline__ void topk_select_token(const float *__restrict__ gsel, int F, int K, TopkLds &L, float *kl,
-                                               int t, uint64_t *slot, uint32_t epoch, int2 *thr_s, int *bs_s)
+// prefetch estimate, b* and then the exact pair published there. MASS: the
+// top-p boundary of mass p (wg_topp_boundary), else the Top-K one of K.
+template <int U, bool MASS>
+__device__ __noinline__ void topk_select_token(const float *__restrict__ gsel, int F, int K, float p,
+                                               SelLds<MASS> &L, float *kl, int t, uint64_t *slot, uint32_t epoch,
+                                               int2 *thr_s, int *bs_s)
 {
     const float *s = gsel + (size_t)t * F;
     if constexpr (U > 0) {
@@ -193,7 +145,11 @@ __device__ __noinline__ void topk_select_token(const float *__restrict__ gsel, i
         wait_vm_lgkm<0>();
         __syncthreads();
     }
-    const int2 r = wg_topk_boundary<U>(s, F, K, L, kl, slot ? slot + 3 : nullptr, slot, epoch);
+    int2 r;
+    if constexpr (MASS)
+        r = wg_topp_boundary<U>(s, F, p, L, kl, slot ? slot + 3 : nullptr, slot, epoch);
+    else
+        r = wg_topk_boundary<U>(s, F, K, L, kl, slot ? slot + 3 : nullptr, slot, epoch);
     if (threadIdx.x == 0) {
         if (slot) {
             __hip_atomic_store(slot + 1, ((uint64_t)epoch << 32) | (uint32_t)r.x, __ATOMIC_RELAXED,
@@ -208,16 +164,17 @@ __device__ __noinline__ void topk_select_token(const float *__restrict__ gsel, i
     }
 }
 
-template <typename TW, int NT, int LPR, int U>
+template <typename TW, int NT, int LPR, int U, bool MASS>
 __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n, int d,
-                                                 const TW *__restrict__ wu, int F, int K, uint8_t *__restrict__ act,
+                                                 const TW *__restrict__ wu, int F, int K, float p,
+                                                 uint8_t *__restrict__ act,
                                                  uint8_t *__restrict__ any, const float *__restrict__ gsel,
                                                  float *__restrict__ hbuf, uint64_t *__restrict__ tslot,
                                                  const int *__restrict__ ctrl, int spin_max)
 {
     constexpr int SUB = 64 / LPR;
     constexpr int R = TopkRows<NT>::v;
-    __shared__ TopkLds L;
+    __shared__ SelLds<MASS> L;
     __shared__ float kl[U > 0 ? U * 256 : 1];  // a select's keys (U > 0)
     __shared__ __align__(16) uint32_t pf_lds[4][256];  // where the prefetch loads land (never read)
     __shared__ int2 thr_s[NT];                 // exact boundaries
@@ -233,7 +190,7 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     uint32_t epoch = 0;
     if (tid < n) epoch = (uint32_t)__hip_atomic_load(ctrl + kCtrlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (b < 8 * n) {  // a select workgroup
-        topk_select_token<U>(gsel, F, K, L, kl, b >> 3, topk_slot(tslot, set, b >> 3), epoch, nullptr,
+        topk_select_token<U, MASS>(gsel, F, K, p, L, kl, b >> 3, topk_slot(tslot, set, b >> 3), epoch, nullptr,
                              nullptr);  // (thread 0, which publishes, has the epoch)
         return;
     }
@@ -296,7 +253,7 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     uint32_t todo = 0;
     for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[0][t] << t;
     for (; todo; todo &= todo - 1)  // uniform over the workgroup
-        topk_select_token<U>(gsel, F, K, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
+        topk_select_token<U, MASS>(gsel, F, K, p, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
     __syncthreads();
 
     // the rows kept by bin, and the rows in b* (computed as if kept)
@@ -337,7 +294,7 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     todo = 0;
     for (int t = 0; t < n; ++t) todo |= (uint32_t)miss_s[1][t] << t;
     for (; todo; todo &= todo - 1)
-        topk_select_token<U>(gsel, F, K, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
+        topk_select_token<U, MASS>(gsel, F, K, p, L, kl, __ffs(todo) - 1, nullptr, 0, thr_s, bs_s);
     __syncthreads();
 
     // the flags: kept by bin, or settled by the exact pair in b*
@@ -704,41 +661,29 @@ static hipError_t run_decode(sffn_ctx &c, const FwdArgs &a)
     }
     if ((e = launch_gate(g)) != hipSuccess) return e;
 
-    // ---- Top-K: the select folded into the up rows ----
-    if (a.mode == SFFN_TOPK) {
+    // ---- Top-K and top-p: the select folded into the up rows ----
+    if (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP) {
         const int lpr = lpr_for(d);
         const dim3 ugrid(8 * n + row_blocks(F, lpr, TopkRows<NT>::v));  // 8 select workgroups per token, then the rows
         uint64_t *tslot = reinterpret_cast<uint64_t *>(ws + c.L.tslot);
         const int *ctrl = reinterpret_cast<const int *>(ws + c.L.ctrl);
-        auto go = [&](auto lpr_c, auto u_c) {
-            hipLaunchKernelGGL((k_up_topk<TW, NT, decltype(lpr_c)::value, decltype(u_c)::value>), ugrid, dim3(256), 0,
-                               st, x, n, d, wu, F, a.k, act, any, gsel, hbuf, tslot, ctrl, c.spin_max);
+        auto go = [&](auto lpr_c, auto u_c, auto mass_c) {
+            hipLaunchKernelGGL(
+                (k_up_topk<TW, NT, decltype(lpr_c)::value, decltype(u_c)::value, decltype(mass_c)::value>), ugrid,
+                dim3(256), 0, st, x, n, d, wu, F, a.k, a.tau, act, any, gsel, hbuf, tslot, ctrl, c.spin_max);
         };
-        auto go_lpr = [&](auto u_c) {
-            if (lpr == 64) go(std::integral_constant<int, 64>{}, u_c);
-            else if (lpr == 32) go(std::integral_constant<int, 32>{}, u_c);
-            else go(std::integral_constant<int, 16>{}, u_c);
+        auto go_lpr = [&](auto u_c, auto mass_c) {
+            if (lpr == 64) go(std::integral_constant<int, 64>{}, u_c, mass_c);
+            else if (lpr == 32) go(std::integral_constant<int, 32>{}, u_c, mass_c);
+            else go(std::integral_constant<int, 16>{}, u_c, mass_c);
         };
-        // the select workgroups keep a token's keys in LDS, or stream them for wider layers
-        if (F <= kTopkLdsKeys) go_lpr(std::integral_constant<int, kTopkLdsKeys / 256>{});
-        else go_lpr(std::integral_constant<int, 0>{});
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    // ---- top-p: select, then the up rows ----
-    if (a.mode == SFFN_TOPP) {
-        int2 *thr = reinterpret_cast<int2 *>(ws + c.L.thr);
-        if ((e = launch_topp_thr(gsel, n, F, a.tau, thr, st)) != hipSuccess) return e;
-        const int lpr = lpr_for(d);
-        const dim3 ugrid(row_blocks(F, lpr, RowsPer<NT>::v));
-        if (lpr == 64)
-            hipLaunchKernelGGL((k_up<TW, NT, 64>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
-                               hbuf);
-        else if (lpr == 32)
-            hipLaunchKernelGGL((k_up<TW, NT, 32>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
-                               hbuf);
-        else
-            hipLaunchKernelGGL((k_up<TW, NT, 16>), ugrid, dim3(256), 0, st, x, n, d, wu, F, thr, act, any, gsel,
-                               hbuf);
+        auto go_u = [&](auto mass_c) {
+            // the select workgroups keep a token's keys in LDS, or stream them for wider layers
+            if (F <= kTopkLdsKeys) go_lpr(std::integral_constant<int, kTopkLdsKeys / 256>{}, mass_c);
+            else go_lpr(std::integral_constant<int, 0>{}, mass_c);
+        };
+        if (a.mode == SFFN_TOPP) go_u(std::true_type{});
+        else go_u(std::false_type{});
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 

@@ -186,6 +186,46 @@ __device__ __forceinline__ uint32_t f2key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+// inverse of f2key (for the keys f2key produces)
+__device__ __forceinline__ float key2f(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Top-p masses (select_mass and the workgroup top-p select): the fixed-point
+// weight of key v against the token's largest key top, round(exp(v - top)
+// 2^44) with exp in fp32 (24 significant bits), so every sum of them is exact
+// and independent of order; and the target mass ceil(p Z) of a total Z,
+// clamped to [1, Z].
+__device__ __forceinline__ unsigned long long topp_mass(float v, float top)
+{
+    return (unsigned long long)(expf(v - top) * 17592186044416.0f + 0.5f);  // 2^44
+}
+
+__device__ __forceinline__ unsigned long long topp_target(float p, unsigned long long Z)
+{
+    const unsigned long long T = (unsigned long long)ceil((double)p * (double)Z);
+    return T < 1ull ? 1ull : T > Z ? Z : T;
+}
+
 // Operand types of __builtin_amdgcn_global_load_lds (global source, LDS
 // destination: each lane's bytes land at the destination + lane * size).
 typedef __attribute__((address_space(1))) const void gmem_t;

@@ -289,30 +289,6 @@ struct __align__(16) SelectMassLds {
     int scan_scratch[16];
 };
 
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v)
-{
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
-    return v;
-}
-
-// inverse of f2key (for the keys f2key produces)
-__device__ __forceinline__ float key2f(uint32_t k)
-{
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
 template <int KPT>
 __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, float p, SelectMassLds &L,
                                             const float (&kf)[KPT > 0 ? KPT : 1])
@@ -355,14 +331,9 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
         hi = fmaxf(hi, L.red[1][w]);
     }
     const float top = hi;
-    auto mass_of = [&](float v) -> unsigned long long {
-        return (unsigned long long)(expf(v - top) * 17592186044416.0f + 0.5f);  // 2^44
-    };
+    auto mass_of = [&](float v) -> unsigned long long { return topp_mass(v, top); };
     // the target mass from the total Z (the sum of the bin masses below)
-    auto target = [&](unsigned long long Z) {
-        const unsigned long long T = (unsigned long long)ceil((double)p * (double)Z);
-        return T < 1ull ? 1ull : T > Z ? Z : T;
-    };
+    auto target = [&](unsigned long long Z) { return topp_target(p, Z); };
 
     // The channels equal to the key kth that the prefix needs, given the
     // mass `need` still missing, are the first ceil(need / u) of them in

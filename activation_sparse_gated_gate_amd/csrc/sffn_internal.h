@@ -73,7 +73,6 @@ struct Layout {
     size_t ubits;     // batched: uint32 [words] union bitmap
     size_t bpart;     // batched split-K partials: fp32 [bpart_rows][max(d_ff, d_model)]
     int bpart_rows;   // splits x tokens that fit in bpart
-    size_t thr;       // top-p: int2 [max(ntp, max_tokens)] per-token boundary key and tie cutoff
     // batched token grouping (groups.hip)
     size_t gbits;     // uint32 [T][words] per-token channel masks
     size_t gcnt;      // int32 [kMaxTokenGroups][d_ff] per-group channel counts
@@ -212,7 +211,6 @@ hipError_t launch_bwd_setup(const Saved &sv, int T, int F, int d, int tp, float2
                             const uint16_t *x, const uint16_t *dy, uint16_t *xt, uint16_t *dyt, hipStream_t st);
 // Top-p: the same per-token pair, found by cumulative softmax mass p
 // (decode), and the batched select + flags.
-hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st);
 hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, uint8_t *act, uint16_t *G,
                                    uint32_t *ubits, hipStream_t st);
 // The union bitmap from the flags act [T][F] (replaces whatever it holds).

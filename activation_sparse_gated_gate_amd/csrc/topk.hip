@@ -1,19 +1,20 @@
-// Per-token Top-K selection over the SiLU gate keys, shared by the decode and
-// batched regimes ("Mixture-of-Channels" blog summary, "Dentro il 'mixture'":
-// each token keeps its K channels of largest SiLU(gate)), and the batched 2:8
+// Per-token Top-K and top-p selection of a batch over the SiLU gate keys
+// ("Mixture-of-Channels" blog summary, "Dentro il 'mixture'": each token
+// keeps its K channels of largest SiLU(gate)), and the batched 2:8
 // structured selection (the same summary's 2:8 option: the top 2 of every
-// aligned group of 8 channels).
+// aligned group of 8 channels). (At one to eight tokens the selects run
+// inside the up kernel's launch, decode.hip.)
 //
-// The select (select.h) finds, per token, the K-th largest key and a tie
-// cutoff. Channel i of token t is then selected iff
+// The select finds, per token, the K-th largest key and a tie cutoff (one
+// 1024-thread workgroup per token, select_kth in select.h; from 256 tokens
+// up, one 256-thread workgroup, wg_topk_boundary in topk_wg.h). Channel i of
+// token t is then selected iff
 //   key > kth  or  (key == kth and i <= cut)
 // (topk_on), so ties at the K-th value go to the lower channel indices and
-// exactly K channels are selected. For a batch, k_topk_select_flags applies it
-// right after the select, to the keys the select holds, and writes the
-// batch's flags, gate values and union bitmap. Top-p (k_topp_*) finds the
-// same pair by cumulative softmax mass instead of a count (select_mass); the
-// decode up kernel applies it where it reads the keys anyway. (The decode
-// Top-K folds its select into the up kernel, decode.hip.)
+// exactly K channels are selected. The select kernels apply it right after
+// the select, to the keys they hold, and write the batch's flags, gate
+// values and union bitmap. Top-p (k_topp_select_flags) finds the same pair
+// by cumulative softmax mass instead of a count (select_mass).
 #include <algorithm>
 
 #include "select.h"
@@ -120,20 +121,6 @@ __global__ __launch_bounds__(256) void k_topk_select_flags_wg(const float *__res
     }
 }
 
-// Top-p (decode): each token's boundary key and tie cutoff.
-template <int KPT>
-__global__ __launch_bounds__(1024) void k_topp_thr(const float *__restrict__ keys, int F, float p,
-                                                   int2 *__restrict__ thr)
-{
-    __shared__ SelectMassLds L;
-    const int t = blockIdx.x;
-    const float *s = keys + (size_t)t * F;
-    float kf[KPT > 0 ? KPT : 1];
-    load_keys<KPT>(s, F, kf);
-    const int2 r = select_mass<KPT>(s, F, p, L, kf);
-    if (threadIdx.x == 0) thr[t] = r;
-}
-
 // Batched top-p: the select of token t, then its flags.
 template <int KPT>
 __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restrict__ keys, int F, float p,
@@ -220,16 +207,6 @@ hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16
     const int tpb = T < 256 ? 1 : std::min(16, T / 128);
     hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + tpb - 1) / tpb), dim3(256), 0, st, keys, T, F, tpb,
                        act, G, ubits);
-    return hipGetLastError();
-}
-
-hipError_t launch_topp_thr(const float *keys, int T, int F, float p, int2 *thr, hipStream_t st)
-{
-    const dim3 grid(T), block(1024);
-    if (F <= 1024 * 4) hipLaunchKernelGGL(k_topp_thr<4>, grid, block, 0, st, keys, F, p, thr);
-    else if (F <= 1024 * 8) hipLaunchKernelGGL(k_topp_thr<8>, grid, block, 0, st, keys, F, p, thr);
-    else if (F <= 1024 * 16) hipLaunchKernelGGL(k_topp_thr<16>, grid, block, 0, st, keys, F, p, thr);
-    else hipLaunchKernelGGL(k_topp_thr<0>, grid, block, 0, st, keys, F, p, thr);
     return hipGetLastError();
 }
 

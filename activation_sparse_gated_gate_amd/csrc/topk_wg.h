@@ -266,4 +266,276 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// Top-p boundary of one token's keys by a workgroup of 256 threads: the
+// first channel, in the Top-K order (key descending, channel ascending), at
+// which the prefix of fixed-point masses (topp_mass against the token's
+// largest key) reaches T = topp_target(p, Z), Z the total mass; returned as
+// the pair topk_on applies. That channel is unique, so this is the result of
+// select_mass exactly.
+//
+// The passes follow wg_topk_boundary with a 64-bit mass per value bin in
+// place of the count: the largest key first; a prefetch estimate from every
+// 8th key (the coarse bin where the sample's mass from the top reaches the
+// target of min(1, 1.25 p)); the bin b* where the mass from the top reaches
+// T (published), need = T minus the mass above it; b*'s keys (up to
+// kToppCand) ranked by the mass ahead of each in the Top-K order, the
+// boundary being the one whose mass ahead is below need and reaches it with
+// its own. A fuller bin goes through an MSD radix select on f2key restricted
+// to b* with a mass per digit, and the ties at the boundary key are taken in
+// channel order: ceil(need left / their mass) of them.
+// ---------------------------------------------------------------------------
+constexpr int kToppCand = 256;
+
+struct __align__(16) ToppLds {
+    unsigned long long mass[kKeyBins];  // value bins, then 256 radix digits
+    unsigned long long hist64m[64];     // the sample's coarse bins
+    unsigned long long cand[kToppCand];  // f2key << 32 | ~channel
+    unsigned long long cand_w[kToppCand];
+    unsigned long long cand_ahead[64];
+    unsigned long long scan64[4];
+    unsigned long long shm[2];  // need at b*; need within the radix digit
+    float red[4];
+    int sh[6];  // b*, -, -, gathered; then the result
+    int scan_scratch[4];
+};
+
+// Inclusive prefix sum of a 64-bit value over the 256 threads; *total gets
+// the sum of all (every thread). Contains a barrier.
+__device__ __forceinline__ unsigned long long block_incl_scan_u64(unsigned long long v, ToppLds &L,
+                                                                  unsigned long long *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_incl_scan_u64(v);
+    if (lane == 63) L.scan64[wave] = v;
+    __syncthreads();
+    unsigned long long add = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) add += w < wave ? L.scan64[w] : 0ull;
+    *total = L.scan64[0] + L.scan64[1] + L.scan64[2] + L.scan64[3];
+    return v + add;
+}
+
+template <int U>
+__device__ __forceinline__ int2 wg_topp_boundary(const float *__restrict__ s, int F, float p, ToppLds &L,
+                                                 const float *__restrict__ kl, uint64_t *eslot, uint64_t *cslot,
+                                                 uint32_t epoch)
+{
+    constexpr int V = U > 0 ? U : 16;  // keys per thread and round
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long *mass = L.mass;
+    int *sh = L.sh;
+    // fn(u, j, v) over this thread's positions j = tid + 256 u, the keys past
+    // F being -inf (mass 0)
+    auto for_keys = [&](auto &&fn) {
+        if constexpr (U > 0) {
+            static_assert(U % 8 == 0, "keys in rounds of 8 per thread");
+#pragma unroll 1
+            for (int u0 = 0; u0 < U; u0 += 8) {
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = kl[(u0 + e) * 256 + tid];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fn(u0 + e, (u0 + e) * 256 + tid, o[e]);
+            }
+        } else {
+            for (int j0 = 0; j0 < F; j0 += 256 * V) {
+                float o[V];
+#pragma unroll
+                for (int u = 0; u < V; ++u) o[u] = s[min(j0 + u * 256 + tid, F - 1)];
+#pragma unroll
+                for (int u = 0; u < V; ++u) fn(u, j0 + u * 256 + tid, j0 + u * 256 + tid < F ? o[u] : -INFINITY);
+            }
+        }
+    };
+
+    // ---- the largest key ----
+    float mx = -INFINITY;
+    for_keys([&](int, int, float v) { mx = fmaxf(mx, v); });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) L.red[wave] = mx;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mass[8 * tid + e] = 0ull;
+    if (tid < 64) L.hist64m[tid] = 0ull;
+    __syncthreads();
+    mx = fmaxf(fmaxf(L.red[0], L.red[1]), fmaxf(L.red[2], L.red[3]));
+
+    if (eslot) {
+        // the prefetch estimate: a sample of every 8th position
+        int cb = 64;  // none: nothing to prefetch (keys not in LDS)
+        if constexpr (U > 0) {
+#pragma unroll
+            for (int v = 0; v < U / 8; ++v) {
+                const float key = kl[8 * (v * 256 + tid)];
+                atomicAdd(&L.hist64m[key_bin(key) >> 5], topp_mass(key, mx));
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const unsigned long long incl = wave_incl_scan_u64(L.hist64m[63 - tid]);  // from the top
+                const unsigned long long ts = topp_target(fminf(1.f, 1.25f * p), __shfl(incl, 63, 64));
+                const uint64_t hit = __ballot(incl >= ts);
+                cb = hit ? 63 - (__ffsll((long long)hit) - 1) : 0;
+            }
+        }
+        if (tid == 0)
+            __hip_atomic_store(eslot, ((uint64_t)epoch << 32) | (uint32_t)cb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- mass per value bin; the bin b* where the mass from the top reaches T ----
+    for_keys([&](int, int, float v) { atomicAdd(&mass[key_bin(v)], topp_mass(v, mx)); });
+    __syncthreads();
+    {
+        // thread tid owns bins 8 tid .. 8 tid + 7
+        unsigned long long c[8], local = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            c[e] = mass[8 * tid + e];
+            local += c[e];
+        }
+        unsigned long long Z = 0;
+        const unsigned long long incl = block_incl_scan_u64(local, L, &Z);
+        const unsigned long long Tm = topp_target(p, Z);
+        unsigned long long run = Z - incl;  // mass in the bins above this thread's
+        if (run < Tm && Tm <= run + local) {
+#pragma unroll
+            for (int e = 7; e >= 0; --e) {
+                if (run < Tm && Tm <= run + c[e]) {
+                    sh[0] = 8 * tid + e;
+                    sh[3] = 0;
+                    L.shm[0] = Tm - run;
+                }
+                run += c[e];
+            }
+        }
+    }
+    __syncthreads();
+    const int bs = sh[0];
+    unsigned long long need = L.shm[0];
+    if (cslot && tid == 0)
+        __hip_atomic_store(cslot, ((uint64_t)epoch << 32) | (uint32_t)bs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- b*'s keys with their masses ----
+    if constexpr (U > 0) {
+        static_assert(U <= 32, "one match bit per key");
+        uint32_t mb = 0;
+        for_keys([&](int u, int, float v) { mb |= (uint32_t)(key_bin(v) == bs) << u; });
+        if (mb) {
+            int slot = atomicAdd(&sh[3], __popc(mb));
+            for (uint32_t m = mb; m; m &= m - 1) {
+                const int j = (__ffs(m) - 1) * 256 + tid;
+                if (slot < kToppCand) {
+                    const float v = kl[j];
+                    L.cand[slot] = (unsigned long long)f2key(v) << 32 | (uint32_t)~j;
+                    L.cand_w[slot] = topp_mass(v, mx);
+                }
+                ++slot;
+            }
+        }
+    } else {
+        for_keys([&](int, int j, float v) {
+            if (key_bin(v) == bs) {
+                const int slot = atomicAdd(&sh[3], 1);
+                if (slot < kToppCand) {
+                    L.cand[slot] = (unsigned long long)f2key(v) << 32 | (uint32_t)~j;
+                    L.cand_w[slot] = topp_mass(v, mx);
+                }
+            }
+        });
+    }
+    if (tid < 64) L.cand_ahead[tid] = 0ull;
+    __syncthreads();
+    const int cnt = sh[3];
+    if (cnt <= kToppCand) {
+        if (cnt <= 64) {
+            // wavefront w sums, for each candidate, the masses of its quarter
+            // of the candidates ahead of it
+            const int c = tid & 63, w = tid >> 6;
+            if (c < cnt) {
+                const unsigned long long me = L.cand[c];
+                unsigned long long ahead = 0;
+                for (int m = w * 16; m < min(cnt, w * 16 + 16); ++m)
+                    if (L.cand[m] > me) ahead += L.cand_w[m];
+                if (ahead) atomicAdd(&L.cand_ahead[c], ahead);
+            }
+            __syncthreads();
+            if (tid < cnt) {
+                const unsigned long long a = L.cand_ahead[tid];
+                if (a < need && need <= a + L.cand_w[tid]) {
+                    const unsigned long long me = L.cand[tid];
+                    sh[4] = (int)(uint32_t)(me >> 32);
+                    sh[5] = (int)~(uint32_t)me;
+                }
+            }
+        } else {
+            for (int c = tid; c < cnt; c += 256) {
+                const unsigned long long me = L.cand[c];
+                unsigned long long a = 0;
+                for (int m = 0; m < cnt; ++m)
+                    if (L.cand[m] > me) a += L.cand_w[m];
+                if (a < need && need <= a + L.cand_w[c]) {
+                    sh[4] = (int)(uint32_t)(me >> 32);
+                    sh[5] = (int)~(uint32_t)me;
+                }
+            }
+        }
+        __syncthreads();
+        const int2 r = make_int2(sh[4], sh[5]);
+        __syncthreads();  // sh and the candidates are reused by the next select
+        return r;
+    }
+    // ---- a full bin: radix select on f2key within b*, a mass per digit ----
+    uint32_t prefix = 0, pmask = 0;
+#pragma unroll 1
+    for (int ps = 0; ps < 4; ++ps) {
+        const int shift = 24 - 8 * ps;
+        mass[tid] = 0ull;
+        __syncthreads();
+        for (int j = tid; j < F; j += 256) {
+            const float v = U > 0 ? kl[j] : s[j];
+            const uint32_t key = f2key(v);
+            if (key_bin(v) == bs && (key & pmask) == prefix) atomicAdd(&mass[(key >> shift) & 255u], topp_mass(v, mx));
+        }
+        __syncthreads();
+        const unsigned long long cm = mass[255 - tid];  // thread tid owns digit 255 - tid: from the top
+        unsigned long long tot = 0;
+        const unsigned long long incl = block_incl_scan_u64(cm, L, &tot);
+        if (incl - cm < need && need <= incl) {
+            sh[0] = 255 - tid;
+            L.shm[1] = need - (incl - cm);
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh[0] << shift;
+        pmask |= 0xffu << shift;
+        need = L.shm[1];
+        __syncthreads();  // mass, sh and shm are rewritten by the next pass
+    }
+    // the keys equal to the boundary key that the prefix needs: the first
+    // ceil(need / their mass) of them in channel order
+    const unsigned long long u = topp_mass(key2f(prefix), mx);
+    const unsigned long long want = u > 0 ? (need + u - 1) / u : 1ull;
+    const int seg = (F + 255) / 256;
+    const int i0 = min(F, tid * seg), i1 = min(F, i0 + seg);
+    int eq = 0;
+    for (int i = i0; i < i1; ++i) eq += f2key(U > 0 ? kl[i] : s[i]) == prefix;
+    const int eq_incl = block_incl_scan(eq, L.scan_scratch), before = eq_incl - eq;
+    if (tid == 255) sh[2] = eq_incl;
+    __syncthreads();
+    const int take = (int)min(want, (unsigned long long)max(1, sh[2]));
+    if (before < take && take <= before + eq) {
+        int left = take - before, cut = i0;
+        for (int i = i0; i < i1 && left > 0; ++i)
+            if (f2key(U > 0 ? kl[i] : s[i]) == prefix) {
+                cut = i;
+                --left;
+            }
+        sh[4] = (int)prefix;
+        sh[5] = cut;
+    }
+    __syncthreads();
+    const int2 r = make_int2(sh[4], sh[5]);
+    __syncthreads();
+    return r;
+}
+
 }  // namespace sffn

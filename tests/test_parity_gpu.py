@@ -437,41 +437,48 @@ def test_topk_select_crowded_bin(n):
 
 
 @pytest.mark.parametrize("n", [1, 3])
-def test_topk_consecutive_forwards_take_their_own_boundary(n):
-    """Forwards in a row on one handle with a different K and input each time:
-    every forward's select must use its own per-token boundary, never one left
-    in the workspace by the forward before."""
+@pytest.mark.parametrize("mode", ["topk", "topp"])
+def test_topk_consecutive_forwards_take_their_own_boundary(n, mode):
+    """Forwards in a row on one handle with a different K (or p) and input
+    each time: every forward's select must use its own per-token boundary,
+    never one left in the workspace by the forward before."""
     d, f = 256, 3000
     lay = inputs.make_layer(38, d, f, "bf16")
     ffn = S.SparseFFN(d, f, 8, "bf16")
-    for q, k in enumerate((37, 1500, 37, 2999, 1)):
-        say(f"case topk consecutive forwards n={n} K={k}")
+    params = (37, 1500, 37, 2999, 1) if mode == "topk" else (0.05, 0.6, 0.05, 1.0, 0.3)
+    for q, v in enumerate(params):
+        say(f"case {mode} consecutive forwards n={n} param={v}")
         x = inputs.make_x(38 + q, n, d, "bf16")
-        ref = oracle_forward(lay, x, "topk", k=k)
-        got = run_gpu(lay, x, "topk", k=k, ffn=ffn)
-        compare(lay, x, "topk", ref, got)
-        assert (got.cnt[:n] == k).all()
+        kw = dict(k=v) if mode == "topk" else dict(tau=v)
+        ref = oracle_forward(lay, x, mode, **kw)
+        got = run_gpu(lay, x, mode, ffn=ffn, **kw)
+        compare(lay, x, mode, ref, got)
+        if mode == "topk":
+            assert (got.cnt[:n] == v).all()
 
 
-def test_topk_select_wait_give_up_selects_locally():
-    """With the poll limit at -1 no workgroup of the Top-K up kernel waits for
-    the select workgroups: each runs the select itself, and the sets are those
-    of a forward that waited (the down projection gives up too, so y is not
-    compared). With the default limit back, the forward matches the oracle."""
-    d, f, n, k = 512, 4096, 3, 500
-    say(f"case topk select give-up d={d} F={f} n={n}")
+@pytest.mark.parametrize("mode", ["topk", "topp"])
+def test_topk_select_wait_give_up_selects_locally(mode):
+    """With the poll limit at -1 no workgroup of the Top-K / top-p up kernel
+    waits for the select workgroups: each runs the select itself, and the sets
+    are those of a forward that waited (the down projection gives up too, so y
+    is not compared). With the default limit back, the forward matches the
+    oracle."""
+    d, f, n = 512, 4096, 3
+    kw = dict(k=500) if mode == "topk" else dict(tau=0.4)
+    say(f"case {mode} select give-up d={d} F={f} n={n}")
     lay = inputs.make_layer(39, d, f, "bf16")
     x = inputs.make_x(39, n, d, "bf16")
     ffn = S.SparseFFN(d, f, n, "bf16")
-    ref = oracle_forward(lay, x, "topk", k=k)
-    waited = run_gpu(lay, x, "topk", k=k, ffn=ffn)
-    compare(lay, x, "topk", ref, waited)
+    ref = oracle_forward(lay, x, mode, **kw)
+    waited = run_gpu(lay, x, mode, ffn=ffn, **kw)
+    compare(lay, x, mode, ref, waited)
     ffn.set_spin_limit(-1)
-    local = run_gpu(lay, x, "topk", k=k, ffn=ffn)
+    local = run_gpu(lay, x, mode, ffn=ffn, **kw)
     assert np.array_equal(local.sets, waited.sets)
     ffn.set_spin_limit(1 << 18)
-    got = run_gpu(lay, x, "topk", k=k, ffn=ffn)
-    compare(lay, x, "topk", ref, got)
+    got = run_gpu(lay, x, mode, ffn=ffn, **kw)
+    compare(lay, x, mode, ref, got)
 
 
 @pytest.mark.parametrize("n", [1, 2, 12])

@@ -55,7 +55,11 @@ Layout make_layout(const sffn_shape &s)
     // splits of 64 tokens (forwards smaller than the handle's maximum)
     const size_t prow = T < 512 ? (size_t)splits_max((int)T) * T : 0, pmin = 16 * (T < 64 ? T : 64);
     L.bpart_rows = batched ? (int)(prow > pmin ? prow : pmin) : 0;
-    L.bpart = take((size_t)L.bpart_rows * (F > d ? F : d) * 4);
+    // and, from 512 tokens, one round of 256 x 256 tiles on kUpRestCUs CUs
+    // (the split rest of the up GEMM)
+    const size_t pel = (size_t)L.bpart_rows * (F > d ? F : d), pround = T >= 512 ? (size_t)kUpRestCUs * 65536 : 0;
+    L.bpart_elems = pel > pround ? pel : pround;
+    L.bpart = take(L.bpart_elems * 4);
     if (batched) {
         const size_t W = (size_t)L.words, NG = kMaxTokenGroups;
         L.gbits = take(T * W * 4);

@@ -53,6 +53,9 @@ enum EpiKind { EPI_GATE = 0, EPI_UP = 1, EPI_DOWN = 2, EPI_BWD = 3, EPI_DOWN_ACC
 
 struct EpiArgs {
     int kind;
+    int upart;          // gate or up GEMM in two launches (0: in one): 1 = the whole rounds of tiles, 2 = the rest
+    int ncu, smax;      // (upart) compute units, and the most K splits of the rest
+    int rest_u;         // (upart) N extent: the gate's d_ff; < 0: the union size, *ucount (up)
     int mode;           // sffn_mode (gate)
     float tau;
     int T, F, d;
@@ -77,6 +80,30 @@ struct EpiArgs {
     uint16_t *H2, *DUT, *DZT, *HT;
     int tp;
 };
+
+// Large gate and up GEMMs in two launches. One launch of BN-wide tiles over N
+// columns can end with a round of tiles that few CUs work on (2048 prefill
+// tokens of a 28672-channel layer: the gate's 896 tiles of 256 x 256 are 3.5
+// rounds on 256 CUs; its union covering 38 % of the channels, the up GEMM's
+// 344 tiles are 1.3 rounds). The first launch takes the N tiles of the whole
+// rounds (ncu / MT N tiles of MT M tiles each, per round), the second the
+// rest, its K split S ways so that rest x S tiles still fill the CUs (never
+// more than ncu tiles: the partial buffer holds ncu tiles of BM x BN). The up
+// GEMM's N, the union (U entries), is known only on the device: the split is
+// taken there, from the union size.
+struct RestSplit {
+    int nfull, ntt, S;  // N tiles of the whole rounds, N tiles in all, K splits of the rest
+};
+__host__ __device__ inline RestSplit rest_split(int U, int BN, int MT, int ncu, int smax)
+{
+    const int ntt = (U + BN - 1) / BN;
+    const int per = ncu / MT > 1 ? ncu / MT : 1;
+    const int nfull = ntt / per * per;
+    const int rest = (ntt - nfull) * MT;
+    int S = rest > 0 ? ncu / rest : 1;
+    S = S < 1 ? 1 : (S > smax ? smax : S);
+    return {nfull, ntt, S};
+}
 
 // Backward values of one (token, channel) from the product v = dy . W_down[i]:
 // du = v g(z), dz = v u g'(z), h = g(z) u; zero where the channel is off.
@@ -151,7 +178,8 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
 // ---------------------------------------------------------------------------
 // Tile epilogue shared by the GEMM kernels. Element (i, j, r) of lane `lane`
 // is row rowof(i, r), column colof(j) of the tile (MFMA accumulator layout).
-// With S > 1 (split K) the fp32 tile goes to part[z][m][n]; otherwise the
+// With S > 1 (split K) the fp32 tile goes to the partial buffer, element
+// (m, n) at poff + (m - m0) part_ld + (n - n0); otherwise the
 // epilogue kind EK (and for the gate the mode GM) is applied. Both are
 // template parameters, and the branches sit outside the unrolled element
 // loops, so the accumulators stay in registers.
@@ -159,7 +187,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
 template <int MF, int TM, int TN, int NTHR, int BN, int EK, int GM, typename AccT>
 __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int lane, int m0, int n0, int arow,
                                               int bcol, int M, int nlim, int S, float *__restrict__ part,
-                                              int part_ld, const EpiArgs &epi, uint32_t *ubits_lds,
+                                              size_t poff, int part_ld, const EpiArgs &epi, uint32_t *ubits_lds,
                                               const int *uloc)
 {
     constexpr int ACC = MF == 32 ? 16 : 4;
@@ -176,7 +204,7 @@ __device__ __forceinline__ void tile_epilogue(AccT (&acc)[TM][TN], int tid, int 
 #pragma unroll
                 for (int r = 0; r < ACC; ++r) {
                     const int m = rowof(i, r), n = colof(j);
-                    if (m < M && n < nlim) part[((size_t)blockIdx.z * M + m) * part_ld + n] = acc[i][j][r];
+                    if (m < M && n < nlim) part[poff + (size_t)(m - m0) * part_ld + (n - n0)] = acc[i][j][r];
                 }
         return;
     }
@@ -423,9 +451,26 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     const int wm = wave / WN, wn = wave % WN;
     // XCD-aware tile order: the M tiles of one N tile run on one XCD
     const int MT = (M + BM - 1) / BM, NTT = (N + BN - 1) / BN;
-    const int xcd = blockIdx.x % 8, jt = blockIdx.x / 8;
-    const int mi = jt % MT, ni = (jt / MT) * 8 + xcd;
-    if (ni >= NTT) return;
+    int mi, ni, z = blockIdx.z, S = gridDim.z, tile_p = -1;
+    if ((EK == EPI_UP || EK == EPI_GATE) && epi.upart == 2) {
+        // the rest after the whole rounds (the union size comes from the up
+        // GEMM's first launch): list position p = (split, N tile, M tile),
+        // dealt to the XCDs in contiguous runs (a run shares weight rows)
+        const RestSplit u = rest_split(epi.rest_u >= 0 ? epi.rest_u : *epi.ucount, BN, MT, epi.ncu, epi.smax);
+        const int tiles = (u.ntt - u.nfull) * MT, len = tiles * u.S, run = (len + 7) / 8;
+        const int slot = blockIdx.x / 8, p = (blockIdx.x % 8) * run + slot;
+        if (slot >= run || p >= len) return;
+        z = p / tiles;
+        S = u.S;
+        mi = (p % tiles) % MT;
+        ni = u.nfull + (p % tiles) / MT;
+        tile_p = p;
+    } else {
+        const int xcd = blockIdx.x % 8, jt = blockIdx.x / 8;
+        mi = jt % MT;
+        ni = (jt / MT) * 8 + xcd;
+        if (ni >= NTT) return;
+    }
     const int m0 = mi * BM, n0 = ni * BN;
     int nlim = N, klim = K;
     if constexpr (EK == EPI_UP) {
@@ -493,10 +538,11 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         }
         __syncthreads();
         nlim = min(N, utot);
+        if (epi.upart == 1) nlim = min(nlim, rest_split(utot, BN, MT, epi.ncu, epi.smax).nfull * BN);
         // one workgroup per N tile publishes its part; the first, the size
-        if (blockIdx.z == 0 && mi == 0) {
+        if (z == 0 && mi == 0) {
             for (int j = tid; j < BN && n0 + j < nlim; j += 64 * WM * WN) epi.uidx[n0 + j] = uloc[j];
-            if (n0 == 0 && tid == 0) *epi.ucount = utot;
+            if (n0 == 0 && tid == 0 && epi.upart != 2) *epi.ucount = utot;
         }
     } else if (ncount) {
         if constexpr (BNN) klim = min(K, *ncount);
@@ -508,13 +554,15 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
             for (int w = tid; w < (epi.F + 31) / 32; w += 64 * WM * WN) epi.ubits[w] = 0;
     }
     if (n0 >= nlim || m0 >= M) return;
-    const int S = gridDim.z;
     int kb = 0, ke = klim;
     if (S > 1) {
         const int steps = (klim + BK - 1) / BK;
-        kb = (int)(((long long)steps * blockIdx.z) / S) * BK;
-        ke = min(klim, (int)(((long long)steps * (blockIdx.z + 1)) / S) * BK);
+        kb = (int)(((long long)steps * z) / S) * BK;
+        ke = min(klim, (int)(((long long)steps * (z + 1)) / S) * BK);
     }
+    // split K: this tile's partials (the up GEMM's rest: tile p at [p][BM][BN])
+    const size_t poff = tile_p >= 0 ? (size_t)tile_p * BM * BN : ((size_t)z * M + m0) * part_ld + n0;
+    const int pld = tile_p >= 0 ? BN : part_ld;
     const int nsteps = ke > kb ? (ke - kb + BK - 1) / BK : 0;
     const bf16_t *zero = reinterpret_cast<const bf16_t *>(g_zero16);
     // BNN: K row r keeps N chunk p at slot p ^ nswz(r)
@@ -724,8 +772,90 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         if constexpr (NS > 3) step(std::integral_constant<int, 3>{}, i + 3);
     }
     wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
-    tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, part_ld, epi,
-                                                ubits_lds, uloc);
+    tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, poff, pld,
+                                                epi, ubits_lds, uloc);
+}
+
+// Sum of the rest launch's split partials (tile p at part[p][BM][BN]) in
+// split order, with the gate or up epilogue (gate: also the union bits; up:
+// zeros in the pad columns up to a multiple of 8). Its extent and split
+// count follow from the N extent as in the GEMM; with one split the GEMM has
+// applied the epilogue itself. BN = 256: a lane takes 4 columns of a tile
+// row, a wavefront 4 rows (their loads in flight together), a workgroup
+// step 16 rows of one tile; the union bits of a step go out as one atomic
+// per word.
+template <int EK>
+__global__ __launch_bounds__(256) void k_rest_sum(const float *__restrict__ part, int M, int BM, int BN, EpiArgs epi)
+{
+    constexpr int RW = 4, RB = 4 * RW;
+    __shared__ uint32_t ub[4][8];
+    const int U = epi.rest_u >= 0 ? epi.rest_u : *epi.ucount, MT = (M + BM - 1) / BM;
+    const RestSplit u = rest_split(U, BN, MT, epi.ncu, epi.smax);
+    if (u.S < 2) return;
+    const int tiles = (u.ntt - u.nfull) * MT, padlim = EK == EPI_UP ? (U + 7) & ~7 : U;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const bool bits = EK == EPI_GATE && epi.mode == SFFN_THRESHOLD;
+    const size_t zs = (size_t)tiles * BM * BN;
+    for (int r0 = blockIdx.x * RB; r0 < tiles * BM; r0 += gridDim.x * RB) {
+        const int t = r0 / BM, rb = r0 % BM + wv * RW;  // BM is a multiple of RB: one tile
+        const int n = (u.nfull + t / MT) * BN + 4 * lane, mb = (t % MT) * BM + rb;
+        const float *src = part + ((size_t)t * BM + rb) * BN + 4 * lane;
+        float4 p[RW][4];
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                p[i][s] = *reinterpret_cast<const float4 *>(src + (size_t)i * BN + zs * min(s, u.S - 1));
+        uint32_t b = 0;
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const int m = mb + i;
+            if (m >= M || n >= padlim) continue;
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (s < u.S) {
+                    v[0] += p[i][s].x;
+                    v[1] += p[i][s].y;
+                    v[2] += p[i][s].z;
+                    v[3] += p[i][s].w;
+                }
+            if constexpr (EK == EPI_UP) {
+                // four bf16 of H in one 8-byte store (n and the row stride are multiples of 4)
+                const int tr = epi.tmap ? epi.tmap[m] : m;
+                uint16_t h[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    h[c] = 0;
+                    if (n + c < U) {
+                        const int ch = epi.uidx[n + c];
+                        h[c] = f2bf(bf2f(epi.G[(size_t)tr * epi.F + ch]) * v[c]);
+                        if (epi.usave) epi.usave[(size_t)tr * epi.F + ch] = v[c];
+                    }
+                }
+                *reinterpret_cast<uint2 *>(epi.H + (size_t)m * epi.hld + n) =
+                    make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (n + c < U && epilogue(epi, m, n + c, v[c])) b |= 1u << c;
+            }
+        }
+        if (bits) {
+            // word k of the tile's 256 columns: lanes 8k .. 8k+7, 4 bits each
+            uint32_t w = b << (4 * (lane & 7));
+            w |= __shfl_xor(w, 1, 64);
+            w |= __shfl_xor(w, 2, 64);
+            w |= __shfl_xor(w, 4, 64);
+            if ((lane & 7) == 0) ub[wv][lane >> 3] = w;
+            __syncthreads();
+            if (threadIdx.x < 8) {
+                const uint32_t o = ub[0][threadIdx.x] | ub[1][threadIdx.x] | ub[2][threadIdx.x] | ub[3][threadIdx.x];
+                if (o) atomicOr(&epi.ubits[((u.nfull + t / MT) * BN) / 32 + threadIdx.x], o);
+            }
+            __syncthreads();
+        }
+    }
 }
 
 // Sum the split-K partials in order and apply the epilogue (gate: also the
@@ -909,6 +1039,58 @@ static int split_for(const sffn_ctx &c, long long tiles, int K, int M, int part_
     return S;
 }
 
+// Gate or up GEMM on 256 x 256 tiles in two launches, whole rounds and the
+// K-split rest (rest_split), plus the rest's partial sum. u_host: the gate's
+// N (d_ff), or -1 for the up GEMM (N = the union, at most d_ff, counted on
+// the device). Returns false, having launched nothing, where the split does
+// not apply: other tiles, no whole round, a rest that one launch runs as
+// well, or a partial buffer smaller than a round of tiles.
+template <int EK>
+static bool launch_rounds_rest(const sffn_ctx &c, const Cfg &cf, int mt, hipStream_t st, int T, int F, int d,
+                               const bf16_t *x, const bf16_t *w, float *part, EpiArgs ep, int u_host, hipError_t &e)
+{
+    constexpr int smax = 4;
+    const int BN = cf.bn(), nt = (F + BN - 1) / BN, per = max(1, c.n_cu / mt), nfull_max = nt / per * per;
+    if (cf.wn != 4 || BN != 256 || cf.bm() % 16 || nfull_max == 0 || c.L.bpart_elems < (size_t)c.n_cu * cf.bm() * BN)
+        return false;
+    // the rest's largest list and row count over the N extents it may meet
+    int len_max = 0, rows_max = 0;
+    for (int u = u_host >= 0 ? nt : 1; u <= nt; ++u) {
+        const RestSplit s = rest_split(u * BN, BN, mt, c.n_cu, smax);
+        const int tiles = (s.ntt - s.nfull) * mt;
+        len_max = max(len_max, tiles * s.S);
+        if (s.S > 1) rows_max = max(rows_max, tiles * cf.bm());
+    }
+    if (u_host >= 0 && rows_max == 0) return false;  // no rest, or one split: one launch
+    ep.ncu = c.n_cu;
+    ep.smax = smax;
+    ep.rest_u = u_host;
+    if (u_host >= 0) {
+        // the gate: the whole rounds are known here
+        const int nfull = rest_split(u_host, BN, mt, c.n_cu, smax).nfull;
+        ep.upart = 0;
+        dispatch_mfma<false, EK>(cf, tile_grid(nfull, mt, 1), st, T, nfull * BN, d, x, d, w, d, nullptr, nullptr, part,
+                                 F, ep);
+    } else {
+        ep.upart = 1;
+        dispatch_mfma<false, EK>(cf, tile_grid(nfull_max, mt, 1), st, T, F, d, x, d, w, d, nullptr, nullptr, part, F,
+                                 ep);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return true;
+    if (len_max > 0) {
+        ep.upart = 2;
+        dispatch_mfma<false, EK>(cf, dim3(8 * ((len_max + 7) / 8)), st, T, F, d, x, d, w, d, nullptr, nullptr, part, F,
+                                 ep);
+        if ((e = hipGetLastError()) != hipSuccess) return true;
+    }
+    if (rows_max > 0) {  // 16 tile rows per workgroup
+        hipLaunchKernelGGL(k_rest_sum<EK>, dim3(min(8192, (rows_max + 15) / 16)), dim3(256), 0, st, part, T, cf.bm(),
+                           BN, ep);
+        e = hipGetLastError();
+    }
+    return true;
+}
+
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
 {
     const sffn_shape &S = c.shape;
@@ -966,11 +1148,15 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         const int nt = (F + cg.bn() - 1) / cg.bn(), mtg = (T + cg.bm() - 1) / cg.bm();
         const int sk = wide ? 2 : split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
-        dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, part, F,
-                                       ep);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (sk > 1) {
-            if ((e = launch_splitk_sum(st, part, sk, T, F, F, nullptr, ep)) != hipSuccess) return e;
+        if (!wide && launch_rounds_rest<EPI_GATE>(c, cg, mtg, st, T, F, d, x, wg, part, ep, F, e)) {
+            if (e != hipSuccess) return e;
+        } else {
+            dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, part,
+                                           F, ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (sk > 1) {
+                if ((e = launch_splitk_sum(st, part, sk, T, F, F, nullptr, ep)) != hipSuccess) return e;
+            }
         }
         if (ev1) hipEventRecord(ev1, st);
     }
@@ -1053,12 +1239,17 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     {
         ep.kind = EPI_UP;
         const int nt = (F + cf.bn() - 1) / cf.bn();
-        const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-        dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, nullptr, nullptr, part, F,
-                                      ep);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (sk > 1) {
-            if ((e = launch_splitk_sum(st, part, sk, T, F, F, ncount, ep)) != hipSuccess) return e;
+        // 256 x 256 tiles: the whole rounds, then the rest split along K
+        if (launch_rounds_rest<EPI_UP>(c, cf, mt, st, T, F, d, x, wu, part, ep, -1, e)) {
+            if (e != hipSuccess) return e;
+        } else {
+            const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
+            dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, nullptr, nullptr, part, F,
+                                          ep);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (sk > 1) {
+                if ((e = launch_splitk_sum(st, part, sk, T, F, F, ncount, ep)) != hipSuccess) return e;
+            }
         }
     }
     // ---- 3. down GEMM, K = union ----

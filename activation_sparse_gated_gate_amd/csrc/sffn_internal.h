@@ -43,6 +43,9 @@ constexpr int kDownGroupsMax = 64;   // channel groups of the split down project
 constexpr int kDownSliceCols = 128;  // output columns per down-projection workgroup
 // Decode Top-K boundary slots: 8 sets x kDecodeMaxTokens tokens x {boundary bin, key, cutoff, prefetch estimate}.
 constexpr int kTopkSlots = 8 * 8 * 4;
+// compute units the batched partial buffer is sized for (the up GEMM's split
+// rest needs one round of 256 x 256 tiles; on more CUs it runs in one launch)
+constexpr int kUpRestCUs = 256;
 constexpr int kDownRangeMax = 8192;  // channels of one down-projection group (32 per thread)
 static_assert(kMaxDffConst <= kDownGroupsMax * kDownRangeMax, "the widest layer fits the groups");
 // Channel groups of the decode down projection for d_ff = F: 16, so that the
@@ -73,6 +76,7 @@ struct Layout {
     size_t ubits;     // batched: uint32 [words] union bitmap
     size_t bpart;     // batched split-K partials: fp32 [bpart_rows][max(d_ff, d_model)]
     int bpart_rows;   // splits x tokens that fit in bpart
+    size_t bpart_elems;  // fp32 elements of bpart
     // batched token grouping (groups.hip)
     size_t gbits;     // uint32 [T][words] per-token channel masks
     size_t gcnt;      // int32 [kMaxTokenGroups][d_ff] per-group channel counts

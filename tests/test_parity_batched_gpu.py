@@ -205,6 +205,29 @@ def test_batched_handle_larger_than_batch_splits_within_its_buffer():
         compare(lay, x, mode, ref, got)
 
 
+@pytest.mark.parametrize("n,f,mode,kw", [
+    (2048, 8448, "dense_silu", {}),           # 33 N tiles: a whole round (32) and a rest of 1
+    (2000, 8195, "dense_relu", {}),           # ragged tokens and union (pad columns in the rest)
+    (2048, 8192, "dense_silu", {}),           # the union ends with the round: no rest
+    (2048, 16000, "threshold", dict(tau=1.0)),
+    (2048, 16000, "topk", dict(k=1500)),
+])
+def test_up_gemm_whole_rounds_and_split_rest(n, f, mode, kw):
+    """From 512 tokens the up GEMM's 256 x 256 tiles run in two launches: the
+    N tiles of the whole rounds (on 256 CUs, 32 N tiles of 8 M tiles at 2048
+    tokens), then the rest with K split so it still fills the CUs, summed in
+    split order by its own pass. Union sizes here put the end of the union in
+    the round, one N tile past it, and several past it."""
+    d = 128
+    say(f"case up GEMM rounds + split rest bf16 d={d} F={f} n={n} {mode} {kw}")
+    lay = inputs.make_layer(50, d, f, "bf16")
+    x = inputs.make_x(50, n, d, "bf16", correlated=True)
+    ref = oracle_forward(lay, x, mode, **kw)
+    got = run_gpu(lay, x, mode, max_tokens=n, **kw)
+    say(f"    union {got.union}")
+    compare(lay, x, mode, ref, got)
+
+
 # ---------------------------------------------------------------------------
 # Token groups: each group's up and down products over its own union
 # ---------------------------------------------------------------------------

@@ -947,6 +947,30 @@ static Cfg cfg_for(int M)
     return {1, 1, 1, 2};                // 32 x 64, 2 wavefronts (two M tiles above 32)
 }
 
+// The down GEMM's N is d_model: 256 x 256 tiles while they give every CU a
+// workgroup, else 256 x 128 (twice the tiles), or 256 x 64 where 256 x 128
+// ones would still leave half the CUs idle and the narrower ones fit in one
+// round (2048 tokens at d_model 2048: 256 tiles instead of 128).
+static Cfg down_cfg(const sffn_ctx &c, const Cfg &cf, int T, int d)
+{
+    if (cf.wn != 4) return cf;
+    const long long mt = (T + 255) / 256;
+    if (mt * ((d + 255) / 256) >= c.n_cu) return cf;
+    if (2 * mt * ((d + 127) / 128) <= c.n_cu && mt * ((d + 63) / 64) <= c.n_cu) return Cfg{2, 2, 4, 1};
+    return Cfg{4, 2, 2, 2};
+}
+
+// 256 x 192 tiles (K-contiguous GEMMs) where 256 x 256 ones leave more than a
+// quarter of the CUs idle and the narrower ones still fit in one round
+// (2048 x 5632 outputs: 240 tiles instead of 176).
+static Cfg narrow_for(const sffn_ctx &c, const Cfg &cf, int M, int N)
+{
+    if (cf.wn != 4) return cf;
+    const long long mt = (M + 255) / 256, t256 = mt * ((N + 255) / 256), t192 = mt * ((N + 191) / 192);
+    if (4 * t256 < 3LL * c.n_cu && t192 <= c.n_cu && t192 > t256) return Cfg{2, 3, 4, 2};
+    return cf;
+}
+
 template <int TM, int TN, int WM, int WN, int BKT, int NS, int OCC, bool BNN, int EK, int GM>
 static void launch_dma(dim3 grid, hipStream_t st, int M, int N, int K, const bf16_t *A, int lda, const bf16_t *B,
                        int ldb, const int32_t *bidx, const int *ncount, float *part, int part_ld, const EpiArgs &e)
@@ -970,6 +994,7 @@ static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, 
         else SFFN_D(1, 1, 1, 2, 64, NSS);
     } else if constexpr (!BNN) {
         if (c.wn == 4) SFFN_D(4, 2, 2, 4, 32, 4);
+        else if (c.tn == 3) SFFN_D(2, 3, 4, 2, 64, 2);  // 256 x 192
         else SFFN_D(2, 2, 4, 1, 64, 3);
     } else {
         if (c.wn == 4) SFFN_D(4, 2, 2, 4, 64, 2);
@@ -1134,7 +1159,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     Cfg cfd = cf;
     // the down GEMM's N is d_model: keep 256 x 256 tiles only while they
     // still give every CU a workgroup, else 256 x 128 (twice the tiles)
-    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{4, 2, 2, 2};
+    cfd = down_cfg(c, cfd, T, d);
     const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- 1. gate GEMM ----
@@ -1144,7 +1169,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         // way, but 256 x 64 tiles re-read the activation block for every
         // 64 channels; 256 x 256 tiles split K in two instead
         const bool wide = T >= 256 && T < 512 && c.L.bpart_rows >= 2 * T;
-        const Cfg cg = wide ? Cfg{4, 2, 2, 4} : cf;
+        const Cfg cg = wide ? Cfg{4, 2, 2, 4} : narrow_for(c, cf, T, F);
         const int nt = (F + cg.bn() - 1) / cg.bn(), mtg = (T + cg.bm() - 1) / cg.bm();
         const int sk = wide ? 2 : split_for(c, (long long)mt * nt, d, T);
         if (ev0) hipEventRecord(ev0, st);
@@ -1243,9 +1268,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         if (launch_rounds_rest<EPI_UP>(c, cf, mt, st, T, F, d, x, wu, part, ep, -1, e)) {
             if (e != hipSuccess) return e;
         } else {
-            const int sk = split_for(c, (long long)mt * nt / 2, d, T);  // the union is a fraction of F
-            dispatch_mfma<false, EPI_UP>(cf, tile_grid(nt, mt, sk), st, T, F, d, x, d, wu, d, nullptr, nullptr, part, F,
-                                          ep);
+            const Cfg cu = narrow_for(c, cf, T, F);  // the union is at most F
+            const int ntu = (F + cu.bn() - 1) / cu.bn();
+            const int sk = split_for(c, (long long)mt * ntu / 2, d, T);  // the union is a fraction of F
+            dispatch_mfma<false, EPI_UP>(cu, tile_grid(ntu, mt, sk), st, T, F, d, x, d, wu, d, nullptr, nullptr, part,
+                                          F, ep);
             if ((e = hipGetLastError()) != hipSuccess) return e;
             if (sk > 1) {
                 if ((e = launch_splitk_sum(st, part, sk, T, F, F, ncount, ep)) != hipSuccess) return e;
@@ -1347,15 +1374,16 @@ hipError_t launch_backward(sffn_ctx &c, const BwdArgs &a)
 
     const Cfg cf = cfg_for(T);
     Cfg cfd = cf;
-    if (cfd.wn == 4 && ((T + 255) / 256) * ((d + 255) / 256) < c.n_cu) cfd = Cfg{4, 2, 2, 2};
+    cfd = down_cfg(c, cfd, T, d);
     const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- dH = dY . W_down[U]^T, with the derivative epilogue ----
     {
         ep.kind = EPI_BWD;
-        const int nt = (F + cf.bn() - 1) / cf.bn();
+        const Cfg cb = narrow_for(c, cf, T, F);
+        const int nt = (F + cb.bn() - 1) / cb.bn();
         const int sk = split_for(c, (long long)mt * nt / 2, d, T, TL.part_rows);
-        dispatch_mfma<false, EPI_BWD>(cf, tile_grid(nt, mt, sk), st, T, F, d, dy, d, wdn, d, uidx, ucount, part, F,
+        dispatch_mfma<false, EPI_BWD>(cb, tile_grid(nt, mt, sk), st, T, F, d, dy, d, wdn, d, uidx, ucount, part, F,
                                       ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (sk > 1 && (e = launch_splitk_sum(st, part, sk, T, F, F, ucount, ep)) != hipSuccess) return e;
@@ -1378,7 +1406,7 @@ hipError_t launch_backward(sffn_ctx &c, const BwdArgs &a)
     }
     // ---- weight gradients: C[d][|U|] over K = tokens, added into rows U[n] ----
     {
-        const Cfg cw = cfg_for(d);
+        const Cfg cw = narrow_for(c, cfg_for(d), d, F);
         const int nt = (F + cw.bn() - 1) / cw.bn(), mw = (d + cw.bm() - 1) / cw.bm();
         ep.kind = EPI_WGRAD;
         const struct {

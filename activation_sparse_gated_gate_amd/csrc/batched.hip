@@ -805,8 +805,11 @@ __global__ __launch_bounds__(256) void k_rest_sum(const float *__restrict__ part
         for (int i = 0; i < RW; ++i)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                p[i][s] = *reinterpret_cast<const float4 *>(src + (size_t)i * BN + zs * min(s, u.S - 1));
+                if (s < u.S) p[i][s] = *reinterpret_cast<const float4 *>(src + (size_t)i * BN + zs * s);
         uint32_t b = 0;
+        // the gate's four columns with one vector store per output (d_ff a
+        // multiple of 4, all four inside it)
+        const bool vec = EK == EPI_GATE && (epi.F & 3) == 0 && n + 3 < U;
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             const int m = mb + i;
@@ -835,6 +838,26 @@ __global__ __launch_bounds__(256) void k_rest_sum(const float *__restrict__ part
                 }
                 *reinterpret_cast<uint2 *>(epi.H + (size_t)m * epi.hld + n) =
                     make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+            } else if (vec) {
+                const size_t o = (size_t)m * epi.F + n;
+                if (epi.debug_z) *reinterpret_cast<float4 *>(epi.debug_z + o) = make_float4(v[0], v[1], v[2], v[3]);
+                if (epi.mode == SFFN_TOPK || epi.mode == SFFN_TOPK_2_8 || epi.mode == SFFN_TOPP) {
+                    *reinterpret_cast<float4 *>(epi.keys + o) = make_float4(silu(v[0]), silu(v[1]), silu(v[2]), silu(v[3]));
+                } else {
+                    uint16_t g[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (epi.mode == SFFN_THRESHOLD) {
+                            const bool a = v[c] > epi.tau;
+                            g[c] = a ? f2bf(v[c] - epi.tau) : (uint16_t)0;
+                            b |= (uint32_t)a << c;
+                        } else {
+                            g[c] = f2bf(epi.mode == SFFN_DENSE ? fmaxf(v[c] - epi.tau, 0.f) : silu(v[c]));
+                        }
+                    }
+                    *reinterpret_cast<uint2 *>(epi.G + o) =
+                        make_uint2(g[0] | (uint32_t)g[1] << 16, g[2] | (uint32_t)g[3] << 16);
+                }
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)

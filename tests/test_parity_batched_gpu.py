@@ -211,13 +211,16 @@ def test_batched_handle_larger_than_batch_splits_within_its_buffer():
     (2048, 8192, "dense_silu", {}),           # the union ends with the round: no rest
     (2048, 16000, "threshold", dict(tau=1.0)),
     (2048, 16000, "topk", dict(k=1500)),
+    (2048, 8448, "threshold", dict(tau=1.0)),  # the gate's rest split four ways: union bits from its sum
+    (2048, 8448, "topk", dict(k=1000)),        # ... and the SiLU keys
 ])
 def test_up_gemm_whole_rounds_and_split_rest(n, f, mode, kw):
     """From 512 tokens the up GEMM's 256 x 256 tiles run in two launches: the
     N tiles of the whole rounds (on 256 CUs, 32 N tiles of 8 M tiles at 2048
     tokens), then the rest with K split so it still fills the CUs, summed in
-    split order by its own pass. Union sizes here put the end of the union in
-    the round, one N tile past it, and several past it."""
+    split order by its own pass; the gate GEMM (N = d_ff) does the same.
+    Union sizes here put the end of the union in the round, one N tile past
+    it, and several past it."""
     d = 128
     say(f"case up GEMM rounds + split rest bf16 d={d} F={f} n={n} {mode} {kw}")
     lay = inputs.make_layer(50, d, f, "bf16")

@@ -29,8 +29,14 @@ namespace sffn {
 //              active. Then as SELECT_UP: flags, union flag, up rows.
 // h is stored channel-major, hbuf[i][t] (8 token slots per channel); SELECT_UP
 // and SELECT_NM also write any[i], whether some token selected channel i.
+// RG rows per lane group: RowsPer<NT> for long gate rows; 2 or 4 for short
+// ones (LoPA's rows of B, 2048-wide layers), so that one wavefront per lane
+// group's rows keeps the layer within the wavefronts the GPU holds at once
+// and the kernel takes one memory round trip instead of two or three. Then
+// each selected up row is read by the whole wavefront, one row at a time
+// (ROWWISE_UP): at high sparsity a wavefront has none or one.
 // ---------------------------------------------------------------------------
-template <typename TW, typename TX, int NT, int LPR, int KIND>
+template <typename TW, typename TX, int NT, int LPR, int KIND, int RG>
 __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, int L,
                                               const TW *__restrict__ xu, int d,
                                               const TW *__restrict__ wg, const TW *__restrict__ wu,
@@ -45,7 +51,8 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
         __hip_atomic_store(ctrl + kCtrlEpoch, (int)(e == 0 ? 1u : e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     constexpr int SUB = 64 / LPR;
-    constexpr int R = RowsPer<NT>::v;
+    constexpr int R = RG;
+    constexpr bool ROWWISE_UP = RG > RowsPer<NT>::v;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int q = lane / LPR, li = lane % LPR;
     const int row0 = ((blockIdx.x * 4 + wave) * SUB + q) * R;
@@ -143,6 +150,28 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
         for (int r = 0; r < R; ++r)
             if (r < nv && li == (r & (LPR - 1))) any[row0 + r] = (amask >> r) & 1u;
         if (__ballot(amask != 0) == 0) return;  // nothing selected in this wavefront
+        if constexpr (ROWWISE_UP) {
+            // lane group q2's selected rows in turn, each by all 64 lanes (one
+            // batch of loads for a row of up to 512 MAXS elements); group q2's
+            // gate values come from its first lane
+            for (int q2 = 0; q2 < SUB; ++q2) {
+                const uint32_t qm = (uint32_t)__shfl((int)amask, q2 * LPR, 64);
+                const int qrow0 = ((blockIdx.x * 4 + wave) * SUB + q2) * R;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (!((qm >> r) & 1u)) continue;  // the same in every lane
+                    const TW *ur[1] = {wu + (size_t)(qrow0 + r) * d};
+                    RowDot<TW, TW, NT, 1, 64, Batch<TW, TW, NT, 1>::v> up;
+                    up.run(ur, 1u, d, lane, xu, d, n);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const float gq = __shfl(gv[r][t], q2 * LPR, 64);
+                        if (t < n && lane == t) hbuf[(size_t)(qrow0 + r) * kDecodeMaxTokens + t] = gq * up.acc[0][t];
+                    }
+                }
+            }
+            return;
+        }
         const TW *urows[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) urows[r] = wu + (size_t)(row0 + r) * d;
@@ -159,65 +188,100 @@ __global__ __launch_bounds__(256) void k_gate(const TX *__restrict__ xg, int n, 
 
 // The gate kernel; with profiling events set, they take the kernel's own
 // begin and end timestamps (hipExtLaunchKernelGGL), not separate markers.
-template <typename TW, typename TX, int NT, int KIND>
+template <typename TW, typename TX, int NT, int KIND, int RG>
 static void launch_gate_k(hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, int lpr, const TX *xg, int n, int L,
                         const TW *xu, int d, const TW *wg, const TW *wu, int F, int mode, float tau, float *gsel,
                         uint8_t *act, uint8_t *any, float *hbuf, float *dz, int *ctrl)
 {
-    const dim3 grid(row_blocks(F, lpr, RowsPer<NT>::v));
-#define SFFN_G(LP)                                                                                               \
-    do {                                                                                                         \
-        if (ev0)                                                                                                 \
-            hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
-                                  xu, d, wg, wu, F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                 \
-        else                                                                                                     \
-            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
-                               F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                                    \
+    const dim3 grid(row_blocks(F, lpr, RG));
+#define SFFN_G(LP)                                                                                                   \
+    do {                                                                                                             \
+        if (ev0)                                                                                                     \
+            hipExtLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND, RG>), grid, dim3(256), 0, st, ev0, ev1, 0, xg, n, L, \
+                                  xu, d, wg, wu, F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                     \
+        else                                                                                                         \
+            hipLaunchKernelGGL((k_gate<TW, TX, NT, LP, KIND, RG>), grid, dim3(256), 0, st, xg, n, L, xu, d, wg, wu,  \
+                               F, mode, tau, gsel, act, any, hbuf, dz, ctrl);                                        \
     } while (0)
     // 2:8 needs whole groups of 8 rows per workgroup: 64 lanes per row only
     // with at least two rows per lane group (the host picks 32 otherwise)
-    constexpr bool full64 = KIND != SELECT_NM || RowsPer<NT>::v >= 2;
+    constexpr bool full64 = KIND != SELECT_NM || RG >= 2;
     if constexpr (full64) {
         if (lpr == 64) {
             SFFN_G(64);
             return;
         }
     }
-    if (lpr == 32) SFFN_G(32);
-    else SFFN_G(16);
+    if constexpr (RG == RowsPer<NT>::v) {
+        if (lpr == 16) {
+            SFFN_G(16);
+            return;
+        }
+    }
+    SFFN_G(32);  // the host takes more rows per lane group only for lpr 32 and 64
 #undef SFFN_G
+}
+
+// Rows per lane group of the gate kernel: more than RowsPer<NT> only for bf16
+// gate rows of at most 4 KB at one or two tokens, and then the fewest (2 or
+// 4) that keep the layer's wavefronts at or below 4096 (the GPU holds about
+// 5000 of this kernel at once). Long rows stay at RowsPer<NT>: the kernel is
+// bandwidth-bound there, and more rows per wavefront measured slower.
+static int gate_rows_per_group(int dtype, int nt, int L, int F, int lpr)
+{
+    if (dtype != SFFN_BF16 || nt > 2 || L * 2 > 4096 || lpr < 32) return nt <= 2 ? 1 : nt / 2;
+    const long long per_wave = 64 / lpr;
+    for (int rg = 1; rg < 4; rg *= 2)
+        if ((F + per_wave * rg - 1) / (per_wave * rg) <= 4096) return rg;
+    return 4;
 }
 
 hipError_t launch_gate(const GateArgs &g)
 {
     hipStream_t st = g.stream;
     hipEvent_t ev0 = static_cast<hipEvent_t>(g.ev_start), ev1 = static_cast<hipEvent_t>(g.ev_stop);
-    auto run = [&](auto tw, auto tx, auto nt) {
+    const int rg = gate_rows_per_group(g.dtype, g.nt, g.L, g.F, g.lpr);
+    auto run_rg = [&](auto tw, auto tx, auto nt, auto rg_c) {
         typedef decltype(tw) TW;
         typedef decltype(tx) TX;
-        constexpr int NT = decltype(nt)::value;
+        constexpr int NT = decltype(nt)::value, RG = decltype(rg_c)::value;
         const TX *xg = static_cast<const TX *>(g.xg);
         const TW *xu = static_cast<const TW *>(g.xu), *wg = static_cast<const TW *>(g.wg);
         const TW *wu = static_cast<const TW *>(g.wu);
         switch (g.kind) {
         case KEYS:
-            launch_gate_k<TW, TX, NT, KEYS>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                            g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
+            launch_gate_k<TW, TX, NT, KEYS, RG>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         case DENSE:
-            launch_gate_k<TW, TX, NT, DENSE>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                             g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
+            launch_gate_k<TW, TX, NT, DENSE, RG>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                 g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         case SELECT_NM:
             if constexpr (std::is_same<TX, TW>::value)  // 2:8 takes the full gate
-                launch_gate_k<TW, TX, NT, SELECT_NM>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                                     g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
+                launch_gate_k<TW, TX, NT, SELECT_NM, RG>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                         g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z,
+                                                         g.ctrl);
             break;
         default:
-            launch_gate_k<TW, TX, NT, SELECT_UP>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
-                                                 g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
+            launch_gate_k<TW, TX, NT, SELECT_UP, RG>(st, ev0, ev1, g.lpr, xg, g.n, g.L, xu, g.d, wg, wu, g.F,
+                                                     g.mode, g.tau, g.gsel, g.act, g.any, g.hbuf, g.debug_z, g.ctrl);
             break;
         }
+    };
+    auto run = [&](auto tw, auto tx, auto nt) {
+        constexpr int NT = decltype(nt)::value;
+        if constexpr (NT <= 2 && sizeof(decltype(tw)) == 2) {  // short bf16 gate rows: 2 or 4 rows per lane group
+            if (rg == 4) {
+                run_rg(tw, tx, nt, std::integral_constant<int, 4>{});
+                return;
+            }
+            if (rg == 2) {
+                run_rg(tw, tx, nt, std::integral_constant<int, 2>{});
+                return;
+            }
+        }
+        run_rg(tw, tx, nt, std::integral_constant<int, RowsPer<NT>::v>{});
     };
     auto by_nt = [&](auto tw, auto tx) {
         switch (g.nt) {

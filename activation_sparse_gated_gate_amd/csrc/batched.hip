@@ -1186,6 +1186,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     const int mt = (T + cf.bm() - 1) / cf.bm(), mtd = (T + cfd.bm() - 1) / cfd.bm();
 
     // ---- 1. gate GEMM ----
+    int gate_split = 0;  // > 0: the select sums this many split-K partials of the gate GEMM
     {
         ep.kind = EPI_GATE;
         // 256 <= T < 512: the gate GEMM reads every weight row once either
@@ -1202,7 +1203,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
             dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, part,
                                            F, ep);
             if ((e = hipGetLastError()) != hipSuccess) return e;
-            if (sk > 1) {
+            // small Top-K / top-p / 2:8 batches: the select sums the partials itself
+            gate_split = !wide && T <= kUnionAtomicMaxTokens &&
+                                 (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP || a.mode == SFFN_TOPK_2_8) &&
+                                 sum_select_fits(F, sk) ? sk : 0;
+            if (sk > 1 && !gate_split) {
                 if ((e = launch_splitk_sum(st, part, sk, T, F, F, nullptr, ep)) != hipSuccess) return e;
             }
         }
@@ -1211,7 +1216,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- Top-K / top-p: per-token select, its flags and the union of the
     // flags (above 64 tokens the union comes from one pass over the flags:
     // per-token atomics on the same few bitmap words would serialise) ----
-    if (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP) {
+    if (gate_split && a.mode != SFFN_TOPK_2_8) {
+        e = launch_sum_select_flags(part, gate_split, T, F, a.mode, a.k, a.tau, a.debug_z, act, G, ubits, st);
+        if (e != hipSuccess) return e;
+    } else if (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP) {
         uint32_t *ub = T > kUnionAtomicMaxTokens ? nullptr : ubits;
         e = a.mode == SFFN_TOPK ? launch_topk_select_flags(keys, T, F, a.k, act, G, ub, st)
                                 : launch_topp_select_flags(keys, T, F, a.tau, act, G, ub, st);
@@ -1220,7 +1228,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     }
     // ---- 2:8: the top 2 of each group of 8 keys, its flags and the union ----
     if (a.mode == SFFN_TOPK_2_8) {
-        if ((e = launch_nm_flags(keys, T, F, act, G, ubits, st)) != hipSuccess) return e;
+        e = gate_split ? launch_nm_flags(keys, T, F, act, G, ubits, st, part, gate_split, a.debug_z)
+                       : launch_nm_flags(keys, T, F, act, G, ubits, st);
+        if (e != hipSuccess) return e;
     }
     // ---- token groups: each group's up and down products over its own union ----
     const int ng = c.token_groups;

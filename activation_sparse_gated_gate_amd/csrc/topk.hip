@@ -16,6 +16,7 @@
 // values and union bitmap. Top-p (k_topp_select_flags) finds the same pair
 // by cumulative softmax mass instead of a count (select_mass).
 #include <algorithm>
+#include <type_traits>
 
 #include "select.h"
 #include "topk_wg.h"
@@ -86,6 +87,75 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
     write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
 }
 
+// Token t's keys from the gate GEMM's split-K partials (the form for small
+// batches, whose gate GEMM splits K): this thread's channels KPT tid .. + KPT-1
+// summed over the S splits in split order, exactly as the split-K sum kernel
+// adds them, then SiLU; the pre-activations also into debug_z when it is set.
+// The select that follows then needs no separate sum launch.
+template <int KPT, int SM>
+__device__ __forceinline__ void sum_split_keys(const float *__restrict__ part, int S, int T, int F, int t,
+                                               float *__restrict__ debug_z, float (&kf)[KPT])
+{
+    static_assert(KPT % 4 == 0, "whole float4 groups per thread");
+    constexpr int EB = SM >= 32 ? 1 : 32 / SM < KPT ? 32 / SM : KPT;  // channels whose partials are in flight together
+    static_assert(KPT % EB == 0 && (EB % 4 == 0 || EB < 4), "whole batches");
+    const int i0 = threadIdx.x * KPT;
+    const bool vec = (F & 3) == 0;  // rows of the partials 16-byte aligned
+#pragma unroll
+    for (int e0 = 0; e0 < KPT; e0 += EB) {
+        float p[SM][EB];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            const float *row = part + ((size_t)min(s, S - 1) * T + t) * F;
+            if (EB >= 4 && vec) {
+#pragma unroll
+                for (int e = 0; e < EB; e += 4) {
+                    const int i = i0 + e0 + e;  // i < F implies i + 3 < F (F, i multiples of 4)
+                    const float4 q = i < F ? *reinterpret_cast<const float4 *>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    p[s][e] = q.x;
+                    p[s][e + 1] = q.y;
+                    p[s][e + 2] = q.z;
+                    p[s][e + 3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int i = i0 + e0 + e;
+                    p[s][e] = i < F ? row[i] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            const int i = i0 + e0 + e;
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < SM; ++s)
+                if (s < S) v += p[s][e];
+            if (debug_z && i < F) debug_z[(size_t)t * F + i] = v;
+            kf[e0 + e] = i < F ? silu(v) : 0.f;
+        }
+    }
+}
+
+// Batched Top-K and top-p of a small batch straight from the gate GEMM's
+// split-K partials: token t's keys (sum_split_keys), its select, its flags.
+template <int KPT, int SM, bool MASS>
+__global__ __launch_bounds__(1024) void k_sum_select_flags(const float *__restrict__ part, int S, int T, int F,
+                                                           int K, float p, float *__restrict__ debug_z,
+                                                           uint8_t *__restrict__ act, uint16_t *__restrict__ G,
+                                                           uint32_t *__restrict__ ubits)
+{
+    __shared__ typename std::conditional<MASS, SelectMassLds, SelectLds>::type L;
+    const int t = blockIdx.x;
+    float kf[KPT];
+    sum_split_keys<KPT, SM>(part, S, T, F, t, debug_z, kf);
+    int2 r;
+    if constexpr (MASS) r = select_mass<KPT>(nullptr, F, p, L, kf);
+    else r = select_kth<KPT>(nullptr, F, K, L, kf);
+    write_flags<KPT>(nullptr, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
+}
+
 // Batched Top-K, one 256-thread workgroup per token (d_ff up to
 // kTopkLdsKeys): its keys staged into LDS, the select (wg_topk_boundary, the
 // same as the decode one), then its flags act[t][i], gate values G[t][i]
@@ -143,9 +213,13 @@ __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restr
 // G[t][i] = bf16 key where kept, else 0. The union bits of the block's tokens
 // are ORed in registers and added with one atomic per 32-bit word: tpb
 // tokens per block keep the atomics on each bitmap word at T / tpb.
+// With part set (a small batch whose gate GEMM split K), a key is the sum of
+// the S split-K partials [S][T][F] in split order, then SiLU (as the split-K
+// sum kernel computes it; the sums also into debug_z when it is set).
 __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F, int tpb,
                                                   uint8_t *__restrict__ act, uint16_t *__restrict__ G,
-                                                  uint32_t *__restrict__ ubits)
+                                                  uint32_t *__restrict__ ubits, const float *__restrict__ part,
+                                                  int S, float *__restrict__ debug_z)
 {
     constexpr int GROUP = 8, KEEP = 2;
     __shared__ float kl[2][256];
@@ -157,7 +231,22 @@ __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys
     for (int t = t0; t < t1; ++t) {
         float *k2 = kl[t & 1];  // two buffers: one barrier per token
         const size_t o = (size_t)t * F + i;
-        const float k = i < F ? keys[o] : 0.f;
+        float k = 0.f;
+        if (i < F) {
+            if (part) {
+                float q[16];  // S <= 16: every partial load in flight, then the sum in split order
+#pragma unroll
+                for (int sp = 0; sp < 16; ++sp) q[sp] = sp < S ? part[((size_t)sp * T + t) * F + i] : 0.f;
+                float v = 0.f;
+#pragma unroll
+                for (int sp = 0; sp < 16; ++sp)
+                    if (sp < S) v += q[sp];
+                if (debug_z) debug_z[o] = v;
+                k = silu(v);
+            } else {
+                k = keys[o];
+            }
+        }
         k2[tid] = k;
         __syncthreads();
         int rank = 0;
@@ -200,13 +289,13 @@ hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits,
 }
 
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
-                           hipStream_t st)
+                           hipStream_t st, const float *part, int S, float *debug_z)
 {
     // one token per block up to 255 tokens (enough blocks to fill the
     // GPU), then up to 16, at most 128 atomics per word
     const int tpb = T < 256 ? 1 : std::min(16, T / 128);
     hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + tpb - 1) / tpb), dim3(256), 0, st, keys, T, F, tpb,
-                       act, G, ubits);
+                       act, G, ubits, part, S, debug_z);
     return hipGetLastError();
 }
 
@@ -219,6 +308,33 @@ hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, ui
     else if (F <= 1024 * 16)
         hipLaunchKernelGGL(k_topp_select_flags<16>, grid, block, 0, st, keys, F, p, act, G, ubits);
     else hipLaunchKernelGGL(k_topp_select_flags<0>, grid, block, 0, st, keys, F, p, act, G, ubits);
+    return hipGetLastError();
+}
+
+bool sum_select_fits(int F, int S) { return F <= 1024 * 16 && S >= 2 && S <= 16; }
+
+hipError_t launch_sum_select_flags(const float *part, int S, int T, int F, int mode, int K, float p, float *debug_z,
+                                   uint8_t *act, uint16_t *G, uint32_t *ubits, hipStream_t st)
+{
+    const dim3 grid(T), block(1024);
+    auto go_sm = [&](auto kpt, auto mass) {
+        constexpr int KPT = decltype(kpt)::value;
+        constexpr bool MASS = decltype(mass)::value;
+#define SFFN_SS(SMV) \
+    hipLaunchKernelGGL((k_sum_select_flags<KPT, SMV, MASS>), grid, block, 0, st, part, S, T, F, K, p, debug_z, act, G, ubits)
+        if (S <= 2) SFFN_SS(2);
+        else if (S <= 4) SFFN_SS(4);
+        else if (S <= 8) SFFN_SS(8);
+        else SFFN_SS(16);
+#undef SFFN_SS
+    };
+    auto go = [&](auto mass) {
+        if (F <= 1024 * 4) go_sm(std::integral_constant<int, 4>{}, mass);
+        else if (F <= 1024 * 8) go_sm(std::integral_constant<int, 8>{}, mass);
+        else go_sm(std::integral_constant<int, 16>{}, mass);
+    };
+    if (mode == SFFN_TOPP) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 

@@ -3,20 +3,22 @@
 #pragma once
 
 #include "device_common.h"
+#include "topk_wg.h"
 
 namespace sffn {
 
 // ---------------------------------------------------------------------------
 // One workgroup (1024 threads) per token.
 //
-// Stage 1 bins the keys by value: 2048 equal-width bins over the token's
-// [min, max]. The bin of a value is a non-decreasing function of it (a
-// subtraction and a scaling, both rounded monotonically, then a floor), so
-// every key of a higher bin is at least as large as every key of a lower one
-// and the K-th largest lies in the bin where the count from the top reaches
-// K. Equal keys share a bin. SiLU keys crowd into a few exponent values, so
-// value bins spread the histogram atomics where a radix digit of the leading
-// bits would pile them onto a handful of LDS words.
+// Stage 1 bins the keys by value: the 2048 equal-width bins of key_bin over
+// [kKeyLo, kKeyLo + 8) that the decode select uses (SiLU keys are >= -0.2785;
+// keys past either end go to the end bins). The bin of a value is a
+// non-decreasing function of it, so every key of a higher bin is at least as
+// large as every key of a lower one and the K-th largest lies in the bin where
+// the count from the top reaches K (found by a block-wide scan, two bins per
+// thread). Equal keys share a bin. SiLU keys crowd into a few exponent values,
+// so value bins spread the histogram atomics where a radix digit of the
+// leading bits would pile them onto a handful of LDS words.
 //
 // Stage 2 resolves that bin exactly. Up to 64 candidates are gathered in LDS
 // and one wavefront ranks them by (key descending, channel ascending).
@@ -52,16 +54,24 @@ __device__ __forceinline__ void load_keys(const float *__restrict__ s, int F, fl
     }
 }
 
+// Clears the bins of a select; the caller runs it before loading the keys
+// (their loads then overlap it), and select_kth's first barrier orders both.
+__device__ __forceinline__ void select_kth_clear(SelectLds &L)
+{
+    reinterpret_cast<int2 *>(L.hist)[threadIdx.x] = make_int2(0, 0);
+}
+
 // The select of one token's keys s[0 .. F) by a block of 1024 threads, with
 // this thread's keys in kf (load_keys) when KPT > 0; returns {K-th key, tie
-// cutoff} in every thread. Contains barriers.
+// cutoff} in every thread. The bins must have been cleared by
+// select_kth_clear. Contains barriers.
 template <int KPT>
 __device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, int K, SelectLds &L,
                                            const float (&kf)[KPT > 0 ? KPT : 1])
 {
-    constexpr int NTHR = 1024, NB = SelectLds::NB, CMAX = SelectLds::CMAX;
+    constexpr int NTHR = 1024, CMAX = SelectLds::CMAX;
+    static_assert(SelectLds::NB == 2 * NTHR && SelectLds::NB == kKeyBins, "two fixed bins per thread");
     int *hist = L.hist;
-    float (*red)[16] = L.red;
     uint32_t *cand_key = L.cand_key;
     int *cand_idx = L.cand_idx;
     int *sh = L.sh;
@@ -79,71 +89,35 @@ __device__ __forceinline__ int2 select_kth(const float *__restrict__ s, int F, i
         }
     };
 
-    // ---- range ----
-    float lo = INFINITY, hi = -INFINITY;
-    for_keys([&](int, float v) {
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-    });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o, 64));
-        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-    }
-    if (lane == 0) {
-        red[0][wave] = lo;
-        red[1][wave] = hi;
-    }
-    for (int b = tid; b < NB; b += NTHR) hist[b] = 0;
+    // ---- stage 1: fixed value bins (key_bin), the bin b* of the K-th ----
+    // (the bins were cleared by select_kth_clear before the keys were loaded)
     __syncthreads();
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-        lo = fminf(lo, red[0][w]);
-        hi = fmaxf(hi, red[1][w]);
-    }
-    if (!(hi > lo))  // every key equal: the first K channels
-        return make_int2((int)f2key(lo), K - 1);
-    float scale = (float)NB / (hi - lo);
-    if (!(scale < 1e30f)) scale = 0.f;  // range too narrow to scale: one bin, resolved below
-    auto bin_of = [&](float v) {
-        const float q = (v - lo) * scale;  // >= 0
-        return q >= (float)NB ? NB - 1 : (int)q;
-    };
-
-    // ---- stage 1: value histogram, bin of the K-th ----
-    for_keys([&](int, float v) { atomicAdd(&hist[bin_of(v)], 1); });
+    for_keys([&](int, float v) { atomicAdd(&hist[key_bin(v)], 1); });
     __syncthreads();
-    if (wave == 0) {
-        // lane l owns bins NB-1-32l .. NB-32-32l (descending); the counts
-        // are read twice (total, then the search) to keep registers low
-        const int4 *row = reinterpret_cast<const int4 *>(&hist[NB - 32 - 32 * lane]);
-        int tot = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int4 v = row[q];
-            tot += v.x + v.y + v.z + v.w;
+    {
+        // thread tid owns bins 2 tid and 2 tid + 1; the count from the top is
+        // F minus the inclusive prefix from bin 0
+        const int2 c2 = reinterpret_cast<const int2 *>(hist)[tid];
+        const int incl = block_incl_scan(c2.x + c2.y, scan_scratch);
+        int run = F - incl;  // keys in the bins above 2 tid + 1
+        if (run < K && K <= run + c2.y) {
+            sh[0] = 2 * tid + 1;
+            sh[1] = K - run;
+            sh[2] = c2.y;
+            sh[3] = 0;
         }
-        int run = wave_incl_scan(tot) - tot;
-        const int need = K;
-#pragma unroll
-        for (int q = 7; q >= 0; --q) {
-            const int4 v = row[q];
-            const int c[4] = {v.w, v.z, v.y, v.x};  // bins NB-32-32l+4q+3 .. +0
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (run < need && need <= run + c[e]) {
-                    sh[0] = NB - 32 - 32 * lane + 4 * q + 3 - e;
-                    sh[1] = need - run;
-                    sh[2] = c[e];
-                    sh[3] = 0;
-                }
-                run += c[e];
-            }
+        run += c2.y;
+        if (run < K && K <= run + c2.x) {
+            sh[0] = 2 * tid;
+            sh[1] = K - run;
+            sh[2] = c2.x;
+            sh[3] = 0;
         }
     }
     __syncthreads();
     const int bstar = sh[0], cnt = sh[2];
     int need = sh[1];
+    auto bin_of = [](float v) { return key_bin(v); };
 
     // ---- stage 2a: few candidates, ranked by one wavefront ----
     if (cnt <= CMAX) {

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
     const int t = blockIdx.x;
     const float *s = keys + (size_t)t * F;
     float kf[KPT > 0 ? KPT : 1];
+    select_kth_clear(L);
     load_keys<KPT>(s, F, kf);
     const int2 r = select_kth<KPT>(s, F, K, L, kf);
     write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(1024) void k_sum_select_flags(const float *__restri
     __shared__ typename std::conditional<MASS, SelectMassLds, SelectLds>::type L;
     const int t = blockIdx.x;
     float kf[KPT];
+    if constexpr (!MASS) select_kth_clear(L);
     sum_split_keys<KPT, SM>(part, S, T, F, t, debug_z, kf);
     int2 r;
     if constexpr (MASS) r = select_mass<KPT>(nullptr, F, p, L, kf);

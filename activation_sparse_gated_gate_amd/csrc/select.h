@@ -259,6 +259,7 @@ struct __align__(16) SelectMassLds {
     int cand_idx[CMAX];
     unsigned long long shm[2];  // mass above the crossing bin; the target T
     float red[2][16];
+    unsigned long long scan64[16];
     int sh[4];  // crossing bin, its count, gathered; then the result
     int scan_scratch[16];
 };
@@ -371,23 +372,37 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
         atomicAdd(&L.mass[b], mass_of(v));
     });
     __syncthreads();
-    if (wave == 0) {
-        // lane l owns bins NB-1-32l .. NB-32-32l (descending)
-        const int b0 = NB - 32 - 32 * lane;
-        unsigned long long tot = 0;
-        for (int q = 0; q < 32; ++q) tot += L.mass[b0 + q];
-        const unsigned long long T = target(wave_sum_u64(tot));
-        unsigned long long run = wave_incl_scan_u64(tot) - tot;
-        if (lane == 0) L.shm[1] = T;
-        for (int q = 31; q >= 0; --q) {
-            const unsigned long long m = L.mass[b0 + q];
-            if (run < T && T <= run + m) {
-                L.sh[0] = b0 + q;
-                L.sh[1] = L.hist[b0 + q];
-                L.sh[2] = 0;
-                L.shm[0] = run;
-            }
-            run += m;
+    {
+        // thread tid owns bins 2 tid and 2 tid + 1: a block-wide inclusive scan
+        // of their masses from bin 0 (16 wavefront scans and their totals);
+        // the mass from the top is the total Z minus it
+        static_assert(NB == 2 * NTHR, "two bins per thread");
+        const unsigned long long m0 = L.mass[2 * tid], m1 = L.mass[2 * tid + 1];
+        unsigned long long incl = wave_incl_scan_u64(m0 + m1);
+        if (lane == 63) L.scan64[wave] = incl;
+        __syncthreads();
+        unsigned long long Z = 0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const unsigned long long t = L.scan64[w];
+            incl += w < wave ? t : 0ull;
+            Z += t;
+        }
+        const unsigned long long T = target(Z);
+        if (tid == 0) L.shm[1] = T;
+        unsigned long long run = Z - incl;  // mass in the bins above 2 tid + 1
+        if (run < T && T <= run + m1) {
+            L.sh[0] = 2 * tid + 1;
+            L.sh[1] = L.hist[2 * tid + 1];
+            L.sh[2] = 0;
+            L.shm[0] = run;
+        }
+        run += m1;
+        if (run < T && T <= run + m0) {
+            L.sh[0] = 2 * tid;
+            L.sh[1] = L.hist[2 * tid];
+            L.sh[2] = 0;
+            L.shm[0] = run;
         }
     }
     __syncthreads();

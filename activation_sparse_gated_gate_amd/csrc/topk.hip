@@ -209,56 +209,80 @@ __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restr
 }
 
 // Batched 2:8 structured selection: block (x, y) takes channels
-// [256 x, 256 x + 256) (32 whole groups of 8) of tokens [tpb y, tpb y + tpb).
-// Per token the keys go through LDS; each channel is ranked within its group
+// [256 x, 256 x + 256) (32 whole groups of 8) of tokens [TPB y, TPB y + TPB).
+// The block's keys of all its tokens are loaded first (one round trip); then
+// per token the keys go through LDS, each channel is ranked within its group
 // by (key descending, channel ascending) and the first 2 are kept: act[t][i],
 // G[t][i] = bf16 key where kept, else 0. The union bits of the block's tokens
-// are ORed in registers and added with one atomic per 32-bit word: tpb
-// tokens per block keep the atomics on each bitmap word at T / tpb.
-// With part set (a small batch whose gate GEMM split K), a key is the sum of
-// the S split-K partials [S][T][F] in split order, then SiLU (as the split-K
-// sum kernel computes it; the sums also into debug_z when it is set).
-__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F, int tpb,
+// are ORed in registers and added with one atomic per 32-bit word: TPB tokens
+// per block keep the atomics on each bitmap word at T / TPB. With part set (a
+// small batch whose gate GEMM split K), a key is the sum of the S split-K
+// partials [S][T][F] in split order, then SiLU (as the split-K sum kernel
+// computes it; the sums also into debug_z when it is set).
+template <int TPB>
+__global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F,
                                                   uint8_t *__restrict__ act, uint16_t *__restrict__ G,
                                                   uint32_t *__restrict__ ubits, const float *__restrict__ part,
                                                   int S, float *__restrict__ debug_z)
 {
     constexpr int GROUP = 8, KEEP = 2;
+    constexpr int SC = 16 / TPB > 1 ? 16 / TPB : 1;  // partials of a key in flight together
     __shared__ float kl[2][256];
     const int i0 = blockIdx.x * 256, tid = threadIdx.x, lane = tid & 63;
     const int i = i0 + tid;
     const int b = tid & ~(GROUP - 1);
-    uint32_t acc_bits = 0;
-    const int t0 = blockIdx.y * tpb, t1 = min(T, t0 + tpb);
-    for (int t = t0; t < t1; ++t) {
-        float *k2 = kl[t & 1];  // two buffers: one barrier per token
-        const size_t o = (size_t)t * F + i;
-        float k = 0.f;
-        if (i < F) {
-            if (part) {
-                float q[16];  // S <= 16: every partial load in flight, then the sum in split order
+    const int t0 = blockIdx.y * TPB;
+    float kv[TPB];
+    if (part) {
+        float v[TPB];
 #pragma unroll
-                for (int sp = 0; sp < 16; ++sp) q[sp] = sp < S ? part[((size_t)sp * T + t) * F + i] : 0.f;
-                float v = 0.f;
+        for (int j = 0; j < TPB; ++j) v[j] = 0.f;
+        for (int s0 = 0; s0 < S; s0 += SC) {
+            float q[TPB][SC];
 #pragma unroll
-                for (int sp = 0; sp < 16; ++sp)
-                    if (sp < S) v += q[sp];
-                if (debug_z) debug_z[o] = v;
-                k = silu(v);
-            } else {
-                k = keys[o];
-            }
+            for (int j = 0; j < TPB; ++j)
+#pragma unroll
+                for (int c = 0; c < SC; ++c) {
+                    const int t = t0 + j, sp = s0 + c;
+                    q[j][c] = t < T && i < F && sp < S ? part[((size_t)sp * T + t) * F + i] : 0.f;
+                }
+#pragma unroll
+            for (int j = 0; j < TPB; ++j)
+#pragma unroll
+                for (int c = 0; c < SC; ++c)
+                    if (s0 + c < S) v[j] += q[j][c];
         }
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+            const int t = t0 + j;
+            if (debug_z && t < T && i < F) debug_z[(size_t)t * F + i] = v[j];
+            kv[j] = silu(v[j]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TPB; ++j) {
+            const int t = t0 + j;
+            kv[j] = t < T && i < F ? keys[(size_t)t * F + i] : 0.f;
+        }
+    }
+    uint32_t acc_bits = 0;
+#pragma unroll
+    for (int j = 0; j < TPB; ++j) {
+        const int t = t0 + j;
+        if (t >= T) break;  // the same in every thread of the block
+        float *k2 = kl[j & 1];  // two buffers: one barrier per token
+        const float k = kv[j];
         k2[tid] = k;
         __syncthreads();
         int rank = 0;
 #pragma unroll
         for (int e = 0; e < GROUP; ++e) {
-            const float v = k2[b + e];
-            rank += i0 + b + e < F && (v > k || (v == k && b + e < tid));
+            const float o = k2[b + e];
+            rank += i0 + b + e < F && (o > k || (o == k && b + e < tid));
         }
         const bool on = i < F && rank < KEEP;
         if (i < F) {
+            const size_t o = (size_t)t * F + i;
             act[o] = on;
             G[o] = on ? f2bf(k) : (uint16_t)0;
         }
@@ -293,11 +317,19 @@ hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits,
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
                            hipStream_t st, const float *part, int S, float *debug_z)
 {
-    // one token per block up to 255 tokens (enough blocks to fill the
-    // GPU), then up to 16, at most 128 atomics per word
-    const int tpb = T < 256 ? 1 : std::min(16, T / 128);
-    hipLaunchKernelGGL(k_nm_flags, dim3((F + 255) / 256, (T + tpb - 1) / tpb), dim3(256), 0, st, keys, T, F, tpb,
-                       act, G, ubits, part, S, debug_z);
+    // one token per block up to 16 tokens (enough blocks to fill the GPU),
+    // 4 up to 255, then 16: at most T / 4 atomics per bitmap word, and a
+    // block's key loads in flight together
+    const dim3 block(256);
+    const int gx = (F + 255) / 256;
+    if (T <= 16)
+        hipLaunchKernelGGL(k_nm_flags<1>, dim3(gx, T), block, 0, st, keys, T, F, act, G, ubits, part, S, debug_z);
+    else if (T < 256)
+        hipLaunchKernelGGL(k_nm_flags<4>, dim3(gx, (T + 3) / 4), block, 0, st, keys, T, F, act, G, ubits, part, S,
+                           debug_z);
+    else
+        hipLaunchKernelGGL(k_nm_flags<16>, dim3(gx, (T + 15) / 16), block, 0, st, keys, T, F, act, G, ubits, part, S,
+                           debug_z);
     return hipGetLastError();
 }
 

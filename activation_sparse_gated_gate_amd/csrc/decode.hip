@@ -86,11 +86,12 @@ __device__ __forceinline__ void read_epoch(const int *ctrl, int tid, uint32_t *e
 // The other workgroups take the rows; each reads its tokens' slots in set
 // b % 8 (one thread per token polls; blocks are dispatched in index order,
 // so the select workgroups, which have the lowest indices, are running).
-// With the estimate they prefetch the W_up rows likely to be kept into the
-// cache (loads into a scratch LDS area that nothing reads). With b* alone a
-// row is kept if its key's bin is above b* and dropped if below; the rows in
-// b* itself (a few per token) are computed as if kept and settled by the
-// exact pair (topk_on), read after their dot products. Then, as k_up: the
+// With the estimate they compute the dot products of the W_up rows it marks
+// as likely kept (the coarse bins at or above it, a 25 % margin), before b*
+// is known. With b* alone a row is kept if its key's bin is above b* and
+// dropped if below (kept rows the estimate missed are computed then); the
+// rows in b* itself (a few per token) are computed as if kept and settled by
+// the exact pair (topk_on), read after their dot products. Then: the
 // flags act[t][i], the union flags any[i] and the W_up rows of the channels
 // some token kept: h[i][t] = g * (x_t . W_up[i]). On a block-dispatch order
 // of 8 XCDs in turn, set s lies on XCD s with its pollers. A wait that
@@ -176,10 +177,9 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     constexpr int R = TopkRows<NT>::v;
     __shared__ SelLds<MASS> L;
     __shared__ float kl[U > 0 ? U * 256 : 1];  // a select's keys (U > 0)
-    __shared__ __align__(16) uint32_t pf_lds[4][256];  // where the prefetch loads land (never read)
     __shared__ int2 thr_s[NT];                 // exact boundaries
     __shared__ int bs_s[NT];                   // boundary bins; -1: thr_s holds the exact pair
-    __shared__ int est_s[NT];                  // prefetch estimates (coarse bins)
+    __shared__ int est_s[NT];                  // estimates of the kept coarse bins
     __shared__ int miss_s[2][NT];              // waits that reached the spin limit
     __shared__ int need_s[NT];                 // this workgroup has rows in the token's b*
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -208,37 +208,31 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
         miss_s[0][tid] = miss_s[1][tid] = 0;
         need_s[tid] = 0;
     }
-    // the prefetch estimates, then the rows likely kept into the cache: one
-    // 16-byte load per 128-byte line of each such row of the wavefront
+    // the prefetch estimates, then the dot products of the rows they mark as
+    // likely kept, before the boundary bin is known (the rows kept in the
+    // end are nearly all among them; the others are computed after b*)
     if (tid < n) {
         uint32_t v = 64;
         est_s[tid] = topk_poll(topk_slot(tslot, set, tid) + 3, epoch, spin_max, v) ? (int)v : 64;
     }
     __syncthreads();
-    {
-        uint32_t pf = 0;
+    const TW *rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
+    uint32_t smask = 0;  // rows computed ahead
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (r < nv && t < n && (key_bin(kv[r][t]) >> 5) >= est_s[t]) smask |= 1u << r;
+    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
+    if (__ballot(smask != 0)) {
+        up.run(rows, smask, d, li, x, d, n);
+    } else {
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (r < nv && t < n && (key_bin(kv[r][t]) >> 5) >= est_s[t]) pf |= 1u << r;
-        uint32_t M = 0;  // bit q R + r: row wrow0 + q R + r, for the whole wavefront
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint64_t bal = __ballot((pf >> r) & 1u);
-#pragma unroll
-            for (int g = 0; g < SUB; ++g) M |= (uint32_t)((bal >> (g * LPR)) & 1u) << (g * R + r);
-        }
-        if (M) {
-            const int lines = (d * (int)sizeof(TW) + 127) / 128;
-            for (int p0 = 0; p0 < SUB * R * lines; p0 += 64) {
-                const int p = p0 + lane, slotr = p / lines, line = p - slotr * lines;
-                if (slotr < SUB * R && ((M >> slotr) & 1u))
-                    __builtin_amdgcn_global_load_lds(
-                        (gmem_t *)(reinterpret_cast<const char *>(wu + (size_t)(wrow0 + slotr) * d) + line * 128),
-                        (lmem_t *)pf_lds[wave], 16, 0, 0);
-            }
-        }
+            for (int t = 0; t < NT; ++t) up.acc[r][t] = 0.f;
     }
 
     // the boundary bins; a wait that reaches the limit selects here
@@ -257,10 +251,7 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
     __syncthreads();
 
     // the rows kept by bin, and the rows in b* (computed as if kept)
-    const TW *rows[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = wu + (size_t)(row0 + r) * d;
-    uint32_t amask = 0;  // rows computed
+    uint32_t amask = 0;  // rows needed
     uint32_t amb = 0;    // bit r * NT + t: row r is in token t's b*
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -277,8 +268,16 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
                     amask |= 1u << r;
                 }
             }
-    RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up;
-    if (__ballot(amask != 0)) up.run(rows, amask, d, li, x, d, n);
+    const uint32_t late = amask & ~smask;  // needed, not computed ahead
+    if (__ballot(late != 0)) {
+        RowDot<TW, TW, NT, R, LPR, Batch<TW, TW, NT, R>::v> up2;
+        up2.run(rows, late, d, li, x, d, n);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if ((late >> r) & 1u)
+#pragma unroll
+                for (int t = 0; t < NT; ++t) up.acc[r][t] = up2.acc[r][t];
+    }
     __syncthreads();  // need_s
     // the exact pairs the rows in b* need; a wait that reaches the limit
     // selects here
@@ -325,7 +324,6 @@ __global__ __launch_bounds__(256) void k_up_topk(const TW *__restrict__ x, int n
         for (int t = 0; t < NT; ++t)
             if (((kmask >> r) & 1u) && t < n && li == ((r * NT + t) & (LPR - 1)))
                 hbuf[(size_t)(row0 + r) * kDecodeMaxTokens + t] = gv[r][t] * up.acc[r][t];
-    wait_vm_lgkm<0>();  // no prefetch is still writing this workgroup's LDS when it ends
 }
 
 // ---------------------------------------------------------------------------

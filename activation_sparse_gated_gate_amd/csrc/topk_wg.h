@@ -131,7 +131,27 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
     reinterpret_cast<int4 *>(hist)[2 * tid] = make_int4(0, 0, 0, 0);
     reinterpret_cast<int4 *>(hist)[2 * tid + 1] = make_int4(0, 0, 0, 0);
     __syncthreads();
-    for_keys([&](int, int, float v) { atomicAdd(&hist[key_bin(v)], 1); });
+    // keys in LDS: the bins of this thread's keys stay in registers, two per
+    // word, for the gather after b* (no second pass over the keys)
+    uint32_t kb2[U > 0 ? U / 2 : 1];
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u0 = 0; u0 < U; u0 += 8) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = kl[(u0 + e) * 256 + tid];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int b0 = key_bin(o[e]), b1 = key_bin(o[e + 1]);
+                atomicAdd(&hist[b0], 1);
+                atomicAdd(&hist[b1], 1);
+                kb2[(u0 + e) >> 1] = (uint32_t)b0 | (uint32_t)b1 << 16;
+            }
+        }
+    } else {
+        kb2[0] = 0;
+        for_keys([&](int, int, float v) { atomicAdd(&hist[key_bin(v)], 1); });
+    }
     __syncthreads();
     {
         // thread tid owns bins 8 tid .. 8 tid + 7
@@ -166,7 +186,8 @@ __device__ __forceinline__ int2 wg_topk_boundary(const float *__restrict__ s, in
         if constexpr (U > 0) {
             static_assert(U <= 32, "one match bit per key");
             uint32_t mb = 0;
-            for_keys([&](int u, int, float v) { mb |= (uint32_t)(key_bin(v) == bs) << u; });
+#pragma unroll
+            for (int u = 0; u < U; ++u) mb |= (uint32_t)((int)((kb2[u >> 1] >> (16 * (u & 1))) & 0xffffu) == bs) << u;
             if (mb) {
                 int slot = atomicAdd(&sh[3], __popc(mb));  // < cnt: the same keys as the count
                 for (uint32_t m = mb; m; m &= m - 1) {

@@ -404,7 +404,26 @@ __device__ __forceinline__ int2 wg_topp_boundary(const float *__restrict__ s, in
     }
 
     // ---- mass per value bin; the bin b* where the mass from the top reaches T ----
-    for_keys([&](int, int, float v) { atomicAdd(&mass[key_bin(v)], topp_mass(v, mx)); });
+    // (keys in LDS: their bins stay in registers, two per word, for the gather)
+    uint32_t kb2[U > 0 ? U / 2 : 1];
+    if constexpr (U > 0) {
+#pragma unroll
+        for (int u0 = 0; u0 < U; u0 += 8) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = kl[(u0 + e) * 256 + tid];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int b0 = key_bin(o[e]), b1 = key_bin(o[e + 1]);
+                atomicAdd(&mass[b0], topp_mass(o[e], mx));
+                atomicAdd(&mass[b1], topp_mass(o[e + 1], mx));
+                kb2[(u0 + e) >> 1] = (uint32_t)b0 | (uint32_t)b1 << 16;
+            }
+        }
+    } else {
+        kb2[0] = 0;
+        for_keys([&](int, int, float v) { atomicAdd(&mass[key_bin(v)], topp_mass(v, mx)); });
+    }
     __syncthreads();
     {
         // thread tid owns bins 8 tid .. 8 tid + 7
@@ -440,7 +459,8 @@ __device__ __forceinline__ int2 wg_topp_boundary(const float *__restrict__ s, in
     if constexpr (U > 0) {
         static_assert(U <= 32, "one match bit per key");
         uint32_t mb = 0;
-        for_keys([&](int u, int, float v) { mb |= (uint32_t)(key_bin(v) == bs) << u; });
+#pragma unroll
+        for (int u = 0; u < U; ++u) mb |= (uint32_t)((int)((kb2[u >> 1] >> (16 * (u & 1))) & 0xffffu) == bs) << u;
         if (mb) {
             int slot = atomicAdd(&sh[3], __popc(mb));
             for (uint32_t m = mb; m; m &= m - 1) {

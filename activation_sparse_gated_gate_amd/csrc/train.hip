@@ -97,6 +97,32 @@ __global__ __launch_bounds__(256) void k_bwd_scatter(const int32_t *__restrict__
     }
 }
 
+// Token t (one block): its whole row of ZU at once, (NaN, 0) for every
+// channel and the stored (z, u) where it has them, built in LDS and written
+// with coalesced stores (one pass over ZU instead of a clear and a scatter;
+// d_ff up to kFillMax). Stored channel indices are unique (ascending, as
+// k_save writes them); indices outside [0, F) are skipped.
+constexpr int kFillMax = 6144;
+__global__ __launch_bounds__(256) void k_bwd_fill(const int32_t *__restrict__ cnt, const int32_t *__restrict__ idx,
+                                                  const float *__restrict__ z, const float *__restrict__ u, int cap,
+                                                  int F, float2 *__restrict__ ZU)
+{
+    __shared__ float2 row[kFillMax];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float2 off = make_float2(__uint_as_float(0x7fc00000u), 0.f);
+    for (int i = tid; i < F; i += 256) row[i] = off;
+    __syncthreads();
+    const int c = min(cnt[t], cap);
+    for (int s = tid; s < c; s += 256) {
+        const size_t o = (size_t)t * cap + s;
+        const int i = idx[o];
+        if (i >= 0 && i < F) row[i] = make_float2(z[o], u[o]);
+    }
+    __syncthreads();
+    float2 *dst = ZU + (size_t)t * F;
+    for (int i = tid; i < F; i += 256) dst[i] = row[i];
+}
+
 // The union bitmap: channel i (one thread) is in it when some token stored
 // it, i.e. some ZU[t][i].x is not NaN; the scan stops at the first such
 // token. Each wavefront writes its 64 channels' two words (no atomics: every
@@ -172,8 +198,14 @@ hipError_t launch_bwd_setup(const Saved &sv, int T, int F, int d, int tp, float2
     const int words = (F + 31) / 32;
     const size_t TF = (size_t)T * F;
     const int blocks = (int)std::min<size_t>(4096, (TF + 255) / 256 + 1);
-    hipLaunchKernelGGL(k_bwd_clear, dim3(blocks), dim3(256), 0, st, ZU, TF, dut, dzt, ht, F, T, tp);
-    hipLaunchKernelGGL(k_bwd_scatter, dim3(T), dim3(256), 0, st, sv.cnt, sv.idx, sv.z, sv.u, sv.cap, F, ZU);
+    if (F <= kFillMax) {
+        // one pass over ZU; the clear kernel only zeroes the padding (if any)
+        if (tp > T) hipLaunchKernelGGL(k_bwd_clear, dim3(blocks), dim3(256), 0, st, ZU, 0, dut, dzt, ht, F, T, tp);
+        hipLaunchKernelGGL(k_bwd_fill, dim3(T), dim3(256), 0, st, sv.cnt, sv.idx, sv.z, sv.u, sv.cap, F, ZU);
+    } else {
+        hipLaunchKernelGGL(k_bwd_clear, dim3(blocks), dim3(256), 0, st, ZU, TF, dut, dzt, ht, F, T, tp);
+        hipLaunchKernelGGL(k_bwd_scatter, dim3(T), dim3(256), 0, st, sv.cnt, sv.idx, sv.z, sv.u, sv.cap, F, ZU);
+    }
     hipLaunchKernelGGL(k_bwd_union, dim3((F + 255) / 256), dim3(256), 0, st, ZU, T, F, words, ubits);
     hipLaunchKernelGGL(k_bwd_list, dim3(1), dim3(1024), 0, st, ubits, words, uidx, ucount);
     hipLaunchKernelGGL(k_transpose_pad, dim3((tp + 63) / 64, (d + 63) / 64, 2), dim3(256), 0, st, x, dy, xt, dyt, T,

@@ -89,6 +89,32 @@ def test_moc_topk_decode(k):
     assert rep.rel_err <= DECODE_GUARD
 
 
+@pytest.mark.parametrize("case", ["lopa_r256", "lopa_r512", "threshold", "topk", "topp", "dense_silu"])
+def test_short_gate_rows_two_tokens(case):
+    """Two tokens on layers whose gate rows are at most 4 KB (LoPA's rows of
+    B at ranks 256 and 512, the 2048-wide MoC layer): the gate kernel takes
+    2 or 4 rows per lane group (more than two tokens ask for) and reads each
+    selected up row with the whole wavefront, lane group by lane group."""
+    n = 2
+    if case.startswith("lopa"):
+        wl = W["lopa_gate_bf16_d4096_f11008"]
+        rank = int(case[len("lopa_r"):])
+        lay = _layer(wl, rank=rank)
+        mode, kw = "lopa", dict(tau=1.2816)
+    else:
+        wl = W["moc_topk_bf16_d2048_f5632"]
+        lay = _layer(wl)
+        mode = case
+        kw = dict(tau=1.2816) if case == "threshold" else dict(k=704) if case == "topk" else \
+            dict(tau=0.3) if case == "topp" else dict(tau=0.0)
+    say(f"case short gate rows n={n} {case} d={wl.d_model} F={wl.d_ff}")
+    x = inputs.make_x(3, n, wl.d_model, wl.dtype)
+    ref = oracle_forward(lay, x, mode, **kw)
+    got = run_gpu(lay, x, mode, **kw)
+    rep = compare(lay, x, mode, ref, got)
+    assert rep.rel_err <= DECODE_GUARD
+
+
 @pytest.mark.parametrize("n", [1, 4, 8])
 def test_moc_2_8_decode(n):
     """The 2:8 structured option at the MoC shape: exactly 2 of every 8

@@ -147,6 +147,21 @@ def test_train_ragged(mode, tau, k, n):
     say(f"    band={band} flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
 
 
+@pytest.mark.parametrize("mode,tau,k", [("threshold", 0.9, 0), ("topk", 0.0, 800)])
+def test_train_wide_layer(mode, tau, k):
+    """d_ff above 6144: the backward's set-up clears the (z, u) buffer and
+    scatters the stored rows in two kernels instead of one pass per token."""
+    d, f, n = 264, 6500, 12
+    say(f"case train wide d={d} F={f} n={n} {mode}")
+    lay = inputs.make_layer(8, d, f, "bf16")
+    x = inputs.make_x(8, n, d, "bf16")
+    dy = inputs.make_x(9, n, d, "bf16")
+    got = run_train(lay, x, dy, mode, tau=tau, k=k)
+    sets, flips, band, ry = check_forward(lay, x, mode, tau, k, got)
+    errs = check_backward(lay, x, dy, mode, tau, sets, got)
+    say(f"    band={band} flips={flips} y={ry:.2e} " + " ".join(f"{a}={b:.2e}" for a, b in errs.items()))
+
+
 def test_train_moc_topk():
     """The MoC layer (d 2048, d_ff 5632) with K = 704 over 64 tokens."""
     wl = inputs.WORKLOADS["moc_topk_bf16_d2048_f5632"]

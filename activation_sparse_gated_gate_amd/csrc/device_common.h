@@ -2,6 +2,8 @@
 // bf16 widening, wavefront reductions and scans, Top-K key encoding.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -193,14 +195,23 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
     return v;
 }
 
+// The same for 64-bit values: the DPP moves of wave_incl_scan on the two
+// 32-bit halves, then one 64-bit add per step (exact: integer sums).
 __device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
+    auto step = [&v](auto ctrl, auto row_mask, auto bound) {
+        const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, decltype(ctrl)::value,
+                                                        decltype(row_mask)::value, 0xf, decltype(bound)::value);
+        const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), decltype(ctrl)::value,
+                                                        decltype(row_mask)::value, 0xf, decltype(bound)::value);
+        v += ((unsigned long long)hi << 32) | lo;
+    };
+    step(std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xf>{}, std::true_type{});   // row_shr:1
+    step(std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xf>{}, std::true_type{});   // row_shr:2
+    step(std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xf>{}, std::true_type{});   // row_shr:4
+    step(std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xf>{}, std::true_type{});   // row_shr:8
+    step(std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xa>{}, std::false_type{});  // row_bcast:15
+    step(std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xc>{}, std::false_type{});  // row_bcast:31
     return v;
 }
 

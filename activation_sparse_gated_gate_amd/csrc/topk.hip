@@ -40,14 +40,32 @@ __device__ __forceinline__ void write_flags(const float *__restrict__ s, int F, 
         // channels KPT tid .. + KPT-1: one 32-bit word, shared by 32 / KPT lanes
         const int i0 = tid * KPT;
         uint32_t m = 0;
+        if (KPT % 8 == 0 && (F & 7) == 0 && i0 + KPT <= F) {
+            // whole groups of 8: the flags in one 8-byte store and the gate
+            // values in one 16-byte store per group (the rows are aligned)
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const int i = i0 + e;
-            if (i < F) {
-                const bool on = topk_on(kf[e], i, r);
-                a[i] = on;
-                g[i] = on ? f2bf(kf[e]) : (uint16_t)0;
-                m |= (uint32_t)on << e;
+            for (int e0 = 0; e0 + 8 <= KPT; e0 += 8) {
+                uint32_t fl[2] = {0u, 0u}, gw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool on = topk_on(kf[e0 + e], i0 + e0 + e, r);
+                    fl[e >> 2] |= (uint32_t)on << (8 * (e & 3));
+                    gw[e >> 1] |= (uint32_t)(on ? f2bf(kf[e0 + e]) : (uint16_t)0) << (16 * (e & 1));
+                    m |= (uint32_t)on << (e0 + e);
+                }
+                *reinterpret_cast<uint2 *>(a + i0 + e0) = make_uint2(fl[0], fl[1]);
+                *reinterpret_cast<uint4 *>(g + i0 + e0) = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int i = i0 + e;
+                if (i < F) {
+                    const bool on = topk_on(kf[e], i, r);
+                    a[i] = on;
+                    g[i] = on ? f2bf(kf[e]) : (uint16_t)0;
+                    m |= (uint32_t)on << e;
+                }
             }
         }
         m <<= i0 & 31;

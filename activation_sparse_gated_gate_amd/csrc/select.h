@@ -286,11 +286,8 @@ __device__ __forceinline__ int2 select_mass(const float *__restrict__ s, int F, 
         lo = fminf(lo, v);
         hi = fmaxf(hi, v);
     });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o, 64));
-        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
-    }
+    lo = wave_minmax<false>(lo);
+    hi = wave_minmax<true>(hi);
     if (lane == 0) {
         L.red[0][wave] = lo;
         L.red[1][wave] = hi;

@@ -32,6 +32,23 @@ namespace sffn {
 // boundary, at rank need - 1 < the channels in b*, is never one of them.
 // ---------------------------------------------------------------------------
 constexpr int kKeyBins = 2048, kCandMax = 512;
+
+// Max (MAX) or min over the 64 lanes, the result in every lane: within each
+// row of 16 lanes by DPP moves (pairs, quads, half-row and row mirrors), then
+// two lane shuffles across the rows. Every lane must be active.
+template <bool MAX>
+__device__ __forceinline__ float wave_minmax(float v)
+{
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+#define SFFN_DPP_MV(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false))
+    v = op(v, SFFN_DPP_MV(v, 0xb1));   // quad_perm [1,0,3,2]
+    v = op(v, SFFN_DPP_MV(v, 0x4e));   // quad_perm [2,3,0,1]
+    v = op(v, SFFN_DPP_MV(v, 0x141));  // row_half_mirror
+    v = op(v, SFFN_DPP_MV(v, 0x140));  // row_mirror
+#undef SFFN_DPP_MV
+    v = op(v, __shfl_xor(v, 16, 64));
+    return op(v, __shfl_xor(v, 32, 64));
+}
 constexpr float kKeyLo = -0.3f, kKeyScale = kKeyBins / 8.0f;
 
 __device__ __forceinline__ int key_bin(float v)
@@ -373,8 +390,7 @@ __device__ __forceinline__ int2 wg_topp_boundary(const float *__restrict__ s, in
     // ---- the largest key ----
     float mx = -INFINITY;
     for_keys([&](int, int, float v) { mx = fmaxf(mx, v); });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_minmax<true>(mx);
     if (lane == 0) L.red[wave] = mx;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mass[8 * tid + e] = 0ull;

@@ -29,6 +29,7 @@
 // out of LDS with transpose reads. When the grid would be too small, K is
 // split and the fp32 partials are summed in order by a second kernel that
 // applies the same epilogue.
+#include <cmath>
 #include <type_traits>
 
 #include "compact.h"
@@ -65,6 +66,9 @@ struct EpiArgs {
     uint32_t *ubits;    // union bitmap (gate and Top-K flags set it, up reads it, down clears it)
     int32_t *uidx;      // union list (up writes, down and the split-K sum read)
     int *ucount;        // union size (up writes)
+    int all_ch;         // up: every channel instead of the union (a small batch whose union is nearly
+                        // every channel; G is 0 where off); its block 0 writes the bitmap's size to *utrue
+    int *utrue;
     uint16_t *H;        // [T][hld] bf16 (up writes)
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
     float *Y;           // [T][d] fp32 (down writes; WGRAD: the gradient [F][d], added into)
@@ -484,7 +488,7 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         // words lie on different lanes, so in parallel), up to the round
         // that passes the tile.
         const int F = epi.F, W = (F + 31) / 32;
-        if (epi.mode == SFFN_DENSE || epi.mode == SFFN_DENSE_SILU) {
+        if (epi.mode == SFFN_DENSE || epi.mode == SFFN_DENSE_SILU || epi.all_ch) {
             for (int j = tid; j < BN; j += 64 * WM * WN) uloc[j] = n0 + j;
             if (tid == 0) utot = F;
         } else if (wave == 0) {
@@ -774,6 +778,18 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
     tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, poff, pld,
                                                 epi, ubits_lds, uloc);
+    if constexpr (EK == EPI_UP) {
+        // every channel computed: the union's own size for the caller, counted
+        // by one workgroup after its tile (off the other tiles' path)
+        if (epi.all_ch && blockIdx.x == 0 && z == 0 && wave == 0) {
+            const int W = (epi.F + 31) / 32;
+            int c = 0;
+            for (int w = lane; w < W; w += 64) c += __popc(epi.ubits[w]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+            if (lane == 0) *epi.utrue = c;
+        }
+    }
 }
 
 // Sum of the rest launch's split partials (tile p at part[p][BM][BN]) in
@@ -918,13 +934,14 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
 // block T writes the union size.
 __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict__ G, const uint8_t *__restrict__ act,
                                                       int T, int F, int mode, const int *__restrict__ ncount,
+                                                      const int *__restrict__ utrue,
                                                       int32_t *__restrict__ active_idx,
                                                       int32_t *__restrict__ active_cnt, int32_t *__restrict__ union_cnt)
 {
     __shared__ int scratch[5];
     const int t = blockIdx.x;
     if (t == T) {
-        if (threadIdx.x == 0 && union_cnt) *union_cnt = *ncount;
+        if (threadIdx.x == 0 && union_cnt) *union_cnt = utrue ? *utrue : *ncount;
         return;
     }
     const bool dense = mode == SFFN_DENSE || mode == SFFN_DENSE_SILU;
@@ -1139,6 +1156,22 @@ static bool launch_rounds_rest(const sffn_ctx &c, const Cfg &cf, int mt, hipStre
     return true;
 }
 
+// Small batches of iid tokens whose union is nearly every channel (Top-K
+// with 1 - (1 - K/F)^T >= 0.97, 2:8 with 0.75^T <= 0.03; up to 64 tokens):
+// the up and down GEMMs run over every channel, which skips each up tile's
+// wait for the union bitmap (the gate values are 0 where a channel is off, so
+// y is the same sum up to the order of additions). Measured at the MoC layer:
+// the up GEMM over every channel takes 9.3 us at 16 tokens against 11.9 over
+// its 88 % union, and 12.6 against 14.9 us at 64 tokens (100 %).
+static bool union_nearly_all(int mode, int T, int F, int K)
+{
+    if (T < 2 || T > 64) return false;
+    double miss = 1.0;
+    if (mode == SFFN_TOPK) miss = std::pow(1.0 - (double)K / F, T);
+    else if (mode == SFFN_TOPK_2_8) miss = std::pow(0.75, T);
+    return miss <= 0.03;
+}
+
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
 {
     const sffn_shape &S = c.shape;
@@ -1287,7 +1320,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
             if (sk > 1 && (e = launch_splitk_sum(st, part, sk, Tg, d, d, nullptr, eg)) != hipSuccess) return e;
         }
         if (a.active_idx || a.active_cnt || a.union_cnt) {
-            hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount,
+            hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount, nullptr,
                                a.active_idx, a.active_cnt, a.union_cnt);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
@@ -1296,6 +1329,8 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {
         ep.kind = EPI_UP;
+        ep.all_ch = union_nearly_all(a.mode, T, F, a.k) ? 1 : 0;
+        ep.utrue = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionTrue;
         const int nt = (F + cf.bn() - 1) / cf.bn();
         // 256 x 256 tiles: the whole rounds, then the rest split along K
         if (launch_rounds_rest<EPI_UP>(c, cf, mt, st, T, F, d, x, wu, part, ep, -1, e)) {
@@ -1326,7 +1361,8 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     }
     // ---- optional outputs ----
     if (a.active_idx || a.active_cnt || a.union_cnt) {
-        hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount, a.active_idx,
+        hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount,
+                           ep.all_ch ? ep.utrue : nullptr, a.active_idx,
                            a.active_cnt, a.union_cnt);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

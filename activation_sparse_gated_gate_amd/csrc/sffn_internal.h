@@ -29,6 +29,7 @@ constexpr int kCtrlInts = 1024;
 constexpr int kCtrlUnionSize = 0;    // batched path: size of the union list
 constexpr int kCtrlError = 1;        // sticky error word (bits kErr*), workspace byte offset 4
 constexpr int kCtrlEpoch = 2;        // decode forward counter (epoch of the slots), advanced by the gate kernel
+constexpr int kCtrlUnionTrue = 3;    // batched path over every channel: the union bitmap's size
 constexpr int kErrDownWait = 1;      // a down-projection sum gave up waiting for a group's slot
 
 // Polls after which a waiting workgroup gives up (sffn_set_spin_limit).

@@ -69,6 +69,11 @@ struct EpiArgs {
     int all_ch;         // up: every channel instead of the union (a small batch whose union is nearly
                         // every channel; G is 0 where off); its block 0 writes the bitmap's size to *utrue
     int *utrue;
+    // gate GEMM with the up GEMM in the same launch (every channel, split K):
+    // N tiles past the gate's read B2 (W_up) and write their partials to part2
+    int dual;
+    const bf16_t *B2;
+    float *part2;
     uint16_t *H;        // [T][hld] bf16 (up writes)
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
     float *Y;           // [T][d] fp32 (down writes; WGRAD: the gradient [F][d], added into)
@@ -150,7 +155,7 @@ __device__ __forceinline__ bool epilogue(const EpiArgs &e, int m, int n, float v
         return true;
     }
     if (e.kind == EPI_UP) {
-        const int i = e.uidx[n];
+        const int i = e.all_ch ? n : e.uidx[n];
         const int tr = e.tmap ? e.tmap[m] : m;
         e.H[(size_t)m * e.hld + n] = f2bf(bf2f(e.G[(size_t)tr * e.F + i]) * v);
         if (e.usave) e.usave[(size_t)tr * e.F + i] = v;
@@ -473,7 +478,13 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         const int xcd = blockIdx.x % 8, jt = blockIdx.x / 8;
         mi = jt % MT;
         ni = (jt / MT) * 8 + xcd;
-        if (ni >= NTT) return;
+        if (ni >= (EK == EPI_GATE && epi.dual ? 2 : 1) * NTT) return;
+        if (EK == EPI_GATE && epi.dual && ni >= NTT) {
+            // an up tile of the gate launch
+            ni -= NTT;
+            B = epi.B2;
+            part = epi.part2;
+        }
     }
     const int m0 = mi * BM, n0 = ni * BN;
     int nlim = N, klim = K;
@@ -908,6 +919,11 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     const int n = blockIdx.x * 256 + threadIdx.x;
     const int m = blockIdx.y;
     if (threadIdx.x < 8) ub[threadIdx.x] = 0;
+    if (epi.kind == EPI_UP && epi.all_ch && m == 0) {
+        // every channel: the identity union list and its size for the down GEMM
+        if (n < N) epi.uidx[n] = n;
+        if (n == 0) *epi.ucount = N;
+    }
     __syncthreads();
     if (n < nlim) {
         // all S (<= SM) partial loads in flight at once, then summed in split
@@ -928,6 +944,15 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     __syncthreads();
     if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
+    if (epi.kind == EPI_UP && epi.all_ch && epi.dual && blockIdx.x == 0 && m == 0 && threadIdx.x < 64) {
+        // the union's own size for the caller (the bitmap the select wrote)
+        const int W = (epi.F + 31) / 32, lane = threadIdx.x;
+        int c = 0;
+        for (int w = lane; w < W; w += 64) c += __popc(epi.ubits[w]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+        if (lane == 0) *epi.utrue = c;
+    }
 }
 
 // Optional outputs for a batch: token t's ascending active list and count;
@@ -1156,20 +1181,22 @@ static bool launch_rounds_rest(const sffn_ctx &c, const Cfg &cf, int mt, hipStre
     return true;
 }
 
-// Small batches of iid tokens whose union is nearly every channel (Top-K
-// with 1 - (1 - K/F)^T >= 0.97, 2:8 with 0.75^T <= 0.03; up to 64 tokens):
-// the up and down GEMMs run over every channel, which skips each up tile's
-// wait for the union bitmap (the gate values are 0 where a channel is off, so
-// y is the same sum up to the order of additions). Measured at the MoC layer:
-// the up GEMM over every channel takes 9.3 us at 16 tokens against 11.9 over
-// its 88 % union, and 12.6 against 14.9 us at 64 tokens (100 %).
-static bool union_nearly_all(int mode, int T, int F, int K)
+// The share of channels a small batch of iid tokens leaves out of its union,
+// where the mode fixes it: (1 - K/F)^T for Top-K, 0.75^T for 2:8 (1 for the
+// others: unknown before the gate). Up to 64 tokens the up and down GEMMs run
+// over every channel when it is small: no up tile waits for the union bitmap,
+// the gate values are 0 where a channel is off (y is the same sum up to the
+// order of additions), and the up GEMM's tiles can join the gate's launch.
+// With that launch every channel pays from a union of ~75 % (MoC layer, 16
+// tokens: Top-K K = 704, union 88 %, 45.6 -> 37.4 us); without it only from
+// ~97 % (the up GEMM over every channel alone: 9.3 us against 11.9 over an
+// 88 % union, 12.6 against 14.9 at 100 %).
+static double union_miss(int mode, int T, int F, int K)
 {
-    if (T < 2 || T > 64) return false;
-    double miss = 1.0;
-    if (mode == SFFN_TOPK) miss = std::pow(1.0 - (double)K / F, T);
-    else if (mode == SFFN_TOPK_2_8) miss = std::pow(0.75, T);
-    return miss <= 0.03;
+    if (T < 2 || T > 64) return 1.0;
+    if (mode == SFFN_TOPK) return std::pow(1.0 - (double)K / F, T);
+    if (mode == SFFN_TOPK_2_8) return std::pow(0.75, T);
+    return 1.0;
 }
 
 hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
@@ -1220,6 +1247,12 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
 
     // ---- 1. gate GEMM ----
     int gate_split = 0;  // > 0: the select sums this many split-K partials of the gate GEMM
+    // every channel for the up and down GEMMs (not with token groups, which
+    // take their own unions)
+    const double miss = union_miss(a.mode, T, F, a.k);
+    bool all_ch = miss <= 0.25 && !(c.token_groups > 1 && T >= c.token_groups * kTokenGroupMinTokens);
+    const bool dense_small = dense && T <= kUnionAtomicMaxTokens;  // every channel by definition
+    int dual_s = 0;  // > 0: the up GEMM ran in the gate's launch, with this many K splits
     {
         ep.kind = EPI_GATE;
         // 256 <= T < 512: the gate GEMM reads every weight row once either
@@ -1233,15 +1266,31 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         if (!wide && launch_rounds_rest<EPI_GATE>(c, cg, mtg, st, T, F, d, x, wg, part, ep, F, e)) {
             if (e != hipSuccess) return e;
         } else {
-            dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr, part,
-                                           F, ep);
+            // every channel: the up GEMM's tiles join the gate's launch (it does
+            // not depend on the gate), each half of the partial buffer for one
+            // (at least two splits: the up tiles leave partials for their sum, which applies the gate values)
+            int skd = (all_ch || dense_small) && !wide ? split_for(c, 2LL * mtg * nt, d, T, c.L.bpart_rows / 2) : 0;
+            if ((all_ch || dense_small) && !wide && skd < 2 && 4 * T <= c.L.bpart_rows) skd = 2;
+            int s_used = sk;
+            if (skd > 1 && T <= kUnionAtomicMaxTokens && sum_select_fits(F, skd)) {
+                ep.dual = 1;
+                ep.B2 = wu;
+                ep.part2 = part + (size_t)skd * T * F;
+                dual_s = s_used = skd;
+                dispatch_mfma<false, EPI_GATE>(cg, tile_grid(2 * nt, mtg, skd), st, T, F, d, x, d, wg, d, nullptr,
+                                               nullptr, part, F, ep);
+            } else {
+                dispatch_mfma<false, EPI_GATE>(cg, tile_grid(nt, mtg, sk), st, T, F, d, x, d, wg, d, nullptr, nullptr,
+                                               part, F, ep);
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (!dual_s && miss > 0.03) all_ch = false;  // every channel pays only with the joined launch
             // small Top-K / top-p / 2:8 batches: the select sums the partials itself
             gate_split = !wide && T <= kUnionAtomicMaxTokens &&
                                  (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP || a.mode == SFFN_TOPK_2_8) &&
-                                 sum_select_fits(F, sk) ? sk : 0;
-            if (sk > 1 && !gate_split) {
-                if ((e = launch_splitk_sum(st, part, sk, T, F, F, nullptr, ep)) != hipSuccess) return e;
+                                 sum_select_fits(F, s_used) ? s_used : 0;
+            if (s_used > 1 && !gate_split) {
+                if ((e = launch_splitk_sum(st, part, s_used, T, F, F, nullptr, ep)) != hipSuccess) return e;
             }
         }
         if (ev1) hipEventRecord(ev1, st);
@@ -1329,11 +1378,15 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {
         ep.kind = EPI_UP;
-        ep.all_ch = union_nearly_all(a.mode, T, F, a.k) ? 1 : 0;
+        ep.all_ch = all_ch || dual_s > 0 ? 1 : 0;
         ep.utrue = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionTrue;
         const int nt = (F + cf.bn() - 1) / cf.bn();
-        // 256 x 256 tiles: the whole rounds, then the rest split along K
-        if (launch_rounds_rest<EPI_UP>(c, cf, mt, st, T, F, d, x, wu, part, ep, -1, e)) {
+        if (dual_s > 0) {
+            // the up partials came with the gate's launch: their sum with the
+            // gate values applied (and the identity union list for the down GEMM)
+            if ((e = launch_splitk_sum(st, ep.part2, dual_s, T, F, F, nullptr, ep)) != hipSuccess) return e;
+        } else if (launch_rounds_rest<EPI_UP>(c, cf, mt, st, T, F, d, x, wu, part, ep, -1, e)) {
+            // 256 x 256 tiles: the whole rounds, then the rest split along K
             if (e != hipSuccess) return e;
         } else {
             const Cfg cu = narrow_for(c, cf, T, F);  // the union is at most F
@@ -1362,7 +1415,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- optional outputs ----
     if (a.active_idx || a.active_cnt || a.union_cnt) {
         hipLaunchKernelGGL(k_emit_batched, dim3(T + 1), dim3(256), 0, st, G, act, T, F, a.mode, ncount,
-                           ep.all_ch ? ep.utrue : nullptr, a.active_idx,
+                           all_ch ? ep.utrue : nullptr, a.active_idx,
                            a.active_cnt, a.union_cnt);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

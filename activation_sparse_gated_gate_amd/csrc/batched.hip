@@ -15,6 +15,13 @@
 //   3. down GEMM   Y = H . W_down[U, :] (rows gathered by U, fp32 output);
 //                  it also clears the bitmap for the next forward
 //
+// Up to 64 tokens the up GEMM's tiles can instead run in the gate GEMM's
+// launch over every channel (it does not depend on the gate): where the
+// mode makes the union nearly every channel the down GEMM then runs over
+// every channel too; otherwise, on a layer whose W_up streams in about one
+// launch's fixed cost, the sum of the up partials keeps the union's channels
+// in the union's order and the down GEMM runs over the union as above.
+//
 // A channel that no token selected reads neither W_up nor W_down: the gate is
 // computed first and the other two matrices only for what it kept ("Model
 // Casting and Low-Parameter Gating", Abstract; "Mixture-of-Channels" blog
@@ -955,6 +962,67 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     }
 }
 
+// The up GEMM's split-K partials over every channel (computed in the gate's
+// launch, before the select) summed for the union's channels only, into the
+// union's compacted order: channel n at union position (set bits of the
+// bitmap below n) takes H = G u there, row 0 writes the union list and each
+// row's first block its size and the zero padding up to a multiple of 8. The
+// down GEMM then runs over the union as after the gathered up GEMM. A block
+// takes 256 channels (8 bitmap words) of one token row; the entries before
+// them are counted from the bitmap, which the select has finished.
+template <int SM>
+__global__ __launch_bounds__(256) void k_up_compact(const float *__restrict__ part, int S, int M, int N, EpiArgs epi)
+{
+    __shared__ int wpre[8], red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int W = (N + 31) / 32, w0 = blockIdx.x * 8, m = blockIdx.y, n = blockIdx.x * 256 + tid;
+    const uint32_t *ub = epi.ubits;
+    // entries before this block (block 0: the union's size instead)
+    const int wlim = blockIdx.x == 0 ? W : w0;
+    int c = 0;
+    for (int w = tid; w < wlim; w += 256) c += __popc(ub[w]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    if (lane == 0) red[wv] = c;
+    if (tid < 8) wpre[tid] = w0 + tid < W ? __popc(ub[w0 + tid]) : 0;
+    __syncthreads();
+    const int cnt = red[0] + red[1] + red[2] + red[3];
+    const int base = blockIdx.x == 0 ? 0 : cnt;
+    int before = 0;
+    for (int j = 0; j < (tid >> 5); ++j) before += wpre[j];
+    const uint32_t word = n < N ? ub[n >> 5] : 0u;
+    const bool on = (word >> (n & 31)) & 1u;
+    if (n < N && (on || epi.usave)) {
+        float p[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) p[s] = part[((size_t)min(s, S - 1) * M + m) * N + n];
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
+            if (s < S) v += p[s];
+        if (epi.usave) epi.usave[(size_t)m * epi.F + n] = v;
+        if (on) {
+            const int pos = base + before + __popc(word & ((1u << (n & 31)) - 1u));
+            epi.H[(size_t)m * epi.hld + pos] = f2bf(bf2f(epi.G[(size_t)m * epi.F + n]) * v);
+            if (m == 0) epi.uidx[pos] = n;
+        }
+    }
+    if (blockIdx.x == 0) {
+        if (tid < ((cnt + 7) & ~7) - cnt) epi.H[(size_t)m * epi.hld + cnt + tid] = 0;
+        if (m == 0 && tid == 0) *epi.ucount = cnt;
+    }
+}
+
+static hipError_t launch_up_compact(hipStream_t st, const float *part, int S, int M, int N, const EpiArgs &e)
+{
+    const dim3 grid((N + 255) / 256, M), block(256);
+    if (S <= 2) hipLaunchKernelGGL(k_up_compact<2>, grid, block, 0, st, part, S, M, N, e);
+    else if (S <= 4) hipLaunchKernelGGL(k_up_compact<4>, grid, block, 0, st, part, S, M, N, e);
+    else if (S <= 8) hipLaunchKernelGGL(k_up_compact<8>, grid, block, 0, st, part, S, M, N, e);
+    else hipLaunchKernelGGL(k_up_compact<16>, grid, block, 0, st, part, S, M, N, e);
+    return hipGetLastError();
+}
+
 // Optional outputs for a batch: token t's ascending active list and count;
 // block T writes the union size.
 __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict__ G, const uint8_t *__restrict__ act,
@@ -990,6 +1058,10 @@ __global__ __launch_bounds__(256) void k_emit_batched(const uint16_t *__restrict
 // Above this many tokens the Top-K / top-p union comes from the flags in a
 // separate pass instead of per-token atomics.
 constexpr int kUnionAtomicMaxTokens = 64;
+// W_up bytes that stream at the HBM rate in about one launch's fixed cost
+// (~5 us): up to this size the up GEMM of a small batch runs over every
+// channel in the gate's launch whatever the union's size
+constexpr long long kSpecUpBytes = 32ll << 20;
 
 // Tile shape of k_mfma_dma: TM x TN 32 x 32 MFMA tiles per wavefront, WM x WN
 // wavefronts.
@@ -1252,6 +1324,12 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     const double miss = union_miss(a.mode, T, F, a.k);
     bool all_ch = miss <= 0.25 && !(c.token_groups > 1 && T >= c.token_groups * kTokenGroupMinTokens);
     const bool dense_small = dense && T <= kUnionAtomicMaxTokens;  // every channel by definition
+    // a union of unknown size (top-p, threshold) or well short of every
+    // channel: while all of W_up streams in about the time of one launch of its
+    // own, the up GEMM still runs over every channel in the gate's launch and
+    // its sum keeps the union's channels only (the down GEMM stays on the union)
+    const bool spec = !dense && !all_ch && T <= kUnionAtomicMaxTokens && (long long)F * d * 2 <= kSpecUpBytes &&
+                      !(c.token_groups > 1 && T >= c.token_groups * kTokenGroupMinTokens);
     int dual_s = 0;  // > 0: the up GEMM ran in the gate's launch, with this many K splits
     {
         ep.kind = EPI_GATE;
@@ -1269,8 +1347,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
             // every channel: the up GEMM's tiles join the gate's launch (it does
             // not depend on the gate), each half of the partial buffer for one
             // (at least two splits: the up tiles leave partials for their sum, which applies the gate values)
-            int skd = (all_ch || dense_small) && !wide ? split_for(c, 2LL * mtg * nt, d, T, c.L.bpart_rows / 2) : 0;
-            if ((all_ch || dense_small) && !wide && skd < 2 && 4 * T <= c.L.bpart_rows) skd = 2;
+            const bool join = (all_ch || dense_small || spec) && !wide;
+            int skd = join ? split_for(c, 2LL * mtg * nt, d, T, c.L.bpart_rows / 2) : 0;
+            if (join && skd < 2 && 4 * T <= c.L.bpart_rows) skd = 2;
             int s_used = sk;
             if (skd > 1 && T <= kUnionAtomicMaxTokens && sum_select_fits(F, skd)) {
                 ep.dual = 1;
@@ -1378,10 +1457,15 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- 2. up GEMM over the union rows (each workgroup lists its part) ----
     {
         ep.kind = EPI_UP;
-        ep.all_ch = all_ch || dual_s > 0 ? 1 : 0;
+        const bool compact = dual_s > 0 && !all_ch && !dense;
+        ep.all_ch = all_ch || (dual_s > 0 && !compact) ? 1 : 0;
         ep.utrue = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionTrue;
         const int nt = (F + cf.bn() - 1) / cf.bn();
-        if (dual_s > 0) {
+        if (compact) {
+            // the up partials came with the gate's launch: the union's channels
+            // summed into the union's order, with its list and size
+            if ((e = launch_up_compact(st, ep.part2, dual_s, T, F, ep)) != hipSuccess) return e;
+        } else if (dual_s > 0) {
             // the up partials came with the gate's launch: their sum with the
             // gate values applied (and the identity union list for the down GEMM)
             if ((e = launch_splitk_sum(st, ep.part2, dual_s, T, F, F, nullptr, ep)) != hipSuccess) return e;

@@ -205,6 +205,42 @@ def test_batched_handle_larger_than_batch_splits_within_its_buffer():
         compare(lay, x, mode, ref, got)
 
 
+@pytest.mark.parametrize("n", [9, 31, 64])
+@pytest.mark.parametrize("f", [1000, 4100])
+@pytest.mark.parametrize("mode,kw", [("threshold", dict(tau=2.0)), ("topk", dict(k=8)), ("topp", dict(tau=0.05)),
+                                     ("threshold", dict(tau=0.0))])
+def test_small_batch_union_compacted_from_every_channel(n, f, mode, kw):
+    """Up to 64 tokens of a layer this small the up GEMM runs over every
+    channel in the gate's launch, and the sum of its partials keeps the
+    union's channels in the union's order for the down GEMM: unions from a
+    few channels (high threshold, small K, small p) to most of them, d_ff
+    neither a multiple of 256 nor of 32."""
+    d = 512
+    say(f"case small batch, union compacted from every channel bf16 d={d} F={f} n={n} {mode} {kw}")
+    lay = inputs.make_layer(61, d, f, "bf16")
+    x = inputs.make_x(61 + n, n, d, "bf16", correlated=True)
+    ref = oracle_forward(lay, x, mode, **kw)
+    got = run_gpu(lay, x, mode, max_tokens=n, **kw)
+    say(f"    union {got.union} of {f}")
+    compare(lay, x, mode, ref, got)
+
+
+def test_small_batch_union_shrinks_on_one_handle():
+    """Consecutive forwards on one handle whose unions shrink (and then grow):
+    the compacted up values of a larger union left past the smaller one's
+    end are never read."""
+    say("case small batch, shrinking unions on one handle")
+    d, f = 512, 2100
+    lay = inputs.make_layer(62, d, f, "bf16")
+    ffn = S.SparseFFN(d, f, 64, "bf16")
+    for n, tau in ((64, 0.0), (40, 1.5), (12, 2.6), (64, 3.5), (33, 0.5)):
+        x = inputs.make_x(62 + n, n, d, "bf16", correlated=True)
+        ref = oracle_forward(lay, x, "threshold", tau=tau)
+        got = run_gpu(lay, x, "threshold", tau=tau, ffn=ffn)
+        say(f"    n={n} tau={tau} union {got.union}")
+        compare(lay, x, "threshold", ref, got)
+
+
 @pytest.mark.parametrize("n,f,mode,kw", [
     (2048, 8448, "dense_silu", {}),           # 33 N tiles: a whole round (32) and a rest of 1
     (2000, 8195, "dense_relu", {}),           # ragged tokens and union (pad columns in the rest)

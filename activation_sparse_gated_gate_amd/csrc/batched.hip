@@ -73,8 +73,9 @@ struct EpiArgs {
     uint32_t *ubits;    // union bitmap (gate and Top-K flags set it, up reads it, down clears it)
     int32_t *uidx;      // union list (up writes, down and the split-K sum read)
     int *ucount;        // union size (up writes)
-    int all_ch;         // up: every channel instead of the union (a small batch whose union is nearly
-                        // every channel; G is 0 where off); its block 0 writes the bitmap's size to *utrue
+    int all_ch;         // up and down: every channel instead of the union (a small batch whose union is
+                        // nearly every channel; G is 0 where off); the down GEMM's block 0 writes the
+                        // bitmap's size to *utrue
     int *utrue;
     // gate GEMM with the up GEMM in the same launch (every channel, split K):
     // N tiles past the gate's read B2 (W_up) and write their partials to part2
@@ -571,9 +572,25 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
         else nlim = min(N, *ncount);
     }
     if constexpr (EK == EPI_DOWN) {
-        // the up GEMM has read the bitmap: clear it for the next forward
-        if (blockIdx.x == 0 && blockIdx.z == 0)
-            for (int w = tid; w < (epi.F + 31) / 32; w += 64 * WM * WN) epi.ubits[w] = 0;
+        // the up GEMM has read the bitmap: clear it for the next forward (over
+        // every channel, the union's own size for the caller is counted first)
+        if (blockIdx.x == 0 && blockIdx.z == 0) {
+            const int W = (epi.F + 31) / 32;
+            if (epi.all_ch) {
+                if (wave == 0) {
+                    int c = 0;
+                    for (int w = lane; w < W; w += 64) {
+                        c += __popc(epi.ubits[w]);
+                        epi.ubits[w] = 0;
+                    }
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+                    if (lane == 0) *epi.utrue = c;
+                }
+            } else {
+                for (int w = tid; w < W; w += 64 * WM * WN) epi.ubits[w] = 0;
+            }
+        }
     }
     if (n0 >= nlim || m0 >= M) return;
     int kb = 0, ke = klim;
@@ -796,18 +813,6 @@ __global__ __launch_bounds__(64 * WM *WN, OCC) void k_mfma_dma(int M, int N, int
     wait_vm_lgkm<0>();  // the trailing (zero) loads land before the LDS is given up
     tile_epilogue<MF, TM, TN, NTHR, BN, EK, GM>(acc, tid, lane, m0, n0, arow, bcol, M, nlim, S, part, poff, pld,
                                                 epi, ubits_lds, uloc);
-    if constexpr (EK == EPI_UP) {
-        // every channel computed: the union's own size for the caller, counted
-        // by one workgroup after its tile (off the other tiles' path)
-        if (epi.all_ch && blockIdx.x == 0 && z == 0 && wave == 0) {
-            const int W = (epi.F + 31) / 32;
-            int c = 0;
-            for (int w = lane; w < W; w += 64) c += __popc(epi.ubits[w]);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-            if (lane == 0) *epi.utrue = c;
-        }
-    }
 }
 
 // Sum of the rest launch's split partials (tile p at part[p][BM][BN]) in
@@ -951,15 +956,6 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     __syncthreads();
     if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
-    if (epi.kind == EPI_UP && epi.all_ch && epi.dual && blockIdx.x == 0 && m == 0 && threadIdx.x < 64) {
-        // the union's own size for the caller (the bitmap the select wrote)
-        const int W = (epi.F + 31) / 32, lane = threadIdx.x;
-        int c = 0;
-        for (int w = lane; w < W; w += 64) c += __popc(epi.ubits[w]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-        if (lane == 0) *epi.utrue = c;
-    }
 }
 
 // The up GEMM's split-K partials over every channel (computed in the gate's
@@ -1377,8 +1373,15 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // ---- Top-K / top-p: per-token select, its flags and the union of the
     // flags (above 64 tokens the union comes from one pass over the flags:
     // per-token atomics on the same few bitmap words would serialise) ----
+    // over every channel with the up GEMM in the gate's launch, the select
+    // kernel also applies the gate values to the up partials (a token's
+    // product row needs only that token's select)
+    UpHalf uh{};
+    if (dual_s > 0 && all_ch && gate_split == dual_s && !dense &&
+        (a.mode == SFFN_TOPK_2_8 || gate_split <= kSelectUpMaxSplits))
+        uh = UpHalf{ep.part2, H, ep.hld, a.usave, uidx, ncount};
     if (gate_split && a.mode != SFFN_TOPK_2_8) {
-        e = launch_sum_select_flags(part, gate_split, T, F, a.mode, a.k, a.tau, a.debug_z, act, G, ubits, st);
+        e = launch_sum_select_flags(part, gate_split, T, F, a.mode, a.k, a.tau, a.debug_z, act, G, ubits, st, uh);
         if (e != hipSuccess) return e;
     } else if (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP) {
         uint32_t *ub = T > kUnionAtomicMaxTokens ? nullptr : ubits;
@@ -1389,7 +1392,7 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     }
     // ---- 2:8: the top 2 of each group of 8 keys, its flags and the union ----
     if (a.mode == SFFN_TOPK_2_8) {
-        e = gate_split ? launch_nm_flags(keys, T, F, act, G, ubits, st, part, gate_split, a.debug_z)
+        e = gate_split ? launch_nm_flags(keys, T, F, act, G, ubits, st, part, gate_split, a.debug_z, uh)
                        : launch_nm_flags(keys, T, F, act, G, ubits, st);
         if (e != hipSuccess) return e;
     }
@@ -1461,7 +1464,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.all_ch = all_ch || (dual_s > 0 && !compact) ? 1 : 0;
         ep.utrue = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionTrue;
         const int nt = (F + cf.bn() - 1) / cf.bn();
-        if (compact) {
+        if (uh.part) {
+            // the select kernel wrote the product rows and the identity union list
+        } else if (compact) {
             // the up partials came with the gate's launch: the union's channels
             // summed into the union's order, with its list and size
             if ((e = launch_up_compact(st, ep.part2, dual_s, T, F, ep)) != hipSuccess) return e;

@@ -220,11 +220,28 @@ hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, ui
                                    uint32_t *ubits, hipStream_t st);
 // The union bitmap from the flags act [T][F] (replaces whatever it holds).
 hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits, hipStream_t st);
+// A small batch whose up GEMM ran over every channel in the gate's launch:
+// its split-K partials [S][T][F] (the gate's split count). A select kernel
+// given them also writes the product rows H[t][i] = bf16(G[t][i] u[t][i]),
+// u the partials summed in split order, zeros in the pad columns up to hld,
+// u into usave when set, and the identity union list and its size (every
+// channel) for the down GEMM. part null: none of this.
+constexpr int kSelectUpMaxSplits = 4;
+struct UpHalf {
+    const float *part;
+    uint16_t *H;
+    int hld;
+    float *usave;
+    int32_t *uidx;
+    int *ucount;
+};
+
 // Batched 2:8: act[t][i], bf16 gate values G[t][i] and the union bitmap from
 // the keys (or from the gate GEMM's S split-K partials when part is set), keeping
 // the top 2 of every aligned group of 8 channels.
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
-                           hipStream_t st, const float *part = nullptr, int S = 0, float *debug_z = nullptr);
+                           hipStream_t st, const float *part = nullptr, int S = 0, float *debug_z = nullptr,
+                           const UpHalf &up = UpHalf{});
 // Batched: the per-token select, then act[t][i], the bf16 gate values
 // G[t][i] and the union bitmap words from it.
 hipError_t launch_topk_select_flags(const float *keys, int T, int F, int K, uint8_t *act, uint16_t *G,
@@ -233,9 +250,11 @@ hipError_t launch_topk_select_flags(const float *keys, int T, int F, int K, uint
 // (p) select straight from the S split-K partials [S][T][F] (summed in split
 // order, then SiLU; the sums into debug_z when it is set), then its flags
 // as launch_topk_select_flags; sum_select_fits says whether F and S allow it.
+// The up half is taken with at most kSelectUpMaxSplits splits.
 bool sum_select_fits(int F, int S);
 hipError_t launch_sum_select_flags(const float *part, int S, int T, int F, int mode, int K, float p, float *debug_z,
-                                   uint8_t *act, uint16_t *G, uint32_t *ubits, hipStream_t st);
+                                   uint8_t *act, uint16_t *G, uint32_t *ubits, hipStream_t st,
+                                   const UpHalf &up = UpHalf{});
 // Decode gate kernel (gate.hip): gate GEMV + activation + select (+ the up
 // rows of the selected channels, or of every channel in the dense modes).
 struct GateArgs {

@@ -106,11 +106,57 @@ __global__ __launch_bounds__(1024) void k_topk_select_flags(const float *__restr
     write_flags<KPT>(s, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
 }
 
+// Token t's row of split-K partials [S][T][F] summed over the S splits in
+// split order (exactly as the split-K sum kernel adds them), this thread's
+// channels KPT tid .. + KPT-1, 0 past F.
+template <int KPT, int SM>
+__device__ __forceinline__ void sum_split_rows(const float *__restrict__ part, int S, int T, int F, int t,
+                                               float (&sum)[KPT])
+{
+    static_assert(KPT % 4 == 0, "whole float4 groups per thread");
+    constexpr int EB = SM >= 32 ? 1 : 32 / SM < KPT ? 32 / SM : KPT;  // channels whose partials are in flight together
+    static_assert(KPT % EB == 0 && (EB % 4 == 0 || EB < 4), "whole batches");
+    const int i0 = threadIdx.x * KPT;
+    const bool vec = (F & 3) == 0;  // rows of the partials 16-byte aligned
+#pragma unroll
+    for (int e0 = 0; e0 < KPT; e0 += EB) {
+        float p[SM][EB];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            const float *row = part + ((size_t)min(s, S - 1) * T + t) * F;
+            if (EB >= 4 && vec) {
+#pragma unroll
+                for (int e = 0; e < EB; e += 4) {
+                    const int i = i0 + e0 + e;  // i < F implies i + 3 < F (F, i multiples of 4)
+                    const float4 q = i < F ? *reinterpret_cast<const float4 *>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    p[s][e] = q.x;
+                    p[s][e + 1] = q.y;
+                    p[s][e + 2] = q.z;
+                    p[s][e + 3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EB; ++e) {
+                    const int i = i0 + e0 + e;
+                    p[s][e] = i < F ? row[i] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < SM; ++s)
+                if (s < S) v += p[s][e];
+            sum[e0 + e] = v;
+        }
+    }
+}
+
 // Token t's keys from the gate GEMM's split-K partials (the form for small
-// batches, whose gate GEMM splits K): this thread's channels KPT tid .. + KPT-1
-// summed over the S splits in split order, exactly as the split-K sum kernel
-// adds them, then SiLU; the pre-activations also into debug_z when it is set.
-// The select that follows then needs no separate sum launch.
+// batches, whose gate GEMM splits K): the sums as sum_split_rows takes them,
+// then SiLU; the pre-activations also into debug_z when it is set. The
+// select that follows then needs no separate sum launch.
 template <int KPT, int SM>
 __device__ __forceinline__ void sum_split_keys(const float *__restrict__ part, int S, int T, int F, int t,
                                                float *__restrict__ debug_z, float (&kf)[KPT])
@@ -157,23 +203,63 @@ __device__ __forceinline__ void sum_split_keys(const float *__restrict__ part, i
     }
 }
 
+// Token t's product rows from the up half's sums u (the select's boundary r
+// and its keys kf): this thread's channels KPT tid .. + KPT-1, H in one 16-byte
+// (or 8-byte) store per 8 (or 4) channels, zeros past F up to hld (a multiple of 8).
+template <int KPT>
+__device__ __forceinline__ void up_rows(const UpHalf &up, int F, int t, int2 r, const float (&kf)[KPT],
+                                        const float (&u)[KPT])
+{
+    const int i0 = threadIdx.x * KPT;
+    constexpr int VB = KPT % 8 == 0 ? 8 : 4;
+#pragma unroll
+    for (int e0 = 0; e0 < KPT; e0 += VB) {
+        if (i0 + e0 >= up.hld) break;
+        uint32_t hw[VB / 2];
+#pragma unroll
+        for (int e = 0; e < VB / 2; ++e) hw[e] = 0u;
+#pragma unroll
+        for (int e = 0; e < VB; ++e) {
+            const int i = i0 + e0 + e;
+            if (i < F) {
+                const uint16_t g = topk_on(kf[e0 + e], i, r) ? f2bf(kf[e0 + e]) : (uint16_t)0;
+                hw[e >> 1] |= (uint32_t)f2bf(bf2f(g) * u[e0 + e]) << (16 * (e & 1));
+                if (up.usave) up.usave[(size_t)t * F + i] = u[e0 + e];
+                if (t == 0) up.uidx[i] = i;
+            }
+        }
+        uint16_t *h = up.H + (size_t)t * up.hld + i0 + e0;
+        if constexpr (VB == 8) *reinterpret_cast<uint4 *>(h) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        else *reinterpret_cast<uint2 *>(h) = make_uint2(hw[0], hw[1]);
+    }
+    if (t == 0 && threadIdx.x == 0) *up.ucount = F;
+}
+
 // Batched Top-K and top-p of a small batch straight from the gate GEMM's
-// split-K partials: token t's keys (sum_split_keys), its select, its flags.
+// split-K partials: token t's keys (sum_split_keys), its select, its flags
+// (and with the up half, its product rows).
 template <int KPT, int SM, bool MASS>
 __global__ __launch_bounds__(1024) void k_sum_select_flags(const float *__restrict__ part, int S, int T, int F,
                                                            int K, float p, float *__restrict__ debug_z,
                                                            uint8_t *__restrict__ act, uint16_t *__restrict__ G,
-                                                           uint32_t *__restrict__ ubits)
+                                                           uint32_t *__restrict__ ubits, UpHalf up)
 {
     __shared__ typename std::conditional<MASS, SelectMassLds, SelectLds>::type L;
     const int t = blockIdx.x;
     float kf[KPT];
     if constexpr (!MASS) select_kth_clear(L);
     sum_split_keys<KPT, SM>(part, S, T, F, t, debug_z, kf);
+    // the up half (up to kSelectUpMaxSplits splits; with more, the registers
+    // would spill): its sums do not depend on the select, so their loads go
+    // out before it
+    constexpr bool UP = SM <= kSelectUpMaxSplits;
+    float u[KPT];
+    if (UP && up.part) sum_split_rows<KPT, SM>(up.part, S, T, F, t, u);
     int2 r;
     if constexpr (MASS) r = select_mass<KPT>(nullptr, F, p, L, kf);
     else r = select_kth<KPT>(nullptr, F, K, L, kf);
     write_flags<KPT>(nullptr, F, r, kf, act + (size_t)t * F, G + (size_t)t * F, ubits);
+    if (UP && up.part) up_rows<KPT>(up, F, t, r, kf, u);
 }
 
 // Batched Top-K, one 256-thread workgroup per token (d_ff up to
@@ -236,12 +322,13 @@ __global__ __launch_bounds__(1024) void k_topp_select_flags(const float *__restr
 // per block keep the atomics on each bitmap word at T / TPB. With part set (a
 // small batch whose gate GEMM split K), a key is the sum of the S split-K
 // partials [S][T][F] in split order, then SiLU (as the split-K sum kernel
-// computes it; the sums also into debug_z when it is set).
+// computes it; the sums also into debug_z when it is set), and with the up
+// half the product rows follow from the same channel's up partials.
 template <int TPB>
 __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys, int T, int F,
                                                   uint8_t *__restrict__ act, uint16_t *__restrict__ G,
                                                   uint32_t *__restrict__ ubits, const float *__restrict__ part,
-                                                  int S, float *__restrict__ debug_z)
+                                                  int S, float *__restrict__ debug_z, UpHalf up)
 {
     constexpr int GROUP = 8, KEEP = 2;
     constexpr int SC = 16 / TPB > 1 ? 16 / TPB : 1;  // partials of a key in flight together
@@ -250,25 +337,32 @@ __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys
     const int i = i0 + tid;
     const int b = tid & ~(GROUP - 1);
     const int t0 = blockIdx.y * TPB;
-    float kv[TPB];
+    float kv[TPB], uv[TPB];
     if (part) {
+        // the gate's partials and (with the up half) the up GEMM's, in flight together
+        const bool two = up.part != nullptr;
         float v[TPB];
 #pragma unroll
-        for (int j = 0; j < TPB; ++j) v[j] = 0.f;
+        for (int j = 0; j < TPB; ++j) v[j] = uv[j] = 0.f;
         for (int s0 = 0; s0 < S; s0 += SC) {
-            float q[TPB][SC];
+            float q[TPB][SC], q2[TPB][SC];
 #pragma unroll
             for (int j = 0; j < TPB; ++j)
 #pragma unroll
                 for (int c = 0; c < SC; ++c) {
                     const int t = t0 + j, sp = s0 + c;
-                    q[j][c] = t < T && i < F && sp < S ? part[((size_t)sp * T + t) * F + i] : 0.f;
+                    const bool in = t < T && i < F && sp < S;
+                    q[j][c] = in ? part[((size_t)sp * T + t) * F + i] : 0.f;
+                    q2[j][c] = in && two ? up.part[((size_t)sp * T + t) * F + i] : 0.f;
                 }
 #pragma unroll
             for (int j = 0; j < TPB; ++j)
 #pragma unroll
                 for (int c = 0; c < SC; ++c)
-                    if (s0 + c < S) v[j] += q[j][c];
+                    if (s0 + c < S) {
+                        v[j] += q[j][c];
+                        uv[j] += q2[j][c];
+                    }
         }
 #pragma unroll
         for (int j = 0; j < TPB; ++j) {
@@ -301,13 +395,22 @@ __global__ __launch_bounds__(256) void k_nm_flags(const float *__restrict__ keys
         const bool on = i < F && rank < KEEP;
         if (i < F) {
             const size_t o = (size_t)t * F + i;
+            const uint16_t g = on ? f2bf(k) : (uint16_t)0;
             act[o] = on;
-            G[o] = on ? f2bf(k) : (uint16_t)0;
+            G[o] = g;
+            if (up.part) {
+                up.H[(size_t)t * up.hld + i] = f2bf(bf2f(g) * uv[j]);
+                if (up.usave) up.usave[o] = uv[j];
+                if (t == 0) up.uidx[i] = i;
+            }
+        } else if (up.part && i < up.hld) {
+            up.H[(size_t)t * up.hld + i] = 0;
         }
         const unsigned long long m = __ballot(on);
         acc_bits |= (uint32_t)(m >> (lane & 32));
     }
     if ((lane & 31) == 0 && acc_bits) atomicOr(&ubits[i >> 5], acc_bits);
+    if (up.part && i == 0 && t0 == 0) *up.ucount = F;
 }
 
 // The union bitmap from the flags of T tokens: channel i (one thread) is in
@@ -333,7 +436,7 @@ hipError_t launch_union_flags(const uint8_t *act, int T, int F, uint32_t *ubits,
 }
 
 hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16_t *G, uint32_t *ubits,
-                           hipStream_t st, const float *part, int S, float *debug_z)
+                           hipStream_t st, const float *part, int S, float *debug_z, const UpHalf &up)
 {
     // one token per block up to 16 tokens (enough blocks to fill the GPU),
     // 4 up to 255, then 16: at most T / 4 atomics per bitmap word, and a
@@ -341,13 +444,13 @@ hipError_t launch_nm_flags(const float *keys, int T, int F, uint8_t *act, uint16
     const dim3 block(256);
     const int gx = (F + 255) / 256;
     if (T <= 16)
-        hipLaunchKernelGGL(k_nm_flags<1>, dim3(gx, T), block, 0, st, keys, T, F, act, G, ubits, part, S, debug_z);
+        hipLaunchKernelGGL(k_nm_flags<1>, dim3(gx, T), block, 0, st, keys, T, F, act, G, ubits, part, S, debug_z, up);
     else if (T < 256)
         hipLaunchKernelGGL(k_nm_flags<4>, dim3(gx, (T + 3) / 4), block, 0, st, keys, T, F, act, G, ubits, part, S,
-                           debug_z);
+                           debug_z, up);
     else
         hipLaunchKernelGGL(k_nm_flags<16>, dim3(gx, (T + 15) / 16), block, 0, st, keys, T, F, act, G, ubits, part, S,
-                           debug_z);
+                           debug_z, up);
     return hipGetLastError();
 }
 
@@ -366,14 +469,15 @@ hipError_t launch_topp_select_flags(const float *keys, int T, int F, float p, ui
 bool sum_select_fits(int F, int S) { return F <= 1024 * 16 && S >= 2 && S <= 16; }
 
 hipError_t launch_sum_select_flags(const float *part, int S, int T, int F, int mode, int K, float p, float *debug_z,
-                                   uint8_t *act, uint16_t *G, uint32_t *ubits, hipStream_t st)
+                                   uint8_t *act, uint16_t *G, uint32_t *ubits, hipStream_t st, const UpHalf &up)
 {
     const dim3 grid(T), block(1024);
     auto go_sm = [&](auto kpt, auto mass) {
         constexpr int KPT = decltype(kpt)::value;
         constexpr bool MASS = decltype(mass)::value;
 #define SFFN_SS(SMV) \
-    hipLaunchKernelGGL((k_sum_select_flags<KPT, SMV, MASS>), grid, block, 0, st, part, S, T, F, K, p, debug_z, act, G, ubits)
+    hipLaunchKernelGGL((k_sum_select_flags<KPT, SMV, MASS>), grid, block, 0, st, part, S, T, F, K, p, debug_z, act, G, \
+                       ubits, up)
         if (S <= 2) SFFN_SS(2);
         else if (S <= 4) SFFN_SS(4);
         else if (S <= 8) SFFN_SS(8);

@@ -225,6 +225,25 @@ def test_small_batch_union_compacted_from_every_channel(n, f, mode, kw):
     compare(lay, x, mode, ref, got)
 
 
+@pytest.mark.parametrize("n", [9, 40, 64])
+@pytest.mark.parametrize("f", [1000, 4097, 4100])
+@pytest.mark.parametrize("mode", ["topk", "topk_2_8"])
+def test_small_batch_every_channel_select_writes_the_products(n, f, mode):
+    """Where the union is nearly every channel (Top-K with a large K, 2:8) the
+    select kernel of a small batch applies each token's gate values to the up
+    GEMM's partials itself: d_ff ragged (pad columns of the product rows, rows
+    not a multiple of 4) and the union size still reported."""
+    d = 512
+    kw = dict(k=3 * f // 8) if mode == "topk" else {}
+    say(f"case small batch, every channel, products from the select bf16 d={d} F={f} n={n} {mode} {kw}")
+    lay = inputs.make_layer(63, d, f, "bf16")
+    x = inputs.make_x(63 + n, n, d, "bf16", correlated=True)
+    ref = oracle_forward(lay, x, mode, **kw)
+    got = run_gpu(lay, x, mode, max_tokens=n, **kw)
+    say(f"    union {got.union} of {f}")
+    compare(lay, x, mode, ref, got)
+
+
 def test_small_batch_union_shrinks_on_one_handle():
     """Consecutive forwards on one handle whose unions shrink (and then grow):
     the compacted up values of a larger union left past the smaller one's

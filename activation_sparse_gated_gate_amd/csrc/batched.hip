@@ -1086,6 +1086,7 @@ static Cfg cfg_for(int M)
 // round (2048 tokens at d_model 2048: 256 tiles instead of 128).
 static Cfg down_cfg(const sffn_ctx &c, const Cfg &cf, int T, int d)
 {
+    if (cf.tn == 1 && cf.wm == 1) return Cfg{1, 1, 1, 4};  // up to 64 tokens: 32 x 128, four wavefronts
     if (cf.wn != 4) return cf;
     const long long mt = (T + 255) / 256;
     if (mt * ((d + 255) / 256) >= c.n_cu) return cf;
@@ -1124,6 +1125,7 @@ static void dispatch_cfg(const Cfg &c, dim3 grid, hipStream_t st, int M, int N, 
     constexpr int NSS = BNN ? 3 : 4;
     if (c.tn == 1) {
         if (c.wm == 2) SFFN_D(2, 1, 2, 2, 64, NSS);
+        else if (BNN && c.wn == 4) SFFN_D(1, 1, 1, 4, 64, NSS);
         else SFFN_D(1, 1, 1, 2, 64, NSS);
     } else if constexpr (!BNN) {
         if (c.wn == 4) SFFN_D(4, 2, 2, 4, 32, 4);
@@ -1493,7 +1495,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     {
         ep.kind = EPI_DOWN;
         const int nt = (d + cfd.bn() - 1) / cfd.bn();
-        const int sk = split_for(c, (long long)mtd * nt, F / 2, T);
+        // K: every channel; a union compacted from every channel (top-p,
+        // threshold: mostly most of them at these sizes) as if it were; else
+        // half of them (the union's size is known only on the device)
+        const int sk = split_for(c, (long long)mtd * nt, ep.all_ch || dual_s > 0 ? F : F / 2, T);
         dispatch_mfma<true, EPI_DOWN>(cfd, tile_grid(nt, mtd, sk), st, T, d, F, H, ep.hld, wdn, d, uidx, ncount, part,
                                       d, ep);
         if ((e = hipGetLastError()) != hipSuccess) return e;

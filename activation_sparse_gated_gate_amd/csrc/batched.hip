@@ -1328,6 +1328,10 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // its sum keeps the union's channels only (the down GEMM stays on the union)
     const bool spec = !dense && !all_ch && T <= kUnionAtomicMaxTokens && (long long)F * d * 2 <= kSpecUpBytes &&
                       !(c.token_groups > 1 && T >= c.token_groups * kTokenGroupMinTokens);
+    // top-p there runs over every channel as well: its select kernel then writes
+    // the product rows itself (no compaction launch), and on such a layer all
+    // of W_down streams in about the time that launch took
+    if (spec && a.mode == SFFN_TOPP) all_ch = true;
     int dual_s = 0;  // > 0: the up GEMM ran in the gate's launch, with this many K splits
     {
         ep.kind = EPI_GATE;

@@ -211,10 +211,11 @@ def test_batched_handle_larger_than_batch_splits_within_its_buffer():
                                      ("threshold", dict(tau=0.0))])
 def test_small_batch_union_compacted_from_every_channel(n, f, mode, kw):
     """Up to 64 tokens of a layer this small the up GEMM runs over every
-    channel in the gate's launch, and the sum of its partials keeps the
-    union's channels in the union's order for the down GEMM: unions from a
-    few channels (high threshold, small K, small p) to most of them, d_ff
-    neither a multiple of 256 nor of 32."""
+    channel in the gate's launch. For the threshold and a small K the sum of
+    its partials keeps the union's channels in the union's order for the down
+    GEMM; top-p runs the down GEMM over every channel, its select writing the
+    product rows. Unions from a few channels (high threshold, small K, small
+    p) to most of them, d_ff neither a multiple of 256 nor of 32."""
     d = 512
     say(f"case small batch, union compacted from every channel bf16 d={d} F={f} n={n} {mode} {kw}")
     lay = inputs.make_layer(61, d, f, "bf16")

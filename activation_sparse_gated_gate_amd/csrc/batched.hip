@@ -82,6 +82,9 @@ struct EpiArgs {
     int dual;
     const bf16_t *B2;
     float *part2;
+    // (gate split-K sum, every channel) the up half's partials [S][M][F]: the
+    // sum also writes H = G u, the pad columns and the identity union list
+    const float *up_part;
     uint16_t *H;        // [T][hld] bf16 (up writes)
     int hld;            // H row stride, d_ff rounded up to 8 (16-byte rows)
     float *Y;           // [T][d] fp32 (down writes; WGRAD: the gradient [F][d], added into)
@@ -937,18 +940,35 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
         if (n == 0) *epi.ucount = N;
     }
     __syncthreads();
+    const bool up = epi.kind == EPI_GATE && epi.up_part;
     if (n < nlim) {
-        // all S (<= SM) partial loads in flight at once, then summed in split
-        // order; splits past S re-read the last one and are not added
-        float p[SM];
+        // all S (<= SM) partial loads in flight at once (with the up half's),
+        // then summed in split order; splits past S re-read the last one and
+        // are not added
+        float p[SM], q[SM];
 #pragma unroll
-        for (int s = 0; s < SM; ++s) p[s] = part[((size_t)min(s, S - 1) * M + m) * part_ld + n];
-        float v = 0.f;
+        for (int s = 0; s < SM; ++s) {
+            const size_t o = ((size_t)min(s, S - 1) * M + m) * part_ld + n;
+            p[s] = part[o];
+            q[s] = up ? epi.up_part[o] : 0.f;
+        }
+        float v = 0.f, u = 0.f;
 #pragma unroll
         for (int s = 0; s < SM; ++s)
-            if (s < S) v += p[s];
+            if (s < S) {
+                v += p[s];
+                u += q[s];
+            }
         if (epilogue(epi, m, n, v) && epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD)
             atomicOr(&ub[threadIdx.x / 32], 1u << (n & 31));
+        if (up) {
+            const size_t o = (size_t)m * epi.F + n;
+            epi.H[(size_t)m * epi.hld + n] = f2bf(bf2f(epi.G[o]) * u);
+            if (epi.usave) epi.usave[o] = u;
+            if (m == 0) epi.uidx[n] = n;
+        }
+    } else if (up && n < ((nlim + 7) & ~7)) {
+        epi.H[(size_t)m * epi.hld + n] = 0;
     } else if ((epi.kind == EPI_UP || epi.kind == EPI_BWD) && n < ((nlim + 7) & ~7)) {
         epi.H[(size_t)m * epi.hld + n] = 0;
         if (epi.kind == EPI_BWD) epi.H2[(size_t)m * epi.hld + n] = 0;
@@ -956,6 +976,7 @@ __global__ __launch_bounds__(256) void k_splitk_epilogue(const float *__restrict
     __syncthreads();
     if (epi.kind == EPI_GATE && epi.mode == SFFN_THRESHOLD && threadIdx.x < 8 && ub[threadIdx.x])
         atomicOr(&epi.ubits[blockIdx.x * 8 + threadIdx.x], ub[threadIdx.x]);
+    if (up && n == 0 && m == 0) *epi.ucount = N;
 }
 
 // The up GEMM's split-K partials over every channel (computed in the gate's
@@ -1328,10 +1349,11 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
     // its sum keeps the union's channels only (the down GEMM stays on the union)
     const bool spec = !dense && !all_ch && T <= kUnionAtomicMaxTokens && (long long)F * d * 2 <= kSpecUpBytes &&
                       !(c.token_groups > 1 && T >= c.token_groups * kTokenGroupMinTokens);
-    // top-p there runs over every channel as well: its select kernel then writes
-    // the product rows itself (no compaction launch), and on such a layer all
-    // of W_down streams in about the time that launch took
-    if (spec && a.mode == SFFN_TOPP) all_ch = true;
+    // top-p and the threshold there run over every channel as well: the select
+    // kernel (top-p) or the gate's split-K sum (threshold) then writes the
+    // product rows itself (no compaction launch), and on such a layer all of
+    // W_down streams in about the time that launch took
+    if (spec && (a.mode == SFFN_TOPP || a.mode == SFFN_THRESHOLD)) all_ch = true;
     int dual_s = 0;  // > 0: the up GEMM ran in the gate's launch, with this many K splits
     {
         ep.kind = EPI_GATE;
@@ -1371,6 +1393,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
                                  (a.mode == SFFN_TOPK || a.mode == SFFN_TOPP || a.mode == SFFN_TOPK_2_8) &&
                                  sum_select_fits(F, s_used) ? s_used : 0;
             if (s_used > 1 && !gate_split) {
+                // over every channel (dense, or the threshold on a small layer)
+                // the gate's sum applies the gate values to the up half as well
+                if (dual_s > 0 && (dense || all_ch)) ep.up_part = ep.part2;
                 if ((e = launch_splitk_sum(st, part, s_used, T, F, F, nullptr, ep)) != hipSuccess) return e;
             }
         }
@@ -1470,8 +1495,9 @@ hipError_t launch_batched(sffn_ctx &c, const FwdArgs &a)
         ep.all_ch = all_ch || (dual_s > 0 && !compact) ? 1 : 0;
         ep.utrue = reinterpret_cast<int *>(ws + c.L.ctrl) + kCtrlUnionTrue;
         const int nt = (F + cf.bn() - 1) / cf.bn();
-        if (uh.part) {
-            // the select kernel wrote the product rows and the identity union list
+        if (uh.part || ep.up_part) {
+            // the select kernel or the gate's sum wrote the product rows and
+            // the identity union list
         } else if (compact) {
             // the up partials came with the gate's launch: the union's channels
             // summed into the union's order, with its list and size

@@ -245,6 +245,24 @@ def test_small_batch_every_channel_select_writes_the_products(n, f, mode):
     compare(lay, x, mode, ref, got)
 
 
+@pytest.mark.parametrize("n,d,f", [(17, 4096, 600), (40, 4096, 1000)])
+@pytest.mark.parametrize("mode", ["threshold", "topk", "topk_2_8", "topp", "dense_silu"])
+def test_small_batch_every_channel_many_splits(n, d, f, mode):
+    """A wide d_model and a narrow d_ff split the joined gate and up GEMM K up
+    to 16 ways: past 4 splits the Top-K and top-p selects leave the up half
+    to its own sum kernel, while 2:8, the threshold and the dense forwards
+    still take it in their own pass."""
+    kw = dict(tau=1.0, k=3 * f // 8, tau_p=0.3)
+    say(f"case small batch, every channel, many K splits bf16 d={d} F={f} n={n} {mode}")
+    lay = inputs.make_layer(64, d, f, "bf16")
+    x = inputs.make_x(64 + n, n, d, "bf16", correlated=True)
+    tau = kw["tau_p"] if mode == "topp" else kw["tau"]
+    ref = oracle_forward(lay, x, mode, tau=tau, k=kw["k"])
+    got = run_gpu(lay, x, mode, tau=tau, k=kw["k"], max_tokens=n)
+    say(f"    union {got.union} of {f}")
+    compare(lay, x, mode, ref, got)
+
+
 def test_small_batch_union_shrinks_on_one_handle():
     """Consecutive forwards on one handle whose unions shrink (and then grow):
     the compacted up values of a larger union left past the smaller one's
